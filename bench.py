@@ -1,0 +1,198 @@
+"""Benchmark: exact causal attention forward on one MI355X.
+
+Default workload: causal self-attention, B=1, H=8, N=32,768, D=64, fp16 q/k/v drawn N(0,1) from
+a fixed seed, all tensors resident in HBM, one monolithic pass per step (the path's steps a1-a6
+in one call: validate, plan, forward kernel with the in-kernel finalise).  Prints one JSON line.
+
+  value         algorithmic TFLOP/s = 4 * D * (visible (query, key) pairs) * B * H / step time
+  roofline      the forward kernel against the dense fp16 matrix-core peak (2.5 PFLOP/s), timed
+                per launch with HIP events on the stream the kernel runs on
+  cpu_baseline  the FP64 reference on this host's cores over a time-bounded sample of rows
+  streamed_4m   (--streamed) 4,194,304-token causal attention from pinned host memory under a
+                16e9-byte device budget: tokens/s and H2D GB/s
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1, help="index of the measured case (default 1)")
+    ap.add_argument("--nk", type=int, default=None, help="context length for the prompt case")
+    ap.add_argument("--kv-chunk", type=int, default=None, help="force a KV split (LSE merges)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--streamed", action="store_true", help="also run the 4M-token host-streamed case")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, seconds: float) -> dict:
+    """The FP64 reference on this host, over seeded random rows until `seconds` of CPU time pass."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(12345)
+    done_rows = 0
+    pairs = 0
+    t0 = time.perf_counter()
+    batch = 2 * threads
+    while time.perf_counter() - t0 < seconds:
+        b = rng.integers(0, w.B, batch)
+        h = rng.integers(0, w.Hq, batch)
+        i = rng.integers(0, w.Nq, batch)
+        rows = np.stack([b, h, i], 1).astype(np.int64)
+        oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
+        done_rows += batch
+        if w.causal:
+            pairs += int(np.sum(i + (w.Nk - w.Nq) + 1))
+        else:
+            pairs += batch * w.Nk
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.D * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_rows} seeded random query rows of the same workload (all their visible keys), "
+                      f"{dt:.1f} s, FP64 C reference on {threads} threads; rows/s = {done_rows / dt:.1f}",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def run_streamed(cqsa, torch, synth) -> dict:
+    w = synth.workload(3)
+    t0 = time.perf_counter()
+    q, k, v, _ = synth.make_inputs(w, pin=True)
+    out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=torch.float16, pin_memory=True)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] streamed inputs ready ({gen_s:.1f} s)", file=sys.stderr, flush=True)
+    # link peak: one pinned 1 GiB H2D copy timed by the host clock between two synchronisations
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    link = 3 * (1 << 30) / (time.perf_counter() - t1) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    t2 = time.perf_counter()
+    _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True)
+    wall = time.perf_counter() - t2
+    tok = w.B * w.Nq / wall
+    h2d_gbs = info["h2d_bytes"] / (info["h2d_ms"] / 1e3) / 1e9 if info["h2d_ms"] > 0 else None
+    return {"workload": w.name, "seconds": round(wall, 3), "tokens_per_s": round(tok, 1),
+            "tflops": round(w.flops() / wall / 1e12, 2), "h2d_bytes": info["h2d_bytes"],
+            "h2d_gbs_during_copies": round(h2d_gbs, 2) if h2d_gbs else None,
+            "h2d_link_peak_gbs_host_timed": round(link, 2),
+            "h2d_frac_of_link": round(h2d_gbs / link, 3) if h2d_gbs else None,
+            "q_chunk": info["q_chunk"], "kv_chunk": info["kv_chunk"], "chunk_pairs": info["chunk_pairs"],
+            "workspace_bytes": info["workspace_bytes"]}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the attention path has no "
+                                   "multi-GPU component (one GPU's share is the measured kernel)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import exact_long_context_cqsa_amd as cqsa
+
+    w = synth.workload(args.workload, nk=args.nk)
+    if w.host_resident:
+        raise SystemExit("use --streamed for the host-resident case")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.perf_counter()
+    q, k, v, _ = synth.make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=w.dtype, device=dev)
+    print(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    kw = {"kv_chunk": args.kv_chunk or w.kv_chunk} if (args.kv_chunk or w.kv_chunk) else {}
+    for _ in range(args.warmup):
+        cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, **kw)
+    torch.cuda.synchronize()
+    info = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, return_info=True, **kw)[1]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, **kw)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_step = wall * 1e3 / args.steps
+    ms_kernel = sum(per) / len(per)
+    flops = w.flops()
+    value = flops / (ms_step / 1e3) / 1e12
+    achieved = flops / (ms_kernel / 1e3) / 1e12
+    print(f"[bench] step {ms_step:.3f} ms (events {ms_kernel:.3f} ms, min {min(per):.3f}) -> {value:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    line = {
+        "metric": "causal attention fwd TFLOP/s & % MFMA peak (1 GPU); tokens/s at 4M ctx",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if w.dtype == torch.float16 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "D": w.D,
+                   "causal": w.causal, "kv_chunk": kw.get("kv_chunk"), "plan": {
+                       k_: info[k_] for k_ in ("kv_splits", "n_kv_chunks", "chunk_pairs", "kernel_launches",
+                                               "block_m")},
+                   "tokens_per_s": round(w.B * w.Nq / (ms_step / 1e3), 1),
+                   "algorithmic_flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd_kernel<D=64,f16>", "kernel_ms": round(ms_kernel, 4),
+                     "launches_per_step": info["kernel_launches"]},
+    }
+    if args.streamed:
+        line["streamed_4m"] = run_streamed(cqsa, torch, synth)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,288 @@
+"""Exact long-context attention for AMD Instinct MI355X: Python binding of ``libcqsa.so``.
+
+Argument marshalling only.  Every step of the computation runs in the HIP library
+(``csrc/``); PyTorch provides device memory, pinned host memory and the stream.
+If the library is not built, importing this package raises: there is no fallback.
+
+    import exact_long_context_cqsa_amd as cqsa
+    out = cqsa.attention(q, k, v, is_causal=True)                 # SDPA semantics, exact
+    out, lse = cqsa.attention(q, k, v, is_causal=True, kv_chunk=4096, return_lse=True)
+
+Names follow the C ABI in ``include/cqsa.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
+           "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libcqsa.so")
+
+F16, BF16, F32 = 0, 1, 2
+WHERE_DETECT, WHERE_DEVICE, WHERE_HOST = 0, 1, 2
+MERGE_AUTO, MERGE_KERNEL, MERGE_FUSED = 0, 1, 2
+_STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "BUDGET", -4: "OOM", -5: "HIP"}
+_DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+
+class CqsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("where", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class CqsaOptions(ctypes.Structure):
+    _fields_ = [("q_chunk", ctypes.c_int64), ("kv_chunk", ctypes.c_int64), ("kv_splits", ctypes.c_int32),
+                ("merge_mode", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
+                ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class CqsaPlanInfo(ctypes.Structure):
+    _fields_ = [("streamed", ctypes.c_int32), ("merge_mode", ctypes.c_int32), ("q_chunk", ctypes.c_int64),
+                ("kv_chunk", ctypes.c_int64), ("n_q_chunks", ctypes.c_int64), ("n_kv_chunks", ctypes.c_int64),
+                ("kv_splits", ctypes.c_int32), ("block_m", ctypes.c_int32), ("chunk_pairs", ctypes.c_int64),
+                ("merges", ctypes.c_int64), ("kernel_launches", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_uint64), ("budget_bytes", ctypes.c_uint64),
+                ("h2d_bytes", ctypes.c_uint64), ("d2h_bytes", ctypes.c_uint64), ("h2d_ms", ctypes.c_double),
+                ("d2h_ms", ctypes.c_double), ("wall_ms", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class CqsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"cqsa {_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load_library():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+    lib = ctypes.CDLL(_LIB_PATH)
+    T = ctypes.POINTER(CqsaTensor)
+    O = ctypes.POINTER(CqsaOptions)
+    I = ctypes.POINTER(CqsaPlanInfo)
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.cqsa_attention.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, T, fp]
+    lib.cqsa_attention.restype = ctypes.c_int
+    lib.cqsa_attention_ex.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, T, fp, O, I]
+    lib.cqsa_attention_ex.restype = ctypes.c_int
+    lib.cqsa_plan.argtypes = [T, T, T, ctypes.c_int, ctypes.c_uint64, T, ctypes.c_int, O, I]
+    lib.cqsa_plan.restype = ctypes.c_int
+    lib.cqsa_fwd_partial.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_int64, fp, fp,
+                                     ctypes.c_void_p]
+    lib.cqsa_fwd_partial.restype = ctypes.c_int
+    lib.cqsa_lse_merge.argtypes = [ctypes.POINTER(fp), ctypes.POINTER(fp), ctypes.c_int32, ctypes.c_int64,
+                                   ctypes.c_int64, fp, fp, ctypes.c_void_p]
+    lib.cqsa_lse_merge.restype = ctypes.c_int
+    lib.cqsa_finalize.argtypes = [fp, fp, T, fp, ctypes.c_void_p]
+    lib.cqsa_finalize.restype = ctypes.c_int
+    lib.cqsa_last_error.argtypes = []
+    lib.cqsa_last_error.restype = ctypes.c_char_p
+    lib.cqsa_version.argtypes = []
+    lib.cqsa_version.restype = ctypes.c_int32
+    lib.cqsa_struct_size.argtypes = [ctypes.c_int32]
+    lib.cqsa_struct_size.restype = ctypes.c_uint64
+    for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo)):
+        if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
+            raise ImportError(f"{cls.__name__} layout differs from the built library")
+    return lib
+
+
+_lib = _load_library()
+
+
+def _check(status: int):
+    if status != 0:
+        raise CqsaError(status, _lib.cqsa_last_error().decode(errors="replace"))
+
+
+def _desc(t: torch.Tensor | None, where: int = WHERE_DETECT) -> CqsaTensor:
+    d = CqsaTensor()
+    if t is None:
+        return d
+    if t.dim() != 4:
+        raise ValueError("tensors are [B, H, N, D]")
+    if t.dtype not in _DT:
+        raise ValueError(f"dtype {t.dtype} is not fp16/bf16/fp32")
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DT[t.dtype]
+    d.where = where
+    for i in range(4):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _fptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    return ctypes.cast(ctypes.c_void_p(t.data_ptr()), ctypes.POINTER(ctypes.c_float))
+
+
+def _device_of(*ts) -> torch.device | None:
+    for t in ts:
+        if t is not None and t.is_cuda:
+            return t.device
+    return None
+
+
+def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=None, workspace=None,
+             num_cus=None) -> CqsaOptions:
+    o = CqsaOptions()
+    o.q_chunk = int(q_chunk or 0)
+    o.kv_chunk = int(kv_chunk or 0)
+    o.kv_splits = int(kv_splits or 0)
+    o.merge_mode = int(merge or 0)
+    o.stream = stream
+    o.num_cus = int(num_cus or 0)
+    if workspace is not None:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    return o
+
+
+def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
+         kv_splits=None, merge=None, where=None, num_cus=None) -> dict:
+    """The plan ``attention`` would run (nothing is allocated or computed).
+
+    ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
+    "device"/"host" per name, for a dry run of shapes that do not exist."""
+    where = where or {}
+
+    def mk(name, t, default_dtype):
+        if isinstance(t, torch.Tensor):
+            return _desc(t)
+        shape, dtype = t if t is not None else (None, default_dtype)
+        d = CqsaTensor()
+        d.dtype = _DT[dtype]
+        d.where = WHERE_HOST if where.get(name, "device") == "host" else WHERE_DEVICE
+        stride = [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+        for i in range(4):
+            d.shape[i] = shape[i]
+            d.stride[i] = stride[i]
+        return d
+
+    dq = mk("q", q, None)
+    dk = mk("k", k, None)
+    dv = mk("v", v, None)
+    if out is None:
+        qshape = tuple(q.shape) if isinstance(q, torch.Tensor) else tuple(q[0])
+        qdt = q.dtype if isinstance(q, torch.Tensor) else q[1]
+        out = (qshape, qdt)
+    do = mk("out", out, None)
+    info = CqsaPlanInfo()
+    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus)
+    _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
+                          int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
+                          ctypes.byref(info)))
+    return info.as_dict()
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False, scale: float | None = None,
+              mem_budget: int | None = None, *, q_chunk: int | None = None, kv_chunk: int | None = None,
+              kv_splits: int | None = None, merge: int | None = None, out: torch.Tensor | None = None,
+              out_dtype: torch.dtype | None = None, return_lse: bool = False, return_info: bool = False,
+              stream: torch.cuda.Stream | None = None):
+    """Exact ``softmax(scale * q k^T [+ causal mask]) v`` (SDPA semantics; causal is bottom-right
+    aligned when Nq < Nk; GQA when k/v have fewer heads).
+
+    q: [B, Hq, Nq, D], k/v: [B, Hkv, Nk, D], fp16 or bf16, D in {64, 128}; each on the GPU or in
+    pinned host memory (then streamed in chunks).  ``mem_budget`` caps the device bytes the call
+    uses (0/None: the free memory).  ``kv_chunk``/``q_chunk`` force a decomposition; ``merge``
+    picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  Returns out (on q's device; pinned
+    host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the plan dict on request."""
+    dev = _device_of(q, k, v, out)
+    if dev is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    B, Hq, Nq, D = q.shape
+    if out is None:
+        odt = out_dtype or q.dtype
+        if q.is_cuda:
+            out = torch.empty((B, Hq, Nq, D), dtype=odt, device=q.device)
+        else:
+            out = torch.empty((B, Hq, Nq, D), dtype=odt, pin_memory=True)
+    lse = None
+    if return_lse:
+        lse = (torch.empty((B, Hq, Nq), dtype=torch.float32, device=out.device) if out.is_cuda
+               else torch.empty((B, Hq, Nq), dtype=torch.float32, pin_memory=True))
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
+        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream)
+        budget = int(mem_budget or 0)
+        # size the workspace first so that device-resident calls take it from PyTorch's allocator
+        # (stream-ordered, no hipMalloc, no synchronisation)
+        pinfo = CqsaPlanInfo()
+        _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0, budget,
+                              ctypes.byref(do), 1 if return_lse else 0, ctypes.byref(opt), ctypes.byref(pinfo)))
+        ws = None
+        if pinfo.workspace_bytes > 0:
+            ws = torch.empty(int(pinfo.workspace_bytes), dtype=torch.uint8, device=dev)
+            opt.workspace = ws.data_ptr()
+            opt.workspace_bytes = int(pinfo.workspace_bytes)
+        info = CqsaPlanInfo()
+        sc = float(scale) if scale is not None else 0.0
+        _check(_lib.cqsa_attention_ex(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
+                                      sc, budget, ctypes.byref(do), _fptr(lse), ctypes.byref(opt),
+                                      ctypes.byref(info)))
+        if ws is not None:
+            ws.record_stream(st)
+    res = (out,)
+    if return_lse:
+        res += (lse,)
+    if return_info:
+        res += (info.as_dict(),)
+    return res[0] if len(res) == 1 else res
+
+
+def fwd_partial(q, k, v, is_causal=False, scale=None, kv_begin=0, kv_end=None, stream=None):
+    """Partial triple of one KV chunk: (O unnormalised fp32 [B,Hq,Nq,D], ml fp32 [B,Hq,Nq,2])."""
+    B, Hq, Nq, D = q.shape
+    kv_end = k.shape[2] if kv_end is None else kv_end
+    o = torch.empty((B, Hq, Nq, D), dtype=torch.float32, device=q.device)
+    ml = torch.empty((B, Hq, Nq, 2), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        dq, dk, dv = _desc(q), _desc(k), _desc(v)
+        _check(_lib.cqsa_fwd_partial(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
+                                     float(scale or 0.0), int(kv_begin), int(kv_end), _fptr(o), _fptr(ml),
+                                     st.cuda_stream))
+    return o, ml
+
+
+def lse_merge(parts, out=None, stream=None):
+    """Merge [(O, ml), ...] partial triples (fp32, [..., D] / [..., 2]) by log-sum-exp."""
+    o0, ml0 = parts[0]
+    D = o0.shape[-1]
+    rows = o0.numel() // D
+    o_out, ml_out = out if out is not None else (torch.empty_like(o0), torch.empty_like(ml0))
+    FP = ctypes.POINTER(ctypes.c_float)
+    op = (FP * len(parts))(*[_fptr(p[0]) for p in parts])
+    mp = (FP * len(parts))(*[_fptr(p[1]) for p in parts])
+    with torch.cuda.device(o0.device):
+        st = stream if stream is not None else torch.cuda.current_stream(o0.device)
+        _check(_lib.cqsa_lse_merge(op, mp, len(parts), rows, D, _fptr(o_out), _fptr(ml_out), st.cuda_stream))
+    return o_out, ml_out
+
+
+def finalize(o, ml, out_dtype=torch.float32, return_lse=True, stream=None):
+    """out = O / l in ``out_dtype`` and lse = m + ln l from a merged triple [B, Hq, Nq, D] / [..., 2]."""
+    B, Hq, Nq, D = o.shape
+    out = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=o.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=o.device) if return_lse else None
+    with torch.cuda.device(o.device):
+        st = stream if stream is not None else torch.cuda.current_stream(o.device)
+        do = _desc(out)
+        _check(_lib.cqsa_finalize(_fptr(o), _fptr(ml), ctypes.byref(do), _fptr(lse), st.cuda_stream))
+    return (out, lse) if return_lse else out

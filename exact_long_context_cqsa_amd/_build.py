@@ -1,0 +1,45 @@
+"""Build libcqsa.so (HIP for gfx950) in the package directory with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libcqsa.so")
+SOURCES = [os.path.join(CSRC, "cqsa_kernels.hip"), os.path.join(CSRC, "cqsa_api.cpp")]
+
+# Packed fp32 instructions are disabled for all device code; hipcc's host pass warns that it does
+# not know the feature, which is harmless.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    errs = [ln for ln in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
+    if verbose and errs:
+        print("\n".join(errs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,1151 @@
+// C ABI of the attention library: argument checks, the chunk planner and the executor.
+//
+// The executor runs a plan as Q chunks x KV chunks.  Each (Q chunk, KV chunk) pair is one launch
+// of the forward kernel over the query rows that can see the chunk; chunks entirely above the
+// causal diagonal are never scheduled.  Partials are merged exactly by log-sum-exp, either by the
+// forward kernel's epilogue (fused) or by the merge kernel, and a final pass normalises.  Operands
+// in pinned host memory are copied chunk by chunk on a side stream into two device buffers that
+// alternate (double buffering), with events ordering each copy after the compute that last read
+// its buffer and each compute after its copy (the two-stream pattern of block-streamer 0.1.0,
+// README section "Streams, residency, and memory budget").  Output bound for host memory leaves
+// on a third stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cqsa.h"
+#include "cqsa_internal.h"
+
+using namespace cqsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+cqsa_status fail(cqsa_status s, const char* fmt, ...) {
+    char buf[1024];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define CQSA_HIP(expr)                                                                                     \
+    do {                                                                                                   \
+        hipError_t e_ = (expr);                                                                            \
+        if (e_ != hipSuccess) return fail(CQSA_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));   \
+    } while (0)
+
+constexpr double kSafety = 0.85;           // fraction of the budget the planner fills
+constexpr int64_t kRowGrain = 256;         // chunk sizes are multiples of this (then clipped)
+constexpr int64_t kKvCap = 262144;         // largest automatic KV chunk (keys)
+constexpr int64_t kKvMinStream = 4096;     // smallest automatic KV chunk worth streaming
+
+int esize_of(int dt) { return dt == CQSA_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------------------------
+// operand views
+
+struct View {
+    char* data = nullptr;
+    int dtype = 0;
+    int es = 2;
+    bool host = false;
+    int64_t B = 0, H = 0, N = 0, D = 0;
+    int64_t sb = 0, sh = 0, sn = 0;
+};
+
+cqsa_status locate(const cqsa_tensor* t, const char* name, bool allow_null, bool* host) {
+    if (!t->data) {
+        if (!allow_null) return fail(CQSA_ERR_INVALID, "%s: data is NULL", name);
+        if (t->where == CQSA_WHERE_DEVICE || t->where == CQSA_WHERE_HOST) {
+            *host = t->where == CQSA_WHERE_HOST;
+            return CQSA_OK;
+        }
+        return fail(CQSA_ERR_INVALID, "%s: NULL data needs where = DEVICE or HOST", name);
+    }
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t e = hipPointerGetAttributes(&attr, t->data);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // clear the sticky error a foreign pointer leaves
+        return fail(CQSA_ERR_INVALID,
+                    "%s: pageable host memory (or an unknown pointer); host operands must be pinned "
+                    "(hipHostMalloc / pin_memory)",
+                    name);
+    }
+    if (attr.type == hipMemoryTypeHost) {
+        *host = true;
+    } else if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+        *host = false;
+    } else {
+        return fail(CQSA_ERR_INVALID, "%s: pageable host memory; host operands must be pinned (hipHostMalloc)",
+                    name);
+    }
+    return CQSA_OK;
+}
+
+cqsa_status make_view(const cqsa_tensor* t, const char* name, bool allow_null, bool detect, View* v) {
+    if (!t) return fail(CQSA_ERR_INVALID, "%s: descriptor is NULL", name);
+    if (t->dtype != CQSA_F16 && t->dtype != CQSA_BF16 && t->dtype != CQSA_F32)
+        return fail(CQSA_ERR_UNSUPPORTED, "%s: dtype %d is not fp16/bf16/fp32", name, t->dtype);
+    for (int i = 0; i < 4; ++i) {
+        if (t->shape[i] < 0) return fail(CQSA_ERR_INVALID, "%s: negative shape", name);
+        if (t->stride[i] < 0) return fail(CQSA_ERR_INVALID, "%s: negative stride", name);
+    }
+    if (t->stride[3] != 1) return fail(CQSA_ERR_INVALID, "%s: the head-dim stride must be 1", name);
+    v->data = static_cast<char*>(t->data);
+    v->dtype = t->dtype;
+    v->es = esize_of(t->dtype);
+    v->B = t->shape[0];
+    v->H = t->shape[1];
+    v->N = t->shape[2];
+    v->D = t->shape[3];
+    v->sb = t->stride[0];
+    v->sh = t->stride[1];
+    v->sn = t->stride[2];
+    v->host = false;
+    if (detect) {
+        const bool empty = v->B == 0 || v->H == 0 || v->N == 0 || v->D == 0;
+        if (t->data || !empty) {
+            cqsa_status s = locate(t, name, allow_null, &v->host);
+            if (s != CQSA_OK) return s;
+        }
+    } else {
+        v->host = t->where == CQSA_WHERE_HOST;
+    }
+    return CQSA_OK;
+}
+
+struct Problem {
+    View q, k, v, out;
+    float* lse = nullptr;
+    bool lse_host = false;
+    bool want_lse = false;
+    int64_t B = 0, Hq = 0, Hkv = 0, Nq = 0, Nk = 0, D = 0;
+    int dtype = 0;
+    bool causal = false;
+    float scale = 0.f;
+    bool empty = false;
+    bool streamed = false;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+cqsa_status check_problem(Problem* P, int is_causal, float scale) {
+    const View &q = P->q, &k = P->k, &v = P->v, &o = P->out;
+    if (q.dtype != k.dtype || q.dtype != v.dtype)
+        return fail(CQSA_ERR_INVALID, "q, k, v must share one dtype");
+    if (q.dtype == CQSA_F32) return fail(CQSA_ERR_UNSUPPORTED, "inputs must be fp16 or bf16 (got fp32)");
+    if (k.B != q.B || v.B != q.B || o.B != q.B) return fail(CQSA_ERR_INVALID, "batch sizes differ");
+    if (k.H != v.H || k.N != v.N || k.D != v.D) return fail(CQSA_ERR_INVALID, "k and v shapes differ");
+    if (k.D != q.D || o.D != q.D) return fail(CQSA_ERR_INVALID, "head dims differ");
+    if (o.H != q.H || o.N != q.N) return fail(CQSA_ERR_INVALID, "out shape must equal q's shape");
+    if (k.H == 0 && q.H != 0) return fail(CQSA_ERR_INVALID, "k has no heads");
+    if (k.H != 0 && q.H % k.H != 0)
+        return fail(CQSA_ERR_INVALID, "query heads (%lld) must be a multiple of key/value heads (%lld)",
+                    (long long)q.H, (long long)k.H);
+    P->B = q.B;
+    P->Hq = q.H;
+    P->Hkv = k.H;
+    P->Nq = q.N;
+    P->Nk = k.N;
+    P->D = q.D;
+    P->dtype = q.dtype;
+    P->causal = is_causal != 0;
+    P->empty = P->B == 0 || P->Hq == 0 || P->Nq == 0;
+    if (P->D != 64 && P->D != 128)
+        return fail(CQSA_ERR_UNSUPPORTED, "head dim %lld is not supported (64 or 128)", (long long)P->D);
+    if (P->empty) return CQSA_OK;
+    if (P->Nk == 0) return fail(CQSA_ERR_INVALID, "no keys: every query row would have nothing to attend to");
+    if (P->causal && P->Nq > P->Nk)
+        return fail(CQSA_ERR_INVALID,
+                    "causal with Nq (%lld) > Nk (%lld): the first rows would see no key (bottom-right alignment)",
+                    (long long)P->Nq, (long long)P->Nk);
+    // vector loads of 8 elements, vector stores of 4
+    for (const View* t : {&q, &k, &v}) {
+        if (t->data && (!aligned16(t->data) || t->sn % 8 || t->sh % 8 || t->sb % 8))
+            return fail(CQSA_ERR_UNSUPPORTED, "q/k/v data and row/head/batch strides must be 16-byte aligned");
+    }
+    if (o.data && ((reinterpret_cast<uintptr_t>(o.data) % (4 * o.es)) || o.sn % 4 || o.sh % 4 || o.sb % 4))
+        return fail(CQSA_ERR_UNSUPPORTED, "out data and strides must be aligned to 4 elements");
+    if (!(scale > 0.f) || !std::isfinite(scale)) scale = 1.0f / std::sqrt((float)P->D);
+    P->scale = scale;
+    P->streamed = q.host || k.host || v.host || o.host || (P->want_lse && P->lse_host);
+    return CQSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// planner
+
+struct Plan {
+    cqsa_plan_info info;
+    int bm = 256;
+    int64_t q_chunk = 0, kv_chunk = 0, n_q = 0, n_kv = 0;
+    int kv_splits = 1;
+    int merge = 0;  // 0 single pass, CQSA_MERGE_KERNEL, CQSA_MERGE_FUSED
+    bool chunked = false;
+    // workspace layout (byte offsets); 0-size pieces are unused
+    uint64_t off_q = 0, off_k[2] = {0, 0}, off_v[2] = {0, 0};
+    uint64_t off_acc_o = 0, off_acc_ml = 0, off_part_o = 0, off_part_ml = 0, off_out = 0, off_lse = 0;
+    uint64_t total = 0;
+};
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Device bytes of a chunked plan with Q chunks of qc rows and KV chunks of kc keys.
+uint64_t chunk_bytes(const Problem& P, int64_t qc, int64_t kc, int merge, bool layout, Plan* pl) {
+    uint64_t off = 0;
+    auto take = [&](uint64_t bytes) {
+        uint64_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const uint64_t rows = (uint64_t)P.B * P.Hq * qc;
+    const uint64_t kvrows = (uint64_t)P.B * P.Hkv * kc;
+    uint64_t o_q = P.q.host ? take(rows * P.D * 2) : 0;
+    uint64_t o_k0 = P.k.host ? take(kvrows * P.D * 2) : 0;
+    uint64_t o_k1 = P.k.host ? take(kvrows * P.D * 2) : 0;
+    uint64_t o_v0 = P.v.host ? take(kvrows * P.D * 2) : 0;
+    uint64_t o_v1 = P.v.host ? take(kvrows * P.D * 2) : 0;
+    const bool multi = kc < P.Nk;
+    uint64_t o_ao = multi ? take(rows * P.D * 4) : 0;
+    uint64_t o_aml = multi ? take(rows * 8) : 0;
+    uint64_t o_po = (multi && merge == CQSA_MERGE_KERNEL) ? take(rows * P.D * 4) : 0;
+    uint64_t o_pml = (multi && merge == CQSA_MERGE_KERNEL) ? take(rows * 8) : 0;
+    uint64_t o_out = P.out.host ? take(rows * P.D * P.out.es) : 0;
+    uint64_t o_lse = (P.want_lse && P.lse_host) ? take(rows * 4) : 0;
+    if (layout) {
+        pl->off_q = o_q;
+        pl->off_k[0] = o_k0;
+        pl->off_k[1] = o_k1;
+        pl->off_v[0] = o_v0;
+        pl->off_v[1] = o_v1;
+        pl->off_acc_o = o_ao;
+        pl->off_acc_ml = o_aml;
+        pl->off_part_o = o_po;
+        pl->off_part_ml = o_pml;
+        pl->off_out = o_out;
+        pl->off_lse = o_lse;
+        pl->total = off;
+    }
+    return off;
+}
+
+// Count launches / merges / pairs of a chunked plan (causal chunks above the diagonal are skipped).
+void count_chunked(const Problem& P, Plan* pl) {
+    int64_t pairs = 0, merges = 0, launches = 0;
+    uint64_t h2d = 0, d2h = 0;
+    int64_t max_kv = 0;
+    for (int64_t qa = 0; qa < P.Nq; qa += pl->q_chunk) {
+        const int64_t qn = std::min(pl->q_chunk, P.Nq - qa);
+        const int64_t last = P.Nk - P.Nq + qa + qn - 1;
+        const int64_t kv_end = P.causal ? std::min(P.Nk, last + 1) : P.Nk;
+        const int64_t nkv = ceil_div(kv_end, pl->kv_chunk);
+        max_kv = std::max(max_kv, nkv);
+        pairs += nkv;
+        launches += nkv;
+        if (nkv > 1) {
+            merges += nkv - 1;
+            if (pl->merge == CQSA_MERGE_KERNEL) launches += nkv - 1;
+            launches += 1;  // finalize
+        }
+        if (P.q.host) h2d += (uint64_t)P.B * P.Hq * qn * P.D * 2;
+        if (P.k.host) h2d += (uint64_t)P.B * P.Hkv * kv_end * P.D * 2;
+        if (P.v.host) h2d += (uint64_t)P.B * P.Hkv * kv_end * P.D * 2;
+        if (P.out.host) d2h += (uint64_t)P.B * P.Hq * qn * P.D * P.out.es;
+        if (P.want_lse && P.lse_host) d2h += (uint64_t)P.B * P.Hq * qn * 4;
+    }
+    pl->info.chunk_pairs = pairs;
+    pl->info.merges = merges;
+    pl->info.kernel_launches = launches;
+    pl->info.h2d_bytes = h2d;
+    pl->info.d2h_bytes = d2h;
+    pl->info.n_kv_chunks = ceil_div(P.Nk, pl->kv_chunk);
+    (void)max_kv;
+}
+
+cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt, int num_cus, Plan* pl) {
+    std::memset(&pl->info, 0, sizeof pl->info);
+    pl->bm = fwd_block_m((int)P.D);
+    pl->info.block_m = pl->bm;
+    pl->info.budget_bytes = budget;
+    pl->info.streamed = P.streamed ? 1 : 0;
+    if (P.empty) {
+        pl->info.q_chunk = 0;
+        return CQSA_OK;
+    }
+    const int req_merge = opt.merge_mode;
+    if (req_merge < 0 || req_merge > 2) return fail(CQSA_ERR_INVALID, "merge_mode %d is not 0, 1 or 2", req_merge);
+    if (opt.q_chunk < 0 || opt.kv_chunk < 0 || opt.kv_splits < 0)
+        return fail(CQSA_ERR_INVALID, "negative chunk option");
+    const bool forced = opt.q_chunk > 0 || opt.kv_chunk > 0;
+
+    if (!P.streamed && !forced) {
+        // one pass over all keys; optional side-by-side KV splits to fill the GPU
+        const int64_t n_qt = ceil_div(P.Nq, pl->bm);
+        const int64_t wgs = P.B * P.Hq * n_qt;
+        int splits = opt.kv_splits;
+        if (splits == 0) {
+            splits = 1;
+            const int64_t target = 2LL * std::max(num_cus, 1);
+            const int64_t min_keys = P.causal ? (P.Nk - P.Nq + 1) : P.Nk;  // fewest keys a row sees
+            if (wgs < target && min_keys >= 16384) {
+                splits = (int)std::min<int64_t>({ceil_div(target, wgs), min_keys / 8192, 16});
+                splits = std::max(splits, 1);
+            }
+        }
+        splits = std::min<int>(std::max(splits, 1), kMaxMergeParts);
+        splits = (int)std::min<int64_t>(splits, ceil_div(P.Nk, 64));
+        const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
+        while (splits > 1 && (uint64_t)splits * rows * (P.D + 2) * 4 + 512 > budget) splits = splits / 2;
+        pl->kv_splits = std::max(splits, 1);
+        pl->q_chunk = P.Nq;
+        pl->kv_chunk = P.Nk;
+        pl->n_q = 1;
+        pl->n_kv = 1;
+        pl->merge = pl->kv_splits > 1 ? CQSA_MERGE_KERNEL : 0;
+        pl->chunked = false;
+        if (pl->kv_splits > 1) {
+            pl->off_part_o = 0;
+            pl->off_part_ml = align_up((uint64_t)pl->kv_splits * rows * P.D * 4, 256);
+            pl->total = align_up(pl->off_part_ml + (uint64_t)pl->kv_splits * rows * 8, 256);
+        } else {
+            pl->total = 0;
+        }
+        pl->info.q_chunk = pl->q_chunk;
+        pl->info.kv_chunk = pl->kv_chunk;
+        pl->info.n_q_chunks = 1;
+        pl->info.n_kv_chunks = 1;
+        pl->info.kv_splits = pl->kv_splits;
+        pl->info.merge_mode = pl->merge;
+        pl->info.chunk_pairs = 1;
+        pl->info.merges = pl->kv_splits > 1 ? pl->kv_splits - 1 : 0;
+        pl->info.kernel_launches = pl->kv_splits > 1 ? 2 : 1;
+        pl->info.workspace_bytes = pl->total;
+        return CQSA_OK;
+    }
+
+    // chunked plan
+    pl->chunked = true;
+    pl->kv_splits = 1;
+    pl->merge = req_merge == 0 ? (P.streamed ? CQSA_MERGE_FUSED : CQSA_MERGE_KERNEL) : req_merge;
+    int64_t qc = opt.q_chunk > 0 ? std::min(opt.q_chunk, P.Nq) : 0;
+    int64_t kc = opt.kv_chunk > 0 ? std::min(opt.kv_chunk, P.Nk) : 0;
+    if (qc > 0 && kc > 0) {
+        // both forced
+    } else if (!P.streamed) {
+        if (qc == 0) qc = P.Nq;
+        if (kc == 0) kc = P.Nk;
+    } else {
+        // streamed: smallest number of Q chunks that leaves room for KV chunks of at least kKvMinStream
+        // keys; when even that does not fit, the smallest chunk grain
+        int64_t best_q = 0, best_k = 0;
+        const int64_t floors[2] = {std::min<int64_t>(kKvMinStream, P.Nk), std::min<int64_t>(kRowGrain, P.Nk)};
+        for (int f = 0; f < 2 && best_q == 0; ++f) {
+            // KV chunk candidates: multiples of the grain, clipped to Nk
+            auto kv_of = [&](int64_t g) { return std::min<int64_t>(P.Nk, g * kRowGrain); };
+            const int64_t g_lo = kc > 0 ? 0 : ceil_div(floors[f], kRowGrain);
+            const int64_t g_hi = kc > 0 ? 0 : std::max<int64_t>(g_lo, ceil_div(std::min<int64_t>(kKvCap, P.Nk), kRowGrain));
+            const int64_t k_first = kc > 0 ? kc : kv_of(g_lo);
+            for (int64_t nq = 1;; ++nq) {
+                const int64_t cand =
+                    qc > 0 ? qc
+                           : std::min<int64_t>(P.Nq, (int64_t)align_up((uint64_t)ceil_div(P.Nq, nq), kRowGrain));
+                if (chunk_bytes(P, cand, k_first, pl->merge, false, pl) <= budget) {
+                    int64_t best = k_first;
+                    if (kc == 0) {
+                        // bisection for the largest feasible grain multiple: bytes grow with the chunk
+                        int64_t lo = g_lo, hi = g_hi;
+                        while (lo < hi) {
+                            const int64_t mid = lo + (hi - lo + 1) / 2;
+                            if (chunk_bytes(P, cand, kv_of(mid), pl->merge, false, pl) <= budget)
+                                lo = mid;
+                            else
+                                hi = mid - 1;
+                        }
+                        best = kv_of(lo);
+                    }
+                    best_q = cand;
+                    best_k = best;
+                    break;
+                }
+                if (qc > 0 || cand <= kRowGrain) break;
+            }
+        }
+        if (best_q == 0) {
+            const uint64_t need = chunk_bytes(P, std::min<int64_t>(P.Nq, qc > 0 ? qc : kRowGrain),
+                                              kc > 0 ? kc : floors[1], pl->merge, false, pl);
+            return fail(CQSA_ERR_BUDGET, "mem_budget too small: the smallest plan needs %llu bytes (x 1/0.85 = %llu)",
+                        (unsigned long long)need, (unsigned long long)(need / kSafety) + 1);
+        }
+        qc = best_q;
+        kc = best_k;
+    }
+    pl->q_chunk = qc;
+    pl->kv_chunk = kc;
+    pl->n_q = ceil_div(P.Nq, qc);
+    pl->n_kv = ceil_div(P.Nk, kc);
+    const uint64_t need = chunk_bytes(P, qc, kc, pl->merge, true, pl);
+    if (need > budget)
+        return fail(CQSA_ERR_BUDGET, "mem_budget too small for q_chunk %lld, kv_chunk %lld: needs %llu bytes (x 1/0.85 = %llu)",
+                    (long long)qc, (long long)kc, (unsigned long long)need,
+                    (unsigned long long)(need / kSafety) + 1);
+    if (pl->n_kv == 1) pl->merge = 0;
+    pl->info.q_chunk = qc;
+    pl->info.kv_chunk = kc;
+    pl->info.n_q_chunks = pl->n_q;
+    pl->info.kv_splits = 1;
+    pl->info.merge_mode = pl->merge;
+    pl->info.workspace_bytes = pl->total;
+    count_chunked(P, pl);
+    return CQSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// device resources
+
+struct DeviceRes {
+    bool init = false;
+    int num_cus = 0;
+    hipStream_t h2d = nullptr;
+    hipStream_t d2h = nullptr;
+};
+std::mutex g_res_mu;
+DeviceRes g_res[64];
+
+cqsa_status device_res(DeviceRes** out) {
+    int dev = 0;
+    CQSA_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= 64) return fail(CQSA_ERR_HIP, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_res_mu);
+    DeviceRes& r = g_res[dev];
+    if (!r.init) {
+        CQSA_HIP(hipDeviceGetAttribute(&r.num_cus, hipDeviceAttributeMultiprocessorCount, dev));
+        r.init = true;
+    }
+    *out = &r;
+    return CQSA_OK;
+}
+
+cqsa_status side_streams(DeviceRes* r) {
+    std::lock_guard<std::mutex> lk(g_res_mu);
+    if (!r->h2d) CQSA_HIP(hipStreamCreateWithFlags(&r->h2d, hipStreamNonBlocking));
+    if (!r->d2h) CQSA_HIP(hipStreamCreateWithFlags(&r->d2h, hipStreamNonBlocking));
+    return CQSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// chunk copies between a [B, H, N, D] tensor (any strides) and a compact device buffer
+
+struct Compact {
+    int64_t sb, sh, sn;
+};
+
+// Device layout for rows [ra, ra + rn) of t: keeps the host's order of heads and rows, so that a
+// token-major host tensor moves in one contiguous block per batch entry.
+Compact compact_for(const View& t, int64_t rn) {
+    const bool token_major = t.H > 1 && t.sh < t.sn;
+    if (token_major) return Compact{rn * t.H * t.D, t.D, t.H * t.D};
+    return Compact{t.H * rn * t.D, rn * t.D, t.D};
+}
+
+// Copy rows [ra, ra + rn) of host/device tensor t to or from the compact device buffer dev.
+cqsa_status copy_rows(const View& t, int64_t ra, int64_t rn, char* dev, bool to_device, hipStream_t st) {
+    if (rn <= 0) return CQSA_OK;
+    const Compact c = compact_for(t, rn);
+    const hipMemcpyKind kind = to_device ? hipMemcpyHostToDevice : hipMemcpyDeviceToHost;
+    const size_t es = (size_t)t.es;
+    const bool token_major = t.H > 1 && t.sh < t.sn;
+    for (int64_t b = 0; b < t.B; ++b) {
+        char* hb = t.data + (size_t)(b * t.sb + ra * t.sn) * es;
+        char* db = dev + (size_t)(b * c.sb) * es;
+        if (token_major && t.sh == t.D && t.sn == t.H * t.D) {
+            const size_t bytes = (size_t)rn * t.H * t.D * es;
+            if (to_device)
+                CQSA_HIP(hipMemcpyAsync(db, hb, bytes, kind, st));
+            else
+                CQSA_HIP(hipMemcpyAsync(hb, db, bytes, kind, st));
+        } else if (!token_major && t.sn == t.D && t.sh >= rn * t.D) {
+            // each head: rn * D contiguous elements; heads at stride sh
+            const size_t width = (size_t)rn * t.D * es;
+            if (to_device)
+                CQSA_HIP(hipMemcpy2DAsync(db, (size_t)c.sh * es, hb, (size_t)t.sh * es, width, (size_t)t.H, kind, st));
+            else
+                CQSA_HIP(hipMemcpy2DAsync(hb, (size_t)t.sh * es, db, (size_t)c.sh * es, width, (size_t)t.H, kind, st));
+        } else {
+            for (int64_t h = 0; h < t.H; ++h) {
+                char* hh = hb + (size_t)(h * t.sh) * es;
+                char* dh = db + (size_t)(h * c.sh) * es;
+                const size_t width = (size_t)t.D * es;
+                if (to_device)
+                    CQSA_HIP(hipMemcpy2DAsync(dh, (size_t)c.sn * es, hh, (size_t)t.sn * es, width, (size_t)rn, kind, st));
+                else
+                    CQSA_HIP(hipMemcpy2DAsync(hh, (size_t)t.sn * es, dh, (size_t)c.sn * es, width, (size_t)rn, kind, st));
+            }
+        }
+    }
+    return CQSA_OK;
+}
+
+// lse rows [ra, ra + rn) of a [B, Hq, Nq] fp32 array <-> compact [B, Hq, rn]
+cqsa_status copy_lse_rows(float* host, const float* dev, int64_t B, int64_t Hq, int64_t Nq, int64_t ra, int64_t rn,
+                          hipStream_t st) {
+    if (rn <= 0) return CQSA_OK;
+    CQSA_HIP(hipMemcpy2DAsync(host + ra, (size_t)Nq * 4, dev, (size_t)rn * 4, (size_t)rn * 4, (size_t)(B * Hq),
+                              hipMemcpyDeviceToHost, st));
+    return CQSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// kernel argument helpers
+
+FwdArgs base_args(const Problem& P) {
+    FwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.B = (int32_t)P.B;
+    a.Hq = (int32_t)P.Hq;
+    a.Hkv = (int32_t)P.Hkv;
+    a.group = (int32_t)(P.Hq / P.Hkv);
+    a.causal = P.causal ? 1 : 0;
+    a.scale_log2 = P.scale * 1.44269504088896340736f;
+    a.n_splits = 1;
+    return a;
+}
+
+void set_q(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
+    a.q = reinterpret_cast<const uint16_t*>(data);
+    a.q_sb = sb;
+    a.q_sh = sh;
+    a.q_sn = sn;
+}
+void set_k(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
+    a.k = reinterpret_cast<const uint16_t*>(data);
+    a.k_sb = sb;
+    a.k_sh = sh;
+    a.k_sn = sn;
+}
+void set_v(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
+    a.v = reinterpret_cast<const uint16_t*>(data);
+    a.v_sb = sb;
+    a.v_sh = sh;
+    a.v_sn = sn;
+}
+
+cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
+    const int bm = fwd_block_m((int)P.D);
+    const int64_t rows = a.r1 - a.r0;
+    if (rows <= 0) return CQSA_OK;
+    const int64_t n_qt = ceil_div(rows, bm);
+    if (n_qt > 0x7FFFFFFF) return fail(CQSA_ERR_UNSUPPORTED, "too many query tiles");
+    a.n_qt = (int32_t)n_qt;
+    const hipError_t e = launch_fwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
+    if (e != hipSuccess) return fail(CQSA_ERR_HIP, "forward kernel launch failed: %s", hipGetErrorString(e));
+    return CQSA_OK;
+}
+
+cqsa_status run_merge(MergeArgs& m, hipStream_t st) {
+    const hipError_t e = launch_merge(m, st);
+    if (e != hipSuccess) return fail(CQSA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+    return CQSA_OK;
+}
+
+int elem_type(int dt) { return dt == CQSA_F16 ? ET_F16 : (dt == CQSA_BF16 ? ET_BF16 : ET_F32); }
+
+// ---------------------------------------------------------------------------------------------
+// executors
+
+// Every operand on the device, no forced chunking: one pass over all keys, optionally as side-by-side
+// KV splits merged by one merge-and-normalise pass.
+cqsa_status exec_single(const Problem& P, const Plan& pl, char* ws, hipStream_t st) {
+    FwdArgs a = base_args(P);
+    set_q(a, P.q.data, P.q.sb, P.q.sh, P.q.sn);
+    set_k(a, P.k.data, P.k.sb, P.k.sh, P.k.sn);
+    set_v(a, P.v.data, P.v.sb, P.v.sh, P.v.sn);
+    a.r0 = 0;
+    a.r1 = P.Nq;
+    a.k_lo = 0;
+    a.k_hi = P.Nk;
+    a.causal_delta = P.Nk - P.Nq;
+    if (pl.kv_splits <= 1) {
+        a.split_len = P.Nk;
+        a.mode = FWD_FINAL;
+        a.out = P.out.data;
+        a.out_dtype = elem_type(P.out.dtype);
+        a.o_sb = P.out.sb;
+        a.o_sh = P.out.sh;
+        a.o_sn = P.out.sn;
+        a.lse = P.want_lse ? P.lse : nullptr;
+        a.l_sb = P.Hq * P.Nq;
+        a.l_sh = P.Nq;
+        return run_fwd(P, a, st);
+    }
+    const int S = pl.kv_splits;
+    a.n_splits = S;
+    a.split_len = align_up(ceil_div(P.Nk, S), 64);
+    a.mode = FWD_PARTIAL;
+    a.acc_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+    a.acc_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
+    a.acc_rows = P.Nq;
+    cqsa_status s = run_fwd(P, a, st);
+    if (s != CQSA_OK) return s;
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
+    for (int p = 0; p < S; ++p) {
+        m.part_o[p] = a.acc_o + (uint64_t)p * rows * P.D;
+        m.part_ml[p] = a.acc_ml + (uint64_t)p * rows * 2;
+    }
+    m.n_parts = S;
+    m.D = (int32_t)P.D;
+    m.B = (int32_t)P.B;
+    m.Hq = (int32_t)P.Hq;
+    m.rows_per_head = P.Nq;
+    m.i_lo = 0;
+    m.i_hi = P.Nq;
+    m.final_out = 1;
+    m.out_dtype = elem_type(P.out.dtype);
+    m.out = P.out.data;
+    m.o_sb = P.out.sb;
+    m.o_sh = P.out.sh;
+    m.o_sn = P.out.sn;
+    m.lse = P.want_lse ? P.lse : nullptr;
+    m.l_sb = P.Hq * P.Nq;
+    m.l_sh = P.Nq;
+    return run_merge(m, st);
+}
+
+struct EventSet {
+    std::vector<hipEvent_t> evs;
+    ~EventSet() {
+        for (hipEvent_t e : evs) (void)hipEventDestroy(e);
+    }
+    cqsa_status make(hipEvent_t* e, bool timing) {
+        hipError_t r = hipEventCreateWithFlags(e, timing ? hipEventDefault : hipEventDisableTiming);
+        if (r != hipSuccess) return fail(CQSA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(r));
+        evs.push_back(*e);
+        return CQSA_OK;
+    }
+};
+
+struct TimedCopy {
+    hipEvent_t start, stop;
+};
+
+#define CQSA_TRY(expr)                        \
+    do {                                      \
+        cqsa_status s_ = (expr);              \
+        if (s_ != CQSA_OK) return s_;         \
+    } while (0)
+
+// Q chunks x KV chunks; operands may live in pinned host memory.
+cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t st, DeviceRes* res,
+                         cqsa_plan_info* info) {
+    const bool need_side = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
+    hipStream_t h2d = st, d2h = st;
+    if (need_side) {
+        CQSA_TRY(side_streams(res));
+        h2d = res->h2d;
+        d2h = res->d2h;
+    }
+    EventSet es;
+    hipEvent_t ev_start, ev_qcopy, ev_qfree, ev_fin, ev_d2h, ev_copy[2], ev_comp[2];
+    CQSA_TRY(es.make(&ev_start, false));
+    CQSA_TRY(es.make(&ev_qcopy, false));
+    CQSA_TRY(es.make(&ev_qfree, false));
+    CQSA_TRY(es.make(&ev_fin, false));
+    CQSA_TRY(es.make(&ev_d2h, false));
+    for (int i = 0; i < 2; ++i) {
+        CQSA_TRY(es.make(&ev_copy[i], false));
+        CQSA_TRY(es.make(&ev_comp[i], false));
+    }
+    std::vector<TimedCopy> h2d_t, d2h_t;
+    auto timed = [&](std::vector<TimedCopy>& v, TimedCopy* tc) -> cqsa_status {
+        CQSA_TRY(es.make(&tc->start, true));
+        CQSA_TRY(es.make(&tc->stop, true));
+        v.push_back(*tc);
+        return CQSA_OK;
+    };
+    // side streams start after the work already queued on the compute stream
+    CQSA_HIP(hipEventRecord(ev_start, st));
+    if (need_side) {
+        CQSA_HIP(hipStreamWaitEvent(h2d, ev_start, 0));
+        CQSA_HIP(hipStreamWaitEvent(d2h, ev_start, 0));
+    }
+    bool qfree_recorded = false, d2h_recorded = false;
+    bool comp_recorded[2] = {false, false};
+    int64_t pair = 0;
+
+    float* acc_o = reinterpret_cast<float*>(ws + pl.off_acc_o);
+    float* acc_ml = reinterpret_cast<float*>(ws + pl.off_acc_ml);
+    float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+    float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
+
+    for (int64_t qa = 0; qa < P.Nq; qa += pl.q_chunk) {
+        const int64_t qn = std::min(pl.q_chunk, P.Nq - qa);
+        FwdArgs a = base_args(P);
+        // ---- Q view
+        if (P.q.host) {
+            if (qfree_recorded) CQSA_HIP(hipStreamWaitEvent(h2d, ev_qfree, 0));
+            TimedCopy tc;
+            CQSA_TRY(timed(h2d_t, &tc));
+            CQSA_HIP(hipEventRecord(tc.start, h2d));
+            CQSA_TRY(copy_rows(P.q, qa, qn, ws + pl.off_q, true, h2d));
+            CQSA_HIP(hipEventRecord(tc.stop, h2d));
+            CQSA_HIP(hipEventRecord(ev_qcopy, h2d));
+            CQSA_HIP(hipStreamWaitEvent(st, ev_qcopy, 0));
+            const Compact c = compact_for(P.q, qn);
+            set_q(a, ws + pl.off_q, c.sb, c.sh, c.sn);
+        } else {
+            set_q(a, P.q.data + (size_t)(qa * P.q.sn) * 2, P.q.sb, P.q.sh, P.q.sn);
+        }
+        // ---- output view for this chunk
+        char* out_base;
+        int64_t o_sb, o_sh, o_sn;
+        if (P.out.host) {
+            const Compact c = compact_for(P.out, qn);
+            out_base = ws + pl.off_out;
+            o_sb = c.sb;
+            o_sh = c.sh;
+            o_sn = c.sn;
+        } else {
+            out_base = P.out.data + (size_t)(qa * P.out.sn) * P.out.es;
+            o_sb = P.out.sb;
+            o_sh = P.out.sh;
+            o_sn = P.out.sn;
+        }
+        float* lse_base = nullptr;
+        int64_t l_sb = 0, l_sh = 0;
+        if (P.want_lse) {
+            if (P.lse_host) {
+                lse_base = reinterpret_cast<float*>(ws + pl.off_lse);
+                l_sb = P.Hq * qn;
+                l_sh = qn;
+            } else {
+                lse_base = P.lse + qa;
+                l_sb = P.Hq * P.Nq;
+                l_sh = P.Nq;
+            }
+        }
+        const int64_t pos0 = P.Nk - P.Nq + qa;  // key position of local query row 0
+        const int64_t kv_end = P.causal ? std::min(P.Nk, pos0 + qn) : P.Nk;
+        const int64_t nkv = ceil_div(kv_end, pl.kv_chunk);
+        const bool single = nkv == 1;
+
+        for (int64_t kc = 0; kc < nkv; ++kc) {
+            const int64_t ka = kc * pl.kv_chunk;
+            const int64_t kn = std::min(pl.kv_chunk, kv_end - ka);
+            const int buf = (int)(pair & 1);
+            // ---- K/V views (copy into buffer `buf` after the compute that last read it)
+            if (P.k.host || P.v.host) {
+                if (comp_recorded[buf]) CQSA_HIP(hipStreamWaitEvent(h2d, ev_comp[buf], 0));
+                TimedCopy tc;
+                CQSA_TRY(timed(h2d_t, &tc));
+                CQSA_HIP(hipEventRecord(tc.start, h2d));
+                if (P.k.host) CQSA_TRY(copy_rows(P.k, ka, kn, ws + pl.off_k[buf], true, h2d));
+                if (P.v.host) CQSA_TRY(copy_rows(P.v, ka, kn, ws + pl.off_v[buf], true, h2d));
+                CQSA_HIP(hipEventRecord(tc.stop, h2d));
+                CQSA_HIP(hipEventRecord(ev_copy[buf], h2d));
+                CQSA_HIP(hipStreamWaitEvent(st, ev_copy[buf], 0));
+            }
+            if (P.k.host) {
+                const Compact c = compact_for(P.k, kn);
+                set_k(a, ws + pl.off_k[buf], c.sb, c.sh, c.sn);
+            } else {
+                set_k(a, P.k.data + (size_t)(ka * P.k.sn) * 2, P.k.sb, P.k.sh, P.k.sn);
+            }
+            if (P.v.host) {
+                const Compact c = compact_for(P.v, kn);
+                set_v(a, ws + pl.off_v[buf], c.sb, c.sh, c.sn);
+            } else {
+                set_v(a, P.v.data + (size_t)(ka * P.v.sn) * 2, P.v.sb, P.v.sh, P.v.sn);
+            }
+            a.k_lo = 0;
+            a.k_hi = kn;
+            a.split_len = kn;
+            a.causal_delta = pos0 - ka;
+            a.r0 = P.causal ? std::max<int64_t>(0, ka - pos0) : 0;
+            a.r1 = qn;
+            a.acc_rows = qn;
+            if (single) {
+                if (P.out.host && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+                a.mode = FWD_FINAL;
+                a.out = out_base;
+                a.out_dtype = elem_type(P.out.dtype);
+                a.o_sb = o_sb;
+                a.o_sh = o_sh;
+                a.o_sn = o_sn;
+                a.lse = lse_base;
+                a.l_sb = l_sb;
+                a.l_sh = l_sh;
+                CQSA_TRY(run_fwd(P, a, st));
+            } else if (kc == 0 || pl.merge == CQSA_MERGE_FUSED) {
+                a.mode = kc == 0 ? FWD_PARTIAL : FWD_ACCUM;
+                a.acc_o = acc_o;
+                a.acc_ml = acc_ml;
+                CQSA_TRY(run_fwd(P, a, st));
+            } else {
+                a.mode = FWD_PARTIAL;
+                a.acc_o = part_o;
+                a.acc_ml = part_ml;
+                CQSA_TRY(run_fwd(P, a, st));
+                MergeArgs m;
+                std::memset(&m, 0, sizeof m);
+                m.part_o[0] = acc_o;
+                m.part_ml[0] = acc_ml;
+                m.part_o[1] = part_o;
+                m.part_ml[1] = part_ml;
+                m.n_parts = 2;
+                m.D = (int32_t)P.D;
+                m.B = (int32_t)P.B;
+                m.Hq = (int32_t)P.Hq;
+                m.rows_per_head = qn;
+                m.i_lo = a.r0;
+                m.i_hi = qn;
+                m.o_out = acc_o;
+                m.ml_out = acc_ml;
+                CQSA_TRY(run_merge(m, st));
+            }
+            CQSA_HIP(hipEventRecord(ev_comp[buf], st));
+            comp_recorded[buf] = true;
+            ++pair;
+        }
+        if (!single) {
+            if (P.out.host && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+            MergeArgs m;
+            std::memset(&m, 0, sizeof m);
+            m.part_o[0] = acc_o;
+            m.part_ml[0] = acc_ml;
+            m.n_parts = 1;
+            m.D = (int32_t)P.D;
+            m.B = (int32_t)P.B;
+            m.Hq = (int32_t)P.Hq;
+            m.rows_per_head = qn;
+            m.i_lo = 0;
+            m.i_hi = qn;
+            m.final_out = 1;
+            m.out_dtype = elem_type(P.out.dtype);
+            m.out = out_base;
+            m.o_sb = o_sb;
+            m.o_sh = o_sh;
+            m.o_sn = o_sn;
+            m.lse = lse_base;
+            m.l_sb = l_sb;
+            m.l_sh = l_sh;
+            CQSA_TRY(run_merge(m, st));
+        }
+        CQSA_HIP(hipEventRecord(ev_qfree, st));
+        qfree_recorded = true;
+        if (P.out.host || (P.want_lse && P.lse_host)) {
+            CQSA_HIP(hipEventRecord(ev_fin, st));
+            CQSA_HIP(hipStreamWaitEvent(d2h, ev_fin, 0));
+            TimedCopy tc;
+            CQSA_TRY(timed(d2h_t, &tc));
+            CQSA_HIP(hipEventRecord(tc.start, d2h));
+            if (P.out.host) CQSA_TRY(copy_rows(P.out, qa, qn, ws + pl.off_out, false, d2h));
+            if (P.want_lse && P.lse_host)
+                CQSA_TRY(copy_lse_rows(P.lse, reinterpret_cast<float*>(ws + pl.off_lse), P.B, P.Hq, P.Nq, qa, qn, d2h));
+            CQSA_HIP(hipEventRecord(tc.stop, d2h));
+            CQSA_HIP(hipEventRecord(ev_d2h, d2h));
+            d2h_recorded = true;
+        }
+    }
+    // join the side streams back into the compute stream
+    if (need_side) {
+        hipEvent_t j1, j2;
+        CQSA_TRY(es.make(&j1, false));
+        CQSA_TRY(es.make(&j2, false));
+        CQSA_HIP(hipEventRecord(j1, h2d));
+        CQSA_HIP(hipEventRecord(j2, d2h));
+        CQSA_HIP(hipStreamWaitEvent(st, j1, 0));
+        CQSA_HIP(hipStreamWaitEvent(st, j2, 0));
+        CQSA_HIP(hipStreamSynchronize(st));
+        double h = 0, d = 0;
+        for (auto& t : h2d_t) {
+            float ms = 0;
+            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            h += ms;
+        }
+        for (auto& t : d2h_t) {
+            float ms = 0;
+            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            d += ms;
+        }
+        if (info) {
+            info->h2d_ms = h;
+            info->d2h_ms = d;
+        }
+    }
+    return CQSA_OK;
+}
+
+cqsa_status build_problem(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                          float scale, const cqsa_tensor* out, float* lse, int want_lse, bool detect, bool allow_null,
+                          Problem* P) {
+    CQSA_TRY(make_view(q, "q", allow_null, detect, &P->q));
+    CQSA_TRY(make_view(k, "k", allow_null, detect, &P->k));
+    CQSA_TRY(make_view(v, "v", allow_null, detect, &P->v));
+    CQSA_TRY(make_view(out, "out", allow_null, detect, &P->out));
+    P->want_lse = want_lse != 0;
+    P->lse = lse;
+    P->lse_host = false;
+    if (P->want_lse && lse && detect) {
+        cqsa_tensor lt;
+        std::memset(&lt, 0, sizeof lt);
+        lt.data = lse;
+        lt.dtype = CQSA_F32;
+        lt.shape[0] = 1;
+        lt.shape[1] = 1;
+        lt.shape[2] = 1;
+        lt.shape[3] = 1;
+        lt.stride[3] = 1;
+        CQSA_TRY(locate(&lt, "lse", false, &P->lse_host));
+    }
+    return check_problem(P, is_causal, scale);
+}
+
+cqsa_status resolve_budget(uint64_t mem_budget, uint64_t* budget) {
+    if (mem_budget > 0) {
+        *budget = (uint64_t)((double)mem_budget * kSafety);
+        return CQSA_OK;
+    }
+    size_t free_b = 0, total_b = 0;
+    CQSA_HIP(hipMemGetInfo(&free_b, &total_b));
+    *budget = (uint64_t)((double)free_b * kSafety);
+    return CQSA_OK;
+}
+
+bool log_enabled() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = std::getenv("CQSA_LOG");
+        v = (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+}  // namespace
+
+// =============================================================================================
+// C ABI
+
+extern "C" {
+
+const char* cqsa_last_error(void) { return g_err.c_str(); }
+
+int32_t cqsa_version(void) { return CQSA_ABI_VERSION; }
+
+uint64_t cqsa_struct_size(int32_t which) {
+    switch (which) {
+        case 0: return sizeof(cqsa_tensor);
+        case 1: return sizeof(cqsa_options);
+        case 2: return sizeof(cqsa_plan_info);
+        default: return 0;
+    }
+}
+
+cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                      uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
+                      cqsa_plan_info* info) {
+    g_err.clear();
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    if (opt) o = *opt;
+    // detect locations only for tensors whose `where` is DETECT
+    Problem P;
+    const bool detect = (q && q->where == CQSA_WHERE_DETECT) || (k && k->where == CQSA_WHERE_DETECT) ||
+                        (v && v->where == CQSA_WHERE_DETECT) || (out && out->where == CQSA_WHERE_DETECT);
+    CQSA_TRY(build_problem(q, k, v, is_causal, 0.f, out, nullptr, want_lse, detect, true, &P));
+    P.lse_host = want_lse && P.out.host;  // lse travels with out
+    P.streamed = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
+    uint64_t budget = 0;
+    CQSA_TRY(resolve_budget(mem_budget, &budget));
+    int cus = o.num_cus;
+    if (cus <= 0) {
+        DeviceRes* r = nullptr;
+        CQSA_TRY(device_res(&r));
+        cus = r->num_cus;
+    }
+    Plan pl;
+    CQSA_TRY(make_plan(P, budget, o, cus, &pl));
+    if (info) *info = pl.info;
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                              float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse,
+                              const cqsa_options* opt, cqsa_plan_info* info) {
+    g_err.clear();
+    const auto t0 = std::chrono::steady_clock::now();
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    if (opt) o = *opt;
+    Problem P;
+    CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, lse, lse != nullptr, true, false, &P));
+    if (P.empty) {
+        if (info) std::memset(info, 0, sizeof *info);
+        return CQSA_OK;
+    }
+    DeviceRes* res = nullptr;
+    CQSA_TRY(device_res(&res));
+    uint64_t budget = 0;
+    CQSA_TRY(resolve_budget(mem_budget, &budget));
+    Plan pl;
+    CQSA_TRY(make_plan(P, budget, o, res->num_cus, &pl));
+    hipStream_t st = static_cast<hipStream_t>(o.stream);
+
+    char* ws = nullptr;
+    bool owned = false;
+    if (pl.total > 0) {
+        if (o.workspace && o.workspace_bytes >= pl.total) {
+            ws = static_cast<char*>(o.workspace);
+        } else {
+            hipError_t e = hipMalloc(reinterpret_cast<void**>(&ws), pl.total);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(CQSA_ERR_OOM, "hipMalloc of %llu workspace bytes failed: %s",
+                            (unsigned long long)pl.total, hipGetErrorString(e));
+            }
+            owned = true;
+        }
+    }
+    cqsa_status s;
+    if (!pl.chunked)
+        s = exec_single(P, pl, ws, st);
+    else
+        s = exec_chunked(P, pl, ws, st, res, &pl.info);
+    const bool sync = owned || P.streamed;
+    if (sync && s == CQSA_OK) {
+        hipError_t e = hipStreamSynchronize(st);
+        if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    }
+    if (owned) {
+        if (s != CQSA_OK) (void)hipStreamSynchronize(st);
+        (void)hipFree(ws);
+    }
+    if (s != CQSA_OK) return s;
+    if (sync) pl.info.wall_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (info) *info = pl.info;
+    if (log_enabled()) {
+        std::fprintf(stderr,
+                     "cqsa: B=%lld Hq=%lld Hkv=%lld Nq=%lld Nk=%lld D=%lld causal=%d | %s q_chunk=%lld kv_chunk=%lld "
+                     "splits=%d merge=%d pairs=%lld launches=%lld ws=%llu h2d=%llu d2h=%llu\n",
+                     (long long)P.B, (long long)P.Hq, (long long)P.Hkv, (long long)P.Nq, (long long)P.Nk,
+                     (long long)P.D, (int)P.causal, P.streamed ? "streamed" : "resident",
+                     (long long)pl.info.q_chunk, (long long)pl.info.kv_chunk, pl.info.kv_splits,
+                     pl.info.merge_mode, (long long)pl.info.chunk_pairs, (long long)pl.info.kernel_launches,
+                     (unsigned long long)pl.info.workspace_bytes, (unsigned long long)pl.info.h2d_bytes,
+                     (unsigned long long)pl.info.d2h_bytes);
+    }
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_attention(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                           float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse) {
+    return cqsa_attention_ex(q, k, v, is_causal, scale, mem_budget, out, lse, nullptr, nullptr);
+}
+
+cqsa_status cqsa_fwd_partial(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                             float scale, int64_t kv_begin, int64_t kv_end, float* o_part, float* ml_part,
+                             void* stream) {
+    g_err.clear();
+    Problem P;
+    // out has q's shape; describe it with q's descriptor (it is not written)
+    CQSA_TRY(build_problem(q, k, v, is_causal, scale, q, nullptr, 0, true, false, &P));
+    if (P.q.host || P.k.host || P.v.host) return fail(CQSA_ERR_INVALID, "cqsa_fwd_partial takes device tensors");
+    if (P.empty) return CQSA_OK;
+    if (kv_begin < 0 || kv_end < kv_begin || kv_end > P.Nk)
+        return fail(CQSA_ERR_INVALID, "key range [%lld, %lld) outside [0, %lld]", (long long)kv_begin,
+                    (long long)kv_end, (long long)P.Nk);
+    if (!o_part || !ml_part) return fail(CQSA_ERR_INVALID, "o_part / ml_part is NULL");
+    FwdArgs a = base_args(P);
+    set_q(a, P.q.data, P.q.sb, P.q.sh, P.q.sn);
+    set_k(a, P.k.data, P.k.sb, P.k.sh, P.k.sn);
+    set_v(a, P.v.data, P.v.sb, P.v.sh, P.v.sn);
+    a.r0 = 0;
+    a.r1 = P.Nq;
+    a.k_lo = kv_begin;
+    a.k_hi = kv_end;
+    a.split_len = std::max<int64_t>(kv_end - kv_begin, 1);
+    a.causal_delta = P.Nk - P.Nq;
+    a.mode = FWD_PARTIAL;
+    a.acc_o = o_part;
+    a.acc_ml = ml_part;
+    a.acc_rows = P.Nq;
+    return run_fwd(P, a, static_cast<hipStream_t>(stream));
+}
+
+cqsa_status cqsa_lse_merge(const float* const* o_parts, const float* const* ml_parts, int32_t num_parts,
+                           int64_t rows, int64_t D, float* o_out, float* ml_out, void* stream) {
+    g_err.clear();
+    if (num_parts < 1 || num_parts > kMaxMergeParts)
+        return fail(CQSA_ERR_INVALID, "num_parts %d outside [1, %d]", num_parts, kMaxMergeParts);
+    if (D != 64 && D != 128) return fail(CQSA_ERR_UNSUPPORTED, "D %lld is not 64 or 128", (long long)D);
+    if (rows < 0) return fail(CQSA_ERR_INVALID, "negative rows");
+    if (!o_parts || !ml_parts || !o_out || !ml_out) return fail(CQSA_ERR_INVALID, "NULL pointer");
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    for (int p = 0; p < num_parts; ++p) {
+        if (!o_parts[p] || !ml_parts[p]) return fail(CQSA_ERR_INVALID, "part %d is NULL", p);
+        if (!aligned16(o_parts[p])) return fail(CQSA_ERR_UNSUPPORTED, "part %d is not 16-byte aligned", p);
+        m.part_o[p] = o_parts[p];
+        m.part_ml[p] = ml_parts[p];
+    }
+    if (!aligned16(o_out)) return fail(CQSA_ERR_UNSUPPORTED, "o_out is not 16-byte aligned");
+    m.n_parts = num_parts;
+    m.D = (int32_t)D;
+    m.B = 1;
+    m.Hq = 1;
+    m.rows_per_head = rows;
+    m.i_lo = 0;
+    m.i_hi = rows;
+    m.o_out = o_out;
+    m.ml_out = ml_out;
+    return run_merge(m, static_cast<hipStream_t>(stream));
+}
+
+cqsa_status cqsa_finalize(const float* o, const float* ml, cqsa_tensor* out, float* lse, void* stream) {
+    g_err.clear();
+    View ov;
+    CQSA_TRY(make_view(out, "out", false, true, &ov));
+    if (ov.host) return fail(CQSA_ERR_INVALID, "cqsa_finalize writes device memory only");
+    if (ov.D != 64 && ov.D != 128) return fail(CQSA_ERR_UNSUPPORTED, "D %lld is not 64 or 128", (long long)ov.D);
+    if (!o || !ml) return fail(CQSA_ERR_INVALID, "NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(ov.data) % (4 * ov.es)) || ov.sn % 4 || ov.sh % 4 || ov.sb % 4)
+        return fail(CQSA_ERR_UNSUPPORTED, "out data and strides must be aligned to 4 elements");
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.part_o[0] = o;
+    m.part_ml[0] = ml;
+    m.n_parts = 1;
+    m.D = (int32_t)ov.D;
+    m.B = (int32_t)ov.B;
+    m.Hq = (int32_t)ov.H;
+    m.rows_per_head = ov.N;
+    m.i_lo = 0;
+    m.i_hi = ov.N;
+    m.final_out = 1;
+    m.out_dtype = elem_type(ov.dtype);
+    m.out = ov.data;
+    m.o_sb = ov.sb;
+    m.o_sh = ov.sh;
+    m.o_sn = ov.sn;
+    m.lse = lse;
+    m.l_sb = ov.H * ov.N;
+    m.l_sh = ov.N;
+    return run_merge(m, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal interface between the runtime (cqsa_api.cpp) and the gfx950 kernels
+// (cqsa_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace cqsa {
+
+// Epilogue of the forward kernel.
+enum FwdMode : int32_t {
+    FWD_FINAL = 0,    // write O / l in the output dtype and lse = m + ln l
+    FWD_PARTIAL = 1,  // write the unnormalised triple (O, m, l) to the partial buffers
+    FWD_ACCUM = 2     // merge the triple into the running (O, m, l) buffers in place
+};
+
+enum ElemType : int32_t { ET_F16 = 0, ET_BF16 = 1, ET_F32 = 2 };
+
+// One forward launch: query rows [r0, r1) of the q view against keys [k_lo, k_hi)
+// of the k/v views, optionally split into n_splits key ranges of split_len keys.
+// Row and key indices are local to the views; the causal rule is
+// key j visible to row i  <=>  j <= i + causal_delta.
+struct FwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t q_sb, q_sh, q_sn;  // element strides
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t r0, r1;
+    int64_t k_lo, k_hi;
+    int64_t split_len;
+    int64_t causal_delta;
+    int32_t B, Hq, Hkv, group;
+    int32_t n_qt, n_splits;
+    int32_t causal, mode;
+    int32_t out_dtype;
+    float scale_log2;          // scale * log2(e)
+    // FWD_FINAL
+    void* out;
+    int64_t o_sb, o_sh, o_sn;
+    float* lse;                // [b * l_sb + h * l_sh + i], may be null
+    int64_t l_sb, l_sh;
+    // FWD_PARTIAL / FWD_ACCUM: row (split, b, h, i) at ((split * B + b) * Hq + h) * acc_rows + i
+    float* acc_o;              // [..][D]
+    float* acc_ml;             // [..][2]
+    int64_t acc_rows;
+};
+
+constexpr int kMaxMergeParts = 64;
+
+// Log-sum-exp merge of n_parts triples for rows (b, h, i), i in [i_lo, i_hi), laid out
+// at (b * Hq + h) * rows_per_head + i.  With final_out set, writes out = O / l and lse
+// instead of the merged triple.
+struct MergeArgs {
+    const float* part_o[kMaxMergeParts];
+    const float* part_ml[kMaxMergeParts];
+    int32_t n_parts;
+    int32_t D;
+    int32_t B, Hq;
+    int64_t rows_per_head;
+    int64_t i_lo, i_hi;
+    float* o_out;
+    float* ml_out;
+    int32_t final_out;
+    int32_t out_dtype;
+    void* out;                 // element (b, h, i - i_lo + out_row0 ...) see below
+    int64_t o_sb, o_sh, o_sn;  // out row for local row i is (i - i_lo)
+    float* lse;
+    int64_t l_sb, l_sh;
+};
+
+// Query rows per workgroup of the forward kernel for a head dim.
+int fwd_block_m(int D);
+
+// Launchers (return the launch status).
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace cqsa

@@ -1,0 +1,459 @@
+// gfx950 (CDNA4) kernels for exact attention by Q-tiles x KV-chunks with a log-sum-exp merge.
+//
+// fwd_kernel    one workgroup = BM query rows of one (batch, query head) against one key range.
+//               Online softmax (the FlashAttention-2 recurrence the Stream-CQSA kernels derive from:
+//               stream-cqsa 2.2.0 -> 2.2.2 diff, README.md, "FlashAttention-2-derived CQS forward")
+//               produces the partial triple (O, m, l) of the range; the epilogue normalises it,
+//               stores it, or folds it into a running triple.
+// merge_kernel  the exact log-sum-exp merge of partial triples, optionally normalising (finalize).
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_{f16,bf16}; wave64; lane = 32*hi + l32):
+//   A operand: lane holds A[row l32][k = 8*hi .. 8*hi+7]
+//   B operand: lane holds B[k = 8*hi .. 8*hi+7][col l32]
+//   C/D:       lane holds C[row = 8*(r/4) + 4*hi + r%4][col l32], r = 0..15
+// Scores are computed transposed, S^T = K Q^T (A = 32 keys from LDS, B = 32 query rows kept in
+// registers), so each lane owns one query column and 16 of its keys: the row max needs one exchange
+// with lane ^ 32, the row sum stays per lane until the end, and the fp32 scores, once turned into
+// probabilities and rounded to fp16/bf16, are already the B operand of O^T = V^T P^T.  That product
+// contracts over keys in the order the score accumulator holds them, so V is written into LDS
+// transposed (V^T[d][key slot]) with each group of 16 keys permuted to match.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "cqsa_internal.h"
+
+namespace cqsa {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 64;       // keys per LDS tile
+constexpr int kWaves = 4;     // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<ET_F16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma32<ET_BF16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// Eight fp32 probabilities -> eight fp16/bf16 (round to nearest even), packed as an MFMA operand.
+template <int DT>
+__device__ __forceinline__ u32x4 pack8(f32x8 x);
+
+template <>
+__device__ __forceinline__ u32x4 pack8<ET_F16>(f32x8 x) {
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(x, f16x8));
+}
+
+template <>
+__device__ __forceinline__ u32x4 pack8<ET_BF16>(f32x8 x) {
+    return __builtin_bit_cast(u32x4, __builtin_convertvector(x, bf16x8));
+}
+
+__device__ __forceinline__ void store4(void* base, int64_t off, int dt, f32x4 v) {
+    if (dt == ET_F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(base) + off) = v;
+    } else if (dt == ET_F16) {
+        *reinterpret_cast<f16x4*>(static_cast<_Float16*>(base) + off) = __builtin_convertvector(v, f16x4);
+    } else {
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(base) + off) = __builtin_convertvector(v, bf16x4);
+    }
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8).  Renumber them so
+// that each XCD receives a contiguous range of work items: items that share a K/V head then share
+// that XCD's L2.  A bijection on [0, G) for any G.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    const int q = G >> 3, r = G & 7;
+    const int xcd = bid & 7, slot = bid >> 3;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + slot;
+}
+
+// Position of key offset o (0..15) inside its 16-key group of the V^T tile.  Score accumulator
+// register 8u+s of a lane in half hi holds key 16u + 8*(s/4) + 4*hi + s%4 of the 32-key block; the
+// PV product's k index 8*hi + s must address that key, so key offset o is stored at slot
+// 8*((o/4)%2) + o%4 + 4*(o/8).  The map swaps the middle two groups of four and is its own inverse;
+// keys 2p and 2p+1 stay adjacent.
+__device__ __forceinline__ int vslot(int j) {
+    const int o = j & 15;
+    return (j & ~15) + (((o >> 2) & 1) << 3) + (o & 3) + ((o >> 3) << 2);
+}
+
+template <int D, int DT, int QB>
+__global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
+    constexpr int QW = 32 * QB;                            // query rows per wave
+    constexpr int BM = kWaves * QW;                        // query rows per workgroup
+    constexpr int KS = D + 8;                              // K tile row stride (elements): 16 B pad
+    constexpr int VS = kKT + 8;                            // V^T tile row stride (elements): 16 B pad
+    constexpr int KTILE = kKT * KS;
+    constexpr int STAGE = KTILE + D * VS;
+    constexpr int KCH = kKT * (D / 8) / kThreads;          // 16-byte K pieces per thread and tile
+    constexpr int VCH = (kKT / 2) * (D / 8) / kThreads;    // (key pair x 8 dims) V pieces per thread
+    constexpr int NDB = D / 32;
+    constexpr int NDK = D / 16;
+    static_assert(KCH >= 1 && VCH >= 1, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // ---- which work item: (b, kv head, split, head in group, query tile), longest tiles first
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = w % a.n_qt;
+    w /= a.n_qt;
+    const int gi = w % a.group;
+    w /= a.group;
+    const int split = w % a.n_splits;
+    w /= a.n_splits;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int hq = hkv * a.group + gi;
+    const int qt = a.n_qt - 1 - qt_idx;
+
+    const int64_t i0 = a.r0 + (int64_t)qt * BM;
+    const int64_t i_end = min(i0 + (int64_t)BM, a.r1);
+    const int64_t iw0 = i0 + (int64_t)wave * QW;
+    const int64_t iw_end = min(iw0 + (int64_t)QW, i_end);
+
+    const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
+    int64_t khi = min(a.k_hi, klo + a.split_len);
+    if (a.causal) khi = min(khi, i_end + a.causal_delta);  // the last row sees keys <= i_end - 1 + delta
+    const int ntiles = khi > klo ? (int)((khi - klo + kKT - 1) / kKT) : 0;
+
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+    // ---- Q fragments, the B operand of S^T = K Q^T
+    u32x4 qf[QB][NDK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t row = iw0 + qb * 32 + l32;
+        const bool ok = row < i_end;
+        const uint16_t* p = qp + row * a.q_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            qf[qb][t] = ok ? *reinterpret_cast<const u32x4*>(p + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    f32x16 oacc[QB][NDB];
+    float mrun[QB], lrun[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mrun[qb] = -INFINITY;
+        lrun[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[qb][db] = f32x16{};
+    }
+
+    // ---- tile staging: global -> registers (next tile) -> LDS (double buffered)
+    u32x4 kreg[KCH];
+    u32x4 vreg[VCH][2];
+    auto load_tile = [&](int64_t j0) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int idx = tid + c * kThreads;
+            const int row = idx / (D / 8), col8 = idx % (D / 8);
+            const int64_t j = j0 + row;
+            kreg[c] = j < khi ? *reinterpret_cast<const u32x4*>(kp + j * a.k_sn + col8 * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = tid + c * kThreads;
+            const int pr = idx % (kKT / 2), col8 = idx / (kKT / 2);
+            const int64_t j = j0 + 2 * pr;
+            vreg[c][0] = j < khi ? *reinterpret_cast<const u32x4*>(vp + j * a.v_sn + col8 * 8) : u32x4{0u, 0u, 0u, 0u};
+            vreg[c][1] = j + 1 < khi ? *reinterpret_cast<const u32x4*>(vp + (j + 1) * a.v_sn + col8 * 8)
+                                     : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_tile = [&](int s) {
+        uint16_t* ks = lds + s * STAGE;
+        uint16_t* vs = ks + KTILE;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int idx = tid + c * kThreads;
+            const int row = idx / (D / 8), col8 = idx % (D / 8);
+            *reinterpret_cast<u32x4*>(ks + row * KS + col8 * 8) = kreg[c];
+        }
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = tid + c * kThreads;
+            const int pr = idx % (kKT / 2), col8 = idx / (kKT / 2);
+            const int slot = vslot(2 * pr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w0 = vreg[c][0][e >> 1], w1 = vreg[c][1][e >> 1];
+                const uint32_t word = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+                *reinterpret_cast<uint32_t*>(vs + (col8 * 8 + e) * VS + slot) = word;
+            }
+        }
+    };
+
+    if (ntiles > 0) {
+        load_tile(klo);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int s = it & 1;
+        const int64_t j0 = klo + (int64_t)it * kKT;
+        if (it + 1 < ntiles) load_tile(j0 + kKT);
+
+        const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + a.causal_delta);
+        if (active) {
+            const uint16_t* ks = lds + s * STAGE;
+            const uint16_t* vs = ks + KTILE;
+
+            // S^T for 64 keys x QW queries
+            f32x16 sacc[2][QB];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16{};
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(ks + (kb * 32 + l32) * KS + 16 * t + 8 * hi);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32<DT>(af, qf[qb][t], sacc[kb][qb]);
+                }
+            }
+
+            // mask keys past the range end and, on diagonal tiles, keys after the query
+            const bool need_mask = (j0 + kKT > khi) || (a.causal && (j0 + kKT - 1 > iw0 + a.causal_delta));
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const int64_t row = iw0 + qb * 32 + l32;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int64_t j = j0 + kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                            if (j >= khi || (a.causal && j > row + a.causal_delta)) sacc[kb][qb][r] = -INFINITY;
+                        }
+                    }
+            }
+
+            // online softmax (base 2: scale * log2(e) folded into one multiply-add)
+            u32x4 pf[QB][4];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(mrun[qb], mx * a.scale_log2);
+                const float muse = mnew == -INFINITY ? 0.f : mnew;   // never (-inf) - (-inf)
+                const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - muse);
+                float rs = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], a.scale_log2, -muse));
+                        sacc[kb][qb][r] = p;
+                        rs += p;
+                    }
+                lrun[qb] = lrun[qb] * alpha + rs;
+                mrun[qb] = mnew;
+                if (__any(alpha != 1.f)) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int kb = t >> 1, u = t & 1;
+                    f32x8 x;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = sacc[kb][qb][8 * u + e];
+                    pf[qb][t] = pack8<DT>(x);
+                }
+            }
+
+            // O^T += V^T P^T
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + (db * 32 + l32) * VS + 16 * t + 8 * hi);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<DT>(vf, pf[qb][t], oacc[qb][db]);
+                }
+            }
+        }
+
+        if (it + 1 < ntiles) store_tile(s ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float ltot = lrun[qb] + __shfl_xor(lrun[qb], 32);
+        const int64_t row = iw0 + qb * 32 + l32;
+        if (row >= i_end) continue;
+        const float mnat = ltot > 0.f ? mrun[qb] * kLn2 : -INFINITY;
+        if (a.mode == FWD_FINAL) {
+            const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+            const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
+                               oacc[qb][db][4 * g + 3]};
+                    store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
+                }
+            if (a.lse && hi == 0)
+                a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
+                    ltot > 0.f ? (mrun[qb] + __log2f(ltot)) * kLn2 : -INFINITY;
+        } else {
+            const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
+            float* op = a.acc_o + ridx * D;
+            float* mlp = a.acc_ml + ridx * 2;
+            if (a.mode == FWD_PARTIAL) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
+                                   oacc[qb][db][4 * g + 3]};
+                        *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
+                    }
+                if (hi == 0) {
+                    mlp[0] = mnat;
+                    mlp[1] = ltot;
+                }
+            } else {
+                const float ma = mlp[0], la = mlp[1];
+                const float mm = fmaxf(ma, mnat);
+                const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
+                const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float* dst = op + db * 32 + 8 * g + 4 * hi;
+                        const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+                        f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
+                                   oacc[qb][db][4 * g + 3]};
+                        *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
+                    }
+                if (hi == 0) {
+                    mlp[0] = mm;
+                    mlp[1] = wa * la + wb * ltot;
+                }
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge: TPR threads per row, four output dims per thread.  The threads of one row
+// sit in one wave, so in-place operation (output == part 0) reads every input before it writes.
+template <int D>
+__global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
+    constexpr int TPR = D / 4;
+    constexpr int RPB = 256 / TPR;
+    const int64_t nloc = a.i_hi - a.i_lo;
+    const int64_t total = (int64_t)a.B * a.Hq * nloc;
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    if (r >= total) return;
+    const int d0 = (threadIdx.x % TPR) * 4;
+    const int64_t bh = r / nloc;
+    const int64_t i = a.i_lo + r % nloc;
+    const int64_t ridx = bh * a.rows_per_head + i;
+
+    float mm = -INFINITY;
+    for (int p = 0; p < a.n_parts; ++p) mm = fmaxf(mm, a.part_ml[p][2 * ridx]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    for (int p = 0; p < a.n_parts; ++p) {
+        const float mp = a.part_ml[p][2 * ridx];
+        const float wgt = mp == -INFINITY ? 0.f : exp2f((mp - mm) * kLog2e);
+        l += wgt * a.part_ml[p][2 * ridx + 1];
+        acc += wgt * *reinterpret_cast<const f32x4*>(a.part_o[p] + ridx * D + d0);
+    }
+    if (a.final_out) {
+        const int64_t b = bh / a.Hq, h = bh % a.Hq;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        store4(a.out, b * a.o_sb + h * a.o_sh + (i - a.i_lo) * a.o_sn + d0, a.out_dtype, acc * inv);
+        if (a.lse && d0 == 0) a.lse[b * a.l_sb + h * a.l_sh + (i - a.i_lo)] = l > 0.f ? mm + logf(l) : -INFINITY;
+    } else {
+        *reinterpret_cast<f32x4*>(a.o_out + ridx * D + d0) = acc;
+        if (d0 == 0) {
+            a.ml_out[2 * ridx] = l > 0.f ? mm : -INFINITY;
+            a.ml_out[2 * ridx + 1] = l;
+        }
+    }
+}
+
+template <int D, int DT, int QB>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_kernel<D, DT, QB>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+constexpr int qb_for(int D) { return D == 64 ? 2 : 1; }
+
+}  // namespace
+
+int fwd_block_m(int D) { return kWaves * 32 * qb_for(D); }
+
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
+    if (D == 64 && dtype == ET_F16) return launch_fwd_t<64, ET_F16, qb_for(64)>(a, stream);
+    if (D == 64 && dtype == ET_BF16) return launch_fwd_t<64, ET_BF16, qb_for(64)>(a, stream);
+    if (D == 128 && dtype == ET_F16) return launch_fwd_t<128, ET_F16, qb_for(128)>(a, stream);
+    if (D == 128 && dtype == ET_BF16) return launch_fwd_t<128, ET_BF16, qb_for(128)>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+    const int64_t total = (int64_t)a.B * a.Hq * (a.i_hi - a.i_lo);
+    if (total <= 0) return hipSuccess;
+    const int rpb = 256 / (a.D / 4);
+    const int64_t blocks = (total + rpb - 1) / rpb;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (a.D == 64) {
+        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    } else if (a.D == 128) {
+        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cqsa

@@ -1,0 +1,213 @@
+/*
+ * cqsa.h -- exact scaled-dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * The attention softmax(scale * Q K^T [+ causal mask]) V is computed as query
+ * chunks x key/value chunks.  Each (query rows, key range) piece yields an
+ * unnormalised partial triple (O, m, l): O = sum_j exp(s_j - m) v_j, m = the
+ * largest scaled logit, l = sum_j exp(s_j - m).  Partials are merged exactly by
+ * the log-sum-exp rule, so a context that does not fit in device memory can be
+ * streamed from pinned host memory and still give the monolithic answer.  This
+ * is the method of the Stream-CQSA pages ("exact out-of-memory recovery for
+ * attention": stream-cqsa 2.2.2 -> 2.2.3 diff, README.md section "Use", and the
+ * attention() docstring in stream_cqsa/api.py of the 2.2.0 -> 2.2.2 diff).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are described by cqsa_tensor: shape [B, H, N, D] and element
+ *     strides; stride[3] (head dim) must be 1.  Any batch/head/row strides work,
+ *     so both [B,H,N,D] and token-major [B,N,H,D] storage are accepted.
+ *   - q is [B, Hq, Nq, D]; k and v are [B, Hkv, Nk, D] with Hq % Hkv == 0.
+ *     Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention,
+ *     the repeat-interleave mapping of PyTorch SDPA's enable_gqa).
+ *   - q, k, v are all CQSA_F16 or all CQSA_BF16; D is 64 or 128.  Products run
+ *     on the matrix cores in that type with fp32 accumulation; softmax is fp32.
+ *   - Causal masking is bottom-right aligned: query row i sits at key position
+ *     i + Nk - Nq and sees keys j <= i + Nk - Nq.  With Nq == Nk this is the
+ *     ordinary lower-triangular mask.  Causal calls need Nq <= Nk (every row must
+ *     see at least one key).  (PyTorch aligns Nq != Nk top-left; the Stream-CQSA
+ *     pages only ever use square calls.)
+ *   - scale <= 0 (or NaN) selects the SDPA default 1/sqrt(D).  The scale is used
+ *     as the given fp32 value.
+ *   - lse, when requested, is fp32 [B, Hq, Nq] contiguous: m + ln(l), natural log
+ *     of the sum of exp(scaled logits).
+ *   - Memory: device pointers or pinned host pointers (hipHostMalloc / torch
+ *     pin_memory).  Pageable host memory is rejected with CQSA_ERR_INVALID before
+ *     any work (block-streamer 0.1.0, README section "Streams, residency, and
+ *     memory budget": an unpinned transfer source must fail loudly).
+ *   - All buffers are caller-owned; the library keeps no pointer after return.
+ *   - The calls run on the current HIP device.  Errors never throw: every call
+ *     returns a cqsa_status, and cqsa_last_error() returns a message for the
+ *     calling thread.  Arguments are validated before any device work starts.
+ */
+#ifndef CQSA_H
+#define CQSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CQSA_ABI_VERSION 1
+
+typedef enum {
+    CQSA_OK = 0,
+    CQSA_ERR_INVALID = -1,     /* bad argument: shape, stride, dtype mix, pageable host memory, no visible key */
+    CQSA_ERR_UNSUPPORTED = -2, /* head dim not 64/128, input dtype not fp16/bf16, misaligned data or rows */
+    CQSA_ERR_BUDGET = -3,      /* mem_budget below the smallest plan; the message names the bytes needed */
+    CQSA_ERR_OOM = -4,         /* hipMalloc failed (no retry: re-planning is the caller's choice) */
+    CQSA_ERR_HIP = -5          /* a HIP runtime call failed; the message carries hipGetErrorString */
+} cqsa_status;
+
+typedef enum { CQSA_F16 = 0, CQSA_BF16 = 1, CQSA_F32 = 2 } cqsa_dtype;
+
+/* Where a tensor lives.  DETECT asks hipPointerGetAttributes. */
+typedef enum { CQSA_WHERE_DETECT = 0, CQSA_WHERE_DEVICE = 1, CQSA_WHERE_HOST = 2 } cqsa_where;
+
+typedef struct {
+    void* data;         /* first element; may be NULL only for cqsa_plan or an empty tensor */
+    int32_t dtype;      /* cqsa_dtype */
+    int32_t where;      /* cqsa_where */
+    int64_t shape[4];   /* [B, H, N, D] */
+    int64_t stride[4];  /* element strides; stride[3] == 1 */
+} cqsa_tensor;
+
+/* Merge strategies for multi-chunk plans. */
+typedef enum {
+    CQSA_MERGE_AUTO = 0,   /* the planner's choice */
+    CQSA_MERGE_KERNEL = 1, /* each KV chunk writes a partial; a separate LSE-merge kernel folds it in */
+    CQSA_MERGE_FUSED = 2   /* the forward kernel folds its partial into the running triple in its epilogue */
+} cqsa_merge_mode;
+
+typedef struct {
+    int64_t q_chunk;          /* query rows per Q chunk; 0 = planner */
+    int64_t kv_chunk;         /* keys per KV chunk; 0 = planner; > 0 forces this split */
+    int32_t kv_splits;        /* single-chunk device calls: KV splits run side by side and merged
+                                 (fills the GPU when there are few query tiles); 0 = planner, 1 = off */
+    int32_t merge_mode;       /* cqsa_merge_mode */
+    void* workspace;          /* device memory the call may use instead of allocating; NULL = allocate */
+    uint64_t workspace_bytes; /* its size */
+    void* stream;             /* hipStream_t carrying the compute; NULL = the null stream */
+    int32_t num_cus;          /* cqsa_plan only: compute units to plan for; 0 = ask the device */
+    int32_t reserved;
+} cqsa_options;
+
+/* What a plan does (filled by cqsa_plan and cqsa_attention_ex). */
+typedef struct {
+    int32_t streamed;          /* 1 when an operand lives in host memory and is copied in chunks */
+    int32_t merge_mode;        /* as planned: 0 single pass, CQSA_MERGE_KERNEL, CQSA_MERGE_FUSED */
+    int64_t q_chunk;           /* query rows per Q chunk */
+    int64_t kv_chunk;          /* keys per KV chunk */
+    int64_t n_q_chunks;
+    int64_t n_kv_chunks;       /* KV chunks of the whole key range */
+    int32_t kv_splits;         /* side-by-side KV splits of a single-chunk call (1 = none) */
+    int32_t block_m;           /* query rows per workgroup of the forward kernel */
+    int64_t chunk_pairs;       /* (Q chunk, KV chunk) pairs that run; causal skipping applied */
+    int64_t merges;            /* log-sum-exp merges (merge-kernel launches or fused epilogues) */
+    int64_t kernel_launches;
+    uint64_t workspace_bytes;  /* device bytes the plan uses (allocated unless a workspace is given) */
+    uint64_t budget_bytes;     /* the byte limit planned against: mem_budget x 0.85 */
+    uint64_t h2d_bytes;        /* host-to-device bytes the plan copies */
+    uint64_t d2h_bytes;        /* device-to-host bytes */
+    double h2d_ms;             /* summed duration of the H2D copies (HIP events; streamed calls) */
+    double d2h_ms;             /* summed duration of the D2H copies */
+    double wall_ms;            /* host wall time of a synchronising call */
+} cqsa_plan_info;
+
+/*
+ * cqsa_attention: out = softmax(scale * q k^T [+ causal mask]) v, exactly.
+ *
+ *   q, k, v     inputs, as described above; device or pinned host memory.
+ *   is_causal   nonzero for the bottom-right causal mask.
+ *   scale       logit scale; <= 0 selects 1/sqrt(D).
+ *   mem_budget  most device bytes the call may use for its own buffers
+ *               (staging, accumulators, partials); the planner keeps to 85% of it,
+ *               the safety margin of the Stream-CQSA planner (stream-cqsa
+ *               2.2.0 -> 2.2.2 diff, stream_cqsa/autoconfig.py, plan(), safety=0.85).
+ *               0 = the free device memory (hipMemGetInfo) x 0.85.
+ *   out         [B, Hq, Nq, D], CQSA_F16, CQSA_BF16 or CQSA_F32 (results are rounded
+ *               to nearest even from fp32); device or pinned host memory.
+ *   lse         NULL, or fp32 [B, Hq, Nq] (device or pinned host).
+ * With every operand on the device and no allocation needed, the call is
+ * ordered on the null stream and returns without waiting; otherwise it returns
+ * after the work is done.
+ */
+cqsa_status cqsa_attention(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                           float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse);
+
+/*
+ * cqsa_attention_ex: cqsa_attention with options and a report.
+ *   opt   NULL = defaults.  opt->stream carries the compute; with a workspace of
+ *         sufficient size the library allocates nothing.  Forced chunk sizes
+ *         (kv_chunk, q_chunk) run the decomposed schedule even when everything fits.
+ *   info  NULL, or filled with the plan and, for synchronising calls, timings.
+ */
+cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                              float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse,
+                              const cqsa_options* opt, cqsa_plan_info* info);
+
+/*
+ * cqsa_plan: the plan cqsa_attention_ex would run, without running it or
+ * allocating (the dry run of the pages' estimate(): stream-cqsa 2.2.2 -> 2.2.3
+ * diff, README.md section "Use").  Tensor data may be NULL; then each tensor's
+ * `where` must say DEVICE or HOST.  With mem_budget > 0, explicit `where` values
+ * and opt->num_cus > 0 the call makes no HIP call at all.
+ */
+cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                      uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
+                      cqsa_plan_info* info);
+
+/*
+ * cqsa_fwd_partial: the partial triple of one KV chunk, for every query row.
+ *   q, k, v            device tensors as above.
+ *   kv_begin, kv_end   the key range [kv_begin, kv_end) of the chunk (0 <= begin <= end <= Nk).
+ *   o_part             fp32 [B, Hq, Nq, D] contiguous: sum over visible keys in the range of
+ *                      exp(s - m) v (unnormalised).
+ *   ml_part            fp32 [B, Hq, Nq, 2] contiguous: (m, l), m in natural-log units of the
+ *                      scaled logits.  A row with no visible key in the range gets the identity
+ *                      (O = 0, m = -inf, l = 0).
+ *   stream             hipStream_t or NULL.  Stream-ordered; returns without waiting.
+ */
+cqsa_status cqsa_fwd_partial(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                             float scale, int64_t kv_begin, int64_t kv_end, float* o_part, float* ml_part,
+                             void* stream);
+
+/*
+ * cqsa_lse_merge: exact log-sum-exp merge of num_parts partial triples, row by row:
+ *   m = max_p m_p,  w_p = exp(m_p - m) (0 when m_p = -inf),  l = sum_p w_p l_p,
+ *   O = sum_p w_p O_p.  Empty partials (m = -inf) are identities and never give NaN.
+ *   o_parts[p]   device fp32 [rows, D];  ml_parts[p]  device fp32 [rows, 2] (m, l).
+ *                The two pointer arrays themselves are host arrays of num_parts entries
+ *                (1 <= num_parts <= 64).
+ *   o_out, ml_out  device fp32 [rows, D] / [rows, 2]; may be the same memory as part 0.
+ *   D            64 or 128.
+ * Stream-ordered; returns without waiting.
+ */
+cqsa_status cqsa_lse_merge(const float* const* o_parts, const float* const* ml_parts, int32_t num_parts,
+                           int64_t rows, int64_t D, float* o_out, float* ml_out, void* stream);
+
+/*
+ * cqsa_finalize: deliver a merged triple: out = O / l rounded to out's dtype, and
+ * lse = m + ln(l).
+ *   o     device fp32 [B, Hq, Nq, D] contiguous (B, Hq, Nq, D taken from out's shape).
+ *   ml    device fp32 [B, Hq, Nq, 2] contiguous.
+ *   out   device tensor, any strides (stride[3] == 1); lse NULL or device fp32 [B, Hq, Nq].
+ * A row with l = 0 (no visible key) gets out = 0 and lse = -inf.
+ */
+cqsa_status cqsa_finalize(const float* o, const float* ml, cqsa_tensor* out, float* lse, void* stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* cqsa_last_error(void);
+
+/* CQSA_ABI_VERSION of the built library. */
+int32_t cqsa_version(void);
+
+/* sizeof of the ABI structs, for bindings to check their layout:
+ * 0 = cqsa_tensor, 1 = cqsa_options, 2 = cqsa_plan_info; 0 for other values. */
+uint64_t cqsa_struct_size(int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CQSA_H */

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports what include/cqsa.h declares, its structs
+match the binding, and the planner (pure host logic) sizes chunks, skips causal chunks and rejects
+impossible budgets.  No compute call is made here."""
+import ctypes
+import importlib.util
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cqsa.h")
+GB = 10**9
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cqsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    import exact_long_context_cqsa_amd as m
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(m.library_path())
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    nm = subprocess.run(["nm", "-D", "--defined-only", m.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (cqsa_\w+)", nm))
+    assert set(names) <= exported
+
+
+def test_struct_layout_and_version():
+    import exact_long_context_cqsa_amd as m
+    lib = m._lib
+    assert lib.cqsa_version() == 1
+    assert lib.cqsa_struct_size(0) == ctypes.sizeof(m.CqsaTensor) == 80
+    assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions)
+    assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo)
+    assert lib.cqsa_struct_size(7) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without libcqsa.so the package refuses to import: there is no CPU fallback."""
+    src = os.path.join(ROOT, "exact_long_context_cqsa_amd")
+    dst = tmp_path / "exact_long_context_cqsa_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    spec = importlib.util.spec_from_file_location("cqsa_copy", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError, match="not built"):
+        spec.loader.exec_module(mod)
+
+
+def plan(q, k, v, causal, budget, where=None, **kw):
+    import exact_long_context_cqsa_amd as m
+    return m.plan(q, k, v, causal, budget, where=where or {}, num_cus=256, **kw)
+
+
+def shp(B, H, N, D, dt=torch.float16):
+    return ((B, H, N, D), dt)
+
+
+def test_plan_streamed_4m_context():
+    """4,194,304 tokens, 8 heads, D=64 in pinned host memory under a 16e9-byte budget: Q must be cut in
+    two, every KV chunk streams once per Q chunk that sees it, and the plan stays inside 85% of the budget."""
+    s = shp(1, 8, 4194304, 64)
+    host = {"q": "host", "k": "host", "v": "host", "out": "host"}
+    p = plan(s, s, s, True, 16 * GB, where=host)
+    assert p["streamed"] == 1 and p["merge_mode"] == 2
+    assert p["n_q_chunks"] == 2 and p["q_chunk"] == 2097152
+    assert p["workspace_bytes"] <= p["budget_bytes"] == int(16 * GB * 0.85)
+    # H2D: Q once (4 GiB) + KV prefix for each Q chunk (K+V: 4 GiB, then 8 GiB)
+    assert p["h2d_bytes"] == 16 * 2**30
+    assert p["d2h_bytes"] == 4 * 2**30
+    kv = p["kv_chunk"]
+    assert p["chunk_pairs"] == -(-2097152 // kv) + -(-4194304 // kv)
+
+
+def test_plan_forced_splits():
+    s = shp(1, 1, 1024, 64)
+    p = plan(s, s, s, True, 16 * GB, kv_chunk=256)
+    assert (p["n_kv_chunks"], p["chunk_pairs"], p["merges"], p["merge_mode"]) == (4, 4, 3, 1)
+    s2 = shp(1, 8, 32768, 64)
+    p2 = plan(s2, s2, s2, True, 16 * GB, kv_chunk=4096)
+    assert (p2["n_kv_chunks"], p2["chunk_pairs"], p2["merges"]) == (8, 8, 7)
+    p3 = plan(s2, s2, s2, True, 16 * GB)
+    assert (p3["chunk_pairs"], p3["merges"], p3["workspace_bytes"], p3["kernel_launches"]) == (1, 0, 0, 1)
+    # causal skipping with Q chunks: chunk pairs above the diagonal are not scheduled
+    p4 = plan(s2, s2, s2, True, 16 * GB, kv_chunk=4096, q_chunk=4096)
+    assert p4["chunk_pairs"] == sum(range(1, 9))
+    p5 = plan(s2, s2, s2, False, 16 * GB, kv_chunk=4096, q_chunk=4096)
+    assert p5["chunk_pairs"] == 64
+
+
+def test_plan_split_kv_when_few_query_tiles():
+    q = shp(1, 4, 256, 128, torch.bfloat16)
+    kv = shp(1, 1, 131072, 128, torch.bfloat16)
+    p = plan(q, kv, kv, True, 16 * GB)
+    assert p["kv_splits"] > 1 and p["merge_mode"] == 1
+    p1 = plan(q, kv, kv, True, 16 * GB, kv_splits=1)
+    assert p1["kv_splits"] == 1 and p1["workspace_bytes"] == 0
+
+
+def test_plan_errors():
+    import exact_long_context_cqsa_amd as m
+    s = shp(1, 8, 4194304, 64)
+    host = {"q": "host", "k": "host", "v": "host", "out": "host"}
+    with pytest.raises(m.CqsaError, match="BUDGET.*needs"):
+        plan(s, s, s, True, 10_000, where=host)
+    with pytest.raises(m.CqsaError, match="UNSUPPORTED"):
+        plan(shp(1, 2, 64, 96), shp(1, 2, 64, 96), shp(1, 2, 64, 96), False, GB)
+    with pytest.raises(m.CqsaError, match="INVALID"):
+        plan(shp(1, 3, 64, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), False, GB)
+    with pytest.raises(m.CqsaError, match="INVALID"):
+        plan(shp(1, 2, 65, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), True, GB)
+    with pytest.raises(m.CqsaError, match="BUDGET"):
+        plan(shp(1, 2, 64, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), True, 1000, kv_chunk=16)
+
+
+def test_plan_budget_monotone():
+    """A larger budget never gives more Q chunks or smaller KV chunks."""
+    s = shp(1, 8, 1 << 20, 64)
+    host = {"q": "host", "k": "host", "v": "host", "out": "host"}
+    prev = None
+    for gb in (1, 2, 4, 8, 16, 32):
+        p = plan(s, s, s, True, gb * GB, where=host)
+        assert p["workspace_bytes"] <= p["budget_bytes"]
+        if prev:
+            assert p["n_q_chunks"] <= prev["n_q_chunks"]
+            if p["n_q_chunks"] == prev["n_q_chunks"]:
+                assert p["kv_chunk"] >= prev["kv_chunk"]
+        prev = p

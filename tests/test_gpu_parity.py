@@ -1,0 +1,315 @@
+"""GPU parity: the HIP library (through its C ABI) against the FP64 oracle on the same seeded inputs.
+
+Small problems are compared element by element; the large measured shapes are compared on sampled
+rows (first/last rows, rows around chunk and tile edges, seeded random rows in every head).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity_util import compare, reference, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def cqsa():
+    import exact_long_context_cqsa_amd as m
+    return m
+
+
+def say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed, sigma=1.0):
+    q = synth.normal((B, Hq, Nq, D), seed=seed, tensor_id=0, sigma=sigma, dtype=dtype)
+    k = synth.normal((B, Hkv, Nk, D), seed=seed, tensor_id=1, sigma=sigma, dtype=dtype)
+    v = synth.normal((B, Hkv, Nk, D), seed=seed, tensor_id=2, dtype=dtype)
+    return q, k, v
+
+
+SMALL = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal
+    (1, 1, 1, 1024, 1024, 64, torch.float16, True),
+    (1, 2, 2, 300, 300, 64, torch.float16, True),        # ragged query and key tails
+    (2, 3, 3, 77, 513, 64, torch.float16, False),        # non-causal, Nq < Nk
+    (1, 2, 2, 700, 129, 64, torch.bfloat16, False),      # non-causal, Nq > Nk
+    (1, 4, 1, 257, 1000, 128, torch.bfloat16, True),     # GQA 4:1, bottom-right causal
+    (2, 8, 2, 130, 130, 128, torch.float16, True),       # GQA, square causal
+    (1, 2, 2, 1, 1, 64, torch.float16, True),            # one query, one key
+    (1, 2, 2, 1, 4099, 128, torch.float16, True),        # one query at the end of 4099 keys
+    (1, 1, 1, 64, 64, 64, torch.bfloat16, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"B{c[0]}H{c[1]}x{c[2]}q{c[3]}k{c[4]}d{c[5]}"
+                         f"{'f16' if c[6] == torch.float16 else 'bf16'}{'c' if c[7] else 'n'}")
+def test_small_full_parity(case):
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal = case
+    say("small", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=1000 + Nq + Nk + D)
+    scale = 1.0 / math.sqrt(D)
+    ref = reference(q, k, v, causal=causal, scale=scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    compare(out, lse, ref, dtype, label=f"mono {case}")
+    # a forced split (LSE merges) in both merge modes, and forced Q chunks
+    for kw in ({"kv_chunk": 96, "merge": 1}, {"kv_chunk": 200, "merge": 2}, {"kv_chunk": 128, "q_chunk": 100}):
+        out2, lse2 = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True, **kw)
+        torch.cuda.synchronize()
+        compare(out2, lse2, ref, dtype, label=f"{kw} {case}")
+
+
+def test_config1_four_kv_chunks_merged():
+    """1024 causal rows, D=64, fp16, KV chunk 256: each Q block folds its visible chunks by LSE."""
+    w = synth.workload(0)
+    say("workload", w.name)
+    q, k, v, _ = synth.make_inputs(w)
+    ref = reference(q, k, v, causal=True, scale=w.scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for merge in (1, 2):
+        out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=256, merge=merge,
+                                          out_dtype=torch.float32, return_lse=True, return_info=True)
+        torch.cuda.synchronize()
+        assert info["n_kv_chunks"] == 4 and info["chunk_pairs"] == 4 and info["merges"] == 3
+        compare(out, lse, ref, torch.float16, label=f"config1 merge={merge}")
+    # the default output dtype is the input's
+    out16 = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=256)
+    assert out16.dtype == torch.float16
+    compare(out16, None, ref, torch.float16, label="config1 fp16 out")
+
+
+def test_fwd_partial_matches_oracle_partial():
+    q, k, v = gen(1, 2, 1, 200, 333, 64, torch.float16, seed=7)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for lo, hi in ((0, 333), (50, 150), (10, 10), (300, 333), (0, 1)):
+        say("partial", lo, hi)
+        o, ml = cqsa().fwd_partial(qd, kd, vd, is_causal=True, scale=0.125, kv_begin=lo, kv_end=hi)
+        torch.cuda.synchronize()
+        ref = reference(q, k, v, causal=True, scale=0.125)  # normalised, for the O scale
+        part = __import__("oracle").attention_rows(q, k, v, causal=True, scale=0.125, key_range=(lo, hi),
+                                                   partial=True)
+        m = ml[..., 0].reshape(-1).double().cpu().numpy()
+        l = ml[..., 1].reshape(-1).double().cpu().numpy()
+        oo = o.reshape(-1, 64).double().cpu().numpy()
+        empty = part["l"] == 0
+        assert np.all(np.isneginf(m[empty])) and np.all(l[empty] == 0) and np.all(oo[empty] == 0)
+        ne = ~empty
+        if ne.any():
+            # compare the normalised partial and its lse, which do not depend on the choice of m
+            np.testing.assert_allclose(oo[ne] / l[ne, None], part["o"][ne] / part["l"][ne, None], atol=4e-3, rtol=0)
+            lse_g = m[ne] + np.log(l[ne])
+            lse_r = part["m"][ne] + np.log(part["l"][ne])
+            assert np.max(np.abs(lse_g - lse_r) / np.maximum(1, np.abs(lse_r))) < 1e-4
+        del ref
+
+
+def test_lse_merge_kernel_matches_oracle_merge():
+    rng = np.random.default_rng(3)
+    rows, D = 1000, 128
+    parts64 = []
+    for p in range(3):
+        m = rng.normal(0, 5, rows)
+        m[rng.random(rows) < 0.2] = -np.inf                  # identities
+        l = np.where(np.isinf(m), 0.0, rng.uniform(1, 50, rows))
+        o = np.where(np.isinf(m)[:, None], 0.0, rng.normal(0, 3, (rows, D)))
+        parts64.append({"o": o.astype(np.float32).astype(np.float64), "m": m.astype(np.float32).astype(np.float64),
+                        "l": l.astype(np.float32).astype(np.float64)})
+    oracle = __import__("oracle")
+    want = oracle.merge(oracle.merge(parts64[0], parts64[1]), parts64[2])
+    dev_parts = [(torch.from_numpy(p["o"]).float().to(DEV),
+                  torch.from_numpy(np.stack([p["m"], p["l"]], 1)).float().to(DEV)) for p in parts64]
+    o, ml = cqsa().lse_merge(dev_parts)
+    torch.cuda.synchronize()
+    got_m = ml[:, 0].double().cpu().numpy()
+    got_l = ml[:, 1].double().cpu().numpy()
+    got_o = o.double().cpu().numpy()
+    empty = want["l"] == 0
+    assert np.all(np.isneginf(got_m[empty])) and np.all(got_l[empty] == 0) and not np.isnan(got_o).any()
+    ne = ~empty
+    # the merged m is the max; compare o/l and lse
+    np.testing.assert_allclose(got_o[ne] / got_l[ne, None], want["o"][ne] / want["l"][ne, None], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(got_m[ne] + np.log(got_l[ne]), want["m"][ne] + np.log(want["l"][ne]), rtol=1e-6,
+                               atol=1e-5)
+    # in place: output aliases part 0
+    o0, ml0 = dev_parts[0][0].clone(), dev_parts[0][1].clone()
+    cqsa().lse_merge([(o0, ml0), dev_parts[1], dev_parts[2]], out=(o0, ml0))
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o) and torch.equal(ml0, ml)
+
+
+def test_finalize():
+    rng = np.random.default_rng(4)
+    B, H, N, D = 2, 3, 50, 64
+    o = torch.from_numpy(rng.normal(0, 1, (B, H, N, D))).float()
+    m = torch.from_numpy(rng.normal(0, 1, (B, H, N))).float()
+    l = torch.from_numpy(rng.uniform(0.5, 9, (B, H, N))).float()
+    ml = torch.stack([m, l], -1)
+    out, lse = cqsa().finalize(o.to(DEV), ml.to(DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    torch.testing.assert_close(out.cpu(), o / l[..., None], rtol=1e-6, atol=1e-6)
+    torch.testing.assert_close(lse.cpu(), m + torch.log(l), rtol=1e-6, atol=1e-6)
+
+
+def test_config2_monolithic_and_8way_split_agree():
+    """B=1, H=8, N=32768, D=64 causal fp16: one pass, and a forced split into 8 KV chunks."""
+    w = synth.workload(1)
+    say("workload", w.name)
+    q, k, v, _ = synth.make_inputs(w)
+    rows = sample_rows(1, 8, w.Nq, seed=2, n_random=96, edge=32, boundaries=range(0, w.Nq, 4096))
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    mono, lse_m = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True)
+    split, lse_s, info = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, out_dtype=torch.float32,
+                                          return_lse=True, return_info=True)
+    torch.cuda.synchronize()
+    assert info["n_kv_chunks"] == 8 and info["chunk_pairs"] == 8
+    r1 = compare(mono, lse_m, ref, torch.float16, rows=rows, label="config2 mono")
+    r2 = compare(split, lse_s, ref, torch.float16, rows=rows, label="config2 split")
+    agree = (mono - split).abs().max().item()
+    say("config2", r1, r2, "max|mono-split|", agree)
+    assert agree <= 1e-3
+    # fused merges give the same answer
+    fused = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, merge=2, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (fused - split).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("nk", [8192, 32768, 131072])
+def test_config3_prompt_gqa(nk):
+    """2048 queries at the end of the context, 32 query heads over 8 KV heads, D=128, bf16."""
+    w = synth.workload(2, nk=nk)
+    say("workload", w.name)
+    q, k, v, _ = synth.make_inputs(w)
+    rows = sample_rows(1, 32, 2048, seed=3, n_random=24, edge=8, boundaries=range(0, 2048, 128),
+                       heads=range(0, 32, 3))
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True,
+                                      return_info=True)
+    torch.cuda.synchronize()
+    say("config3", nk, info["kv_splits"], compare(out, lse, ref, torch.bfloat16, rows=rows, label=f"config3 {nk}"))
+    # split-KV across the GPU merges to the same answer
+    out2, lse2 = cqsa().attention(qd, kd, vd, is_causal=True, kv_splits=4, out_dtype=torch.float32,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    compare(out2, lse2, ref, torch.bfloat16, rows=rows, label=f"config3 {nk} splits=4")
+
+
+def test_config5_softmax_stress_reduced():
+    """Large logits (N(0, 9^2)) with +20 spikes on 5% of keys, uniform v, non-causal, bf16, KV chunk
+    16384; the batch, heads and length are cut so the reference runs in seconds."""
+    w = synth.workload(4)
+    say("workload", w.name, "reduced")
+    q, k, v, pos = synth.make_inputs(w, nq=2048, nk=65536, batch=2, heads=(2, 2))
+    rows = sample_rows(2, 2, 2048, seed=5, n_random=48, edge=16)
+    ref = reference(q, k, v, causal=False, scale=w.scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=False, kv_chunk=16384, out_dtype=torch.float32,
+                                      return_lse=True, return_info=True)
+    torch.cuda.synchronize()
+    assert info["n_kv_chunks"] == 4
+    say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 reduced"))
+
+
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+def test_streamed_from_pinned_host(layout):
+    """Host-resident q/k/v/out under a small budget: the planner must chunk Q and KV."""
+    B, Hq, Hkv, N, D = 1, 4, 2, 6000, 64
+    q, k, v = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=44)
+    ref = reference(q, k, v, causal=True, scale=0.125)
+
+    def host(t):
+        if layout == "bhnd":
+            h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+        else:
+            h = torch.empty((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), dtype=t.dtype,
+                            pin_memory=True).transpose(1, 2)
+        h.copy_(t)
+        return h
+
+    qh, kh, vh = host(q), host(k), host(v)
+    out = host(torch.zeros(B, Hq, N, D, dtype=torch.float32))
+    budget = 2_000_000
+    say("streamed", layout)
+    o, lse, info = cqsa().attention(qh, kh, vh, is_causal=True, mem_budget=budget, out=out, return_lse=True,
+                                    return_info=True)
+    assert info["streamed"] == 1 and info["n_q_chunks"] > 1 and info["n_kv_chunks"] > 1
+    assert info["workspace_bytes"] <= budget * 0.85
+    assert o.data_ptr() == out.data_ptr() and not o.is_cuda
+    compare(o, lse, ref, torch.float16, label=f"streamed {layout}")
+    # the resident call gives the same numbers up to the merge order
+    od = cqsa().attention(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (od.cpu() - o).abs().max().item() <= 1e-3
+
+
+def test_mixed_residency_device_q_host_kv():
+    q, k, v = gen(1, 2, 2, 3000, 5000, 128, torch.bfloat16, seed=45)
+    ref = reference(q, k, v, causal=True, scale=1 / math.sqrt(128))
+    kh, vh = k.pin_memory(), v.pin_memory()
+    out, lse, info = cqsa().attention(q.to(DEV), kh, vh, is_causal=True, mem_budget=12_000_000,
+                                      out_dtype=torch.float32, return_lse=True, return_info=True)
+    assert info["streamed"] == 1 and out.is_cuda
+    compare(out, lse, ref, torch.bfloat16, label="device q, host kv")
+
+
+def test_deterministic():
+    q, k, v = gen(1, 4, 4, 2000, 2000, 64, torch.float16, seed=46)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=512)
+    b = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=512)
+    c = cqsa().attention(qd, kd, vd, is_causal=True)
+    d = cqsa().attention(qd, kd, vd, is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_q_zero_gives_mean_of_visible_values():
+    """q = 0: every probability is exactly 1, so row i is the mean of its visible values."""
+    Nq, Nk = 100, 300
+    _, k, v = gen(1, 2, 2, Nq, Nk, 64, torch.float16, seed=47)
+    q = torch.zeros(1, 2, Nq, 64, dtype=torch.float16)
+    out, lse = cqsa().attention(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True, out_dtype=torch.float32,
+                                return_lse=True)
+    torch.cuda.synchronize()
+    for i in (0, 1, 50, 99):
+        cnt = Nk - Nq + i + 1
+        torch.testing.assert_close(out[:, :, i].cpu().double(), v[:, :, :cnt].double().mean(2), rtol=0, atol=1e-5)
+        torch.testing.assert_close(lse[:, :, i].cpu().double(), torch.full((1, 2), math.log(cnt), dtype=torch.float64),
+                                   rtol=0, atol=1e-5)
+
+
+def test_strided_device_inputs():
+    q, k, v = gen(2, 4, 2, 333, 333, 64, torch.bfloat16, seed=48)
+    ref = reference(q, k, v, causal=True, scale=0.125)
+    tm = lambda t: t.transpose(1, 2).contiguous().transpose(1, 2).to(DEV)   # [B,N,H,D] storage
+    out, lse = cqsa().attention(tm(q), tm(k), tm(v), is_causal=True, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    compare(out, lse, ref, torch.bfloat16, label="token-major device inputs")
+
+
+def test_errors():
+    m = cqsa()
+    q, k, v = gen(1, 2, 2, 64, 64, 64, torch.float16, seed=49)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    with pytest.raises(m.CqsaError, match="INVALID.*pinned"):
+        m.attention(q, k, v, is_causal=True, out=torch.empty(1, 2, 64, 64, dtype=torch.float16, device=DEV))
+    with pytest.raises(m.CqsaError, match="UNSUPPORTED"):
+        m.attention(qd[..., :32].contiguous(), kd[..., :32].contiguous(), vd[..., :32].contiguous())
+    with pytest.raises(m.CqsaError, match="INVALID"):
+        m.attention(torch.cat([qd, qd[:, :1]], 1), kd, vd)           # 3 query heads over 2
+    with pytest.raises(m.CqsaError, match="INVALID"):
+        m.attention(torch.cat([qd, qd], 2), kd, vd, is_causal=True)  # causal Nq > Nk
+    with pytest.raises(m.CqsaError, match="BUDGET"):
+        m.attention(q.pin_memory(), k.pin_memory(), v.pin_memory(), mem_budget=1000)
+    # empty query set: nothing to do, no error
+    e = m.attention(qd[:, :, :0], kd, vd, is_causal=True)
+    assert e.shape == (1, 2, 0, 64)
