@@ -21,6 +21,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "cqsa_internal.h"
 
@@ -36,9 +37,6 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKT = 64;       // keys per LDS tile
-constexpr int kWaves = 4;     // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.693147180559945309417f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -100,19 +98,38 @@ __device__ __forceinline__ int vslot(int j) {
     return (j & ~15) + (((o >> 2) & 1) << 3) + (o & 3) + ((o >> 3) << 2);
 }
 
-template <int D, int DT, int QB>
-__global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts: 32-bit data format,
+// no swizzle.  Loads at or past num_records bytes return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A buffer resource covering rows [j0, j0 + nvalid) of a K or V view with row stride sn (elements):
+// rows at or past nvalid read as zero, so the ragged end of a key range needs no branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t sn, int64_t j0,
+                                                            int64_t nvalid, int D) {
+    const uint16_t* p = base + j0 * sn;
+    const uint32_t bytes = nvalid > 0 ? (uint32_t)((nvalid - 1) * sn * 2 + (int64_t)D * 2) : 0u;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// D: head dim; DT: fp16/bf16; QB: 32-row query blocks per wave; NW: waves per workgroup;
+// KT: keys per LDS tile.
+template <int D, int DT, int QB, int NW, int KT>
+__global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
+    constexpr int NT = NW * 64;
     constexpr int QW = 32 * QB;                            // query rows per wave
-    constexpr int BM = kWaves * QW;                        // query rows per workgroup
+    constexpr int BM = NW * QW;                            // query rows per workgroup
     constexpr int KS = D + 8;                              // K tile row stride (elements): 16 B pad
-    constexpr int VS = kKT + 8;                            // V^T tile row stride (elements): 16 B pad
-    constexpr int KTILE = kKT * KS;
+    constexpr int VS = KT + 8;                             // V^T tile row stride (elements): 16 B pad
+    constexpr int KTILE = KT * KS;
     constexpr int STAGE = KTILE + D * VS;
-    constexpr int KCH = kKT * (D / 8) / kThreads;          // 16-byte K pieces per thread and tile
-    constexpr int VCH = (kKT / 2) * (D / 8) / kThreads;    // (key pair x 8 dims) V pieces per thread
+    constexpr int KITEMS = KT * (D / 8);                   // 16-byte K pieces per tile
+    constexpr int VITEMS = (KT / 2) * (D / 8);             // (key pair x 8 dims) V pieces per tile
+    constexpr int KCH = (KITEMS + NT - 1) / NT;
+    constexpr int VCH = (VITEMS + NT - 1) / NT;
+    constexpr int NKB = KT / 32;                           // 32-key score blocks per tile
+    constexpr int NPK = KT / 16;                           // 16-key steps of the PV product
     constexpr int NDB = D / 32;
     constexpr int NDK = D / 16;
-    static_assert(KCH >= 1 && VCH >= 1, "tile split");
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
 
@@ -141,11 +158,12 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
     const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
     int64_t khi = min(a.k_hi, klo + a.split_len);
     if (a.causal) khi = min(khi, i_end + a.causal_delta);  // the last row sees keys <= i_end - 1 + delta
-    const int ntiles = khi > klo ? (int)((khi - klo + kKT - 1) / kKT) : 0;
+    const int ntiles = khi > klo ? (int)((khi - klo + KT - 1) / KT) : 0;
 
     const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
     const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
     const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
 
     // ---- Q fragments, the B operand of S^T = K Q^T
     u32x4 qf[QB][NDK];
@@ -153,10 +171,11 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
         const int64_t row = iw0 + qb * 32 + l32;
         const bool ok = row < i_end;
-        const uint16_t* p = qp + row * a.q_sn + 8 * hi;
+        const uint16_t* p = qp + (ok ? row : 0) * a.q_sn + 8 * hi;
 #pragma unroll
         for (int t = 0; t < NDK; ++t) {
-            qf[qb][t] = ok ? *reinterpret_cast<const u32x4*>(p + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * t);
+            qf[qb][t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
         }
     }
 
@@ -174,21 +193,26 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
     u32x4 kreg[KCH];
     u32x4 vreg[VCH][2];
     auto load_tile = [&](int64_t j0) {
+        const int64_t nvalid = min(khi - j0, (int64_t)KT);
+        const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, k_sn, j0, nvalid, D);
+        const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, v_sn, j0, nvalid, D);
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / (D / 8), col8 = idx % (D / 8);
-            const int64_t j = j0 + row;
-            kreg[c] = j < khi ? *reinterpret_cast<const u32x4*>(kp + j * a.k_sn + col8 * 8) : u32x4{0u, 0u, 0u, 0u};
+            const int idx = tid + c * NT;
+            if (KITEMS % NT == 0 || idx < KITEMS) {
+                const int row = idx / (D / 8), col8 = idx % (D / 8);
+                kreg[c] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)((row * k_sn + col8 * 8) * 2), 0, 0);
+            }
         }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
-            const int idx = tid + c * kThreads;
-            const int pr = idx % (kKT / 2), col8 = idx / (kKT / 2);
-            const int64_t j = j0 + 2 * pr;
-            vreg[c][0] = j < khi ? *reinterpret_cast<const u32x4*>(vp + j * a.v_sn + col8 * 8) : u32x4{0u, 0u, 0u, 0u};
-            vreg[c][1] = j + 1 < khi ? *reinterpret_cast<const u32x4*>(vp + (j + 1) * a.v_sn + col8 * 8)
-                                     : u32x4{0u, 0u, 0u, 0u};
+            const int idx = tid + c * NT;
+            if (VITEMS % NT == 0 || idx < VITEMS) {
+                const int pr = idx % (KT / 2), col8 = idx / (KT / 2);
+                const int off = (int)((2 * pr * v_sn + col8 * 8) * 2);
+                vreg[c][0] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+                vreg[c][1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + (int)(v_sn * 2), 0, 0);
+            }
         }
     };
     auto store_tile = [&](int s) {
@@ -196,20 +220,25 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
         uint16_t* vs = ks + KTILE;
 #pragma unroll
         for (int c = 0; c < KCH; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / (D / 8), col8 = idx % (D / 8);
-            *reinterpret_cast<u32x4*>(ks + row * KS + col8 * 8) = kreg[c];
+            const int idx = tid + c * NT;
+            if (KITEMS % NT == 0 || idx < KITEMS) {
+                const int row = idx / (D / 8), col8 = idx % (D / 8);
+                *reinterpret_cast<u32x4*>(ks + row * KS + col8 * 8) = kreg[c];
+            }
         }
 #pragma unroll
         for (int c = 0; c < VCH; ++c) {
-            const int idx = tid + c * kThreads;
-            const int pr = idx % (kKT / 2), col8 = idx / (kKT / 2);
-            const int slot = vslot(2 * pr);
+            const int idx = tid + c * NT;
+            if (VITEMS % NT == 0 || idx < VITEMS) {
+                const int pr = idx % (KT / 2), col8 = idx / (KT / 2);
+                const int slot = vslot(2 * pr);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t w0 = vreg[c][0][e >> 1], w1 = vreg[c][1][e >> 1];
-                const uint32_t word = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
-                *reinterpret_cast<uint32_t*>(vs + (col8 * 8 + e) * VS + slot) = word;
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w0 = vreg[c][0][e >> 1], w1 = vreg[c][1][e >> 1];
+                    const uint32_t word =
+                        (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+                    *reinterpret_cast<uint32_t*>(vs + (col8 * 8 + e) * VS + slot) = word;
+                }
             }
         }
     };
@@ -222,53 +251,60 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
 
     for (int it = 0; it < ntiles; ++it) {
         const int s = it & 1;
-        const int64_t j0 = klo + (int64_t)it * kKT;
-        if (it + 1 < ntiles) load_tile(j0 + kKT);
+        const int64_t j0 = klo + (int64_t)it * KT;
+        if (it + 1 < ntiles) load_tile(j0 + KT);
 
         const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + a.causal_delta);
         if (active) {
             const uint16_t* ks = lds + s * STAGE;
             const uint16_t* vs = ks + KTILE;
 
-            // S^T for 64 keys x QW queries
-            f32x16 sacc[2][QB];
+            // S^T for KT keys x QW queries
+            f32x16 sacc[NKB][QB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = f32x16{};
 #pragma unroll
             for (int t = 0; t < NDK; ++t) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     const u32x4 af = *reinterpret_cast<const u32x4*>(ks + (kb * 32 + l32) * KS + 16 * t + 8 * hi);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) sacc[kb][qb] = mfma32<DT>(af, qf[qb][t], sacc[kb][qb]);
                 }
             }
 
-            // mask keys past the range end and, on diagonal tiles, keys after the query
-            const bool need_mask = (j0 + kKT > khi) || (a.causal && (j0 + kKT - 1 > iw0 + a.causal_delta));
+            // mask keys past the range end and, on diagonal tiles, keys after the query:
+            // key offset t in the tile is visible to this lane's row iff t < lim
+            const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + a.causal_delta));
             if (need_mask) {
+                const int lim_range = (int)min(khi - j0, (int64_t)KT);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
+                for (int qb = 0; qb < QB; ++qb) {
+                    int lim = lim_range;
+                    if (a.causal) {
                         const int64_t row = iw0 + qb * 32 + l32;
+                        const int64_t c = row + a.causal_delta - j0 + 1;
+                        lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int64_t j = j0 + kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
-                            if (j >= khi || (a.causal && j > row + a.causal_delta)) sacc[kb][qb][r] = -INFINITY;
+                            const int t = kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                            if (t >= lim) sacc[kb][qb][r] = -INFINITY;
                         }
-                    }
+                }
             }
 
             // online softmax (base 2: scale * log2(e) folded into one multiply-add)
-            u32x4 pf[QB][4];
+            u32x4 pf[QB][NPK];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -277,7 +313,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
                 const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - muse);
                 float rs = 0.f;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], a.scale_log2, -muse));
@@ -291,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
                     for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
                 }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int t = 0; t < NPK; ++t) {
                     const int kb = t >> 1, u = t & 1;
                     f32x8 x;
 #pragma unroll
@@ -304,7 +340,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const FwdArgs a) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int t = 0; t < NPK; ++t) {
                     const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + (db * 32 + l32) * VS + 16 * t + 8 * hi);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32<DT>(vf, pf[qb][t], oacc[qb][db]);
@@ -417,26 +453,65 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
     }
 }
 
-template <int D, int DT, int QB>
+template <int D, int DT, int QB, int NW, int KT>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_kernel<D, DT, QB>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, DT, QB, NW, KT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-constexpr int qb_for(int D) { return D == 64 ? 2 : 1; }
+// Tile shapes (query blocks per wave, waves per workgroup, keys per tile), per head dim.  Variant 0 is
+// the default; CQSA_FWD_VARIANT picks another one for measurement.
+struct Shape {
+    int qb, nw, kt;
+};
+constexpr Shape kShapes64[] = {{1, 8, 128}, {1, 8, 64}, {2, 4, 64}, {1, 4, 64}};
+constexpr Shape kShapes128[] = {{1, 8, 64}, {1, 8, 128}, {1, 4, 64}, {1, 4, 128}};
+
+int variant() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("CQSA_FWD_VARIANT");
+        v = (e && *e) ? atoi(e) : 0;
+        if (v < 0 || v > 3) v = 0;
+    }
+    return v;
+}
+
+template <int D, int DT>
+hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+    const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
+#define CQSA_SHAPE(QB_, NW_, KT_) \
+    if (sh.qb == QB_ && sh.nw == NW_ && sh.kt == KT_) return launch_fwd_t<D, DT, QB_, NW_, KT_>(a, st)
+    if constexpr (D == 64) {
+        CQSA_SHAPE(1, 8, 128);
+        CQSA_SHAPE(1, 8, 64);
+        CQSA_SHAPE(2, 4, 64);
+        CQSA_SHAPE(1, 4, 64);
+    } else {
+        CQSA_SHAPE(1, 8, 64);
+        CQSA_SHAPE(1, 8, 128);
+        CQSA_SHAPE(1, 4, 64);
+        CQSA_SHAPE(1, 4, 128);
+    }
+#undef CQSA_SHAPE
+    return hipErrorInvalidValue;
+}
 
 }  // namespace
 
-int fwd_block_m(int D) { return kWaves * 32 * qb_for(D); }
+int fwd_block_m(int D) {
+    const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
+    return sh.nw * 32 * sh.qb;
+}
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
-    if (D == 64 && dtype == ET_F16) return launch_fwd_t<64, ET_F16, qb_for(64)>(a, stream);
-    if (D == 64 && dtype == ET_BF16) return launch_fwd_t<64, ET_BF16, qb_for(64)>(a, stream);
-    if (D == 128 && dtype == ET_F16) return launch_fwd_t<128, ET_F16, qb_for(128)>(a, stream);
-    if (D == 128 && dtype == ET_BF16) return launch_fwd_t<128, ET_BF16, qb_for(128)>(a, stream);
+    if (D == 64 && dtype == ET_F16) return launch_d<64, ET_F16>(a, stream);
+    if (D == 64 && dtype == ET_BF16) return launch_d<64, ET_BF16>(a, stream);
+    if (D == 128 && dtype == ET_F16) return launch_d<128, ET_F16>(a, stream);
+    if (D == 128 && dtype == ET_BF16) return launch_d<128, ET_BF16>(a, stream);
     return hipErrorInvalidValue;
 }
 
