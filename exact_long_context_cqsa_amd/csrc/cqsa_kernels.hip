@@ -98,6 +98,97 @@ __device__ __forceinline__ int vslot(int j) {
     return (j & ~15) + (((o >> 2) & 1) << 3) + (o & 3) + ((o >> 3) << 2);
 }
 
+// Row maximum / sum of a lane's NKB x 16 score registers with 8 independent partial chains, so the
+// reduction is not one long dependency chain (two waves per SIMD cannot hide its latency).
+template <int NKB>
+__device__ __forceinline__ float lane_max(const f32x16 (&s)[NKB]) {
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m[(kb * 16 + r) & 7] = fmaxf(m[(kb * 16 + r) & 7], s[kb][r]);
+    return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
+}
+
+// p = 2^(s * c - mu) in place, returning the lane's sum of p (8 partial sums).
+template <int NKB>
+__device__ __forceinline__ float lane_exp_sum(f32x16 (&s)[NKB], float c, float mu) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mu));
+            s[kb][r] = p;
+            acc[(kb * 16 + r) & 7] += p;
+        }
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+// Online softmax of one key tile for one 32-row query block (lane = one row, NKB x 16 of its keys).
+// The running shift m (base 2) is kept while no probability of the tile exceeds 2^8: then
+// p = 2^(s c - m) needs no max at all.  The exact result does not depend on which m is used, only
+// on using the same m for p, l and O; the bound keeps p within fp16 range and its rounding
+// relative.  When some lane's partial sum exceeds 2^8 (which also catches the first tile, where
+// m = -inf, and any overflow), the wave takes the exact path: the tile's true row maximum becomes
+// the new shift, and l and O are rescaled by 2^(m_old - m_new).  Never forms (-inf) - (-inf) in
+// a value that is kept.  Probabilities are rounded to fp16/bf16 into the PV operand pf; the row
+// sum l accumulates the fp32 probabilities.
+template <int NKB, int NDB, int DT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
+                                             f32x16 (&o)[NDB], float c) {
+    constexpr float kLazyBound = 256.f;
+    float acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) {
+        const int kb = t >> 1, u = t & 1;
+        f32x8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * u + e], c, -m));
+            x[e] = p;
+            acc[e & 3] += p;
+        }
+        pf[t] = pack8<DT>(x);
+    }
+    float rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (__any(!(rs <= kLazyBound))) {
+        float mx = lane_max<NKB>(s);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m, mx * c);
+        const float muse = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - muse);   // m = -inf gives 0
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2 * NKB; ++t) {
+            const int kb = t >> 1, u = t & 1;
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * u + e], c, -muse));
+                x[e] = p;
+                acc[e & 3] += p;
+            }
+            pf[t] = pack8<DT>(x);
+        }
+        rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        l *= alpha;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        }
+        m = mnew;
+    }
+    l += rs;
+}
+
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts: 32-bit data format,
 // no swizzle.  Loads at or past num_records bytes return zero.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -302,38 +393,10 @@ __global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
             u32x4 pf[QB][NPK];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float mx = -INFINITY;
+                f32x16 sq[NKB];
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mnew = fmaxf(mrun[qb], mx * a.scale_log2);
-                const float muse = mnew == -INFINITY ? 0.f : mnew;   // never (-inf) - (-inf)
-                const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - muse);
-                float rs = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][qb][r], a.scale_log2, -muse));
-                        sacc[kb][qb][r] = p;
-                        rs += p;
-                    }
-                lrun[qb] = lrun[qb] * alpha + rs;
-                mrun[qb] = mnew;
-                if (__any(alpha != 1.f)) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
-                }
-#pragma unroll
-                for (int t = 0; t < NPK; ++t) {
-                    const int kb = t >> 1, u = t & 1;
-                    f32x8 x;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = sacc[kb][qb][8 * u + e];
-                    pf[qb][t] = pack8<DT>(x);
-                }
+                for (int kb = 0; kb < NKB; ++kb) sq[kb] = sacc[kb][qb];
+                softmax_tile<NKB, NDB, DT>(sq, pf[qb], mrun[qb], lrun[qb], oacc[qb], a.scale_log2);
             }
 
             // O^T += V^T P^T
@@ -414,6 +477,276 @@ __global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
     }
 }
 
+// Ping-pong forward kernel: 8 waves, each with 32 query rows.  Waves 0-3 (group A) and 4-7 (group B)
+// share the four SIMDs and run half an iteration apart: while one group issues the matrix-core work
+// of its iteration (PV of the previous tile, then S of the current tile) the other group runs the
+// softmax of its tile on the vector ALU, so the two units overlap instead of taking turns.
+// Two barriers per iteration keep the groups in alternating phases; group B enters the loop one
+// phase late and group A leaves one phase late, so both execute the same number of barriers.
+// LDS holds two K tiles and two V^T tiles.  With phases numbered from 0, K_j is read in phases
+// 2j (A) and 2j+1 (B) and V_j in phases 2j+2 (A) and 2j+3 (B); group A writes K_{j} during its
+// softmax phase 2j-1 and group B writes V_{j} during its softmax phase 2j, each into the buffer
+// whose previous tile was last read before that phase.  Global loads are issued one iteration
+// before their LDS write.
+template <int D, int DT, int KT>
+__global__ void __launch_bounds__(512) fwd_pp_kernel(const FwdArgs a) {
+    constexpr int NT = 512;
+    constexpr int GT = 256;                                // threads per group
+    constexpr int BM = 256;                                // query rows per workgroup
+    constexpr int KS = D + 8;
+    constexpr int VS = KT + 8;
+    constexpr int KTILE = KT * KS;
+    constexpr int VTILE = D * VS;
+    constexpr int KITEMS = KT * (D / 8);
+    constexpr int VITEMS = (KT / 2) * (D / 8);
+    constexpr int KCH = KITEMS / GT;
+    constexpr int VCH = VITEMS / GT;
+    constexpr int NREG = KCH > 2 * VCH ? KCH : 2 * VCH;
+    constexpr int NKB = KT / 32;
+    constexpr int NPK = KT / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NDK = D / 16;
+    static_assert(KITEMS % GT == 0 && VITEMS % GT == 0, "tile split");
+    (void)NT;
+
+    __shared__ __attribute__((aligned(16))) uint16_t kls[2 * KTILE];
+    __shared__ __attribute__((aligned(16))) uint16_t vls[2 * VTILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int grp = wave >> 2;
+    const int gtid = tid & (GT - 1);
+
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = w % a.n_qt;
+    w /= a.n_qt;
+    const int gi = w % a.group;
+    w /= a.group;
+    const int split = w % a.n_splits;
+    w /= a.n_splits;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int hq = hkv * a.group + gi;
+    const int qt = a.n_qt - 1 - qt_idx;
+
+    const int64_t i0 = a.r0 + (int64_t)qt * BM;
+    const int64_t i_end = min(i0 + (int64_t)BM, a.r1);
+    const int64_t iw0 = i0 + (int64_t)wave * 32;
+    const int64_t iw_end = min(iw0 + 32, i_end);
+
+    const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
+    int64_t khi = min(a.k_hi, klo + a.split_len);
+    if (a.causal) khi = min(khi, i_end + a.causal_delta);
+    const int ntiles = khi > klo ? (int)((khi - klo + KT - 1) / KT) : 0;
+
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
+
+    u32x4 qf[NDK];
+    {
+        const int64_t row = iw0 + l32;
+        const bool ok = row < i_end;
+        const uint16_t* p = qp + (ok ? row : 0) * a.q_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * t);
+            qf[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float mrun = -INFINITY, lrun = 0.f;
+
+    // group A stages K tiles, group B stages V tiles, through the same registers
+    u32x4 sreg[NREG];
+    auto issue_k = [&](int j) {
+        if (j >= ntiles) return;
+        const int64_t j0 = klo + (int64_t)j * KT;
+        const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, k_sn, j0, min(khi - j0, (int64_t)KT), D);
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int idx = gtid + c * GT;
+            const int row = idx / (D / 8), col8 = idx % (D / 8);
+            sreg[c] = __builtin_amdgcn_raw_buffer_load_b128(kr, (int)((row * k_sn + col8 * 8) * 2), 0, 0);
+        }
+    };
+    auto write_k = [&](int j) {
+        if (j >= ntiles) return;
+        uint16_t* ks = kls + (j & 1) * KTILE;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            const int idx = gtid + c * GT;
+            const int row = idx / (D / 8), col8 = idx % (D / 8);
+            *reinterpret_cast<u32x4*>(ks + row * KS + col8 * 8) = sreg[c];
+        }
+    };
+    auto issue_v = [&](int j) {
+        if (j >= ntiles) return;
+        const int64_t j0 = klo + (int64_t)j * KT;
+        const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, v_sn, j0, min(khi - j0, (int64_t)KT), D);
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = gtid + c * GT;
+            const int pr = idx % (KT / 2), col8 = idx / (KT / 2);
+            const int off = (int)((2 * pr * v_sn + col8 * 8) * 2);
+            sreg[2 * c] = __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0);
+            sreg[2 * c + 1] = __builtin_amdgcn_raw_buffer_load_b128(vr, off + (int)(v_sn * 2), 0, 0);
+        }
+    };
+    auto write_v = [&](int j) {
+        if (j >= ntiles) return;
+        uint16_t* vs = vls + (j & 1) * VTILE;
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) {
+            const int idx = gtid + c * GT;
+            const int pr = idx % (KT / 2), col8 = idx / (KT / 2);
+            const int slot = vslot(2 * pr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w0 = sreg[2 * c][e >> 1], w1 = sreg[2 * c + 1][e >> 1];
+                const uint32_t word = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+                *reinterpret_cast<uint32_t*>(vs + (col8 * 8 + e) * VS + slot) = word;
+            }
+        }
+    };
+
+    // prologue: tile 0 into buffer 0, and tile 1 in flight in registers
+    if (grp == 0) {
+        issue_k(0);
+        write_k(0);
+        issue_k(1);
+    } else {
+        issue_v(0);
+        write_v(0);
+        issue_v(1);
+    }
+    __syncthreads();
+
+    f32x16 sacc[NKB];
+    u32x4 pf[NPK];
+    bool pv_pending = false;
+    if (grp == 1) __syncthreads();  // group B runs one phase behind
+    for (int it = 0; it <= ntiles; ++it) {
+        const int64_t j0 = klo + (int64_t)it * KT;
+        const bool active = it < ntiles && iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + a.causal_delta);
+        // ---- matrix-core phase: PV of the previous tile, then S of this tile
+        if (pv_pending) {
+            const uint16_t* vs = vls + ((it - 1) & 1) * VTILE;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int t = 0; t < NPK; ++t) {
+                    const u32x4 vf = *reinterpret_cast<const u32x4*>(vs + (db * 32 + l32) * VS + 16 * t + 8 * hi);
+                    oacc[db] = mfma32<DT>(vf, pf[t], oacc[db]);
+                }
+        }
+        if (active) {
+            const uint16_t* ks = kls + (it & 1) * KTILE;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+            for (int t = 0; t < NDK; ++t)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(ks + (kb * 32 + l32) * KS + 16 * t + 8 * hi);
+                    sacc[kb] = mfma32<DT>(af, qf[t], sacc[kb]);
+                }
+        }
+        __syncthreads();
+        // ---- vector phase: softmax of this tile, then stage a later tile
+        pv_pending = active;
+        if (active) {
+            const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + a.causal_delta));
+            if (need_mask) {
+                int lim = (int)min(khi - j0, (int64_t)KT);
+                if (a.causal) {
+                    const int64_t c = iw0 + l32 + a.causal_delta - j0 + 1;
+                    lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int t = kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                        if (t >= lim) sacc[kb][r] = -INFINITY;
+                    }
+            }
+            softmax_tile<NKB, NDB, DT>(sacc, pf, mrun, lrun, oacc, a.scale_log2);
+        }
+        if (it < ntiles) {
+            if (grp == 0) {
+                write_k(it + 1);
+                issue_k(it + 2);
+            } else {
+                write_v(it + 1);
+                issue_v(it + 2);
+            }
+        }
+        __syncthreads();
+    }
+    if (grp == 0) __syncthreads();  // group A leaves one phase late
+
+    // ---- epilogue (as in fwd_kernel, one 32-row block per wave)
+    const float ltot = lrun + __shfl_xor(lrun, 32);
+    const int64_t row = iw0 + l32;
+    if (row >= i_end) return;
+    const float mnat = ltot > 0.f ? mrun * kLn2 : -INFINITY;
+    if (a.mode == FWD_FINAL) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
+            }
+        if (a.lse && hi == 0)
+            a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
+                ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : -INFINITY;
+        return;
+    }
+    const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
+    float* op = a.acc_o + ridx * D;
+    float* mlp = a.acc_ml + ridx * 2;
+    if (a.mode == FWD_PARTIAL) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
+            }
+        if (hi == 0) {
+            mlp[0] = mnat;
+            mlp[1] = ltot;
+        }
+        return;
+    }
+    const float ma = mlp[0], la = mlp[1];
+    const float mm = fmaxf(ma, mnat);
+    const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
+    const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float* dst = op + db * 32 + 8 * g + 4 * hi;
+            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+            f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
+        }
+    if (hi == 0) {
+        mlp[0] = mm;
+        mlp[1] = wa * la + wb * ltot;
+    }
+}
+
 // Log-sum-exp merge: TPR threads per row, four output dims per thread.  The threads of one row
 // sit in one wave, so in-place operation (output == part 0) reads every input before it writes.
 template <int D>
@@ -453,6 +786,15 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
     }
 }
 
+template <int D, int DT, int KT>
+hipError_t launch_pp_t(const FwdArgs& a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, DT, KT>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D, int DT, int QB, int NW, int KT>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
@@ -462,13 +804,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile shapes (query blocks per wave, waves per workgroup, keys per tile), per head dim.  Variant 0 is
-// the default; CQSA_FWD_VARIANT picks another one for measurement.
+// Tile shapes (query blocks per wave, waves per workgroup, keys per tile), per head dim; qb = 0 is the
+// ping-pong kernel (8 waves x 32 rows).  Variant 0 is the default; CQSA_FWD_VARIANT picks another one
+// for measurement.
 struct Shape {
     int qb, nw, kt;
 };
-constexpr Shape kShapes64[] = {{1, 8, 128}, {1, 8, 64}, {2, 4, 64}, {1, 4, 64}};
-constexpr Shape kShapes128[] = {{1, 8, 64}, {1, 8, 128}, {1, 4, 64}, {1, 4, 128}};
+constexpr Shape kShapes64[] = {{0, 8, 128}, {1, 8, 128}, {0, 8, 64}, {1, 8, 64}};
+constexpr Shape kShapes128[] = {{0, 8, 64}, {1, 8, 64}, {1, 8, 128}, {0, 8, 64}};
 
 int variant() {
     static int v = -1;
@@ -483,20 +826,13 @@ int variant() {
 template <int D, int DT>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-#define CQSA_SHAPE(QB_, NW_, KT_) \
-    if (sh.qb == QB_ && sh.nw == NW_ && sh.kt == KT_) return launch_fwd_t<D, DT, QB_, NW_, KT_>(a, st)
-    if constexpr (D == 64) {
-        CQSA_SHAPE(1, 8, 128);
-        CQSA_SHAPE(1, 8, 64);
-        CQSA_SHAPE(2, 4, 64);
-        CQSA_SHAPE(1, 4, 64);
-    } else {
-        CQSA_SHAPE(1, 8, 64);
-        CQSA_SHAPE(1, 8, 128);
-        CQSA_SHAPE(1, 4, 64);
-        CQSA_SHAPE(1, 4, 128);
+    if (sh.qb == 0) {
+        if (sh.kt == 64) return launch_pp_t<D, DT, 64>(a, st);
+        if (sh.kt == 128) return launch_pp_t<D, DT, 128>(a, st);
+        return hipErrorInvalidValue;
     }
-#undef CQSA_SHAPE
+    if (sh.kt == 64) return launch_fwd_t<D, DT, 1, 8, 64>(a, st);
+    if (sh.kt == 128) return launch_fwd_t<D, DT, 1, 8, 128>(a, st);
     return hipErrorInvalidValue;
 }
 
@@ -504,7 +840,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
 
 int fwd_block_m(int D) {
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-    return sh.nw * 32 * sh.qb;
+    return sh.nw * 32 * (sh.qb == 0 ? 1 : sh.qb);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
