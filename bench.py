@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--streamed", action="store_true", help="also run the 4M-token host-streamed case")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
+    ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
+                    "(default profiles/fwd_kernel_<workload>.md)")
     return ap.parse_args()
 
 
@@ -80,6 +84,15 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def measured_traffic(path: str):
+    """HBM bytes per launch from a committed rocprofv3 summary, if it measured the current kernel source."""
+    from exact_long_context_cqsa_amd import profiling
+    prof = profiling.read_profile(path)
+    if not prof or prof.get("kernel_source_sha256") != profiling.kernel_source_sha256():
+        return None, ("no profile" if not prof else "kernel changed since the counters were taken")
+    return int(float(prof["traffic_bytes_per_launch"])), os.path.relpath(path, ROOT)
+
+
 def run_streamed(cqsa, torch, synth) -> dict:
     w = synth.workload(3)
     t0 = time.perf_counter()
@@ -104,13 +117,28 @@ def run_streamed(cqsa, torch, synth) -> dict:
     wall = time.perf_counter() - t2
     tok = w.B * w.Nq / wall
     h2d_gbs = info["h2d_bytes"] / (info["h2d_ms"] / 1e3) / 1e9 if info["h2d_ms"] > 0 else None
+    # parity on sampled rows against the FP64 reference (first/last rows, Q-chunk edges, seeded rows)
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(4)
+    qc = info["q_chunk"]
+    idx = sorted({0, 1, w.Nq - 1, w.Nq - 2, qc - 1, qc, *rng.integers(0, w.Nq, 10).tolist()})
+    rows = np.array([(0, h, i) for h in (0, 5) for i in idx if 0 <= i < w.Nq], dtype=np.int64)
+    t3 = time.perf_counter()
+    ref = oracle.attention_rows(q, k, v, causal=True, scale=w.scale, rows=rows)
+    got = out[0, torch.from_numpy(rows[:, 1]), torch.from_numpy(rows[:, 2])].double().numpy()
+    max_abs = float(np.abs(got - ref["o"]).max())
+    print(f"[bench] streamed parity on {len(rows)} rows: max_abs {max_abs:.2e} ({time.perf_counter() - t3:.1f} s)",
+          file=sys.stderr, flush=True)
     return {"workload": w.name, "seconds": round(wall, 3), "tokens_per_s": round(tok, 1),
             "tflops": round(w.flops() / wall / 1e12, 2), "h2d_bytes": info["h2d_bytes"],
             "h2d_gbs_during_copies": round(h2d_gbs, 2) if h2d_gbs else None,
             "h2d_link_peak_gbs_host_timed": round(link, 2),
             "h2d_frac_of_link": round(h2d_gbs / link, 3) if h2d_gbs else None,
             "q_chunk": info["q_chunk"], "kv_chunk": info["kv_chunk"], "chunk_pairs": info["chunk_pairs"],
-            "workspace_bytes": info["workspace_bytes"]}
+            "workspace_bytes": info["workspace_bytes"], "budget_bytes": info["budget_bytes"],
+            "parity_rows": int(len(rows)), "parity_max_abs_fp16_out": max_abs,
+            "note": "wall time includes PCIe transfers from/to pinned host memory; not the headline value"}
 
 
 def main():
@@ -155,6 +183,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms_step = wall * 1e3 / args.steps
     ms_kernel = sum(per) / len(per)
     flops = w.flops()
@@ -163,6 +197,8 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms (events {ms_kernel:.3f} ms, min {min(per):.3f}) -> {value:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
+    prof_path = args.profile or os.path.join(ROOT, "profiles", f"fwd_kernel_{w.name}.md")
+    traffic, traffic_src = measured_traffic(prof_path)
     line = {
         "metric": "causal attention fwd TFLOP/s & % MFMA peak (1 GPU); tokens/s at 4M ctx",
         "value": round(value, 2),
@@ -183,8 +219,10 @@ def main():
                    "tokens_per_s": round(w.B * w.Nq / (ms_step / 1e3), 1),
                    "algorithmic_flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_kernel<D=64,f16>", "kernel_ms": round(ms_kernel, 4),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                     "traffic_source": traffic_src,
+                     "kernel": "fwd_kernel (D=%d, %s)" % (w.D, "f16" if w.dtype == torch.float16 else "bf16"),
+                     "kernel_ms": round(ms_kernel, 4),
                      "launches_per_step": info["kernel_launches"]},
     }
     if args.streamed:

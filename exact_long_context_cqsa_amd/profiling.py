@@ -1,0 +1,141 @@
+"""Summaries of rocprofv3 runs for the attention kernels (text files under profiles/).
+
+    python -m exact_long_context_cqsa_amd.profiling \
+        --name fwd_kernel_causal_n32768_h8_d64_f16 --kernel fwd_ \
+        --trace <kernel_trace.csv> --fetch <fetch counter_collection.csv> --write <write counter_collection.csv> \
+        --command "<the rocprofv3 command lines that produced the CSVs>"
+
+The kernel trace gives the per-launch duration of the kernel whose name contains --kernel.  FETCH_SIZE and
+WRITE_SIZE (KiB per dispatch) are scaled by what the same counters read for the plain 1 GiB device copy in
+the same run (bench.py --copy-calibration), giving HBM bytes per launch.  The summary records the SHA-256 of
+the kernel source it measured; bench.py reports the traffic only while the source is unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+KERNEL_SOURCE = os.path.join(PKG, "csrc", "cqsa_kernels.hip")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_sha256() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def trace_stats(path: str, kernel: str) -> dict:
+    durs = []
+    name = None
+    for r in _rows(path):
+        kn = r.get("Kernel_Name", "")
+        if kernel in kn:
+            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            name = kn
+    if not durs:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel!r} in {path}")
+    return {"kernel_name": name, "calls": len(durs), "avg_ns": statistics.mean(durs), "min_ns": min(durs),
+            "max_ns": max(durs), "median_ns": statistics.median(durs)}
+
+
+def counter_per_dispatch(path: str, counter: str, kernel: str) -> tuple[float, float]:
+    """(mean value for the attention kernel's dispatches, value for the 1 GiB copy dispatch)."""
+    kvals, cvals = [], []
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        kn = r.get("Kernel_Name", "")
+        v = float(r["Counter_Value"])
+        if kernel in kn:
+            kvals.append(v)
+        elif int(r.get("Grid_Size", "0") or 0) > 0 and ("copy" in kn.lower() or "elementwise" in kn.lower()):
+            cvals.append(v)
+    if not kvals or not cvals:
+        raise SystemExit(f"{counter}: kernel or copy dispatch missing in {path}")
+    return statistics.mean(kvals), max(cvals)
+
+
+def summarise(args) -> str:
+    ts = trace_stats(args.trace, args.kernel)
+    fk, fc = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
+    wk, wc = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    f_scale = COPY_BYTES / (fc * 1024.0)     # the copy reads 1 GiB
+    w_scale = COPY_BYTES / (wc * 1024.0)     # and writes 1 GiB
+    fetch_b = fk * 1024.0 * f_scale
+    write_b = wk * 1024.0 * w_scale
+    lines = [
+        f"# {args.name}",
+        "",
+        f"kernel: `{ts['kernel_name']}`",
+        f"kernel_source_sha256: {kernel_source_sha256()}",
+        "",
+        "## Commands",
+        "",
+        "```",
+        args.command.strip(),
+        "```",
+        "",
+        "## Kernel trace (rocprofv3 --kernel-trace --stats)",
+        "",
+        f"calls: {ts['calls']}",
+        f"avg_ns: {ts['avg_ns']:.0f}",
+        f"median_ns: {ts['median_ns']:.0f}",
+        f"min_ns: {ts['min_ns']}",
+        f"max_ns: {ts['max_ns']}",
+        "",
+        "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)",
+        "",
+        f"fetch_kib_per_dispatch: {fk:.1f}  (1 GiB copy reads {fc:.1f} KiB: scale {f_scale:.3f})",
+        f"write_kib_per_dispatch: {wk:.1f}  (1 GiB copy writes {wc:.1f} KiB: scale {w_scale:.3f})",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+    ]
+    if args.note:
+        lines += ["", "## Notes", "", args.note.strip()]
+    return "\n".join(lines) + "\n"
+
+
+def read_profile(path: str) -> dict:
+    """Key: value pairs of a summary written by this module."""
+    out = {}
+    if not os.path.exists(path):
+        return out
+    for ln in open(path):
+        m = re.match(r"^([a-z_0-9]+):\s*(\S+)", ln.strip())
+        if m:
+            out[m.group(1)] = m.group(2)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--name", required=True)
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--command", required=True)
+    ap.add_argument("--note", default="")
+    ap.add_argument("--out", default=None)
+    args = ap.parse_args()
+    text = summarise(args)
+    out = args.out or os.path.join(ROOT, "profiles", args.name + ".md")
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
