@@ -199,8 +199,8 @@ def make_inputs(w: Workload, *, nq: int | None = None, nk: int | None = None, ba
     ``nq``/``nk``/``batch``/``heads`` shrink the problem (same recipe, same seed), for tests that
     need a size the checker finishes quickly.  The spike recipe (softmax stress) realises the +20
     logit spikes in the inputs: every query gets q[..., 0] = q_sigma, and the chosen keys get
-    k[..., 0] += spike_logit / (q_sigma * scale), so each logit towards a spike key rises by
-    spike_logit before k is rounded to the storage format."""
+    k[..., 0] += spike_logit / (q_sigma * scale) (added to the fp32-rounded draw), so each logit
+    towards a spike key rises by spike_logit before k is rounded to the storage format."""
     B = batch if batch is not None else w.B
     Hq, Hkv = heads if heads is not None else (w.Hq, w.Hkv)
     Nq = nq if nq is not None else w.Nq
@@ -209,18 +209,27 @@ def make_inputs(w: Workload, *, nq: int | None = None, nk: int | None = None, ba
     seed = w.seed
     spike_pos = None
     if w.spikes > 0.0:
-        # draw in fp64 so that the spike is added before the one rounding to the storage format
-        q = normal((B, Hq, Nq, D), seed=seed, tensor_id=TENSOR_Q, sigma=w.q_sigma, dtype=torch.float64,
-                   threads=threads)
-        k = normal((B, Hkv, Nk, D), seed=seed, tensor_id=TENSOR_K, sigma=w.k_sigma, dtype=torch.float64,
-                   threads=threads)
-        q[..., 0] = w.q_sigma
+        # one (b, h) slice at a time: draws rounded to fp32, the spike added in fp32, then one
+        # rounding to the storage format (the same two roundings as every other draw)
         count = int(math.floor(w.spikes * Nk))
         spike_pos = choose_without_replacement(Nk, count, seed=seed)
+        sp = torch.from_numpy(spike_pos)
         delta = w.spike_logit / (w.q_sigma * w.scale)
-        k[:, :, torch.from_numpy(spike_pos), 0] += delta
-        q = _round_from_f64(q, w.dtype, pin)
-        k = _round_from_f64(k, w.dtype, pin)
+        q = torch.empty((B, Hq, Nq, D), dtype=w.dtype, pin_memory=pin)
+        k = torch.empty((B, Hkv, Nk, D), dtype=w.dtype, pin_memory=pin)
+        tmp_q = torch.empty((Nq, D), dtype=torch.float32)
+        tmp_k = torch.empty((Nk, D), dtype=torch.float32)
+        for b in range(B):
+            for h in range(Hq):
+                fill_(tmp_q, seed=seed, tensor_id=TENSOR_Q, dist="normal", a=0.0, b=w.q_sigma,
+                      element_offset=((b * Hq + h) * Nq) * D, threads=threads)
+                tmp_q[:, 0] = w.q_sigma
+                q[b, h].copy_(tmp_q)
+            for h in range(Hkv):
+                fill_(tmp_k, seed=seed, tensor_id=TENSOR_K, dist="normal", a=0.0, b=w.k_sigma,
+                      element_offset=((b * Hkv + h) * Nk) * D, threads=threads)
+                tmp_k[sp, 0] += delta
+                k[b, h].copy_(tmp_k)
     else:
         q = normal((B, Hq, Nq, D), seed=seed, tensor_id=TENSOR_Q, sigma=w.q_sigma, dtype=w.dtype, pin=pin,
                    threads=threads)
@@ -235,9 +244,3 @@ def make_inputs(w: Workload, *, nq: int | None = None, nk: int | None = None, ba
     return q, k, v, spike_pos
 
 
-def _round_from_f64(x: torch.Tensor, dtype, pin: bool) -> torch.Tensor:
-    """fp64 -> binary32 (RNE) -> fp16/bf16 (RNE), the same two roundings the C generator applies."""
-    f = x.to(torch.float32)
-    out = torch.empty(f.shape, dtype=dtype, pin_memory=pin)
-    out.copy_(f)
-    return out

@@ -313,3 +313,40 @@ def test_errors():
     # empty query set: nothing to do, no error
     e = m.attention(qd[:, :, :0], kd, vd, is_causal=True)
     assert e.shape == (1, 2, 0, 64)
+
+
+def test_config4_streamed_4m_full_size():
+    """4,194,304-token causal attention, H=8, D=64, fp16, q/k/v and out in pinned host memory, device budget
+    16e9 bytes: the planner must cut Q in two and stream KV; sampled rows against the FP64 reference."""
+    w = synth.workload(3)
+    say("workload", w.name, "full size")
+    q, k, v, _ = synth.make_inputs(w, pin=True)
+    out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=torch.float16, pin_memory=True)
+    o, lse, info = cqsa().attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_lse=True,
+                                    return_info=True)
+    say("config4", {x: info[x] for x in ("q_chunk", "kv_chunk", "chunk_pairs", "workspace_bytes", "h2d_bytes",
+                                         "h2d_ms")})
+    assert info["streamed"] == 1 and info["n_q_chunks"] == 2
+    assert info["workspace_bytes"] <= 16e9 * 0.85
+    assert info["h2d_bytes"] == 16 * 2**30
+    rows = sample_rows(1, 8, w.Nq, seed=6, n_random=4, edge=2, boundaries=[info["q_chunk"]] +
+                       list(range(0, w.Nq, info["kv_chunk"])), cap=8, heads=(0, 7))
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    say("config4", compare(o, lse, ref, torch.float16, rows=rows, label="config4 streamed"))
+
+
+def test_config5_softmax_stress_full_size():
+    """B=2, H=16, N=262,144, D=128, bf16, non-causal, logits N(0, 9^2) with +20 spikes on 5% of keys,
+    KV chunk 16,384 (16 LSE merges); sampled rows against the FP64 reference."""
+    w = synth.workload(4)
+    say("workload", w.name, "full size")
+    q, k, v, pos = synth.make_inputs(w)
+    assert len(pos) == 13107
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=False, kv_chunk=16384, out_dtype=torch.float32,
+                                      return_lse=True, return_info=True)
+    torch.cuda.synchronize()
+    assert info["n_kv_chunks"] == 16 and info["merges"] == 15
+    rows = sample_rows(2, 16, w.Nq, seed=7, n_random=2, edge=1, heads=(0, 9, 15))
+    ref = reference(q, k, v, causal=False, scale=w.scale, rows=rows)
+    say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 full"))
