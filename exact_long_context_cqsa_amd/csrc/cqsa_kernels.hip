@@ -747,6 +747,261 @@ __global__ void __launch_bounds__(512) fwd_pp_kernel(const FwdArgs a) {
     }
 }
 
+// DMA forward kernel: 8 waves x 32 query rows, K and V tiles copied from global memory straight into
+// LDS by the buffer unit (buffer_load ... lds: no registers, no vector-ALU work), one tile ahead.
+// Both tiles keep the natural row-major [key][dim] layout with the 16-byte granules of each row
+// permuted by an XOR with a per-row mask, which spreads the matrix-operand reads over all LDS banks:
+//   K: granule g of row r sits at g ^ fk(r); fk = (r >> 1) & 7 (D = 64) or r & 15 (D = 128), so the
+//      32 key rows x 16 bytes of one S operand read are conflict free.
+//   V: granule g of row r sits at g ^ fv(r); fv = 4 ((r >> 1) & 1) (D = 64) or 4 (r & 3) (D = 128).
+// The PV product needs V^T (each lane: 8 keys of one dim).  ds_read_b64_tr_b16 provides it from the
+// row-major tile: within each 16-lane group, output lane i receives element i % 4 of the 8-byte reads
+// made by source lanes i / 4 + 4 j (j = 0..3).  Source lane s therefore reads 4 consecutive dims of key
+// row kbase + s / 4, and every lane ends up with 4 keys of its own dim; two such reads fill one MFMA
+// operand (8 key slots), in the key order the score accumulator holds them.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    return D == 64 ? (4 * ((r >> 1) & 1)) : (4 * (r & 3));
+}
+
+// Issue this wave's share of one K tile and one V tile as LDS DMA (1 KiB per instruction).  The body is
+// compiled in the device pass only: the host pass cannot type the LDS-DMA builtin, and a host-side failure
+// there silently drops the kernel's host launch stub.
+template <int TILE, int NW, int BPW, int D>
+__device__ __forceinline__ void dma_tile(uint16_t* st, const uint16_t* kp, int64_t k_sn, const uint16_t* vp,
+                                         int64_t v_sn, int64_t j0, int64_t nvalid, const int (&koff)[BPW],
+                                         const int (&voff)[BPW], int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, k_sn, j0, nvalid, D);
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, v_sn, j0, nvalid, D);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int n = wave + i * NW;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(st + n * 512), 16,
+                                                 koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(st + TILE + n * 512),
+                                                 16, voff[i], 0, 0, 0);
+    }
+#endif
+}
+
+template <int D, int DT, int KT>
+__global__ void __launch_bounds__(512) fwd_dma_kernel(const FwdArgs a) {
+    constexpr int NW = 8;
+    constexpr int BM = NW * 32;
+    constexpr int TILE = KT * D;                           // elements of one K (or V) tile
+    constexpr int STAGE = 2 * TILE;                        // K then V
+    constexpr int GPR = D / 8;                             // 16-byte granules per row
+    constexpr int RPI = 64 / GPR;                          // rows per DMA instruction (1 KiB)
+    constexpr int NBLK = KT / RPI;                         // DMA instructions per tensor and tile
+    constexpr int BPW = (NBLK + NW - 1) / NW;              // per wave
+    constexpr int NKB = KT / 32;
+    constexpr int NPK = KT / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NDK = D / 16;
+    static_assert(NBLK % NW == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = w % a.n_qt;
+    w /= a.n_qt;
+    const int gi = w % a.group;
+    w /= a.group;
+    const int split = w % a.n_splits;
+    w /= a.n_splits;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int hq = hkv * a.group + gi;
+    const int qt = a.n_qt - 1 - qt_idx;
+
+    const int64_t i0 = a.r0 + (int64_t)qt * BM;
+    const int64_t i_end = min(i0 + (int64_t)BM, a.r1);
+    const int64_t iw0 = i0 + (int64_t)wave * 32;
+    const int64_t iw_end = min(iw0 + 32, i_end);
+
+    const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
+    int64_t khi = min(a.k_hi, klo + a.split_len);
+    if (a.causal) khi = min(khi, i_end + a.causal_delta);
+    const int ntiles = khi > klo ? (int)((khi - klo + KT - 1) / KT) : 0;
+
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
+
+    u32x4 qf[NDK];
+    {
+        const int64_t row = iw0 + l32;
+        const bool ok = row < i_end;
+        const uint16_t* p = qp + (ok ? row : 0) * a.q_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * t);
+            qf[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // per-lane byte offsets of this wave's DMA blocks within a tile (same for every tile)
+    int koff[BPW], voff[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int n = wave + i * NW;
+        const int r = n * RPI + lane / GPR;
+        const int pg = lane % GPR;
+        koff[i] = (int)((r * k_sn + ((pg ^ kswz<D>(r)) * 8)) * 2);
+        voff[i] = (int)((r * v_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+    }
+    // issue the DMA of key tile j into LDS stage j & 1
+#define CQSA_ISSUE_TILE(j)                                                                                  \
+    do {                                                                                                  \
+        const int64_t j0_ = klo + (int64_t)(j) * KT;                                                      \
+        const int64_t nv_ = min(khi - j0_, (int64_t)KT);                                                  \
+        dma_tile<TILE, NW, BPW, D>(lds + ((j) & 1) * STAGE, kp, k_sn, vp, v_sn, j0_, nv_, koff, voff, wave); \
+    } while (0)
+
+    // per-lane LDS element offsets of the matrix-operand reads (relative to a stage)
+    int kread[NDK];
+#pragma unroll
+    for (int t = 0; t < NDK; ++t) kread[t] = l32 * D + (((2 * t + hi) ^ kswz<D>(l32)) * 8);
+    int vread[NDB];
+    {
+        const int src = lane & 15;
+        const int row = 4 * hi + src / 4;                       // + 16 t + 8 r at use
+        const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vread[db] = TILE + row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float mrun = -INFINITY, lrun = 0.f;
+
+    if (ntiles > 0) CQSA_ISSUE_TILE(0);
+    for (int it = 0; it < ntiles; ++it) {
+        __syncthreads();   // tile it is in LDS; every wave is done with tile it - 1
+        if (it + 1 < ntiles) CQSA_ISSUE_TILE(it + 1);
+        const int64_t j0 = klo + (int64_t)it * KT;
+        const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + a.causal_delta);
+        if (!active) continue;
+        const uint16_t* st = lds + (it & 1) * STAGE;
+
+        f32x16 sacc[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < NDK; ++t)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const u32x4 af = *reinterpret_cast<const u32x4*>(st + kread[t] + kb * 32 * D);
+                sacc[kb] = mfma32<DT>(af, qf[t], sacc[kb]);
+            }
+
+        const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + a.causal_delta));
+        if (need_mask) {
+            int lim = (int)min(khi - j0, (int64_t)KT);
+            if (a.causal) {
+                const int64_t c = iw0 + l32 + a.causal_delta - j0 + 1;
+                lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                    if (t >= lim) sacc[kb][r] = -INFINITY;
+                }
+        }
+
+        u32x4 pf[NPK];
+        softmax_tile<NKB, NDB, DT>(sacc, pf, mrun, lrun, oacc, a.scale_log2);
+
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int t = 0; t < NPK; ++t) {
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t) * D));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t + 8) * D));
+                u32x4 vf;
+                vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
+                vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
+                vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
+                vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
+                oacc[db] = mfma32<DT>(vf, pf[t], oacc[db]);
+            }
+    }
+
+#undef CQSA_ISSUE_TILE
+
+    // ---- epilogue
+    const float ltot = lrun + __shfl_xor(lrun, 32);
+    const int64_t row = iw0 + l32;
+    if (row >= i_end) return;
+    const float mnat = ltot > 0.f ? mrun * kLn2 : -INFINITY;
+    if (a.mode == FWD_FINAL) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
+            }
+        if (a.lse && hi == 0)
+            a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
+                ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : -INFINITY;
+        return;
+    }
+    const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
+    float* op = a.acc_o + ridx * D;
+    float* mlp = a.acc_ml + ridx * 2;
+    if (a.mode == FWD_PARTIAL) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
+            }
+        if (hi == 0) {
+            mlp[0] = mnat;
+            mlp[1] = ltot;
+        }
+        return;
+    }
+    const float ma = mlp[0], la = mlp[1];
+    const float mm = fmaxf(ma, mnat);
+    const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
+    const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float* dst = op + db * 32 + 8 * g + 4 * hi;
+            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+            f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
+        }
+    if (hi == 0) {
+        mlp[0] = mm;
+        mlp[1] = wa * la + wb * ltot;
+    }
+}
+
 // Log-sum-exp merge: TPR threads per row, four output dims per thread.  The threads of one row
 // sit in one wave, so in-place operation (output == part 0) reads every input before it writes.
 template <int D>
@@ -787,6 +1042,15 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
 }
 
 template <int D, int DT, int KT>
+hipError_t launch_dma_t(const FwdArgs& a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int DT, int KT>
 hipError_t launch_pp_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
     if (blocks <= 0) return hipSuccess;
@@ -804,14 +1068,14 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Tile shapes (query blocks per wave, waves per workgroup, keys per tile), per head dim; qb = 0 is the
-// ping-pong kernel (8 waves x 32 rows).  Variant 0 is the default; CQSA_FWD_VARIANT picks another one
+// Kernel choice per head dim: qb = 2 the DMA kernel, qb = 0 the ping-pong kernel, qb = 1 the
+// register-staged kernel (all 8 waves x 32 rows), with kt keys per tile.  Variant 0 is the default; CQSA_FWD_VARIANT picks another one
 // for measurement.
 struct Shape {
     int qb, nw, kt;
 };
-constexpr Shape kShapes64[] = {{0, 8, 128}, {1, 8, 128}, {0, 8, 64}, {1, 8, 64}};
-constexpr Shape kShapes128[] = {{0, 8, 64}, {1, 8, 64}, {1, 8, 128}, {0, 8, 64}};
+constexpr Shape kShapes64[] = {{2, 8, 128}, {0, 8, 128}, {1, 8, 128}, {2, 8, 64}};
+constexpr Shape kShapes128[] = {{2, 8, 64}, {0, 8, 64}, {1, 8, 64}, {1, 8, 128}};
 
 int variant() {
     static int v = -1;
@@ -826,6 +1090,11 @@ int variant() {
 template <int D, int DT>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
+    if (sh.qb == 2) {
+        if (sh.kt == 64) return launch_dma_t<D, DT, 64>(a, st);
+        if (sh.kt == 128) return launch_dma_t<D, DT, 128>(a, st);
+        return hipErrorInvalidValue;
+    }
     if (sh.qb == 0) {
         if (sh.kt == 64) return launch_pp_t<D, DT, 64>(a, st);
         if (sh.kt == 128) return launch_pp_t<D, DT, 128>(a, st);
@@ -840,7 +1109,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
 
 int fwd_block_m(int D) {
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-    return sh.nw * 32 * (sh.qb == 0 ? 1 : sh.qb);
+    return sh.nw * 32;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
