@@ -1,11 +1,14 @@
 // gfx950 (CDNA4) kernels for exact attention by Q-tiles x KV-chunks with a log-sum-exp merge.
 //
-// fwd_kernel    one workgroup = BM query rows of one (batch, query head) against one key range.
-//               Online softmax (the FlashAttention-2 recurrence the Stream-CQSA kernels derive from:
-//               stream-cqsa 2.2.0 -> 2.2.2 diff, README.md, "FlashAttention-2-derived CQS forward")
-//               produces the partial triple (O, m, l) of the range; the epilogue normalises it,
-//               stores it, or folds it into a running triple.
-// merge_kernel  the exact log-sum-exp merge of partial triples, optionally normalising (finalize).
+// Forward kernels: one workgroup = BM query rows of one (batch, query head) against one key range.
+// The online softmax (the FlashAttention-2 recurrence that the pages' CQS forward kernel builds on:
+// stream-cqsa 2.2.0 -> 2.2.2 diff, README.md) produces the partial triple (O, m, l) of the range;
+// the epilogue normalises it, stores it, or folds it into a running triple.
+//   fwd_dma_kernel  K/V tiles staged into LDS by buffer-load DMA, V read with transpose loads
+//                   (the default);
+//   fwd_kernel      K/V tiles staged through registers, V written to LDS transposed;
+//   fwd_pp_kernel   as fwd_kernel, with the two halves of the workgroup half a tile apart.
+// merge_kernel      the exact log-sum-exp merge of partial triples, optionally normalising (finalize).
 //
 // Matrix-core layout (v_mfma_f32_32x32x16_{f16,bf16}; wave64; lane = 32*hi + l32):
 //   A operand: lane holds A[row l32][k = 8*hi .. 8*hi+7]
@@ -15,8 +18,9 @@
 // registers), so each lane owns one query column and 16 of its keys: the row max needs one exchange
 // with lane ^ 32, the row sum stays per lane until the end, and the fp32 scores, once turned into
 // probabilities and rounded to fp16/bf16, are already the B operand of O^T = V^T P^T.  That product
-// contracts over keys in the order the score accumulator holds them, so V is written into LDS
-// transposed (V^T[d][key slot]) with each group of 16 keys permuted to match.
+// contracts over keys in the order the score accumulator holds them, so V must reach the matrix
+// cores as V^T[d][key slot] with each group of 16 keys permuted to match: fwd_kernel writes it into
+// LDS that way, fwd_dma_kernel assembles it from row-major tiles with transpose loads.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -98,7 +102,7 @@ __device__ __forceinline__ int vslot(int j) {
     return (j & ~15) + (((o >> 2) & 1) << 3) + (o & 3) + ((o >> 3) << 2);
 }
 
-// Row maximum / sum of a lane's NKB x 16 score registers with 8 independent partial chains, so the
+// Row maximum of a lane's NKB x 16 score registers with 8 independent partial chains, so the
 // reduction is not one long dependency chain (two waves per SIMD cannot hide its latency).
 template <int NKB>
 __device__ __forceinline__ float lane_max(const f32x16 (&s)[NKB]) {
@@ -112,36 +116,12 @@ __device__ __forceinline__ float lane_max(const f32x16 (&s)[NKB]) {
     return fmaxf(fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3])), fmaxf(fmaxf(m[4], m[5]), fmaxf(m[6], m[7])));
 }
 
-// p = 2^(s * c - mu) in place, returning the lane's sum of p (8 partial sums).
-template <int NKB>
-__device__ __forceinline__ float lane_exp_sum(f32x16 (&s)[NKB], float c, float mu) {
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mu));
-            s[kb][r] = p;
-            acc[(kb * 16 + r) & 7] += p;
-        }
-    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-}
+constexpr float kLazyBound = 256.f;
 
-// Online softmax of one key tile for one 32-row query block (lane = one row, NKB x 16 of its keys).
-// The running shift m (base 2) is kept while no probability of the tile exceeds 2^8: then
-// p = 2^(s c - m) needs no max at all.  The exact result does not depend on which m is used, only
-// on using the same m for p, l and O; the bound keeps p within fp16 range and its rounding
-// relative.  When some lane's partial sum exceeds 2^8 (which also catches the first tile, where
-// m = -inf, and any overflow), the wave takes the exact path: the tile's true row maximum becomes
-// the new shift, and l and O are rescaled by 2^(m_old - m_new).  Never forms (-inf) - (-inf) in
-// a value that is kept.  Probabilities are rounded to fp16/bf16 into the PV operand pf; the row
-// sum l accumulates the fp32 probabilities.
-template <int NKB, int NDB, int DT>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
-                                             f32x16 (&o)[NDB], float c) {
-    constexpr float kLazyBound = 256.f;
+// Fast half of the online-softmax step: p = 2^(s c - m) with the running shift m unchanged, rounded
+// into the PV operand pf; returns the lane's sum of the fp32 p (4 partial chains).
+template <int NKB, int DT>
+__device__ __forceinline__ float softmax_fast(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float m, float c) {
     float acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = 0.f;
@@ -157,35 +137,42 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)
         }
         pf[t] = pack8<DT>(x);
     }
-    float rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    if (__any(!(rs <= kLazyBound))) {
-        float mx = lane_max<NKB>(s);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m, mx * c);
-        const float muse = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - muse);   // m = -inf gives 0
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Exact half, taken by the whole wave when some lane's fast sum is not <= 2^8: the tile's row maximum
+// (exchanged with lane ^ 32) becomes the new shift, p and its sum rs are recomputed, and l and O are
+// rescaled by 2^(m_old - m_new) (0 when m_old = -inf; a row with no visible key so far keeps m = -inf
+// and gets p = 0, with no (-inf) - (-inf) ever kept).
+template <int NKB, int NDB, int DT>
+__device__ __forceinline__ void softmax_exact(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
+                                              f32x16 (&o)[NDB], float c, float& rs) {
+    float mx = lane_max<NKB>(s);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx * c);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m - muse);   // m = -inf gives 0
+    rs = softmax_fast<NKB, DT>(s, pf, muse, c);
+    l *= alpha;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2 * NKB; ++t) {
-            const int kb = t >> 1, u = t & 1;
-            f32x8 x;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * u + e], c, -muse));
-                x[e] = p;
-                acc[e & 3] += p;
-            }
-            pf[t] = pack8<DT>(x);
-        }
-        rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        l *= alpha;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-        }
-        m = mnew;
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
     }
+    m = mnew;
+}
+
+// Online softmax of one key tile for one 32-row query block (lane = one row, NKB x 16 of its keys).
+// The running shift m (base 2) is kept while no probability of the tile exceeds 2^8: then
+// p = 2^(s c - m) needs no max at all.  The exact result does not depend on which m is used, only
+// on using the same m for p, l and O; the bound keeps p within fp16 range and its rounding
+// relative.  When some lane's partial sum exceeds 2^8 (which also catches the first tile, where
+// m = -inf, and any overflow), the wave takes the exact path.  Probabilities are rounded to fp16/bf16
+// into the PV operand pf; the row sum l accumulates the fp32 probabilities.
+template <int NKB, int NDB, int DT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
+                                             f32x16 (&o)[NDB], float c) {
+    float rs = softmax_fast<NKB, DT>(s, pf, m, c);
+    if (__any(!(rs <= kLazyBound))) softmax_exact<NKB, NDB, DT>(s, pf, m, l, o, c, rs);
     l += rs;
 }
 
@@ -200,6 +187,85 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
     const uint16_t* p = base + j0 * sn;
     const uint32_t bytes = nvalid > 0 ? (uint32_t)((nvalid - 1) * sn * 2 + (int64_t)D * 2) : 0u;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// One wave's share of the DMA of one K or V tile: rows [j0, j0 + nvalid) of the view at base (row
+// stride sn) into LDS at st, 1 KiB per instruction, lane byte offsets off (swizzle included).  Rows at
+// or past nvalid read as zero.  Compiled in the device pass only (the host pass cannot type the LDS-DMA builtin, and a failure there
+// silently drops the kernel's host launch stub).
+template <int NW, int BPW, int D>
+__device__ __forceinline__ void dma_rows(uint16_t* st, const uint16_t* base, int64_t sn, int64_t j0, int64_t nvalid,
+                                         const int (&off)[BPW], int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t r = rows_rsrc(base, sn, j0, nvalid, D);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(st + (wave + i * NW) * 512),
+                                                 16, off[i], 0, 0, 0);
+#endif
+}
+
+// Epilogue shared by the forward kernels: the lane pair (l32, l32 + 32) holds one query row's
+// unnormalised O^T column (NDB x 16 dims each), its base-2 shift m and half of its sum l.
+//   FWD_FINAL:   O / l in the output dtype, lse = (m + log2 l) ln 2 (natural log of the scaled logits)
+//   FWD_PARTIAL: the raw triple (O, m ln 2, l) into the fp32 accumulator slot of this split
+//   FWD_ACCUM:   the exact log-sum-exp fold of the triple into the accumulator slot.
+template <int NDB>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&oacc)[NDB], float mrun, float lrun, int b,
+                                             int hq, int split, int64_t row, bool valid, int hi) {
+    constexpr int D = NDB * 32;
+    const float ltot = lrun + __shfl_xor(lrun, 32);
+    if (!valid) return;
+    const float mnat = ltot > 0.f ? mrun * kLn2 : -INFINITY;
+    if (a.mode == FWD_FINAL) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
+            }
+        if (a.lse && hi == 0)
+            a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
+                ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : -INFINITY;
+        return;
+    }
+    const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
+    float* op = a.acc_o + ridx * D;
+    float* mlp = a.acc_ml + ridx * 2;
+    if (a.mode == FWD_PARTIAL) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
+            }
+        if (hi == 0) {
+            mlp[0] = mnat;
+            mlp[1] = ltot;
+        }
+        return;
+    }
+    const float ma = mlp[0], la = mlp[1];
+    const float mm = fmaxf(ma, mnat);
+    const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
+    const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float* dst = op + db * 32 + 8 * g + 4 * hi;
+            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+            f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+            *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
+        }
+    if (hi == 0) {
+        mlp[0] = mm;
+        mlp[1] = wa * la + wb * ltot;
+    }
 }
 
 // D: head dim; DT: fp16/bf16; QB: 32-row query blocks per wave; NW: waves per workgroup;
@@ -415,65 +481,10 @@ __global__ void __launch_bounds__(NW * 64) fwd_kernel(const FwdArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const float ltot = lrun[qb] + __shfl_xor(lrun[qb], 32);
         const int64_t row = iw0 + qb * 32 + l32;
-        if (row >= i_end) continue;
-        const float mnat = ltot > 0.f ? mrun[qb] * kLn2 : -INFINITY;
-        if (a.mode == FWD_FINAL) {
-            const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-            const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
-                               oacc[qb][db][4 * g + 3]};
-                    store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
-                }
-            if (a.lse && hi == 0)
-                a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
-                    ltot > 0.f ? (mrun[qb] + __log2f(ltot)) * kLn2 : -INFINITY;
-        } else {
-            const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
-            float* op = a.acc_o + ridx * D;
-            float* mlp = a.acc_ml + ridx * 2;
-            if (a.mode == FWD_PARTIAL) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
-                                   oacc[qb][db][4 * g + 3]};
-                        *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
-                    }
-                if (hi == 0) {
-                    mlp[0] = mnat;
-                    mlp[1] = ltot;
-                }
-            } else {
-                const float ma = mlp[0], la = mlp[1];
-                const float mm = fmaxf(ma, mnat);
-                const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
-                const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float* dst = op + db * 32 + 8 * g + 4 * hi;
-                        const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-                        f32x4 x = {oacc[qb][db][4 * g], oacc[qb][db][4 * g + 1], oacc[qb][db][4 * g + 2],
-                                   oacc[qb][db][4 * g + 3]};
-                        *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
-                    }
-                if (hi == 0) {
-                    mlp[0] = mm;
-                    mlp[1] = wa * la + wb * ltot;
-                }
-            }
-        }
+        fwd_epilogue<NDB>(a, oacc[qb], mrun[qb], lrun[qb], b, hq, split, row, row < i_end, hi);
     }
 }
 
@@ -691,60 +702,8 @@ __global__ void __launch_bounds__(512) fwd_pp_kernel(const FwdArgs a) {
     }
     if (grp == 0) __syncthreads();  // group A leaves one phase late
 
-    // ---- epilogue (as in fwd_kernel, one 32-row block per wave)
-    const float ltot = lrun + __shfl_xor(lrun, 32);
     const int64_t row = iw0 + l32;
-    if (row >= i_end) return;
-    const float mnat = ltot > 0.f ? mrun * kLn2 : -INFINITY;
-    if (a.mode == FWD_FINAL) {
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-                store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
-            }
-        if (a.lse && hi == 0)
-            a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
-                ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : -INFINITY;
-        return;
-    }
-    const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
-    float* op = a.acc_o + ridx * D;
-    float* mlp = a.acc_ml + ridx * 2;
-    if (a.mode == FWD_PARTIAL) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-                *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
-            }
-        if (hi == 0) {
-            mlp[0] = mnat;
-            mlp[1] = ltot;
-        }
-        return;
-    }
-    const float ma = mlp[0], la = mlp[1];
-    const float mm = fmaxf(ma, mnat);
-    const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
-    const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float* dst = op + db * 32 + 8 * g + 4 * hi;
-            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-            f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
-        }
-    if (hi == 0) {
-        mlp[0] = mm;
-        mlp[1] = wa * la + wb * ltot;
-    }
+    fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
 // DMA forward kernel: 8 waves x 32 query rows, K and V tiles copied from global memory straight into
@@ -768,30 +727,12 @@ __device__ __forceinline__ int vswz(int r) {
     return D == 64 ? (4 * ((r >> 1) & 1)) : (4 * (r & 3));
 }
 
-// Issue this wave's share of one K tile and one V tile as LDS DMA (1 KiB per instruction).  The body is
-// compiled in the device pass only: the host pass cannot type the LDS-DMA builtin, and a host-side failure
-// there silently drops the kernel's host launch stub.
-template <int TILE, int NW, int BPW, int D>
-__device__ __forceinline__ void dma_tile(uint16_t* st, const uint16_t* kp, int64_t k_sn, const uint16_t* vp,
-                                         int64_t v_sn, int64_t j0, int64_t nvalid, const int (&koff)[BPW],
-                                         const int (&voff)[BPW], int wave) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t kr = rows_rsrc(kp, k_sn, j0, nvalid, D);
-    const __amdgpu_buffer_rsrc_t vr = rows_rsrc(vp, v_sn, j0, nvalid, D);
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-        const int n = wave + i * NW;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(st + n * 512), 16,
-                                                 koff[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(st + TILE + n * 512),
-                                                 16, voff[i], 0, 0, 0);
-    }
-#endif
-}
-
-template <int D, int DT, int KT>
-__global__ void __launch_bounds__(512) fwd_dma_kernel(const FwdArgs a) {
-    constexpr int NW = 8;
+// NW waves per workgroup (32 query rows each); WPE asks the compiler for registers that leave room for
+// WPE waves per SIMD (several small workgroups per CU drift out of phase, so one's softmax overlaps
+// another's matrix products).
+template <int D, int DT, int KT, int NW, int WPE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+fwd_dma_kernel(const FwdArgs a) {
     constexpr int BM = NW * 32;
     constexpr int TILE = KT * D;                           // elements of one K (or V) tile
     constexpr int STAGE = 2 * TILE;                        // K then V
@@ -865,7 +806,9 @@ __global__ void __launch_bounds__(512) fwd_dma_kernel(const FwdArgs a) {
     do {                                                                                                  \
         const int64_t j0_ = klo + (int64_t)(j) * KT;                                                      \
         const int64_t nv_ = min(khi - j0_, (int64_t)KT);                                                  \
-        dma_tile<TILE, NW, BPW, D>(lds + ((j) & 1) * STAGE, kp, k_sn, vp, v_sn, j0_, nv_, koff, voff, wave); \
+        uint16_t* st_ = lds + ((j) & 1) * STAGE;                                                           \
+        dma_rows<NW, BPW, D>(st_, kp, k_sn, j0_, nv_, koff, wave);                                         \
+        dma_rows<NW, BPW, D>(st_ + TILE, vp, v_sn, j0_, nv_, voff, wave);                                  \
     } while (0)
 
     // per-lane LDS element offsets of the matrix-operand reads (relative to a stage)
@@ -946,60 +889,8 @@ __global__ void __launch_bounds__(512) fwd_dma_kernel(const FwdArgs a) {
 
 #undef CQSA_ISSUE_TILE
 
-    // ---- epilogue
-    const float ltot = lrun + __shfl_xor(lrun, 32);
     const int64_t row = iw0 + l32;
-    if (row >= i_end) return;
-    const float mnat = ltot > 0.f ? mrun * kLn2 : -INFINITY;
-    if (a.mode == FWD_FINAL) {
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        const int64_t ob = (int64_t)b * a.o_sb + (int64_t)hq * a.o_sh + row * a.o_sn;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-                store4(a.out, ob + db * 32 + 8 * g + 4 * hi, a.out_dtype, x * inv);
-            }
-        if (a.lse && hi == 0)
-            a.lse[(int64_t)b * a.l_sb + (int64_t)hq * a.l_sh + row] =
-                ltot > 0.f ? (mrun + __log2f(ltot)) * kLn2 : -INFINITY;
-        return;
-    }
-    const int64_t ridx = (((int64_t)split * a.B + b) * a.Hq + hq) * a.acc_rows + row;
-    float* op = a.acc_o + ridx * D;
-    float* mlp = a.acc_ml + ridx * 2;
-    if (a.mode == FWD_PARTIAL) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-                *reinterpret_cast<f32x4*>(op + db * 32 + 8 * g + 4 * hi) = x;
-            }
-        if (hi == 0) {
-            mlp[0] = mnat;
-            mlp[1] = ltot;
-        }
-        return;
-    }
-    const float ma = mlp[0], la = mlp[1];
-    const float mm = fmaxf(ma, mnat);
-    const float wa = ma == -INFINITY ? 0.f : exp2f((ma - mm) * kLog2e);
-    const float wb = mnat == -INFINITY ? 0.f : exp2f((mnat - mm) * kLog2e);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float* dst = op + db * 32 + 8 * g + 4 * hi;
-            const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
-            f32x4 x = {oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-            *reinterpret_cast<f32x4*>(dst) = old * wa + x * wb;
-        }
-    if (hi == 0) {
-        mlp[0] = mm;
-        mlp[1] = wa * la + wb * ltot;
-    }
+    fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
 // Log-sum-exp merge: TPR threads per row, four output dims per thread.  The threads of one row
@@ -1041,12 +932,12 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
     }
 }
 
-template <int D, int DT, int KT>
+template <int D, int DT, int KT, int NW, int WPE>
 hipError_t launch_dma_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT, NW, WPE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1068,40 +959,48 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Kernel choice per head dim: qb = 2 the DMA kernel, qb = 0 the ping-pong kernel, qb = 1 the
-// register-staged kernel (all 8 waves x 32 rows), with kt keys per tile.  Variant 0 is the default; CQSA_FWD_VARIANT picks another one
-// for measurement.
+// Kernel choice per head dim: kind 2 the DMA kernel (nw waves, kt keys per tile, wpe waves per SIMD
+// asked of the register allocator), kind 1 the register-staged kernel, kind 0 the ping-pong kernel.
+// Entry 0 is the default; the environment variable CQSA_FWD_VARIANT (read at every launch) selects
+// another entry, for measurement and for the tests that cover every kernel.
 struct Shape {
-    int qb, nw, kt;
+    int kind, nw, kt, wpe;
 };
-constexpr Shape kShapes64[] = {{2, 8, 128}, {0, 8, 128}, {1, 8, 128}, {2, 8, 64}};
-constexpr Shape kShapes128[] = {{2, 8, 64}, {0, 8, 64}, {1, 8, 64}, {1, 8, 128}};
+constexpr Shape kShapes64[] = {{2, 4, 64, 3}, {2, 8, 128, 2}, {1, 8, 128, 2}, {0, 8, 128, 2}};
+constexpr Shape kShapes128[] = {{2, 8, 64, 2}, {2, 8, 32, 2}, {1, 8, 64, 2}, {0, 8, 64, 2}};
+constexpr int kNumShapes = 4;
 
 int variant() {
-    static int v = -1;
-    if (v < 0) {
-        const char* e = getenv("CQSA_FWD_VARIANT");
-        v = (e && *e) ? atoi(e) : 0;
-        if (v < 0 || v > 3) v = 0;
-    }
-    return v;
+    const char* e = getenv("CQSA_FWD_VARIANT");
+    const int v = (e && *e) ? atoi(e) : 0;
+    return (v < 0 || v >= kNumShapes) ? 0 : v;
 }
 
 template <int D, int DT>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-    if (sh.qb == 2) {
-        if (sh.kt == 64) return launch_dma_t<D, DT, 64>(a, st);
-        if (sh.kt == 128) return launch_dma_t<D, DT, 128>(a, st);
+    if (sh.kind == 2) {
+#define CQSA_DMA_CASE(NW_, KT_, WPE_) \
+    if (sh.nw == NW_ && sh.kt == KT_ && sh.wpe == WPE_) return launch_dma_t<D, DT, KT_, NW_, WPE_>(a, st);
+        if constexpr (D == 64) {
+            CQSA_DMA_CASE(4, 64, 3)
+            CQSA_DMA_CASE(8, 128, 2)
+        } else {
+            CQSA_DMA_CASE(8, 64, 2)
+            CQSA_DMA_CASE(8, 32, 2)
+        }
+#undef CQSA_DMA_CASE
         return hipErrorInvalidValue;
     }
-    if (sh.qb == 0) {
+    if (sh.kind == 0) {
         if (sh.kt == 64) return launch_pp_t<D, DT, 64>(a, st);
-        if (sh.kt == 128) return launch_pp_t<D, DT, 128>(a, st);
+        if constexpr (D == 64)
+            if (sh.kt == 128) return launch_pp_t<D, DT, 128>(a, st);
         return hipErrorInvalidValue;
     }
     if (sh.kt == 64) return launch_fwd_t<D, DT, 1, 8, 64>(a, st);
-    if (sh.kt == 128) return launch_fwd_t<D, DT, 1, 8, 128>(a, st);
+    if constexpr (D == 64)
+        if (sh.kt == 128) return launch_fwd_t<D, DT, 1, 8, 128>(a, st);
     return hipErrorInvalidValue;
 }
 

@@ -7,9 +7,9 @@
  * largest scaled logit, l = sum_j exp(s_j - m).  Partials are merged exactly by
  * the log-sum-exp rule, so a context that does not fit in device memory can be
  * streamed from pinned host memory and still give the monolithic answer.  This
- * is the method of the Stream-CQSA pages ("exact out-of-memory recovery for
- * attention": stream-cqsa 2.2.2 -> 2.2.3 diff, README.md section "Use", and the
- * attention() docstring in stream_cqsa/api.py of the 2.2.0 -> 2.2.2 diff).
+ * is the method of the Stream-CQSA pages (exact attention for contexts past
+ * device memory: stream-cqsa 2.2.2 -> 2.2.3 diff, README.md section "Use", and
+ * the attention() docstring in stream_cqsa/api.py of the 2.2.0 -> 2.2.2 diff).
  *
  * Conventions shared by every entry point
  *   - Tensors are described by cqsa_tensor: shape [B, H, N, D] and element

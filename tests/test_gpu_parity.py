@@ -67,6 +67,26 @@ def test_small_full_parity(case):
         compare(out2, lse2, ref, dtype, label=f"{kw} {case}")
 
 
+VARIANT_CASES = [SMALL[1], SMALL[2], SMALL[3], SMALL[4], SMALL[7]]
+
+
+@pytest.mark.parametrize("variant", [1, 2, 3])
+def test_every_forward_kernel_variant(variant, monkeypatch):
+    """The non-default forward kernels (selected per launch by CQSA_FWD_VARIANT) on ragged, GQA,
+    non-causal and long-key cases, monolithic and with a forced KV split."""
+    monkeypatch.setenv("CQSA_FWD_VARIANT", str(variant))
+    for case in VARIANT_CASES:
+        B, Hq, Hkv, Nq, Nk, D, dtype, causal = case
+        say("variant", variant, case)
+        q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=2000 + Nq + Nk + D)
+        ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D))
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        for kw in ({}, {"kv_chunk": 200, "merge": 2}):
+            out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True, **kw)
+            torch.cuda.synchronize()
+            compare(out, lse, ref, dtype, label=f"variant {variant} {kw} {case}")
+
+
 def test_config1_four_kv_chunks_merged():
     """1024 causal rows, D=64, fp16, KV chunk 256: each Q block folds its visible chunks by LSE."""
     w = synth.workload(0)
