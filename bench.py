@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
-                    "(default profiles/fwd_kernel_<workload>.md)")
+                    "(default profiles/<forward kernel>_<workload>.md)")
     return ap.parse_args()
 
 
@@ -197,7 +197,8 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms (events {ms_kernel:.3f} ms, min {min(per):.3f}) -> {value:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
-    prof_path = args.profile or os.path.join(ROOT, "profiles", f"fwd_kernel_{w.name}.md")
+    kernel = cqsa.fwd_kernel_name(w.D)
+    prof_path = args.profile or os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_{w.name}.md")
     traffic, traffic_src = measured_traffic(prof_path)
     line = {
         "metric": "causal attention fwd TFLOP/s & % MFMA peak (1 GPU); tokens/s at 4M ctx",
@@ -221,7 +222,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic,
                      "traffic_source": traffic_src,
-                     "kernel": "fwd_kernel (D=%d, %s)" % (w.D, "f16" if w.dtype == torch.float16 else "bf16"),
+                     "kernel": kernel,
                      "kernel_ms": round(ms_kernel, 4),
                      "launches_per_step": info["kernel_launches"]},
     }

@@ -18,6 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
+           "fwd_kernel_name",
            "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +61,11 @@ class CqsaError(RuntimeError):
         self.status = status
 
 
+def fwd_kernel_name(head_dim: int) -> str:
+    """The forward kernel (name and shape) a call with this head dim launches."""
+    return _lib.cqsa_fwd_kernel_name(int(head_dim)).decode()
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -93,6 +99,8 @@ def _load_library():
     lib.cqsa_version.restype = ctypes.c_int32
     lib.cqsa_struct_size.argtypes = [ctypes.c_int32]
     lib.cqsa_struct_size.restype = ctypes.c_uint64
+    lib.cqsa_fwd_kernel_name.argtypes = [ctypes.c_int64]
+    lib.cqsa_fwd_kernel_name.restype = ctypes.c_char_p
     for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo)):
         if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"{cls.__name__} layout differs from the built library")

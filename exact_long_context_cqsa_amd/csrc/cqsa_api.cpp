@@ -956,6 +956,10 @@ uint64_t cqsa_struct_size(int32_t which) {
     }
 }
 
+const char* cqsa_fwd_kernel_name(int64_t head_dim) {
+    return (head_dim == 64 || head_dim == 128) ? fwd_kernel_name((int)head_dim) : "";
+}
+
 cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
                       uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
                       cqsa_plan_info* info) {

@@ -74,6 +74,9 @@ struct MergeArgs {
 // Query rows per workgroup of the forward kernel for a head dim.
 int fwd_block_m(int D);
 
+// Name and shape of the forward kernel launched for a head dim ("" if none).
+const char* fwd_kernel_name(int D);
+
 // Launchers (return the launch status).
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -1011,6 +1011,22 @@ int fwd_block_m(int D) {
     return sh.nw * 32;
 }
 
+const char* fwd_kernel_name(int D) {
+    static const char* const k64[kNumShapes] = {
+        "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32",
+        "fwd_dma_kernel waves=8 keys_per_tile=128 rows_per_wave=32",
+        "fwd_kernel waves=8 keys_per_tile=128 rows_per_wave=32",
+        "fwd_pp_kernel waves=8 keys_per_tile=128 rows_per_wave=32"};
+    static const char* const k128[kNumShapes] = {
+        "fwd_dma_kernel waves=8 keys_per_tile=64 rows_per_wave=32",
+        "fwd_dma_kernel waves=8 keys_per_tile=32 rows_per_wave=32",
+        "fwd_kernel waves=8 keys_per_tile=64 rows_per_wave=32",
+        "fwd_pp_kernel waves=8 keys_per_tile=64 rows_per_wave=32"};
+    if (D == 64) return k64[variant()];
+    if (D == 128) return k128[variant()];
+    return "";
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
     if (D == 64 && dtype == ET_F16) return launch_d<64, ET_F16>(a, stream);
     if (D == 64 && dtype == ET_BF16) return launch_d<64, ET_BF16>(a, stream);

@@ -132,6 +132,7 @@ def main():
     args = ap.parse_args()
     text = summarise(args)
     out = args.out or os.path.join(ROOT, "profiles", args.name + ".md")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     with open(out, "w") as f:
         f.write(text)
     print(text)

@@ -206,6 +206,12 @@ int32_t cqsa_version(void);
  * 0 = cqsa_tensor, 1 = cqsa_options, 2 = cqsa_plan_info; 0 for other values. */
 uint64_t cqsa_struct_size(int32_t which);
 
+/* Name and shape of the forward kernel a call with this head dim (64 or 128) launches, e.g.
+ * "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32"; "" for another head dim.  The choice
+ * follows the environment variable CQSA_FWD_VARIANT (0 or unset = the default kernel), read at
+ * every launch.  The string is static; no HIP call is made. */
+const char* cqsa_fwd_kernel_name(int64_t head_dim);
+
 #ifdef __cplusplus
 }
 #endif

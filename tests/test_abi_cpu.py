@@ -35,6 +35,18 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+def test_forward_kernel_name(monkeypatch):
+    import exact_long_context_cqsa_amd as m
+    monkeypatch.delenv("CQSA_FWD_VARIANT", raising=False)
+    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
+    assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ")
+    assert m.fwd_kernel_name(96) == ""
+    monkeypatch.setenv("CQSA_FWD_VARIANT", "2")
+    assert m.fwd_kernel_name(64).startswith("fwd_kernel ")
+    monkeypatch.setenv("CQSA_FWD_VARIANT", "99")   # out of range: the default
+    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
+
+
 def test_struct_layout_and_version():
     import exact_long_context_cqsa_amd as m
     lib = m._lib
