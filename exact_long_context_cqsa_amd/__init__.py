@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
-           "fwd_kernel_name",
+           "fwd_kernel_name", "cqs_assign", "cqs_default_set",
            "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -39,7 +39,8 @@ class CqsaTensor(ctypes.Structure):
 class CqsaOptions(ctypes.Structure):
     _fields_ = [("q_chunk", ctypes.c_int64), ("kv_chunk", ctypes.c_int64), ("kv_splits", ctypes.c_int32),
                 ("merge_mode", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
-                ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("cqs_c", ctypes.c_int32),
+                ("cqs_l", ctypes.c_int32), ("reserved", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32))]
 
 
 class CqsaPlanInfo(ctypes.Structure):
@@ -49,7 +50,8 @@ class CqsaPlanInfo(ctypes.Structure):
                 ("merges", ctypes.c_int64), ("kernel_launches", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_uint64), ("budget_bytes", ctypes.c_uint64),
                 ("h2d_bytes", ctypes.c_uint64), ("d2h_bytes", ctypes.c_uint64), ("h2d_ms", ctypes.c_double),
-                ("d2h_ms", ctypes.c_double), ("wall_ms", ctypes.c_double)]
+                ("d2h_ms", ctypes.c_double), ("wall_ms", ctypes.c_double), ("cqs_c", ctypes.c_int32),
+                ("cqs_subproblems", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -101,6 +103,11 @@ def _load_library():
     lib.cqsa_struct_size.restype = ctypes.c_uint64
     lib.cqsa_fwd_kernel_name.argtypes = [ctypes.c_int64]
     lib.cqsa_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.cqsa_cqs_assign.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32)]
+    lib.cqsa_cqs_assign.restype = ctypes.c_int
+    lib.cqsa_cqs_default_set.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    lib.cqsa_cqs_default_set.restype = ctypes.c_int32
     for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo)):
         if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"{cls.__name__} layout differs from the built library")
@@ -145,9 +152,39 @@ def _device_of(*ts) -> torch.device | None:
     return None
 
 
+def _int_array(xs):
+    return (ctypes.c_int32 * len(xs))(*[int(x) for x in xs])
+
+
+def cqs_default_set(c: int) -> tuple:
+    """The library's built-in interest set for c parts (empty tuple if none)."""
+    buf = (ctypes.c_int32 * 64)()
+    n = _lib.cqsa_cqs_default_set(int(c), buf, 64)
+    return tuple(buf[i] for i in range(n))
+
+
+def cqs_assign(c: int, interest_set) -> list:
+    """owner[a][b]: the subproblem of the quorum-set schedule that computes (query part a, key part b)."""
+    arr = _int_array(interest_set)
+    own = (ctypes.c_int32 * (int(c) * int(c)))()
+    _check(_lib.cqsa_cqs_assign(int(c), arr, len(arr), own))
+    return [[own[a * c + b] for b in range(c)] for a in range(c)]
+
+
 def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=None, workspace=None,
-             num_cus=None) -> CqsaOptions:
+             num_cus=None, cqs=None) -> CqsaOptions:
+    """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set)."""
     o = CqsaOptions()
+    if cqs is not None:
+        if isinstance(cqs, int):
+            o.cqs_c = cqs
+        else:
+            c, iset = cqs
+            o.cqs_c = int(c)
+            arr = _int_array(iset)
+            o.cqs_l = len(arr)
+            o.cqs_set = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32))
+            o._keep = arr   # the array lives as long as the options
     o.q_chunk = int(q_chunk or 0)
     o.kv_chunk = int(kv_chunk or 0)
     o.kv_splits = int(kv_splits or 0)
@@ -161,7 +198,7 @@ def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=Non
 
 
 def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
-         kv_splits=None, merge=None, where=None, num_cus=None) -> dict:
+         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None) -> dict:
     """The plan ``attention`` would run (nothing is allocated or computed).
 
     ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
@@ -190,7 +227,7 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
         out = (qshape, qdt)
     do = mk("out", out, None)
     info = CqsaPlanInfo()
-    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus)
+    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs)
     _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
                           int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
                           ctypes.byref(info)))
@@ -201,15 +238,17 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
               mem_budget: int | None = None, *, q_chunk: int | None = None, kv_chunk: int | None = None,
               kv_splits: int | None = None, merge: int | None = None, out: torch.Tensor | None = None,
               out_dtype: torch.dtype | None = None, return_lse: bool = False, return_info: bool = False,
-              stream: torch.cuda.Stream | None = None):
+              stream: torch.cuda.Stream | None = None, cqs=None):
     """Exact ``softmax(scale * q k^T [+ causal mask]) v`` (SDPA semantics; causal is bottom-right
     aligned when Nq < Nk; GQA when k/v have fewer heads).
 
     q: [B, Hq, Nq, D], k/v: [B, Hkv, Nk, D], fp16 or bf16, D in {64, 128}; each on the GPU or in
     pinned host memory (then streamed in chunks).  ``mem_budget`` caps the device bytes the call
     uses (0/None: the free memory).  ``kv_chunk``/``q_chunk`` force a decomposition; ``merge``
-    picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  Returns out (on q's device; pinned
-    host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the plan dict on request."""
+    picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  ``cqs`` runs the cyclic quorum-set
+    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set).  Returns out
+    (on q's device; pinned host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the
+    plan dict on request."""
     dev = _device_of(q, k, v, out)
     if dev is None:
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -227,7 +266,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)
         dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
-        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream)
+        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs)
         budget = int(mem_budget or 0)
         # size the workspace first so that device-resident calls take it from PyTorch's allocator
         # (stream-ordered, no hipMalloc, no synchronisation)

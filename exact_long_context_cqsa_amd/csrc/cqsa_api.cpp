@@ -9,6 +9,10 @@
 // its buffer and each compute after its copy (the two-stream pattern of block-streamer 0.1.0,
 // README section "Streams, residency, and memory budget").  Output bound for host memory leaves
 // on a third stream.
+//
+// A second schedule runs the cyclic quorum-set decomposition of the Stream-CQSA pages (depth 1):
+// c parts, subproblem i holding parts (i + s) mod c for s in the interest set, each (query part, key
+// part) pair computed once by its owner subproblem and folded into a device accumulator.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,6 +49,12 @@ cqsa_status fail(cqsa_status s, const char* fmt, ...) {
     do {                                                                                                   \
         hipError_t e_ = (expr);                                                                            \
         if (e_ != hipSuccess) return fail(CQSA_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));   \
+    } while (0)
+
+#define CQSA_TRY(expr)                        \
+    do {                                      \
+        cqsa_status s_ = (expr);              \
+        if (s_ != CQSA_OK) return s_;         \
     } while (0)
 
 constexpr double kSafety = 0.85;           // fraction of the budget the planner fills
@@ -200,6 +210,13 @@ struct Plan {
     uint64_t off_q = 0, off_k[2] = {0, 0}, off_v[2] = {0, 0};
     uint64_t off_acc_o = 0, off_acc_ml = 0, off_part_o = 0, off_part_ml = 0, off_out = 0, off_lse = 0;
     uint64_t total = 0;
+    // cyclic quorum-set schedule
+    bool cqs = false;
+    int cqs_c = 0;
+    int cqs_nbuf = 0;                      // staging sets (1 or 2)
+    std::vector<int> cqs_owner;            // owner[a * c + b]
+    uint64_t off_stage[2] = {0, 0}, stage_bytes = 0;
+    int64_t out_rows = 0;                  // query rows per finalize chunk (host output)
 };
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -277,6 +294,167 @@ void count_chunked(const Problem& P, Plan* pl) {
     (void)max_kv;
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// cyclic quorum-set schedule
+
+// Perfect difference sets (every nonzero residue mod c is exactly one difference of two elements).
+struct QuorumSet {
+    int c, l;
+    int s[8];
+};
+constexpr QuorumSet kQuorumSets[] = {
+    {3, 2, {0, 1}}, {7, 3, {0, 1, 3}}, {13, 4, {0, 1, 3, 9}}, {21, 5, {0, 1, 4, 14, 16}}, {31, 6, {0, 1, 3, 8, 12, 18}}};
+
+int default_quorum_set(int c, int* out, int max_l) {
+    for (const QuorumSet& q : kQuorumSets)
+        if (q.c == c) {
+            for (int i = 0; i < q.l && i < max_l; ++i) out[i] = q.s[i];
+            return q.l;
+        }
+    return 0;
+}
+
+// Validates the set and fills owner[a * c + b]: the smallest subproblem i whose parts
+// {(i + s) mod c} contain both a and b.
+cqsa_status quorum_owner(int c, const int* set, int l, std::vector<int>* owner) {
+    if (c < 1 || c > 4096) return fail(CQSA_ERR_INVALID, "cqs: c = %d is outside [1, 4096]", c);
+    if (l < 1 || l > c) return fail(CQSA_ERR_INVALID, "cqs: interest set size %d is outside [1, c = %d]", l, c);
+    if (!set) return fail(CQSA_ERR_INVALID, "cqs: interest set is NULL");
+    std::vector<char> in(c, 0);
+    for (int u = 0; u < l; ++u) {
+        if (set[u] < 0 || set[u] >= c) return fail(CQSA_ERR_INVALID, "cqs: set element %d is outside [0, %d)", set[u], c);
+        if (in[set[u]]) return fail(CQSA_ERR_INVALID, "cqs: set element %d is repeated", set[u]);
+        in[set[u]] = 1;
+    }
+    owner->assign((size_t)c * c, -1);
+    for (int a = 0; a < c; ++a)
+        for (int u = 0; u < l; ++u) {
+            const int i = ((a - set[u]) % c + c) % c;       // a is in subproblem i
+            for (int v = 0; v < l; ++v) {
+                const int b = (i + set[v]) % c;             // so is b
+                int& o = (*owner)[(size_t)a * c + b];
+                if (o < 0 || i < o) o = i;
+            }
+        }
+    for (int a = 0; a < c; ++a)
+        for (int b = 0; b < c; ++b)
+            if ((*owner)[(size_t)a * c + b] < 0)
+                return fail(CQSA_ERR_INVALID, "cqs: parts %d and %d share no subproblem (not a quorum set mod %d)", a, b, c);
+    return CQSA_OK;
+}
+
+int64_t part_lo(int64_t n, int c, int p) { return n * p / c; }
+
+// Does any key of key part b lie at or before the last row of query part a (causal)?
+bool pair_visible(const Problem& P, int c, int a, int b) {
+    const int64_t qa = part_lo(P.Nq, c, a), qe = part_lo(P.Nq, c, a + 1);
+    const int64_t ka = part_lo(P.Nk, c, b), ke = part_lo(P.Nk, c, b + 1);
+    if (qe <= qa || ke <= ka) return false;
+    if (!P.causal) return true;
+    return ka <= (P.Nk - P.Nq) + qe - 1;
+}
+
+cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options& opt, Plan* pl) {
+    const int c = opt.cqs_c;
+    int dflt[8];
+    const int* set = opt.cqs_set;
+    int l = opt.cqs_l;
+    if (!set) {
+        l = default_quorum_set(c, dflt, 8);
+        if (l == 0) return fail(CQSA_ERR_INVALID, "cqs: no built-in interest set for c = %d; pass cqs_set", c);
+        set = dflt;
+    }
+    CQSA_TRY(quorum_owner(c, set, l, &pl->cqs_owner));
+    if (opt.q_chunk > 0 || opt.kv_chunk > 0 || opt.kv_splits > 1)
+        return fail(CQSA_ERR_INVALID, "cqs: q_chunk, kv_chunk and kv_splits do not apply to the quorum-set schedule");
+    pl->cqs = true;
+    pl->chunked = true;
+    pl->cqs_c = c;
+    pl->merge = CQSA_MERGE_FUSED;
+    pl->kv_splits = 1;
+    // staging per subproblem (host operands only) and the traffic of the whole schedule
+    const uint64_t qrow = (uint64_t)P.B * P.Hq * P.D * 2, kvrow = (uint64_t)P.B * P.Hkv * P.D * 2;
+    uint64_t stage = 0, h2d = 0;
+    int64_t pairs = 0, subs = 0, max_q = 0, max_k = 0;
+    for (int i = 0; i < c; ++i) {
+        std::vector<char> qp(c, 0), kp(c, 0);
+        bool any = false;
+        for (int a = 0; a < c; ++a)
+            for (int b = 0; b < c; ++b)
+                if (pl->cqs_owner[(size_t)a * c + b] == i && pair_visible(P, c, a, b)) {
+                    qp[a] = kp[b] = 1;
+                    any = true;
+                    ++pairs;
+                }
+        if (!any) continue;
+        ++subs;
+        uint64_t bytes = 0;
+        for (int a = 0; a < c; ++a) {
+            const int64_t n = part_lo(P.Nq, c, a + 1) - part_lo(P.Nq, c, a);
+            max_q = std::max(max_q, n);
+            if (qp[a] && P.q.host) {
+                bytes = align_up(bytes + (uint64_t)n * qrow, 256);
+                h2d += (uint64_t)n * qrow;
+            }
+        }
+        for (int b = 0; b < c; ++b) {
+            const int64_t n = part_lo(P.Nk, c, b + 1) - part_lo(P.Nk, c, b);
+            max_k = std::max(max_k, n);
+            if (kp[b] && P.k.host) {
+                bytes = align_up(bytes + (uint64_t)n * kvrow, 256);
+                h2d += (uint64_t)n * kvrow;
+            }
+            if (kp[b] && P.v.host) {
+                bytes = align_up(bytes + (uint64_t)n * kvrow, 256);
+                h2d += (uint64_t)n * kvrow;
+            }
+        }
+        stage = std::max(stage, bytes);
+    }
+    const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
+    uint64_t off = 0;
+    auto take = [&](uint64_t b) {
+        const uint64_t at = off;
+        off = align_up(off + b, 256);
+        return at;
+    };
+    pl->off_acc_o = take(rows * P.D * 4);
+    pl->off_acc_ml = take(rows * 8);
+    pl->out_rows = max_q;
+    const uint64_t orows = (uint64_t)P.B * P.Hq * max_q;
+    pl->off_out = P.out.host ? take(orows * P.D * P.out.es) : 0;
+    pl->off_lse = (P.want_lse && P.lse_host) ? take(orows * 4) : 0;
+    const uint64_t base = off;
+    pl->stage_bytes = stage;
+    int nbuf = stage == 0 ? 0 : 2;
+    if (nbuf == 2 && base + 2 * align_up(stage, 256) > budget) nbuf = 1;
+    pl->cqs_nbuf = nbuf;
+    for (int i = 0; i < nbuf; ++i) pl->off_stage[i] = take(stage);
+    pl->total = off;
+    if (pl->total > budget)
+        return fail(CQSA_ERR_BUDGET,
+                    "mem_budget too small for the quorum-set schedule over c = %d parts: needs %llu bytes "
+                    "(x 1/0.85 = %llu)", c, (unsigned long long)pl->total,
+                    (unsigned long long)(pl->total / kSafety) + 1);
+    cqsa_plan_info& in = pl->info;
+    in.merge_mode = CQSA_MERGE_FUSED;
+    in.q_chunk = max_q;
+    in.kv_chunk = max_k;
+    in.n_q_chunks = c;
+    in.n_kv_chunks = c;
+    in.kv_splits = 1;
+    in.chunk_pairs = pairs;
+    in.merges = pairs;
+    in.kernel_launches = pairs + 1 + (P.out.host ? c : 1);   // pairs, accumulator fill, finalize
+    in.workspace_bytes = pl->total;
+    in.h2d_bytes = h2d;
+    in.d2h_bytes = P.out.host ? rows * P.D * P.out.es + ((P.want_lse && P.lse_host) ? rows * 4 : 0) : 0;
+    in.cqs_c = c;
+    in.cqs_subproblems = (int32_t)subs;
+    return CQSA_OK;
+}
+
 cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt, int num_cus, Plan* pl) {
     std::memset(&pl->info, 0, sizeof pl->info);
     pl->bm = fwd_block_m((int)P.D);
@@ -287,6 +465,8 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
         pl->info.q_chunk = 0;
         return CQSA_OK;
     }
+    if (opt.cqs_c < 0) return fail(CQSA_ERR_INVALID, "cqs_c %d is negative", opt.cqs_c);
+    if (opt.cqs_c > 0) return make_plan_cqs(P, budget, opt, pl);
     const int req_merge = opt.merge_mode;
     if (req_merge < 0 || req_merge > 2) return fail(CQSA_ERR_INVALID, "merge_mode %d is not 0, 1 or 2", req_merge);
     if (opt.q_chunk < 0 || opt.kv_chunk < 0 || opt.kv_splits < 0)
@@ -644,11 +824,6 @@ struct TimedCopy {
     hipEvent_t start, stop;
 };
 
-#define CQSA_TRY(expr)                        \
-    do {                                      \
-        cqsa_status s_ = (expr);              \
-        if (s_ != CQSA_OK) return s_;         \
-    } while (0)
 
 // Q chunks x KV chunks; operands may live in pinned host memory.
 cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t st, DeviceRes* res,
@@ -891,6 +1066,233 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
     return CQSA_OK;
 }
 
+// The quorum-set schedule (make_plan_cqs): the accumulator for every query row starts as the
+// identity (0, -inf, 0); each subproblem stages the parts of its owned non-empty pairs (host
+// operands, into one of two staging sets that alternate) and folds one forward launch per pair into
+// the accumulator rows of the pair's query part; a last pass normalises (and ships host output in
+// query-part-sized pieces).
+cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st, DeviceRes* res,
+                     cqsa_plan_info* info) {
+    const int c = pl.cqs_c;
+    const bool host_in = P.q.host || P.k.host || P.v.host;
+    const bool host_out = P.out.host || (P.want_lse && P.lse_host);
+    hipStream_t h2d = st, d2h = st;
+    if (host_in || host_out) {
+        CQSA_TRY(side_streams(res));
+        h2d = res->h2d;
+        d2h = res->d2h;
+    }
+    EventSet es;
+    hipEvent_t ev_start, ev_fin, ev_d2h, ev_copy[2], ev_comp[2];
+    CQSA_TRY(es.make(&ev_start, false));
+    CQSA_TRY(es.make(&ev_fin, false));
+    CQSA_TRY(es.make(&ev_d2h, false));
+    for (int i = 0; i < 2; ++i) {
+        CQSA_TRY(es.make(&ev_copy[i], false));
+        CQSA_TRY(es.make(&ev_comp[i], false));
+    }
+    std::vector<TimedCopy> h2d_t, d2h_t;
+    auto timed = [&](std::vector<TimedCopy>& v, TimedCopy* tc) -> cqsa_status {
+        CQSA_TRY(es.make(&tc->start, true));
+        CQSA_TRY(es.make(&tc->stop, true));
+        v.push_back(*tc);
+        return CQSA_OK;
+    };
+    CQSA_HIP(hipEventRecord(ev_start, st));
+    if (host_in || host_out) {
+        CQSA_HIP(hipStreamWaitEvent(h2d, ev_start, 0));
+        CQSA_HIP(hipStreamWaitEvent(d2h, ev_start, 0));
+    }
+    float* acc_o = reinterpret_cast<float*>(ws + pl.off_acc_o);
+    float* acc_ml = reinterpret_cast<float*>(ws + pl.off_acc_ml);
+    {
+        MergeArgs m;   // no parts: writes the identity triple
+        std::memset(&m, 0, sizeof m);
+        m.n_parts = 0;
+        m.D = (int32_t)P.D;
+        m.B = (int32_t)P.B;
+        m.Hq = (int32_t)P.Hq;
+        m.rows_per_head = P.Nq;
+        m.i_lo = 0;
+        m.i_hi = P.Nq;
+        m.o_out = acc_o;
+        m.ml_out = acc_ml;
+        CQSA_TRY(run_merge(m, st));
+    }
+    const uint64_t qrow = (uint64_t)P.B * P.Hq * P.D * 2, kvrow = (uint64_t)P.B * P.Hkv * P.D * 2;
+    bool comp_recorded[2] = {false, false};
+    int run = 0;
+    std::vector<uint64_t> qoff(c), koff(c), voff(c);
+    for (int i = 0; i < c; ++i) {
+        std::vector<std::pair<int, int>> prs;
+        std::vector<char> qp(c, 0), kp(c, 0);
+        for (int a = 0; a < c; ++a)
+            for (int b = 0; b < c; ++b)
+                if (pl.cqs_owner[(size_t)a * c + b] == i && pair_visible(P, c, a, b)) {
+                    prs.emplace_back(a, b);
+                    qp[a] = kp[b] = 1;
+                }
+        if (prs.empty()) continue;
+        const int buf = pl.cqs_nbuf == 2 ? (run & 1) : 0;
+        char* stg = ws + pl.off_stage[buf];
+        if (host_in) {
+            if (comp_recorded[buf]) CQSA_HIP(hipStreamWaitEvent(h2d, ev_comp[buf], 0));
+            TimedCopy tc;
+            CQSA_TRY(timed(h2d_t, &tc));
+            CQSA_HIP(hipEventRecord(tc.start, h2d));
+            uint64_t o = 0;
+            for (int a = 0; a < c; ++a)
+                if (qp[a] && P.q.host) {
+                    const int64_t lo = part_lo(P.Nq, c, a), n = part_lo(P.Nq, c, a + 1) - lo;
+                    qoff[a] = o;
+                    CQSA_TRY(copy_rows(P.q, lo, n, stg + o, true, h2d));
+                    o = align_up(o + (uint64_t)n * qrow, 256);
+                }
+            for (int b = 0; b < c; ++b)
+                if (kp[b]) {
+                    const int64_t lo = part_lo(P.Nk, c, b), n = part_lo(P.Nk, c, b + 1) - lo;
+                    if (P.k.host) {
+                        koff[b] = o;
+                        CQSA_TRY(copy_rows(P.k, lo, n, stg + o, true, h2d));
+                        o = align_up(o + (uint64_t)n * kvrow, 256);
+                    }
+                    if (P.v.host) {
+                        voff[b] = o;
+                        CQSA_TRY(copy_rows(P.v, lo, n, stg + o, true, h2d));
+                        o = align_up(o + (uint64_t)n * kvrow, 256);
+                    }
+                }
+            CQSA_HIP(hipEventRecord(tc.stop, h2d));
+            CQSA_HIP(hipEventRecord(ev_copy[buf], h2d));
+            CQSA_HIP(hipStreamWaitEvent(st, ev_copy[buf], 0));
+        }
+        for (const auto& pr : prs) {
+            const int a = pr.first, b = pr.second;
+            const int64_t qa = part_lo(P.Nq, c, a), qn = part_lo(P.Nq, c, a + 1) - qa;
+            const int64_t ka = part_lo(P.Nk, c, b), kn = part_lo(P.Nk, c, b + 1) - ka;
+            FwdArgs fa = base_args(P);
+            if (P.q.host) {
+                const Compact cq = compact_for(P.q, qn);
+                set_q(fa, stg + qoff[a], cq.sb, cq.sh, cq.sn);
+            } else {
+                set_q(fa, P.q.data + (size_t)(qa * P.q.sn) * 2, P.q.sb, P.q.sh, P.q.sn);
+            }
+            if (P.k.host) {
+                const Compact ck = compact_for(P.k, kn);
+                set_k(fa, stg + koff[b], ck.sb, ck.sh, ck.sn);
+            } else {
+                set_k(fa, P.k.data + (size_t)(ka * P.k.sn) * 2, P.k.sb, P.k.sh, P.k.sn);
+            }
+            if (P.v.host) {
+                const Compact cv = compact_for(P.v, kn);
+                set_v(fa, stg + voff[b], cv.sb, cv.sh, cv.sn);
+            } else {
+                set_v(fa, P.v.data + (size_t)(ka * P.v.sn) * 2, P.v.sb, P.v.sh, P.v.sn);
+            }
+            const int64_t pos0 = P.Nk - P.Nq + qa;  // key position of the part's first query row
+            fa.k_lo = 0;
+            fa.k_hi = kn;
+            fa.split_len = kn;
+            fa.causal_delta = pos0 - ka;
+            fa.r0 = P.causal ? std::max<int64_t>(0, ka - pos0) : 0;
+            fa.r1 = qn;
+            fa.mode = FWD_ACCUM;
+            fa.acc_o = acc_o + qa * P.D;
+            fa.acc_ml = acc_ml + qa * 2;
+            fa.acc_rows = P.Nq;
+            CQSA_TRY(run_fwd(P, fa, st));
+        }
+        CQSA_HIP(hipEventRecord(ev_comp[buf], st));
+        comp_recorded[buf] = true;
+        ++run;
+    }
+    // normalise
+    MergeArgs m;
+    std::memset(&m, 0, sizeof m);
+    m.part_o[0] = acc_o;
+    m.part_ml[0] = acc_ml;
+    m.n_parts = 1;
+    m.D = (int32_t)P.D;
+    m.B = (int32_t)P.B;
+    m.Hq = (int32_t)P.Hq;
+    m.rows_per_head = P.Nq;
+    m.final_out = 1;
+    m.out_dtype = elem_type(P.out.dtype);
+    const bool lse_host = P.want_lse && P.lse_host;
+    const int64_t step = host_out ? std::max<int64_t>(pl.out_rows, 1) : P.Nq;
+    bool d2h_recorded = false;
+    for (int64_t qa = 0; qa < P.Nq; qa += step) {
+        const int64_t qn = std::min(step, P.Nq - qa);
+        m.i_lo = qa;
+        m.i_hi = qa + qn;
+        if (P.out.host) {
+            const Compact co = compact_for(P.out, qn);
+            m.out = ws + pl.off_out;
+            m.o_sb = co.sb;
+            m.o_sh = co.sh;
+            m.o_sn = co.sn;
+        } else {
+            m.out = P.out.data + (size_t)(qa * P.out.sn) * P.out.es;
+            m.o_sb = P.out.sb;
+            m.o_sh = P.out.sh;
+            m.o_sn = P.out.sn;
+        }
+        m.lse = nullptr;
+        if (P.want_lse) {
+            if (lse_host) {
+                m.lse = reinterpret_cast<float*>(ws + pl.off_lse);
+                m.l_sb = P.Hq * qn;
+                m.l_sh = qn;
+            } else {
+                m.lse = P.lse + qa;
+                m.l_sb = P.Hq * P.Nq;
+                m.l_sh = P.Nq;
+            }
+        }
+        if (host_out && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+        CQSA_TRY(run_merge(m, st));
+        if (host_out) {
+            CQSA_HIP(hipEventRecord(ev_fin, st));
+            CQSA_HIP(hipStreamWaitEvent(d2h, ev_fin, 0));
+            TimedCopy tc;
+            CQSA_TRY(timed(d2h_t, &tc));
+            CQSA_HIP(hipEventRecord(tc.start, d2h));
+            if (P.out.host) CQSA_TRY(copy_rows(P.out, qa, qn, ws + pl.off_out, false, d2h));
+            if (lse_host)
+                CQSA_TRY(copy_lse_rows(P.lse, reinterpret_cast<float*>(ws + pl.off_lse), P.B, P.Hq, P.Nq, qa, qn, d2h));
+            CQSA_HIP(hipEventRecord(tc.stop, d2h));
+            CQSA_HIP(hipEventRecord(ev_d2h, d2h));
+            d2h_recorded = true;
+        }
+    }
+    if (host_in || host_out) {
+        hipEvent_t j1, j2;
+        CQSA_TRY(es.make(&j1, false));
+        CQSA_TRY(es.make(&j2, false));
+        CQSA_HIP(hipEventRecord(j1, h2d));
+        CQSA_HIP(hipEventRecord(j2, d2h));
+        CQSA_HIP(hipStreamWaitEvent(st, j1, 0));
+        CQSA_HIP(hipStreamWaitEvent(st, j2, 0));
+        CQSA_HIP(hipStreamSynchronize(st));
+        double h = 0, d = 0;
+        for (auto& t : h2d_t) {
+            float ms = 0;
+            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            h += ms;
+        }
+        for (auto& t : d2h_t) {
+            float ms = 0;
+            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            d += ms;
+        }
+        if (info) {
+            info->h2d_ms = h;
+            info->d2h_ms = d;
+        }
+    }
+    return CQSA_OK;
+}
+
 cqsa_status build_problem(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
                           float scale, const cqsa_tensor* out, float* lse, int want_lse, bool detect, bool allow_null,
                           Problem* P) {
@@ -954,6 +1356,24 @@ uint64_t cqsa_struct_size(int32_t which) {
         case 2: return sizeof(cqsa_plan_info);
         default: return 0;
     }
+}
+
+cqsa_status cqsa_cqs_assign(int32_t c, const int32_t* interest_set, int32_t l, int32_t* owner) {
+    g_err.clear();
+    if (!owner) return fail(CQSA_ERR_INVALID, "owner is NULL");
+    std::vector<int> set(interest_set ? interest_set : nullptr, interest_set ? interest_set + std::max(l, 0) : nullptr);
+    std::vector<int> own;
+    CQSA_TRY(quorum_owner(c, interest_set ? set.data() : nullptr, l, &own));
+    for (size_t i = 0; i < own.size(); ++i) owner[i] = own[i];
+    return CQSA_OK;
+}
+
+int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l) {
+    int tmp[8];
+    const int l = default_quorum_set(c, tmp, 8);
+    if (set)
+        for (int i = 0; i < l && i < max_l; ++i) set[i] = tmp[i];
+    return l;
 }
 
 const char* cqsa_fwd_kernel_name(int64_t head_dim) {
@@ -1026,7 +1446,9 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
         }
     }
     cqsa_status s;
-    if (!pl.chunked)
+    if (pl.cqs)
+        s = exec_cqs(P, pl, ws, st, res, &pl.info);
+    else if (!pl.chunked)
         s = exec_single(P, pl, ws, st);
     else
         s = exec_chunked(P, pl, ws, st, res, &pl.info);

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define CQSA_ABI_VERSION 1
+#define CQSA_ABI_VERSION 2
 
 typedef enum {
     CQSA_OK = 0,
@@ -89,7 +89,12 @@ typedef struct {
     uint64_t workspace_bytes; /* its size */
     void* stream;             /* hipStream_t carrying the compute; NULL = the null stream */
     int32_t num_cus;          /* cqsa_plan only: compute units to plan for; 0 = ask the device */
+    int32_t cqs_c;            /* > 0: run the cyclic quorum-set schedule over cqs_c parts (below);
+                                 0 = the Q-chunk x KV-chunk grid */
+    int32_t cqs_l;            /* size of the interest set cqs_set */
     int32_t reserved;
+    const int32_t* cqs_set;   /* the interest set: cqs_l distinct part offsets in [0, cqs_c);
+                                 NULL = the built-in set for cqs_c (see cqsa_cqs_default_set) */
 } cqsa_options;
 
 /* What a plan does (filled by cqsa_plan and cqsa_attention_ex). */
@@ -112,6 +117,8 @@ typedef struct {
     double h2d_ms;             /* summed duration of the H2D copies (HIP events; streamed calls) */
     double d2h_ms;             /* summed duration of the D2H copies */
     double wall_ms;            /* host wall time of a synchronising call */
+    int32_t cqs_c;             /* parts of a quorum-set schedule (0 = grid schedule) */
+    int32_t cqs_subproblems;   /* subproblems that run (those owning at least one non-empty part pair) */
 } cqsa_plan_info;
 
 /*
@@ -205,6 +212,32 @@ int32_t cqsa_version(void);
 /* sizeof of the ABI structs, for bindings to check their layout:
  * 0 = cqsa_tensor, 1 = cqsa_options, 2 = cqsa_plan_info; 0 for other values. */
 uint64_t cqsa_struct_size(int32_t which);
+
+/*
+ * Cyclic quorum-set (CQS) schedule.  The method decomposes one attention call into c^itr
+ * subproblems over c parts of the sequence, each subproblem holding an interest set of l parts,
+ * with work factor (l^2/c)^itr (stream-cqsa 2.2.0 -> 2.2.2 diff, stream_cqsa/autoconfig.py, plan()
+ * docstring; the default set (0, 1, 3) for c = 7 in stream_cqsa/api.py).  This library runs depth
+ * itr = 1: the query rows and the keys are each split into c contiguous parts (part p covers
+ * [floor(p n / c), floor((p + 1) n / c))), and subproblem i holds the parts (i + s) mod c for s in the
+ * set.  The set must be a cyclic quorum set: every pair of parts meets in some subproblem, i.e. every
+ * d in 1..c-1 is a difference of two set elements mod c.  The pair (query part a, key part b) is
+ * computed by exactly one subproblem, its owner: the smallest i whose parts contain both a and b.
+ * Each subproblem stages its parts (from pinned host memory when the inputs live there), runs one
+ * forward launch per owned non-empty pair, and folds the partial into a device accumulator for all
+ * query rows by the log-sum-exp rule; the accumulator is normalised at the end.  Causal pairs with
+ * no visible key are skipped.  Needs budget for the fp32 accumulator (B Hq Nq (D + 2) 4 bytes) plus
+ * one subproblem's staging; CQSA_ERR_BUDGET otherwise.
+ */
+
+/* owner[a * c + b] = the subproblem that computes the pair (query part a, key part b), for a valid
+ * cyclic quorum set; CQSA_ERR_INVALID (with a message) when c < 1, l < 1, l > c, an element is
+ * outside [0, c) or repeated, or some pair of parts shares no subproblem.  Host-only. */
+cqsa_status cqsa_cqs_assign(int32_t c, const int32_t* interest_set, int32_t l, int32_t* owner);
+
+/* The built-in interest set for c parts (perfect difference sets: c = 3, 7, 13, 21, 31): writes up to
+ * max_l elements to set and returns its size, or 0 when there is none for c. */
+int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l);
 
 /* Name and shape of the forward kernel a call with this head dim (64 or 128) launches, e.g.
  * "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32"; "" for another head dim.  The choice

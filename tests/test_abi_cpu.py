@@ -50,10 +50,10 @@ def test_forward_kernel_name(monkeypatch):
 def test_struct_layout_and_version():
     import exact_long_context_cqsa_amd as m
     lib = m._lib
-    assert lib.cqsa_version() == 1
+    assert lib.cqsa_version() == 2
     assert lib.cqsa_struct_size(0) == ctypes.sizeof(m.CqsaTensor) == 80
-    assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions)
-    assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo)
+    assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions) == 72
+    assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo) == 136
     assert lib.cqsa_struct_size(7) == 0
 
 

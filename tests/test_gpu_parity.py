@@ -87,6 +87,72 @@ def test_every_forward_kernel_variant(variant, monkeypatch):
             compare(out, lse, ref, dtype, label=f"variant {variant} {kw} {case}")
 
 
+CQS_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, cqs
+    (1, 2, 2, 1000, 1000, 64, torch.float16, True, 7),                  # c = 7, set (0, 1, 3)
+    (1, 2, 2, 1001, 1001, 64, torch.float16, False, 7),                 # ragged parts, non-causal
+    (1, 4, 1, 513, 1300, 128, torch.bfloat16, True, (3, (0, 1))),       # GQA, bottom-right causal
+    (2, 2, 2, 777, 777, 64, torch.bfloat16, True, (10, (0, 1, 2, 3, 6))),  # a covering, non-perfect set
+    (1, 1, 1, 30, 30, 64, torch.float16, True, 31),                     # parts of zero and one row
+]
+
+
+@pytest.mark.parametrize("case", CQS_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}-cqs{c[8]}")
+def test_cqs_schedule_parity(case):
+    """The cyclic quorum-set schedule against the oracle, device-resident and streamed from pinned
+    host memory (out and lse on the host too)."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, cqs = case
+    say("cqs", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=3000 + Nq + Nk + D)
+    ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
+                                      return_info=True, cqs=cqs)
+    torch.cuda.synchronize()
+    compare(out, lse, ref, dtype, label=f"cqs device {case}")
+    c = cqs if isinstance(cqs, int) else cqs[0]
+    assert info["cqs_c"] == c and info["chunk_pairs"] >= 1
+    qh, kh, vh = q.pin_memory(), k.pin_memory(), v.pin_memory()
+    out_h, lse_h, info_h = cqsa().attention(qh, kh, vh, is_causal=causal, out_dtype=torch.float32,
+                                            return_lse=True, return_info=True, cqs=cqs)
+    assert not out_h.is_cuda and info_h["streamed"] == 1 and info_h["h2d_bytes"] > 0
+    compare(out_h, lse_h, ref, dtype, label=f"cqs host {case}")
+
+
+def test_cqs_config2_shape_matches_grid_and_oracle():
+    """The 32K causal bench shape under the quorum-set schedule (c = 7 and c = 31): sampled rows
+    against the oracle, and the whole output against the monolithic pass."""
+    w = synth.workload(1)
+    say("cqs workload", w.name)
+    q, k, v, _ = synth.make_inputs(w)
+    rows = sample_rows(1, w.Hq, w.Nq, seed=7, n_random=64, edge=16,
+                       boundaries=[w.Nq * p // 7 for p in range(8)] + [w.Nq * p // 31 for p in range(32)])
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    mono = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32)
+    for c in (7, 31):
+        out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True,
+                                          return_info=True, cqs=c)
+        torch.cuda.synchronize()
+        assert info["chunk_pairs"] == c * (c + 1) // 2
+        compare(out, lse, ref, w.dtype, rows=rows, label=f"cqs c={c}")
+        assert (out - mono).abs().max().item() <= 1e-3
+
+
+def test_cqs_streamed_from_host_reduced():
+    """Host-resident 131072-token causal case (the 4M recipe, shrunk) under c = 13 with a small budget."""
+    w = synth.workload(3)
+    say("cqs streamed reduced")
+    q, k, v, _ = synth.make_inputs(w, nq=131072, nk=131072, pin=True)
+    out, lse, info = cqsa().attention(q, k, v, is_causal=True, mem_budget=2 * 10**9, return_lse=True,
+                                      return_info=True, cqs=13)
+    assert info["streamed"] == 1 and info["cqs_subproblems"] == 13
+    rows = sample_rows(1, w.Hq, 131072, seed=9, n_random=48, edge=8,
+                       boundaries=[131072 * p // 13 for p in range(14)], heads=range(0, w.Hq, 3))
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    compare(out, lse, ref, w.dtype, rows=rows, label="cqs streamed 131072")
+
+
 def test_config1_four_kv_chunks_merged():
     """1024 causal rows, D=64, fp16, KV chunk 256: each Q block folds its visible chunks by LSE."""
     w = synth.workload(0)
