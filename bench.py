@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--streamed", action="store_true", help="also run the 4M-token host-streamed case")
+    ap.add_argument("--cqs", type=int, default=0,
+                    help="also time the cyclic quorum-set schedule with this many parts (resident workload, "
+                         "and the streamed case with --streamed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
@@ -93,13 +96,20 @@ def measured_traffic(path: str):
     return int(float(prof["traffic_bytes_per_launch"])), os.path.relpath(path, ROOT)
 
 
-def run_streamed(cqsa, torch, synth) -> dict:
+def run_streamed(cqsa, torch, synth, cqs=None) -> dict:
     w = synth.workload(3)
     t0 = time.perf_counter()
     q, k, v, _ = synth.make_inputs(w, pin=True)
     out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=torch.float16, pin_memory=True)
     gen_s = time.perf_counter() - t0
     print(f"[bench] streamed inputs ready ({gen_s:.1f} s)", file=sys.stderr, flush=True)
+    res = streamed_run(cqsa, torch, w, q, k, v, out, None)
+    if cqs:
+        res["cqs"] = streamed_run(cqsa, torch, w, q, k, v, out, cqs)
+    return res
+
+
+def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
     # link peak: one pinned 1 GiB H2D copy timed by the host clock between two synchronisations
     src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -113,8 +123,9 @@ def run_streamed(cqsa, torch, synth) -> dict:
     del src, dst
     torch.cuda.empty_cache()
     t2 = time.perf_counter()
-    _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True)
+    _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True, cqs=cqs)
     wall = time.perf_counter() - t2
+    print(f"[bench] streamed {'grid' if not cqs else f'cqs c={cqs}'}: {wall:.2f} s", file=sys.stderr, flush=True)
     tok = w.B * w.Nq / wall
     h2d_gbs = info["h2d_bytes"] / (info["h2d_ms"] / 1e3) / 1e9 if info["h2d_ms"] > 0 else None
     # parity on sampled rows against the FP64 reference (first/last rows, Q-chunk edges, seeded rows)
@@ -122,7 +133,8 @@ def run_streamed(cqsa, torch, synth) -> dict:
     import oracle
     rng = np.random.default_rng(4)
     qc = info["q_chunk"]
-    idx = sorted({0, 1, w.Nq - 1, w.Nq - 2, qc - 1, qc, *rng.integers(0, w.Nq, 10).tolist()})
+    edges = [w.Nq * p // cqs for p in range(1, cqs)][:6] if cqs else [qc - 1, qc]
+    idx = sorted({0, 1, w.Nq - 1, w.Nq - 2, *edges, *[e - 1 for e in edges], *rng.integers(0, w.Nq, 10).tolist()})
     rows = np.array([(0, h, i) for h in (0, 5) for i in idx if 0 <= i < w.Nq], dtype=np.int64)
     t3 = time.perf_counter()
     ref = oracle.attention_rows(q, k, v, causal=True, scale=w.scale, rows=rows)
@@ -130,12 +142,14 @@ def run_streamed(cqsa, torch, synth) -> dict:
     max_abs = float(np.abs(got - ref["o"]).max())
     print(f"[bench] streamed parity on {len(rows)} rows: max_abs {max_abs:.2e} ({time.perf_counter() - t3:.1f} s)",
           file=sys.stderr, flush=True)
-    return {"workload": w.name, "seconds": round(wall, 3), "tokens_per_s": round(tok, 1),
+    return {"workload": w.name, "schedule": "grid" if not cqs else f"cyclic quorum sets, c={cqs}",
+            "seconds": round(wall, 3), "tokens_per_s": round(tok, 1),
             "tflops": round(w.flops() / wall / 1e12, 2), "h2d_bytes": info["h2d_bytes"],
             "h2d_gbs_during_copies": round(h2d_gbs, 2) if h2d_gbs else None,
             "h2d_link_peak_gbs_host_timed": round(link, 2),
             "h2d_frac_of_link": round(h2d_gbs / link, 3) if h2d_gbs else None,
             "q_chunk": info["q_chunk"], "kv_chunk": info["kv_chunk"], "chunk_pairs": info["chunk_pairs"],
+            "cqs_subproblems": info["cqs_subproblems"],
             "workspace_bytes": info["workspace_bytes"], "budget_bytes": info["budget_bytes"],
             "parity_rows": int(len(rows)), "parity_max_abs_fp16_out": max_abs,
             "note": "wall time includes PCIe transfers from/to pinned host memory; not the headline value"}
@@ -197,6 +211,21 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms (events {ms_kernel:.3f} ms, min {min(per):.3f}) -> {value:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
+    cqs_resident = None
+    if args.cqs:
+        for _ in range(2):
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        n_cqs = max(3, args.steps // 4)
+        for _ in range(n_cqs):
+            cinfo = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, return_info=True)[1]
+        torch.cuda.synchronize()
+        cms = (time.perf_counter() - c0) * 1e3 / n_cqs
+        cqs_resident = {"c": args.cqs, "ms_per_call": round(cms, 4), "tflops": round(flops / (cms / 1e3) / 1e12, 2),
+                        "pairs": cinfo["chunk_pairs"], "subproblems": cinfo["cqs_subproblems"],
+                        "kernel_launches": cinfo["kernel_launches"]}
+        print(f"[bench] cqs c={args.cqs}: {cms:.3f} ms per call", file=sys.stderr, flush=True)
     kernel = cqsa.fwd_kernel_name(w.D)
     prof_path = args.profile or os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_{w.name}.md")
     traffic, traffic_src = measured_traffic(prof_path)
@@ -226,8 +255,10 @@ def main():
                      "kernel_ms": round(ms_kernel, 4),
                      "launches_per_step": info["kernel_launches"]},
     }
+    if cqs_resident:
+        line["cqs_resident"] = cqs_resident
     if args.streamed:
-        line["streamed_4m"] = run_streamed(cqsa, torch, synth)
+        line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(line), flush=True)
