@@ -25,6 +25,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 #include <stdlib.h>
 
 #include "cqsa_internal.h"
@@ -1012,19 +1013,14 @@ int fwd_block_m(int D) {
 }
 
 const char* fwd_kernel_name(int D) {
-    static const char* const k64[kNumShapes] = {
-        "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32",
-        "fwd_dma_kernel waves=8 keys_per_tile=128 rows_per_wave=32",
-        "fwd_kernel waves=8 keys_per_tile=128 rows_per_wave=32",
-        "fwd_pp_kernel waves=8 keys_per_tile=128 rows_per_wave=32"};
-    static const char* const k128[kNumShapes] = {
-        "fwd_dma_kernel waves=8 keys_per_tile=64 rows_per_wave=32",
-        "fwd_dma_kernel waves=8 keys_per_tile=32 rows_per_wave=32",
-        "fwd_kernel waves=8 keys_per_tile=64 rows_per_wave=32",
-        "fwd_pp_kernel waves=8 keys_per_tile=64 rows_per_wave=32"};
-    if (D == 64) return k64[variant()];
-    if (D == 128) return k128[variant()];
-    return "";
+    static char names[2][kNumShapes][96];
+    if (D != 64 && D != 128) return "";
+    const int v = variant();
+    const Shape sh = (D == 64 ? kShapes64 : kShapes128)[v];
+    static const char* const kind[3] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel"};
+    char* out = names[D == 64 ? 0 : 1][v];
+    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32", kind[sh.kind], sh.nw, sh.kt);
+    return out;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
