@@ -40,7 +40,7 @@ class CqsaOptions(ctypes.Structure):
     _fields_ = [("q_chunk", ctypes.c_int64), ("kv_chunk", ctypes.c_int64), ("kv_splits", ctypes.c_int32),
                 ("merge_mode", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("cqs_c", ctypes.c_int32),
-                ("cqs_l", ctypes.c_int32), ("reserved", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32))]
+                ("cqs_l", ctypes.c_int32), ("precision", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32))]
 
 
 class CqsaPlanInfo(ctypes.Structure):
@@ -63,9 +63,9 @@ class CqsaError(RuntimeError):
         self.status = status
 
 
-def fwd_kernel_name(head_dim: int) -> str:
-    """The forward kernel (name and shape) a call with this head dim launches."""
-    return _lib.cqsa_fwd_kernel_name(int(head_dim)).decode()
+def fwd_kernel_name(head_dim: int, precision: int = 0) -> str:
+    """The forward kernel (name and shape) a call with this head dim and precision launches."""
+    return _lib.cqsa_fwd_kernel_name(int(head_dim), int(precision)).decode()
 
 
 def library_path() -> str:
@@ -101,7 +101,7 @@ def _load_library():
     lib.cqsa_version.restype = ctypes.c_int32
     lib.cqsa_struct_size.argtypes = [ctypes.c_int32]
     lib.cqsa_struct_size.restype = ctypes.c_uint64
-    lib.cqsa_fwd_kernel_name.argtypes = [ctypes.c_int64]
+    lib.cqsa_fwd_kernel_name.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.cqsa_fwd_kernel_name.restype = ctypes.c_char_p
     lib.cqsa_cqs_assign.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]
@@ -172,9 +172,11 @@ def cqs_assign(c: int, interest_set) -> list:
 
 
 def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=None, workspace=None,
-             num_cus=None, cqs=None) -> CqsaOptions:
-    """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set)."""
+             num_cus=None, cqs=None, precision=0) -> CqsaOptions:
+    """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set).
+    precision: 0 (P rounded to the input dtype) or 1 (split P, hi + lo)."""
     o = CqsaOptions()
+    o.precision = int(precision or 0)
     if cqs is not None:
         if isinstance(cqs, int):
             o.cqs_c = cqs
@@ -198,7 +200,7 @@ def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=Non
 
 
 def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
-         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None) -> dict:
+         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0) -> dict:
     """The plan ``attention`` would run (nothing is allocated or computed).
 
     ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
@@ -227,7 +229,7 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
         out = (qshape, qdt)
     do = mk("out", out, None)
     info = CqsaPlanInfo()
-    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs)
+    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision)
     _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
                           int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
                           ctypes.byref(info)))
@@ -238,7 +240,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
               mem_budget: int | None = None, *, q_chunk: int | None = None, kv_chunk: int | None = None,
               kv_splits: int | None = None, merge: int | None = None, out: torch.Tensor | None = None,
               out_dtype: torch.dtype | None = None, return_lse: bool = False, return_info: bool = False,
-              stream: torch.cuda.Stream | None = None, cqs=None):
+              stream: torch.cuda.Stream | None = None, cqs=None, precision: int = 0):
     """Exact ``softmax(scale * q k^T [+ causal mask]) v`` (SDPA semantics; causal is bottom-right
     aligned when Nq < Nk; GQA when k/v have fewer heads).
 
@@ -246,7 +248,9 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     pinned host memory (then streamed in chunks).  ``mem_budget`` caps the device bytes the call
     uses (0/None: the free memory).  ``kv_chunk``/``q_chunk`` force a decomposition; ``merge``
     picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  ``cqs`` runs the cyclic quorum-set
-    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set).  Returns out
+    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set).
+    ``precision=1`` feeds P to the PV product as a hi part plus a lo residual (two accumulator
+    chains), for results near fp32 accuracy at about twice the PV work.  Returns out
     (on q's device; pinned host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the
     plan dict on request."""
     dev = _device_of(q, k, v, out)
@@ -266,7 +270,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)
         dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
-        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs)
+        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs, precision=precision)
         budget = int(mem_budget or 0)
         # size the workspace first so that device-resident calls take it from PyTorch's allocator
         # (stream-ordered, no hipMalloc, no synchronisation)

@@ -149,6 +149,7 @@ struct Problem {
     float scale = 0.f;
     bool empty = false;
     bool streamed = false;
+    int p_split = 0;   // precision 1: split-P PV product
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -457,7 +458,7 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
 
 cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt, int num_cus, Plan* pl) {
     std::memset(&pl->info, 0, sizeof pl->info);
-    pl->bm = fwd_block_m((int)P.D);
+    pl->bm = fwd_block_m((int)P.D, P.p_split);
     pl->info.block_m = pl->bm;
     pl->info.budget_bytes = budget;
     pl->info.streamed = P.streamed ? 1 : 0;
@@ -702,6 +703,7 @@ FwdArgs base_args(const Problem& P) {
     a.causal = P.causal ? 1 : 0;
     a.scale_log2 = P.scale * 1.44269504088896340736f;
     a.n_splits = 1;
+    a.p_split = P.p_split;
     return a;
 }
 
@@ -725,7 +727,7 @@ void set_v(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
 }
 
 cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
-    const int bm = fwd_block_m((int)P.D);
+    const int bm = fwd_block_m((int)P.D, P.p_split);
     const int64_t rows = a.r1 - a.r0;
     if (rows <= 0) return CQSA_OK;
     const int64_t n_qt = ceil_div(rows, bm);
@@ -1318,6 +1320,13 @@ cqsa_status build_problem(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa
     return check_problem(P, is_causal, scale);
 }
 
+cqsa_status set_precision(const cqsa_options& o, Problem* P) {
+    if (o.precision != 0 && o.precision != 1)
+        return fail(CQSA_ERR_INVALID, "precision %d is not 0 (operand-rounded P) or 1 (split P)", o.precision);
+    P->p_split = o.precision;
+    return CQSA_OK;
+}
+
 cqsa_status resolve_budget(uint64_t mem_budget, uint64_t* budget) {
     if (mem_budget > 0) {
         *budget = (uint64_t)((double)mem_budget * kSafety);
@@ -1376,8 +1385,8 @@ int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l) {
     return l;
 }
 
-const char* cqsa_fwd_kernel_name(int64_t head_dim) {
-    return (head_dim == 64 || head_dim == 128) ? fwd_kernel_name((int)head_dim) : "";
+const char* cqsa_fwd_kernel_name(int64_t head_dim, int32_t precision) {
+    return (head_dim == 64 || head_dim == 128) ? fwd_kernel_name((int)head_dim, precision == 1 ? 1 : 0) : "";
 }
 
 cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
@@ -1392,6 +1401,7 @@ cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_ten
     const bool detect = (q && q->where == CQSA_WHERE_DETECT) || (k && k->where == CQSA_WHERE_DETECT) ||
                         (v && v->where == CQSA_WHERE_DETECT) || (out && out->where == CQSA_WHERE_DETECT);
     CQSA_TRY(build_problem(q, k, v, is_causal, 0.f, out, nullptr, want_lse, detect, true, &P));
+    CQSA_TRY(set_precision(o, &P));
     P.lse_host = want_lse && P.out.host;  // lse travels with out
     P.streamed = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
     uint64_t budget = 0;
@@ -1418,6 +1428,7 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
     if (opt) o = *opt;
     Problem P;
     CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, lse, lse != nullptr, true, false, &P));
+    CQSA_TRY(set_precision(o, &P));
     if (P.empty) {
         if (info) std::memset(info, 0, sizeof *info);
         return CQSA_OK;

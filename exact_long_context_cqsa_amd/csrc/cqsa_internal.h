@@ -46,6 +46,7 @@ struct FwdArgs {
     float* acc_o;              // [..][D]
     float* acc_ml;             // [..][2]
     int64_t acc_rows;
+    int32_t p_split;           // 1: P enters the PV product as an fp16/bf16 hi part plus a lo residual
 };
 
 constexpr int kMaxMergeParts = 64;
@@ -71,11 +72,11 @@ struct MergeArgs {
     int64_t l_sb, l_sh;
 };
 
-// Query rows per workgroup of the forward kernel for a head dim.
-int fwd_block_m(int D);
+// Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
+int fwd_block_m(int D, int p_split);
 
 // Name and shape of the forward kernel launched for a head dim ("" if none).
-const char* fwd_kernel_name(int D);
+const char* fwd_kernel_name(int D, int p_split);
 
 // Launchers (return the launch status).
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);

@@ -119,10 +119,27 @@ __device__ __forceinline__ float lane_max(const f32x16 (&s)[NKB]) {
 
 constexpr float kLazyBound = 256.f;
 
+// fp16/bf16 operand -> the eight fp32 values it holds (exact).
+template <int DT>
+__device__ __forceinline__ f32x8 unpack8(u32x4 u);
+
+template <>
+__device__ __forceinline__ f32x8 unpack8<ET_F16>(u32x4 u) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x8, u), f32x8);
+}
+
+template <>
+__device__ __forceinline__ f32x8 unpack8<ET_BF16>(u32x4 u) {
+    return __builtin_convertvector(__builtin_bit_cast(bf16x8, u), f32x8);
+}
+
 // Fast half of the online-softmax step: p = 2^(s c - m) with the running shift m unchanged, rounded
-// into the PV operand pf; returns the lane's sum of the fp32 p (4 partial chains).
-template <int NKB, int DT>
-__device__ __forceinline__ float softmax_fast(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float m, float c) {
+// into the PV operand pf; returns the lane's sum of the fp32 p (4 partial chains).  With SPLIT, plo
+// receives the rounding residual p - pf, rounded again: pf + plo carries p to about twice the
+// operand precision (the hi / lo split of P for the PV product).
+template <int NKB, int DT, bool SPLIT>
+__device__ __forceinline__ float softmax_fast(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], u32x4 (&plo)[2 * NKB],
+                                              float m, float c) {
     float acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = 0.f;
@@ -137,27 +154,32 @@ __device__ __forceinline__ float softmax_fast(const f32x16 (&s)[NKB], u32x4 (&pf
             acc[e & 3] += p;
         }
         pf[t] = pack8<DT>(x);
+        if constexpr (SPLIT) plo[t] = pack8<DT>(x - unpack8<DT>(pf[t]));
     }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Exact half, taken by the whole wave when some lane's fast sum is not <= 2^8: the tile's row maximum
-// (exchanged with lane ^ 32) becomes the new shift, p and its sum rs are recomputed, and l and O are
-// rescaled by 2^(m_old - m_new) (0 when m_old = -inf; a row with no visible key so far keeps m = -inf
-// and gets p = 0, with no (-inf) - (-inf) ever kept).
-template <int NKB, int NDB, int DT>
-__device__ __forceinline__ void softmax_exact(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
-                                              f32x16 (&o)[NDB], float c, float& rs) {
+// (exchanged with lane ^ 32) becomes the new shift, p and its sum rs are recomputed, and l and O
+// (both accumulator chains with SPLIT) are rescaled by 2^(m_old - m_new) (0 when m_old = -inf; a row
+// with no visible key so far keeps m = -inf and gets p = 0, with no (-inf) - (-inf) ever kept).
+template <int NKB, int NDB, int DT, bool SPLIT>
+__device__ __forceinline__ void softmax_exact(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], u32x4 (&plo)[2 * NKB],
+                                              float& m, float& l, f32x16 (&o)[NDB], f32x16 (&olo)[NDB], float c,
+                                              float& rs) {
     float mx = lane_max<NKB>(s);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx * c);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(m - muse);   // m = -inf gives 0
-    rs = softmax_fast<NKB, DT>(s, pf, muse, c);
+    rs = softmax_fast<NKB, DT, SPLIT>(s, pf, plo, muse, c);
     l *= alpha;
     if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        for (int db = 0; db < NDB; ++db) {
+            o[db] *= alpha;
+            if constexpr (SPLIT) olo[db] *= alpha;
+        }
     }
     m = mnew;
 }
@@ -168,13 +190,21 @@ __device__ __forceinline__ void softmax_exact(const f32x16 (&s)[NKB], u32x4 (&pf
 // on using the same m for p, l and O; the bound keeps p within fp16 range and its rounding
 // relative.  When some lane's partial sum exceeds 2^8 (which also catches the first tile, where
 // m = -inf, and any overflow), the wave takes the exact path.  Probabilities are rounded to fp16/bf16
-// into the PV operand pf; the row sum l accumulates the fp32 probabilities.
+// into the PV operand pf (plus the residual plo with SPLIT); the row sum l accumulates the fp32
+// probabilities.
+template <int NKB, int NDB, int DT, bool SPLIT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], u32x4 (&plo)[2 * NKB],
+                                             float& m, float& l, f32x16 (&o)[NDB], f32x16 (&olo)[NDB], float c) {
+    float rs = softmax_fast<NKB, DT, SPLIT>(s, pf, plo, m, c);
+    if (__any(!(rs <= kLazyBound))) softmax_exact<NKB, NDB, DT, SPLIT>(s, pf, plo, m, l, o, olo, c, rs);
+    l += rs;
+}
+
 template <int NKB, int NDB, int DT>
 __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], float& m, float& l,
                                              f32x16 (&o)[NDB], float c) {
-    float rs = softmax_fast<NKB, DT>(s, pf, m, c);
-    if (__any(!(rs <= kLazyBound))) softmax_exact<NKB, NDB, DT>(s, pf, m, l, o, c, rs);
-    l += rs;
+    u32x4 unused_lo[2 * NKB];
+    softmax_tile<NKB, NDB, DT, false>(s, pf, unused_lo, m, l, o, o, c);
 }
 
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts: 32-bit data format,
@@ -731,7 +761,7 @@ __device__ __forceinline__ int vswz(int r) {
 // NW waves per workgroup (32 query rows each); WPE asks the compiler for registers that leave room for
 // WPE waves per SIMD (several small workgroups per CU drift out of phase, so one's softmax overlaps
 // another's matrix products).
-template <int D, int DT, int KT, int NW, int WPE>
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd_dma_kernel(const FwdArgs a) {
     constexpr int BM = NW * 32;
@@ -826,9 +856,12 @@ fwd_dma_kernel(const FwdArgs a) {
             vread[db] = TILE + row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
     }
 
-    f32x16 oacc[NDB];
+    f32x16 oacc[NDB], olo[NDB];   // olo: the lo chain of the split-P product (SPLIT only)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    for (int db = 0; db < NDB; ++db) {
+        oacc[db] = f32x16{};
+        if constexpr (SPLIT) olo[db] = f32x16{};
+    }
     float mrun = -INFINITY, lrun = 0.f;
 
     if (ntiles > 0) CQSA_ISSUE_TILE(0);
@@ -867,8 +900,8 @@ fwd_dma_kernel(const FwdArgs a) {
                 }
         }
 
-        u32x4 pf[NPK];
-        softmax_tile<NKB, NDB, DT>(sacc, pf, mrun, lrun, oacc, a.scale_log2);
+        u32x4 pf[NPK], plo[NPK];
+        softmax_tile<NKB, NDB, DT, SPLIT>(sacc, pf, plo, mrun, lrun, oacc, olo, a.scale_log2);
 
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -885,11 +918,17 @@ fwd_dma_kernel(const FwdArgs a) {
                 vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
                 vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
                 oacc[db] = mfma32<DT>(vf, pf[t], oacc[db]);
+                if constexpr (SPLIT) olo[db] = mfma32<DT>(vf, plo[t], olo[db]);
             }
     }
 
 #undef CQSA_ISSUE_TILE
 
+    // the two chains of the split product meet in one fp32 add
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] += olo[db];
+    }
     const int64_t row = iw0 + l32;
     fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
@@ -933,12 +972,13 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
     }
 }
 
-template <int D, int DT, int KT, int NW, int WPE>
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT = false>
 hipError_t launch_dma_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT, NW, WPE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT, NW, WPE, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -977,8 +1017,23 @@ int variant() {
     return (v < 0 || v >= kNumShapes) ? 0 : v;
 }
 
+// The split-P product (two PV chains) runs on the DMA kernel in one shape per head dim.
+constexpr Shape kSplit64 = {2, 8, 64, 2};
+constexpr Shape kSplit128 = {2, 8, 32, 2};
+
+Shape shape_of(int D, int p_split) {
+    if (p_split) return D == 64 ? kSplit64 : kSplit128;
+    return (D == 64 ? kShapes64 : kShapes128)[variant()];
+}
+
 template <int D, int DT>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+    if (a.p_split) {
+        if constexpr (D == 64)
+            return launch_dma_t<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true>(a, st);
+        else
+            return launch_dma_t<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true>(a, st);
+    }
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
     if (sh.kind == 2) {
 #define CQSA_DMA_CASE(NW_, KT_, WPE_) \
@@ -1007,19 +1062,17 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int fwd_block_m(int D) {
-    const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-    return sh.nw * 32;
-}
+int fwd_block_m(int D, int p_split) { return shape_of(D, p_split).nw * 32; }
 
-const char* fwd_kernel_name(int D) {
-    static char names[2][kNumShapes][96];
+const char* fwd_kernel_name(int D, int p_split) {
+    static char names[2][kNumShapes + 1][112];
     if (D != 64 && D != 128) return "";
-    const int v = variant();
-    const Shape sh = (D == 64 ? kShapes64 : kShapes128)[v];
+    const int v = p_split ? kNumShapes : variant();
+    const Shape sh = shape_of(D, p_split);
     static const char* const kind[3] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel"};
     char* out = names[D == 64 ? 0 : 1][v];
-    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32", kind[sh.kind], sh.nw, sh.kt);
+    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s", kind[sh.kind], sh.nw, sh.kt,
+             p_split ? " split_p" : "");
     return out;
 }
 

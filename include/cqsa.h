@@ -92,7 +92,11 @@ typedef struct {
     int32_t cqs_c;            /* > 0: run the cyclic quorum-set schedule over cqs_c parts (below);
                                  0 = the Q-chunk x KV-chunk grid */
     int32_t cqs_l;            /* size of the interest set cqs_set */
-    int32_t reserved;
+    int32_t precision;        /* 0: P is rounded to the input dtype for the PV product (the default);
+                                 1: split P: the PV product takes P as an fp16/bf16 hi part plus the
+                                 rounded residual as a lo part, in two accumulator chains summed in
+                                 fp32 at the end (the hi/lo split with separate chains of Strata pull
+                                 request #800); about twice the PV work, error near the fp32 class */
     const int32_t* cqs_set;   /* the interest set: cqs_l distinct part offsets in [0, cqs_c);
                                  NULL = the built-in set for cqs_c (see cqsa_cqs_default_set) */
 } cqsa_options;
@@ -239,11 +243,12 @@ cqsa_status cqsa_cqs_assign(int32_t c, const int32_t* interest_set, int32_t l, i
  * max_l elements to set and returns its size, or 0 when there is none for c. */
 int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l);
 
-/* Name and shape of the forward kernel a call with this head dim (64 or 128) launches, e.g.
- * "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32"; "" for another head dim.  The choice
- * follows the environment variable CQSA_FWD_VARIANT (0 or unset = the default kernel), read at
- * every launch.  The string is static; no HIP call is made. */
-const char* cqsa_fwd_kernel_name(int64_t head_dim);
+/* Name and shape of the forward kernel a call with this head dim (64 or 128) and precision (see
+ * cqsa_options) launches, e.g. "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32"; "" for
+ * another head dim.  With precision 0 the choice follows the environment variable CQSA_FWD_VARIANT
+ * (0 or unset = the default kernel), read at every launch.  The string is static; no HIP call is
+ * made. */
+const char* cqsa_fwd_kernel_name(int64_t head_dim, int32_t precision);
 
 #ifdef __cplusplus
 }

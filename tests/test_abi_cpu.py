@@ -45,6 +45,10 @@ def test_forward_kernel_name(monkeypatch):
     assert m.fwd_kernel_name(64).startswith("fwd_kernel ")
     monkeypatch.setenv("CQSA_FWD_VARIANT", "99")   # out of range: the default
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
+    # split-P runs the DMA kernel in its own shape whatever the variant
+    monkeypatch.setenv("CQSA_FWD_VARIANT", "2")
+    assert m.fwd_kernel_name(64, 1).startswith("fwd_dma_kernel ") and m.fwd_kernel_name(64, 1).endswith("split_p")
+    assert m.fwd_kernel_name(128, 1).endswith("split_p")
 
 
 def test_struct_layout_and_version():
@@ -53,6 +57,7 @@ def test_struct_layout_and_version():
     assert lib.cqsa_version() == 2
     assert lib.cqsa_struct_size(0) == ctypes.sizeof(m.CqsaTensor) == 80
     assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions) == 72
+    assert [f for f, _ in m.CqsaOptions._fields_][-2:] == ["precision", "cqs_set"]
     assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo) == 136
     assert lib.cqsa_struct_size(7) == 0
 
@@ -132,6 +137,16 @@ def test_plan_errors():
         plan(shp(1, 2, 65, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), True, GB)
     with pytest.raises(m.CqsaError, match="BUDGET"):
         plan(shp(1, 2, 64, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), True, 1000, kv_chunk=16)
+    with pytest.raises(m.CqsaError, match="precision"):
+        plan(shp(1, 2, 64, 64), shp(1, 2, 64, 64), shp(1, 2, 64, 64), True, GB, precision=2)
+
+
+def test_plan_split_p_block_m():
+    """The split-P product runs in its own kernel shape (256-row workgroups at both head dims)."""
+    a = plan(shp(1, 2, 1000, 64), shp(1, 2, 1000, 64), shp(1, 2, 1000, 64), True, GB, precision=1)
+    assert a["block_m"] == 256
+    b = plan(shp(1, 2, 1000, 128), shp(1, 2, 1000, 128), shp(1, 2, 1000, 128), True, GB, precision=1)
+    assert b["block_m"] == 256
 
 
 def test_plan_budget_monotone():

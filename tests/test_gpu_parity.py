@@ -153,6 +153,55 @@ def test_cqs_streamed_from_host_reduced():
     compare(out, lse, ref, w.dtype, rows=rows, label="cqs streamed 131072")
 
 
+# Split-P mode (P = hi + lo, two PV accumulator chains): error bound from the arithmetic that
+# remains (fp32 score accumulation, v_exp_f32, the lo part's rounding: 2^-22 of p for fp16, 2^-16 for
+# bf16, fp32 accumulation), with a margin of about ten.
+SPLIT_TOL = {torch.float16: 2e-5, torch.bfloat16: 1e-4}
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[3], SMALL[4], SMALL[5], SMALL[7]],
+                         ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'f16' if c[6] == torch.float16 else 'bf16'}")
+def test_split_p_precision(case):
+    """precision=1 against the oracle at the tight bound, and tighter than the default mode;
+    monolithic, with a forced KV split, and streamed from pinned host memory."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal = case
+    say("split-P", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=4000 + Nq + Nk + D)
+    ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+
+    def err(out):
+        return float(np.abs(out.detach().double().cpu().numpy() - ref["o"].reshape(out.shape)).max())
+
+    base = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    e_base = err(base)
+    for kw in ({}, {"kv_chunk": 200}):
+        out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
+                                    precision=1, **kw)
+        torch.cuda.synchronize()
+        compare(out, lse, ref, dtype, label=f"split {kw} {case}")
+        e = err(out)
+        assert e <= SPLIT_TOL[dtype], (kw, e)
+        assert e < e_base or e_base <= SPLIT_TOL[dtype] / 4, (e, e_base)
+    outh = cqsa().attention(q.pin_memory(), k.pin_memory(), v.pin_memory(), is_causal=causal,
+                            out_dtype=torch.float32, precision=1)
+    assert err(outh) <= SPLIT_TOL[dtype]
+
+
+def test_split_p_bench_shape_sampled():
+    """The 32K causal D=64 fp16 workload in split-P mode, sampled rows, at the tight bound."""
+    w = synth.workload(1)
+    q, k, v, _ = synth.make_inputs(w)
+    rows = sample_rows(1, w.Hq, w.Nq, seed=11, n_random=48, edge=8)
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    out = cqsa().attention(q.to(DEV), k.to(DEV), v.to(DEV), is_causal=True, out_dtype=torch.float32, precision=1)
+    torch.cuda.synchronize()
+    b, h, i = (torch.from_numpy(rows[:, c]) for c in range(3))
+    got = out.cpu()[b, h, i].double().numpy()
+    assert float(np.abs(got - ref["o"]).max()) <= SPLIT_TOL[torch.float16]
+
+
 def test_config1_four_kv_chunks_merged():
     """1024 causal rows, D=64, fp16, KV chunk 256: each Q block folds its visible chunks by LSE."""
     w = synth.workload(0)
