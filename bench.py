@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--streamed", action="store_true", help="also run the 4M-token host-streamed case")
+    ap.add_argument("--split-p", action="store_true",
+                    help="also time the split-P precision mode on the resident workload and check it on sampled rows")
     ap.add_argument("--cqs", type=int, default=0,
                     help="also time the cyclic quorum-set schedule with this many parts (resident workload, "
                          "and the streamed case with --streamed)")
@@ -226,6 +228,33 @@ def main():
                         "pairs": cinfo["chunk_pairs"], "subproblems": cinfo["cqs_subproblems"],
                         "kernel_launches": cinfo["kernel_launches"]}
         print(f"[bench] cqs c={args.cqs}: {cms:.3f} ms per call", file=sys.stderr, flush=True)
+    split_p = None
+    if args.split_p:
+        import numpy as np
+        import oracle
+        for _ in range(2):
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, precision=1)
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        n_sp = max(3, args.steps // 2)
+        for _ in range(n_sp):
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, precision=1)
+        torch.cuda.synchronize()
+        sms = (time.perf_counter() - s0) * 1e3 / n_sp
+        rng = np.random.default_rng(12)
+        rows = np.array([(0, h, int(i)) for h in range(0, w.Hq, 3) for i in rng.integers(0, w.Nq, 24)], dtype=np.int64)
+        ref = oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
+        errs = {}
+        for prec in (0, 1):
+            o32 = cqsa.attention(qd, kd, vd, is_causal=w.causal, out_dtype=torch.float32, precision=prec)
+            b_, h_, i_ = (torch.from_numpy(rows[:, c]) for c in range(3))
+            errs[prec] = float(np.abs(o32.cpu()[b_, h_, i_].double().numpy() - ref["o"]).max())
+            del o32
+        split_p = {"kernel": cqsa.fwd_kernel_name(w.D, 1), "ms_per_call": round(sms, 4),
+                   "tflops": round(flops / (sms / 1e3) / 1e12, 2), "rows_checked": int(len(rows)),
+                   "max_abs_vs_fp64_split": errs[1], "max_abs_vs_fp64_default": errs[0]}
+        print(f"[bench] split-P: {sms:.3f} ms per call, max_abs {errs[1]:.2e} (default {errs[0]:.2e})",
+              file=sys.stderr, flush=True)
     kernel = cqsa.fwd_kernel_name(w.D)
     prof_path = args.profile or os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_{w.name}.md")
     traffic, traffic_src = measured_traffic(prof_path)
@@ -257,6 +286,8 @@ def main():
     }
     if cqs_resident:
         line["cqs_resident"] = cqs_resident
+    if split_p:
+        line["split_p"] = split_p
     if args.streamed:
         line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
     if not args.no_cpu_baseline:
