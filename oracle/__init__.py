@@ -59,6 +59,9 @@ def _load():
         lib.oracle_rows.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [ctypes.c_int64, ctypes.c_int64, dp, dp, dp, dp, dp, dp, dp, dp, dp]
         lib.oracle_merge.restype = None
+        lib.oracle_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                        dp, dp, dp, ctypes.c_int32]
+        lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_double.restype = ctypes.c_double
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -147,6 +150,23 @@ def attention(q, k, v, *, causal: bool, scale: float, threads: int | None = None
     o = torch.from_numpy(r["o"]).reshape(B, Hq, Nq, D)
     lse = torch.from_numpy(r["lse"]).reshape(B, Hq, Nq)
     return o, lse
+
+
+def backward(q, k, v, dout, *, causal: bool, scale: float, threads: int | None = None):
+    """Reference gradients (dq, dk, dv) as float64 tensors for the upstream gradient ``dout``
+    (q's dtype and shape, unit head-dim stride)."""
+    p = _problem(q, k, v, causal, scale)
+    if dout.dtype != q.dtype or dout.shape != q.shape or dout.stride(3) != 1 or dout.device.type != "cpu":
+        raise ValueError("dout must be a CPU tensor of q's dtype and shape with a unit head-dim stride")
+    dq = np.zeros(tuple(q.shape), dtype=np.float64)
+    dk = np.zeros(tuple(k.shape), dtype=np.float64)
+    dv = np.zeros(tuple(v.shape), dtype=np.float64)
+    st = (ctypes.c_int64 * 3)(dout.stride(0), dout.stride(1), dout.stride(2))
+    rc = _load().oracle_backward(ctypes.byref(p), dout.data_ptr(), st, _dp(dq), _dp(dk), _dp(dv),
+                                 int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_backward failed ({rc})")
+    return torch.from_numpy(dq), torch.from_numpy(dk), torch.from_numpy(dv)
 
 
 def merge(a: dict, b: dict) -> dict:

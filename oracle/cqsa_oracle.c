@@ -237,3 +237,189 @@ void oracle_merge(int64_t nrows, int64_t D, const double* oa, const double* ma, 
         m[r] = mm;
     }
 }
+
+/*
+ * Gradients of the same attention for an upstream gradient dO (fp16 / bf16, like q), by the
+ * definition (the derivative of softmax(sigma q k^T) v), for the backward the Stream-CQSA pages ship
+ * beside the forward (stream-cqsa 2.2.0 -> 2.2.2 diff, README.md, kernel table):
+ *
+ *     P_ij  = exp(s_ij - m_i) / l_i                        (j in V(i), 0 otherwise)
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = dO_i . v_j
+ *     D_i   = sum_j P_ij dP_ij
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = sigma sum_j dS_ij k_j
+ *     dK_j  = sigma sum_i dS_ij q_i
+ *
+ * With GQA, dK and dV of key/value head h' sum over the query heads h with floor(h / g) = h'.
+ * Two passes: per query row (m_i, l_i, D_i and dQ_i), then per key row (dK_j and dV_j), each spread
+ * over threads with no shared accumulator.  Plain double sums (the test sizes keep them far below
+ * the tolerances compared against).
+ */
+typedef struct {
+    const oracle_problem* p;
+    const uint16_t* dout;
+    int64_t do_stride[3];
+    double* stats;      /* [B][Hq][Nq][3]: m, l, D */
+    double* dq;         /* [B][Hq][Nq][D] */
+    double* dk;         /* [B][Hkv][Nk][D] */
+    double* dv;
+    int64_t begin, end; /* rows of the pass */
+    int32_t status;
+} oracle_bwd_job;
+
+static double dot_row(const oracle_problem* p, const uint16_t* a, uint64_t ao, const uint16_t* b, uint64_t bo) {
+    double d = 0.0;
+    for (int64_t t = 0; t < p->D; ++t) d += elem(p, a, ao + (uint64_t)t) * elem(p, b, bo + (uint64_t)t);
+    return d;
+}
+
+static void visible_keys(const oracle_problem* p, int64_t i, int64_t* hi) {
+    *hi = p->Nk;
+    if (p->causal) {
+        const int64_t last = i + (p->Nk - p->Nq);
+        if (*hi > last + 1) *hi = last + 1;
+    }
+}
+
+/* pass 1: one query row (b, h, i) per step */
+static void* bwd_query_worker(void* arg) {
+    oracle_bwd_job* job = (oracle_bwd_job*)arg;
+    const oracle_problem* p = job->p;
+    const int64_t D = p->D, g = p->Hq / p->Hkv;
+    const double sigma = (double)p->scale;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(p->Nk > 0 ? p->Nk : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(p->Nk > 0 ? p->Nk : 1));
+    if (!s || !dp) {
+        job->status = -2;
+        free(s); free(dp);
+        return NULL;
+    }
+    for (int64_t r = job->begin; r < job->end; ++r) {
+        const int64_t i = r % p->Nq, h = (r / p->Nq) % p->Hq, b = r / (p->Nq * p->Hq), hk = h / g;
+        int64_t hi;
+        visible_keys(p, i, &hi);
+        const uint64_t qo = (uint64_t)(b * p->q_stride[0] + h * p->q_stride[1] + i * p->q_stride[2]);
+        const uint64_t oo = (uint64_t)(b * job->do_stride[0] + h * job->do_stride[1] + i * job->do_stride[2]);
+        double m = -INFINITY;
+        for (int64_t j = 0; j < hi; ++j) {
+            const uint64_t ko = (uint64_t)(b * p->k_stride[0] + hk * p->k_stride[1] + j * p->k_stride[2]);
+            const uint64_t vo = (uint64_t)(b * p->v_stride[0] + hk * p->v_stride[1] + j * p->v_stride[2]);
+            s[j] = sigma * dot_row(p, p->q, qo, p->k, ko);
+            dp[j] = dot_row(p, job->dout, oo, p->v, vo);
+            if (s[j] > m) m = s[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < hi; ++j) l += exp(s[j] - m);
+        double Di = 0.0;
+        for (int64_t j = 0; j < hi; ++j) Di += exp(s[j] - m) / l * dp[j];
+        double* st = job->stats + 3 * (size_t)r;
+        st[0] = m;
+        st[1] = l;
+        st[2] = Di;
+        double* dq = job->dq + (size_t)r * (size_t)D;
+        for (int64_t t = 0; t < D; ++t) dq[t] = 0.0;
+        for (int64_t j = 0; j < hi; ++j) {
+            const double ds = exp(s[j] - m) / l * (dp[j] - Di);
+            const uint64_t ko = (uint64_t)(b * p->k_stride[0] + hk * p->k_stride[1] + j * p->k_stride[2]);
+            for (int64_t t = 0; t < D; ++t) dq[t] += sigma * ds * elem(p, p->k, ko + (uint64_t)t);
+        }
+    }
+    free(s); free(dp);
+    job->status = 0;
+    return NULL;
+}
+
+/* pass 2: one key row (b, h', j) per step, summing over the group's query heads and rows */
+static void* bwd_key_worker(void* arg) {
+    oracle_bwd_job* job = (oracle_bwd_job*)arg;
+    const oracle_problem* p = job->p;
+    const int64_t D = p->D, g = p->Hq / p->Hkv;
+    const double sigma = (double)p->scale;
+    for (int64_t r = job->begin; r < job->end; ++r) {
+        const int64_t j = r % p->Nk, hk = (r / p->Nk) % p->Hkv, b = r / (p->Nk * p->Hkv);
+        const uint64_t ko = (uint64_t)(b * p->k_stride[0] + hk * p->k_stride[1] + j * p->k_stride[2]);
+        const uint64_t vo = (uint64_t)(b * p->v_stride[0] + hk * p->v_stride[1] + j * p->v_stride[2]);
+        double* dk = job->dk + (size_t)r * (size_t)D;
+        double* dv = job->dv + (size_t)r * (size_t)D;
+        for (int64_t t = 0; t < D; ++t) dk[t] = dv[t] = 0.0;
+        for (int64_t h = hk * g; h < (hk + 1) * g; ++h) {
+            /* rows that see key j: all, or i >= j - (Nk - Nq) when causal */
+            int64_t i0 = 0;
+            if (p->causal) i0 = j - (p->Nk - p->Nq) > 0 ? j - (p->Nk - p->Nq) : 0;
+            for (int64_t i = i0; i < p->Nq; ++i) {
+                const int64_t qr = (b * p->Hq + h) * p->Nq + i;
+                const double* st = job->stats + 3 * (size_t)qr;
+                const uint64_t qo = (uint64_t)(b * p->q_stride[0] + h * p->q_stride[1] + i * p->q_stride[2]);
+                const uint64_t oo = (uint64_t)(b * job->do_stride[0] + h * job->do_stride[1] + i * job->do_stride[2]);
+                const double sij = sigma * dot_row(p, p->q, qo, p->k, ko);
+                const double P = exp(sij - st[0]) / st[1];
+                const double dP = dot_row(p, job->dout, oo, p->v, vo);
+                const double ds = P * (dP - st[2]);
+                for (int64_t t = 0; t < D; ++t) {
+                    dv[t] += P * elem(p, job->dout, oo + (uint64_t)t);
+                    dk[t] += sigma * ds * elem(p, p->q, qo + (uint64_t)t);
+                }
+            }
+        }
+    }
+    job->status = 0;
+    return NULL;
+}
+
+static int run_pass(void* (*fn)(void*), oracle_bwd_job* base, int64_t n, int32_t nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > n) nthreads = (int32_t)(n > 0 ? n : 1);
+    pthread_t th[256];
+    int joinable[256];
+    oracle_bwd_job jobs[256];
+    const int64_t per = (n + nthreads - 1) / nthreads;
+    int njobs = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *base;
+        jobs[t].begin = (int64_t)t * per;
+        jobs[t].end = jobs[t].begin + per < n ? jobs[t].begin + per : n;
+        jobs[t].status = 0;
+        if (jobs[t].begin >= jobs[t].end) break;
+        njobs = t + 1;
+        joinable[t] = pthread_create(&th[t], NULL, fn, &jobs[t]) == 0;
+        if (!joinable[t]) fn(&jobs[t]);
+    }
+    int status = 0;
+    for (int t = 0; t < njobs; ++t) {
+        if (joinable[t]) pthread_join(th[t], NULL);
+        if (jobs[t].status != 0) status = jobs[t].status;
+    }
+    return status;
+}
+
+/*
+ * dq [B][Hq][Nq][D], dk and dv [B][Hkv][Nk][D] (contiguous, double) for the problem p and the
+ * upstream gradient dout (p's dtype, [B][Hq][Nq][D] with element strides do_stride and a unit
+ * head-dim stride).  Causal calls need Nq <= Nk.  Returns 0, -1 on a bad argument, -2 when memory
+ * runs out.
+ */
+int oracle_backward(const oracle_problem* p, const uint16_t* dout, const int64_t* do_stride, double* dq, double* dk,
+                    double* dv, int32_t nthreads) {
+    if (!p || !dout || !do_stride || !dq || !dk || !dv) return -1;
+    if (p->Hkv <= 0 || p->Hq % p->Hkv != 0 || p->D <= 0 || (p->causal && p->Nq > p->Nk)) return -1;
+    const int64_t nq = p->B * p->Hq * p->Nq, nk = p->B * p->Hkv * p->Nk;
+    double* stats = (double*)malloc(sizeof(double) * 3 * (size_t)(nq > 0 ? nq : 1));
+    if (!stats) return -2;
+    oracle_bwd_job base;
+    memset(&base, 0, sizeof base);
+    base.p = p;
+    base.dout = dout;
+    base.do_stride[0] = do_stride[0];
+    base.do_stride[1] = do_stride[1];
+    base.do_stride[2] = do_stride[2];
+    base.stats = stats;
+    base.dq = dq;
+    base.dk = dk;
+    base.dv = dv;
+    int rc = run_pass(bwd_query_worker, &base, nq, nthreads);
+    if (rc == 0) rc = run_pass(bwd_key_worker, &base, nk, nthreads);
+    free(stats);
+    return rc;
+}
