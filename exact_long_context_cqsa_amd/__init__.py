@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
-           "fwd_kernel_name", "cqs_assign", "cqs_default_set",
+           "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward",
            "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -103,6 +103,9 @@ def _load_library():
     lib.cqsa_struct_size.restype = ctypes.c_uint64
     lib.cqsa_fwd_kernel_name.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.cqsa_fwd_kernel_name.restype = ctypes.c_char_p
+    lib.cqsa_attention_backward.argtypes = [T, T, T, T, T, fp, ctypes.c_int, ctypes.c_float, T, T, T, fp,
+                                            ctypes.c_void_p]
+    lib.cqsa_attention_backward.restype = ctypes.c_int
     lib.cqsa_cqs_assign.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]
     lib.cqsa_cqs_assign.restype = ctypes.c_int
@@ -295,6 +298,29 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     if return_info:
         res += (info.as_dict(),)
     return res[0] if len(res) == 1 else res
+
+
+def attention_backward(q, k, v, out, dout, lse, is_causal: bool = False, scale: float | None = None, *,
+                       grad_dtype: torch.dtype | None = None, stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of ``attention`` for the upstream gradient ``dout``, from the forward's
+    ``out`` and ``lse`` (all on the GPU).  dk/dv have k's shape (GQA heads summed)."""
+    gd = grad_dtype or q.dtype
+    dev = _device_of(q, k, v, out, dout) or torch.device("cuda", torch.cuda.current_device())
+    dq = torch.empty(q.shape, dtype=gd, device=dev)
+    dk = torch.empty(k.shape, dtype=gd, device=dev)
+    dv = torch.empty(v.shape, dtype=gd, device=dev)
+    B, Hq, Nq, _ = q.shape
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        stats = torch.empty(max(1, 2 * B * Hq * Nq), dtype=torch.float32, device=dev)
+        sc = float(scale) if scale is not None else 0.0
+        _check(_lib.cqsa_attention_backward(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)),
+                                            ctypes.byref(_desc(out)), ctypes.byref(_desc(dout)), _fptr(lse),
+                                            1 if is_causal else 0, sc, ctypes.byref(_desc(dq)),
+                                            ctypes.byref(_desc(dk)), ctypes.byref(_desc(dv)), _fptr(stats),
+                                            st.cuda_stream))
+        stats.record_stream(st)
+    return dq, dk, dv
 
 
 def fwd_partial(q, k, v, is_causal=False, scale=None, kv_begin=0, kv_end=None, stream=None):

@@ -1494,6 +1494,102 @@ cqsa_status cqsa_attention(const cqsa_tensor* q, const cqsa_tensor* k, const cqs
     return cqsa_attention_ex(q, k, v, is_causal, scale, mem_budget, out, lse, nullptr, nullptr);
 }
 
+cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                    const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
+                                    float scale, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv, float* stats_ws,
+                                    void* stream) {
+    g_err.clear();
+    Problem P;
+    CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, nullptr, 0, true, false, &P));
+    View vdo, vdq, vdk, vdv;
+    CQSA_TRY(make_view(dout, "dout", false, true, &vdo));
+    CQSA_TRY(make_view(dq, "dq", false, true, &vdq));
+    CQSA_TRY(make_view(dk, "dk", false, true, &vdk));
+    CQSA_TRY(make_view(dv, "dv", false, true, &vdv));
+    if (vdo.dtype != P.dtype) return fail(CQSA_ERR_INVALID, "dout must have q's dtype");
+    if (vdo.B != P.B || vdo.H != P.Hq || vdo.N != P.Nq || vdo.D != P.D) return fail(CQSA_ERR_INVALID, "dout must have q's shape");
+    if (vdq.B != P.B || vdq.H != P.Hq || vdq.N != P.Nq || vdq.D != P.D) return fail(CQSA_ERR_INVALID, "dq must have q's shape");
+    for (const View* g : {&vdk, &vdv})
+        if (g->B != P.B || g->H != P.Hkv || g->N != P.Nk || g->D != P.D)
+            return fail(CQSA_ERR_INVALID, "dk and dv must have k's shape");
+    if (vdk.dtype != vdq.dtype || vdv.dtype != vdq.dtype) return fail(CQSA_ERR_INVALID, "dq, dk, dv must share one dtype");
+    if (P.empty || P.Nk == 0) return CQSA_OK;
+    if (P.streamed || vdo.host || vdq.host || vdk.host || vdv.host)
+        return fail(CQSA_ERR_UNSUPPORTED, "the backward needs q, k, v, out, dout and the gradients in device memory");
+    if (!lse) return fail(CQSA_ERR_INVALID, "lse is NULL");
+    {
+        cqsa_tensor lt;
+        std::memset(&lt, 0, sizeof lt);
+        lt.data = const_cast<float*>(lse);
+        lt.dtype = CQSA_F32;
+        lt.shape[0] = 1; lt.shape[1] = 1; lt.shape[2] = 1; lt.shape[3] = 1;
+        lt.stride[3] = 1;
+        bool host = false;
+        CQSA_TRY(locate(&lt, "lse", false, &host));
+        if (host) return fail(CQSA_ERR_UNSUPPORTED, "lse must be in device memory");
+    }
+    if (!aligned16(vdo.data) || vdo.sn % 8 || vdo.sh % 8 || vdo.sb % 8)
+        return fail(CQSA_ERR_UNSUPPORTED, "dout data and strides must be 16-byte aligned");
+    for (const View* g : {&vdq, &vdk, &vdv})
+        if ((reinterpret_cast<uintptr_t>(g->data) % (4 * g->es)) || g->sn % 4 || g->sh % 4 || g->sb % 4)
+            return fail(CQSA_ERR_UNSUPPORTED, "gradient data and strides must be aligned to 4 elements");
+    if (P.out.dtype == CQSA_F32 ? (!aligned16(P.out.data) || P.out.sn % 4 || P.out.sh % 4 || P.out.sb % 4)
+                                : (!aligned16(P.out.data) || P.out.sn % 8 || P.out.sh % 8 || P.out.sb % 8))
+        return fail(CQSA_ERR_UNSUPPORTED, "out data and strides must be 16-byte aligned for the backward");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float* stats = stats_ws;
+    bool owned = false;
+    if (!stats) {
+        const size_t bytes = (size_t)P.B * P.Hq * P.Nq * 2 * sizeof(float);
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&stats), bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(CQSA_ERR_OOM, "hipMalloc of %llu bytes for the row statistics failed: %s",
+                        (unsigned long long)bytes, hipGetErrorString(e));
+        }
+        owned = true;
+    }
+    BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.q = reinterpret_cast<const uint16_t*>(P.q.data);
+    a.k = reinterpret_cast<const uint16_t*>(P.k.data);
+    a.v = reinterpret_cast<const uint16_t*>(P.v.data);
+    a.dout = reinterpret_cast<const uint16_t*>(vdo.data);
+    a.out = P.out.data;
+    a.lse = lse;
+    a.q_sb = P.q.sb; a.q_sh = P.q.sh; a.q_sn = P.q.sn;
+    a.k_sb = P.k.sb; a.k_sh = P.k.sh; a.k_sn = P.k.sn;
+    a.v_sb = P.v.sb; a.v_sh = P.v.sh; a.v_sn = P.v.sn;
+    a.do_sb = vdo.sb; a.do_sh = vdo.sh; a.do_sn = vdo.sn;
+    a.o_sb = P.out.sb; a.o_sh = P.out.sh; a.o_sn = P.out.sn;
+    a.l_sb = P.Hq * P.Nq;
+    a.l_sh = P.Nq;
+    a.stats = stats;
+    a.dq = vdq.data; a.dk = vdk.data; a.dv = vdv.data;
+    a.dq_sb = vdq.sb; a.dq_sh = vdq.sh; a.dq_sn = vdq.sn;
+    a.dk_sb = vdk.sb; a.dk_sh = vdk.sh; a.dk_sn = vdk.sn;
+    a.dv_sb = vdv.sb; a.dv_sh = vdv.sh; a.dv_sn = vdv.sn;
+    a.Nq = P.Nq;
+    a.Nk = P.Nk;
+    a.B = (int32_t)P.B;
+    a.Hq = (int32_t)P.Hq;
+    a.Hkv = (int32_t)P.Hkv;
+    a.group = (int32_t)(P.Hq / P.Hkv);
+    a.causal = P.causal ? 1 : 0;
+    a.out_dtype = elem_type(P.out.dtype);
+    a.grad_dtype = elem_type(vdq.dtype);
+    a.scale = P.scale;
+    a.scale_log2 = P.scale * 1.44269504088896340736f;
+    hipError_t e = launch_bwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
+    cqsa_status s = CQSA_OK;
+    if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    if (owned) {
+        (void)hipStreamSynchronize(st);
+        (void)hipFree(stats);
+    }
+    return s;
+}
+
 cqsa_status cqsa_fwd_partial(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
                              float scale, int64_t kv_begin, int64_t kv_end, float* o_part, float* ml_part,
                              void* stream) {

@@ -72,6 +72,42 @@ struct MergeArgs {
     int64_t l_sb, l_sh;
 };
 
+// Backward: gradients of out = softmax(scale q k^T [+ causal]) v for an upstream gradient dout.
+// stats is a compact fp32 [B][Hq][Nq][2] array of (lse * log2 e, Delta = rowsum(dout * out)),
+// written by the first pass and read by the two gradient kernels.  Causal is bottom-right aligned
+// (key j visible to row i iff j <= i + Nk - Nq).  dq is [B, Hq, Nq, D]; dk, dv are [B, Hkv, Nk, D]
+// and sum over the query heads of their group.
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    const void* out;
+    const float* lse;
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t do_sb, do_sh, do_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int64_t l_sb, l_sh;
+    float* stats;
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t dq_sb, dq_sh, dq_sn;
+    int64_t dk_sb, dk_sh, dk_sn;
+    int64_t dv_sb, dv_sh, dv_sn;
+    int64_t Nq, Nk;
+    int32_t B, Hq, Hkv, group;
+    int32_t causal;
+    int32_t out_dtype;   // ElemType of out
+    int32_t grad_dtype;  // ElemType of dq, dk, dv
+    float scale;
+    float scale_log2;
+};
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
+
 // Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
 int fwd_block_m(int D, int p_split);
 

@@ -933,6 +933,396 @@ fwd_dma_kernel(const FwdArgs a) {
     fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
+// =============================================================================================
+// Backward.  Three launches: bwd_stats_kernel (Delta_i = dO_i . O_i and the base-2 lse per row),
+// bwd_dq_kernel (per query tile, over key tiles: dQ^T += K^T dS^T) and bwd_dkdv_kernel (per key
+// tile, over the group's query heads and query tiles: dV^T += dO^T P, dK^T += Q^T dS).  Each
+// gradient element is accumulated by one wave in a fixed order: no atomics, deterministic.  The
+// derivative itself: P = exp(s - lse), dP = dO V^T, dS = P (dP - Delta), dQ = scale dS K,
+// dK = scale dS^T Q, dV = P^T dO.  All tiles in LDS use the V swizzle (vswz), which serves both the
+// row reads (A operand = rows of the tile) and the transpose reads (A operand = the tile transposed,
+// in the key-slot order of the packed B operand).
+
+template <int D>
+__device__ __forceinline__ int rows_read(int l32, int t, int hi) {
+    return l32 * D + (((2 * t + hi) ^ vswz<D>(l32)) * 8);
+}
+
+template <int D>
+__device__ __forceinline__ int tr_read(int lane, int db) {
+    const int hi = lane >> 5;
+    const int src = lane & 15;
+    const int row = 4 * hi + src / 4;
+    const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    return row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
+}
+
+// The transposed operand of one 16-slot group: p = tile + tr_read + 16 t D.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8 * D));
+    u32x4 x;
+    x[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
+    x[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
+    x[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
+    x[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
+    return x;
+}
+
+template <int DT>
+__device__ __forceinline__ f32x8 load8(const void* base, int64_t off, int dt) {
+    if (dt == ET_F32) {
+        const float* p = static_cast<const float*>(base) + off;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+        return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    }
+    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + off);
+    return dt == ET_F16 ? unpack8<ET_F16>(u) : unpack8<ET_BF16>(u);
+}
+
+// stats[row] = (lse * log2 e, sum_d dO O); D / 8 threads per row, 8 dims each.
+template <int D, int DT>
+__global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
+    constexpr int TPR = D / 8;
+    constexpr int RPB = 256 / TPR;
+    const int64_t total = (int64_t)a.B * a.Hq * a.Nq;
+    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int d0 = (threadIdx.x % TPR) * 8;
+    float acc = 0.f;
+    int64_t b = 0, h = 0, i = 0;
+    if (r < total) {
+        i = r % a.Nq;
+        h = (r / a.Nq) % a.Hq;
+        b = r / (a.Nq * a.Hq);
+        const f32x8 dov = unpack8<DT>(*reinterpret_cast<const u32x4*>(a.dout + b * a.do_sb + h * a.do_sh + i * a.do_sn + d0));
+        const f32x8 ov = load8<DT>(a.out, b * a.o_sb + h * a.o_sh + i * a.o_sn + d0, a.out_dtype);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(dov[e], ov[e], acc);
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (r < total && d0 == 0) {
+        const float l = a.lse[b * a.l_sb + h * a.l_sh + i];
+        a.stats[2 * r] = l == -INFINITY ? INFINITY : l * kLog2e;   // no visible key: P = 0
+        a.stats[2 * r + 1] = acc;
+    }
+}
+
+// dQ for BM = 32 NW query rows of one (b, query head): the forward's tiling with dS^T in place of P^T.
+template <int D, int DT, int KT, int NW>
+__global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a, int n_qt) {
+    constexpr int BM = NW * 32;
+    constexpr int TILE = KT * D;
+    constexpr int STAGE = 2 * TILE;
+    constexpr int GPR = D / 8, RPI = 64 / GPR, NBLK = KT / RPI, BPW = NBLK / NW;
+    constexpr int NKB = KT / 32, NPK = KT / 16, NDB = D / 32, NDK = D / 16;
+    static_assert(NBLK % NW == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = w % n_qt;
+    w /= n_qt;
+    const int hq = w % a.Hq;
+    const int b = w / a.Hq;
+    const int hkv = hq / a.group;
+    const int qt = n_qt - 1 - qt_idx;
+    const int64_t delta_c = a.Nk - a.Nq;
+
+    const int64_t i0 = (int64_t)qt * BM;
+    const int64_t i_end = min(i0 + (int64_t)BM, a.Nq);
+    const int64_t iw0 = i0 + (int64_t)wave * 32;
+    const int64_t iw_end = min(iw0 + 32, i_end);
+    int64_t khi = a.Nk;
+    if (a.causal) khi = min(khi, i_end + delta_c);
+    const int ntiles = khi > 0 ? (int)((khi + KT - 1) / KT) : 0;
+
+    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+
+    // B operands: this lane's query row of q and of dO; its (lse2, Delta)
+    const int64_t row = iw0 + l32;
+    const bool row_ok = row < i_end;
+    u32x4 qf[NDK], dof[NDK];
+    {
+        const uint16_t* qr = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh + (row_ok ? row : 0) * a.q_sn + 8 * hi;
+        const uint16_t* dr = a.dout + (int64_t)b * a.do_sb + (int64_t)hq * a.do_sh + (row_ok ? row : 0) * a.do_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qr + 16 * t);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(dr + 16 * t);
+            qf[t] = row_ok ? x : u32x4{0u, 0u, 0u, 0u};
+            dof[t] = row_ok ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float lse2 = INFINITY, dlt = 0.f;
+    if (row_ok) {
+        const float* sp = a.stats + 2 * (((int64_t)b * a.Hq + hq) * a.Nq + row);
+        lse2 = sp[0];
+        dlt = sp[1];
+    }
+
+    int koff[BPW], voff[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int r = (wave + i * NW) * RPI + lane / GPR;
+        const int pg = lane % GPR;
+        koff[i] = (int)((r * a.k_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+        voff[i] = (int)((r * a.v_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+    }
+    int rread[NDK], tread[NDB];
+#pragma unroll
+    for (int t = 0; t < NDK; ++t) rread[t] = rows_read<D>(l32, t, hi);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db);
+
+    f32x16 dqacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
+
+#define CQSA_BWD_DQ_TILE(j)                                                                                 \
+    do {                                                                                                  \
+        const int64_t j0_ = (int64_t)(j) * KT;                                                            \
+        const int64_t nv_ = min(khi - j0_, (int64_t)KT);                                                  \
+        uint16_t* st_ = lds + ((j) & 1) * STAGE;                                                           \
+        dma_rows<NW, BPW, D>(st_, kp, a.k_sn, j0_, nv_, koff, wave);                                       \
+        dma_rows<NW, BPW, D>(st_ + TILE, vp, a.v_sn, j0_, nv_, voff, wave);                                \
+    } while (0)
+
+    if (ntiles > 0) CQSA_BWD_DQ_TILE(0);
+    for (int it = 0; it < ntiles; ++it) {
+        __syncthreads();
+        if (it + 1 < ntiles) CQSA_BWD_DQ_TILE(it + 1);
+        const int64_t j0 = (int64_t)it * KT;
+        const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + delta_c);
+        if (!active) continue;
+        const uint16_t* st = lds + (it & 1) * STAGE;
+
+        f32x16 sacc[NKB], dpacc[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            sacc[kb] = f32x16{};
+            dpacc[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int t = 0; t < NDK; ++t)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const u32x4 kf = *reinterpret_cast<const u32x4*>(st + rread[t] + kb * 32 * D);
+                const u32x4 vf = *reinterpret_cast<const u32x4*>(st + TILE + rread[t] + kb * 32 * D);
+                sacc[kb] = mfma32<DT>(kf, qf[t], sacc[kb]);
+                dpacc[kb] = mfma32<DT>(vf, dof[t], dpacc[kb]);
+            }
+        const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + delta_c));
+        if (need_mask) {
+            int lim = (int)min(khi - j0, (int64_t)KT);
+            if (a.causal) {
+                const int64_t cl = row + delta_c - j0 + 1;
+                lim = min(lim, (int)max(min(cl, (int64_t)KT), (int64_t)0));
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                    if (t >= lim) sacc[kb][r] = -INFINITY;
+                }
+        }
+        u32x4 pf[NPK];
+#pragma unroll
+        for (int t = 0; t < NPK; ++t) {
+            const int kb = t >> 1, u = t & 1;
+            f32x8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + e], a.scale_log2, -lse2));
+                x[e] = p * (dpacc[kb][8 * u + e] - dlt);
+            }
+            pf[t] = pack8<DT>(x);
+        }
+#pragma unroll
+        for (int t = 0; t < NPK; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                dqacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), pf[t], dqacc[db]);
+    }
+#undef CQSA_BWD_DQ_TILE
+
+    if (!row_ok) return;
+    const int64_t ob = (int64_t)b * a.dq_sb + (int64_t)hq * a.dq_sh + row * a.dq_sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
+            store4(a.dq, ob + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
+        }
+}
+
+// dK and dV for BN = 32 NW keys of one (b, key/value head), summed over the group's query heads:
+// each wave keeps 32 keys (and their values) as B operands and streams query tiles of QT rows.
+template <int D, int DT, int QT, int NW>
+__global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdArgs a, int n_kt) {
+    constexpr int BN = NW * 32;
+    constexpr int TILE = QT * D;
+    constexpr int STAGE = 2 * TILE;                    // Q tile, then dO tile
+    constexpr int GPR = D / 8, RPI = 64 / GPR, NBLK = QT / RPI, BPW = NBLK / NW;
+    constexpr int NQB = QT / 32, NPQ = QT / 16, NDB = D / 32, NDK = D / 16;
+    static_assert(NBLK % NW == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float stl[2][2][QT];   // [stage][lse2 | Delta][row]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int kt = w % n_kt;                          // low key tiles (most query rows) first
+    w /= n_kt;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int64_t delta_c = a.Nk - a.Nq;
+
+    const int64_t jw0 = (int64_t)kt * BN + (int64_t)wave * 32;
+    const int64_t key = jw0 + l32;
+    const bool key_ok = key < a.Nk;
+    u32x4 kf[NDK], vf[NDK];
+    {
+        const uint16_t* kr = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh + (key_ok ? key : 0) * a.k_sn + 8 * hi;
+        const uint16_t* vr = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh + (key_ok ? key : 0) * a.v_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(kr + 16 * t);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(vr + 16 * t);
+            kf[t] = key_ok ? x : u32x4{0u, 0u, 0u, 0u};
+            vf[t] = key_ok ? y : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // query rows that see a key of this workgroup: i >= first key - delta (causal)
+    const int64_t kb0 = (int64_t)kt * BN;
+    const int64_t i_start = a.causal ? max((int64_t)0, kb0 - delta_c) : 0;
+    const int nqt = i_start < a.Nq ? (int)((a.Nq - i_start + QT - 1) / QT) : 0;
+    const int total = nqt * a.group;
+
+    int qoff[BPW], doff[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int r = (wave + i * NW) * RPI + lane / GPR;
+        const int pg = lane % GPR;
+        qoff[i] = (int)((r * a.q_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+        doff[i] = (int)((r * a.do_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+    }
+    int rread[NDK], tread[NDB];
+#pragma unroll
+    for (int t = 0; t < NDK; ++t) rread[t] = rows_read<D>(l32, t, hi);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db);
+
+    f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        dkacc[db] = f32x16{};
+        dvacc[db] = f32x16{};
+    }
+
+    // tile T: head hkv * group + T / nqt, query rows from i_start + (T % nqt) QT; its rows' stats
+#define CQSA_BWD_KV_TILE(T)                                                                                 \
+    do {                                                                                                  \
+        const int h_ = hkv * a.group + (T) / nqt;                                                         \
+        const int64_t q0_ = i_start + (int64_t)((T) % nqt) * QT;                                          \
+        const int64_t nv_ = min(a.Nq - q0_, (int64_t)QT);                                                 \
+        uint16_t* st_ = lds + ((T) & 1) * STAGE;                                                           \
+        dma_rows<NW, BPW, D>(st_, a.q + (int64_t)b * a.q_sb + (int64_t)h_ * a.q_sh, a.q_sn, q0_, nv_, qoff, wave); \
+        dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_,   \
+                             nv_, doff, wave);                                                            \
+        if (tid < QT) {                                                                                   \
+            const bool ok_ = tid < nv_;                                                                   \
+            const float* sp_ = a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + (ok_ ? q0_ + tid : 0));   \
+            stl[(T) & 1][0][tid] = ok_ ? sp_[0] : INFINITY;                                               \
+            stl[(T) & 1][1][tid] = ok_ ? sp_[1] : 0.f;                                                    \
+        }                                                                                                 \
+    } while (0)
+
+    if (total > 0) CQSA_BWD_KV_TILE(0);
+    for (int it = 0; it < total; ++it) {
+        __syncthreads();
+        if (it + 1 < total) CQSA_BWD_KV_TILE(it + 1);
+        const int64_t q0 = i_start + (int64_t)(it % nqt) * QT;
+        // the wave works on the tile when some row of it sees some valid key of the wave
+        const bool active = jw0 < a.Nk && (!a.causal || q0 + QT - 1 + delta_c >= jw0);
+        if (!active) continue;
+        const uint16_t* st = lds + (it & 1) * STAGE;
+        const float* sl = stl[it & 1][0];
+        const float* sd = stl[it & 1][1];
+        const bool need_mask = (q0 + QT > a.Nq) || (jw0 + 32 > a.Nk) || (a.causal && q0 + delta_c < jw0 + 31);
+
+        u32x4 pp[NPQ], ps[NPQ];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int t = 0; t < NDK; ++t) {
+                const u32x4 qa = *reinterpret_cast<const u32x4*>(st + rread[t] + qb * 32 * D);
+                const u32x4 da = *reinterpret_cast<const u32x4*>(st + TILE + rread[t] + qb * 32 * D);
+                sacc = mfma32<DT>(qa, kf[t], sacc);
+                dpacc = mfma32<DT>(da, vf[t], dpacc);
+            }
+            // register r of the lane holds query row qb 32 + 8 (r / 4) + 4 hi + r % 4 of the tile
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                f32x8 xp, xs;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int rr = qb * 32 + 8 * (2 * u + g) + 4 * hi;    // rows rr .. rr + 3
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + rr);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + rr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 8 * u + 4 * g + e;
+                        float s = sacc[r];
+                        if (need_mask) {
+                            const int64_t qi = q0 + rr + e;
+                            const bool vis = key_ok && qi < a.Nq && (!a.causal || key <= qi + delta_c);
+                            if (!vis) s = -INFINITY;
+                        }
+                        const float p = __builtin_amdgcn_exp2f(fmaf(s, a.scale_log2, -l4[e]));
+                        xp[4 * g + e] = p;
+                        xs[4 * g + e] = p * (dpacc[r] - d4[e]);
+                    }
+                }
+                pp[2 * qb + u] = pack8<DT>(xp);
+                ps[2 * qb + u] = pack8<DT>(xs);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NPQ; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dvacc[db] = mfma32<DT>(tr_operand<D>(st + TILE + tread[db] + 16 * t * D), pp[t], dvacc[db]);
+                dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), ps[t], dkacc[db]);
+            }
+    }
+#undef CQSA_BWD_KV_TILE
+
+    if (!key_ok) return;
+    const int64_t kbase = (int64_t)b * a.dk_sb + (int64_t)hkv * a.dk_sh + key * a.dk_sn;
+    const int64_t vbase = (int64_t)b * a.dv_sb + (int64_t)hkv * a.dv_sh + key * a.dv_sn;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 x = {dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
+            const f32x4 y = {dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+            store4(a.dk, kbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
+            store4(a.dv, vbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, y);
+        }
+}
+
 // Log-sum-exp merge: TPR threads per row, four output dims per thread.  The threads of one row
 // sit in one wave, so in-place operation (output == part 0) reads every input before it writes.
 template <int D>
@@ -1081,6 +1471,53 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
     if (D == 64 && dtype == ET_BF16) return launch_d<64, ET_BF16>(a, stream);
     if (D == 128 && dtype == ET_F16) return launch_d<128, ET_F16>(a, stream);
     if (D == 128 && dtype == ET_BF16) return launch_d<128, ET_BF16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int D, int DT>
+hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+    if (rows <= 0) return hipSuccess;
+    {
+        constexpr int RPB = 256 / (D / 8);
+        const int64_t blocks = (rows + RPB - 1) / RPB;
+        if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_stats_kernel<D, DT>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int DQ_NW = 4, DQ_KT = 64;
+    constexpr int KV_NW = 4, KV_QT = 32;
+    {
+        const int64_t n_qt = (a.Nq + DQ_NW * 32 - 1) / (DQ_NW * 32);
+        const int64_t blocks = (int64_t)a.B * a.Hq * n_qt;
+        if (blocks > 0x7FFFFFFF || n_qt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        if (blocks > 0)
+            hipLaunchKernelGGL((bwd_dq_kernel<D, DT, DQ_KT, DQ_NW>), dim3((unsigned)blocks), dim3(DQ_NW * 64), 0, st, a,
+                               (int)n_qt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        const int64_t n_kt = (a.Nk + KV_NW * 32 - 1) / (KV_NW * 32);
+        const int64_t blocks = (int64_t)a.B * a.Hkv * n_kt;
+        if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+        if (blocks > 0)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0, st,
+                               a, (int)n_kt);
+        return hipGetLastError();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
+    if (D == 64 && dtype == ET_F16) return launch_bwd_d<64, ET_F16>(a, stream);
+    if (D == 64 && dtype == ET_BF16) return launch_bwd_d<64, ET_BF16>(a, stream);
+    if (D == 128 && dtype == ET_F16) return launch_bwd_d<128, ET_F16>(a, stream);
+    if (D == 128 && dtype == ET_BF16) return launch_bwd_d<128, ET_BF16>(a, stream);
     return hipErrorInvalidValue;
 }
 

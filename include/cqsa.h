@@ -207,6 +207,30 @@ cqsa_status cqsa_lse_merge(const float* const* o_parts, const float* const* ml_p
  */
 cqsa_status cqsa_finalize(const float* o, const float* ml, cqsa_tensor* out, float* lse, void* stream);
 
+/*
+ * cqsa_attention_backward: the gradients of out = softmax(scale q k^T [+ causal mask]) v for an
+ * upstream gradient dout, by the derivative of the same expression (P = exp(s - lse),
+ * dV = P^T dO, dS = P (dO V^T - rowsum(dO * out)), dQ = scale dS K, dK = scale dS^T Q): the
+ * backward the Stream-CQSA pages ship beside the forward (stream-cqsa 2.2.0 -> 2.2.2 diff, README.md,
+ * kernel table).  Device memory only.
+ *
+ *   q, k, v     the forward's inputs (fp16 or bf16, D 64 or 128, causal bottom-right as above).
+ *   out, lse    the forward's output (any dtype) and fp32 lse [B, Hq, Nq] contiguous (device).
+ *   dout        [B, Hq, Nq, D] in q's dtype; rows 16-byte aligned.
+ *   dq          [B, Hq, Nq, D]; dk, dv [B, Hkv, Nk, D] (with GQA, summed over each key/value
+ *               head's query heads); one dtype among fp16, bf16, fp32.  Written, not accumulated.
+ *   stats_ws    device scratch of 2 B Hq Nq floats (row statistics), or NULL: the library then
+ *               allocates it and the call returns after the work is done.
+ *   stream      hipStream_t (NULL = null stream); with stats_ws the call is stream-ordered and
+ *               returns without waiting.
+ * Deterministic (every gradient element is summed by one wave in a fixed order).  Host-resident
+ * operands give CQSA_ERR_UNSUPPORTED.
+ */
+cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                    const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
+                                    float scale, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv, float* stats_ws,
+                                    void* stream);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* cqsa_last_error(void);
 

@@ -9,7 +9,7 @@ tensor can be regenerated piecewise and in any storage layout.
 The five workloads (``workload(i)``) follow the input recipe of the method's
 measured cases: fp16/bf16 q/k/v drawn i.i.d. from N(0, sigma^2), causal or not,
 GQA for the prompt case, large logits with +20 spikes for the softmax-stress
-case.  Seeds are ``0xC05A0000 + i``; tensor ids are q=0, k=1, v=2, spikes=3.
+case.  Seeds are ``0xC05A0000 + i``; tensor ids are q=0, k=1, v=2, spikes=3, upstream gradient=4.
 """
 from __future__ import annotations
 
@@ -27,7 +27,7 @@ _SRC = os.path.join(_HERE, "synth_gen.c")
 _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SPIKES = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SPIKES, TENSOR_DO = 0, 1, 2, 3, 4
 SEED_BASE = 0xC05A0000
 
 _DT = {torch.float16: 0, torch.bfloat16: 1, torch.float32: 2, torch.float64: 3}

@@ -1,0 +1,102 @@
+"""GPU parity of the backward (dQ, dK, dV through cqsa_attention_backward) against the FP64 oracle.
+
+Metric: max |g - g_ref| / max(1, max |g_ref|) per gradient tensor (the floor keeps a gradient that is
+exactly zero, e.g. dQ and dK of a row that sees one key, measured in absolute terms: the inputs are
+N(0, 1), so gradients are of order one).  Bound: each product takes its operands rounded to the input
+format (P, dS and the forward output rounded with unit u = 2^-11 for fp16, 2^-8 for bf16), so the
+error is a few u of the gradient's scale; the tests allow 8 u.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = {torch.float16: 2.0 ** -11, torch.bfloat16: 2.0 ** -8}
+
+
+def cqsa():
+    import exact_long_context_cqsa_amd as m
+    return m
+
+
+def say(*a):
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed):
+    q = synth.normal((B, Hq, Nq, D), seed=seed, tensor_id=0, dtype=dtype)
+    k = synth.normal((B, Hkv, Nk, D), seed=seed, tensor_id=1, dtype=dtype)
+    v = synth.normal((B, Hkv, Nk, D), seed=seed, tensor_id=2, dtype=dtype)
+    do = synth.normal((B, Hq, Nq, D), seed=seed, tensor_id=synth.TENSOR_DO, dtype=dtype)
+    return q, k, v, do
+
+
+def rel_err(got, ref):
+    g = got.detach().double().cpu()
+    return float((g - ref).abs().max()) / max(1.0, float(ref.abs().max()))
+
+
+CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal
+    (1, 1, 1, 1024, 1024, 64, torch.float16, True),
+    (1, 2, 2, 300, 300, 64, torch.float16, True),        # ragged tails
+    (2, 3, 3, 77, 513, 64, torch.float16, False),        # Nq < Nk
+    (1, 2, 2, 700, 129, 64, torch.bfloat16, False),      # Nq > Nk
+    (1, 4, 1, 257, 1000, 128, torch.bfloat16, True),     # GQA 4:1, bottom-right causal
+    (2, 8, 2, 130, 130, 128, torch.float16, True),       # GQA, square causal
+    (1, 2, 2, 1, 1, 64, torch.float16, True),            # one query, one key
+    (1, 2, 2, 1, 4099, 128, torch.float16, True),        # one query at the end of 4099 keys
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}H{c[1]}x{c[2]}q{c[3]}k{c[4]}d{c[5]}"
+                         f"{'f16' if c[6] == torch.float16 else 'bf16'}{'c' if c[7] else 'n'}")
+def test_backward_parity(case):
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal = case
+    say("backward", case)
+    q, k, v, do = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=5000 + Nq + Nk + D)
+    scale = 1.0 / math.sqrt(D)
+    rq, rk, rv = oracle.backward(q, k, v, do, causal=causal, scale=scale)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, return_lse=True)   # out in the input dtype
+    dq, dk, dv = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=causal, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    errs = {n: rel_err(g, r) for n, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))}
+    say("errors", errs)
+    for n, e in errs.items():
+        assert e <= 8 * U[dtype], (n, e)
+    assert all(torch.isfinite(g).all() for g in (dq, dk, dv))
+
+
+def test_backward_deterministic_and_grad_dtypes():
+    B, Hq, Hkv, N, D = 1, 4, 2, 777, 64
+    q, k, v, do = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=77)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=True, return_lse=True)
+    a = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=True, grad_dtype=torch.float32)
+    b = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=True, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    h = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=True)   # fp16 gradients
+    torch.cuda.synchronize()
+    for x, y in zip(a, h):
+        assert y.dtype == torch.float16
+        assert (x - y.float()).abs().max().item() <= 2e-3 * max(1.0, x.abs().max().item())
+
+
+def test_backward_errors():
+    m = cqsa()
+    q, k, v, do = (t.to(DEV) for t in gen(1, 2, 2, 64, 64, 64, torch.float16, seed=1))
+    out, lse = m.attention(q, k, v, is_causal=True, return_lse=True)
+    with pytest.raises(m.CqsaError, match="UNSUPPORTED"):
+        m.attention_backward(q.cpu().pin_memory(), k, v, out, do, lse, is_causal=True)
+    with pytest.raises(m.CqsaError, match="INVALID"):
+        m.attention_backward(q, k, v, out, do.to(torch.bfloat16), lse, is_causal=True)
