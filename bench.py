@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--streamed", action="store_true", help="also run the 4M-token host-streamed case")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the backward (dQ, dK, dV) on the resident workload")
     ap.add_argument("--split-p", action="store_true",
                     help="also time the split-P precision mode on the resident workload and check it on sampled rows")
     ap.add_argument("--cqs", type=int, default=0,
@@ -255,6 +257,26 @@ def main():
                    "max_abs_vs_fp64_split": errs[1], "max_abs_vs_fp64_default": errs[0]}
         print(f"[bench] split-P: {sms:.3f} ms per call, max_abs {errs[1]:.2e} (default {errs[0]:.2e})",
               file=sys.stderr, flush=True)
+    backward = None
+    if args.backward:
+        out_b, lse_b = cqsa.attention(qd, kd, vd, is_causal=w.causal, return_lse=True)
+        dout = torch.randn_like(out_b)
+        for _ in range(2):
+            cqsa.attention_backward(qd, kd, vd, out_b, dout, lse_b, is_causal=w.causal)
+        torch.cuda.synchronize()
+        b0 = time.perf_counter()
+        n_b = max(3, args.steps // 2)
+        for _ in range(n_b):
+            grads = cqsa.attention_backward(qd, kd, vd, out_b, dout, lse_b, is_causal=w.causal)
+        torch.cuda.synchronize()
+        bms = (time.perf_counter() - b0) * 1e3 / n_b
+        bflops = 2.5 * flops      # the five products of the derivative: 10 D per visible pair
+        backward = {"ms_per_call": round(bms, 4), "tflops": round(bflops / (bms / 1e3) / 1e12, 2),
+                    "algorithmic_flop": bflops,
+                    "note": "dQ, dK, dV from the forward's out and lse; 10 D FLOP per visible pair (the dQ "
+                            "kernel recomputes S and dP, so 14 D per pair are executed)"}
+        del grads, out_b, lse_b, dout
+        print(f"[bench] backward: {bms:.3f} ms per call ({backward['tflops']} TFLOP/s)", file=sys.stderr, flush=True)
     kernel = cqsa.fwd_kernel_name(w.D)
     prof_path = args.profile or os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_{w.name}.md")
     traffic, traffic_src = measured_traffic(prof_path)
@@ -288,6 +310,8 @@ def main():
         line["cqs_resident"] = cqs_resident
     if split_p:
         line["split_p"] = split_p
+    if backward:
+        line["backward"] = backward
     if args.streamed:
         line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
     if not args.no_cpu_baseline:
