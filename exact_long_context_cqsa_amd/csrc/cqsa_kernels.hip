@@ -1011,8 +1011,8 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
 }
 
 // dQ for BM = 32 NW query rows of one (b, query head): the forward's tiling with dS^T in place of P^T.
-template <int D, int DT, int KT, int NW>
-__global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a, int n_qt) {
+template <int D, int DT, int KT, int NW, int WPE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dq_kernel(const BwdArgs a, int n_qt) {
     constexpr int BM = NW * 32;
     constexpr int TILE = KT * D;
     constexpr int STAGE = 2 * TILE;
@@ -1166,8 +1166,8 @@ __global__ void __launch_bounds__(NW * 64) bwd_dq_kernel(const BwdArgs a, int n_
 
 // dK and dV for BN = 32 NW keys of one (b, key/value head), summed over the group's query heads:
 // each wave keeps 32 keys (and their values) as B operands and streams query tiles of QT rows.
-template <int D, int DT, int QT, int NW>
-__global__ void __launch_bounds__(NW * 64) bwd_dkdv_kernel(const BwdArgs a, int n_kt) {
+template <int D, int DT, int QT, int NW, int WPE>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(const BwdArgs a, int n_kt) {
     constexpr int BN = NW * 32;
     constexpr int TILE = QT * D;
     constexpr int STAGE = 2 * TILE;                    // Q tile, then dO tile
@@ -1488,14 +1488,14 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int DQ_NW = 4, DQ_KT = 64;
-    constexpr int KV_NW = 4, KV_QT = 32;
+    constexpr int DQ_NW = 4, DQ_KT = D == 64 ? 64 : 32, DQ_WPE = 2;
+    constexpr int KV_NW = 4, KV_QT = 32, KV_WPE = D == 64 ? 2 : 1;   // D=128 holds 256 accumulator and operand registers
     {
         const int64_t n_qt = (a.Nq + DQ_NW * 32 - 1) / (DQ_NW * 32);
         const int64_t blocks = (int64_t)a.B * a.Hq * n_qt;
         if (blocks > 0x7FFFFFFF || n_qt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (blocks > 0)
-            hipLaunchKernelGGL((bwd_dq_kernel<D, DT, DQ_KT, DQ_NW>), dim3((unsigned)blocks), dim3(DQ_NW * 64), 0, st, a,
+            hipLaunchKernelGGL((bwd_dq_kernel<D, DT, DQ_KT, DQ_NW, DQ_WPE>), dim3((unsigned)blocks), dim3(DQ_NW * 64), 0, st, a,
                                (int)n_qt);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1505,7 +1505,7 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         const int64_t blocks = (int64_t)a.B * a.Hkv * n_kt;
         if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (blocks > 0)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0, st,
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0, st,
                                a, (int)n_kt);
         return hipGetLastError();
     }
