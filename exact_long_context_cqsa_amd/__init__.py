@@ -255,7 +255,15 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     ``precision=1`` feeds P to the PV product as a hi part plus a lo residual (two accumulator
     chains), for results near fp32 accuracy at about twice the PV work.  Returns out
     (on q's device; pinned host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the
-    plan dict on request."""
+    plan dict on request.  When q, k or v requires grad (and grad mode is on), the call records an
+    autograd node whose backward runs ``attention_backward`` (device-resident inputs only)."""
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        if out is not None or return_info:
+            raise ValueError("out= and return_info are not available on the autograd path")
+        res = _AttentionFn.apply(q, k, v, bool(is_causal), scale, dict(
+            mem_budget=mem_budget, q_chunk=q_chunk, kv_chunk=kv_chunk, kv_splits=kv_splits, merge=merge,
+            out_dtype=out_dtype, stream=stream, cqs=cqs, precision=precision))
+        return res if return_lse else res[0]
     dev = _device_of(q, k, v, out)
     if dev is None:
         dev = torch.device("cuda", torch.cuda.current_device())
@@ -298,6 +306,25 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     if return_info:
         res += (info.as_dict(),)
     return res[0] if len(res) == 1 else res
+
+
+class _AttentionFn(torch.autograd.Function):
+    """Autograd node: the forward kernels, then cqsa_attention_backward from the saved out and lse."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, is_causal, scale, kw):
+        with torch.no_grad():
+            out, lse = attention(q.detach(), k.detach(), v.detach(), is_causal, scale, return_lse=True, **kw)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.is_causal, ctx.scale = is_causal, scale
+        ctx.mark_non_differentiable(lse)
+        return out, lse
+
+    @staticmethod
+    def backward(ctx, dout, _dlse):
+        q, k, v, out, lse = ctx.saved_tensors
+        g = attention_backward(q, k, v, out, dout.to(q.dtype).contiguous(), lse, ctx.is_causal, ctx.scale)
+        return g[0], g[1], g[2], None, None, None
 
 
 def attention_backward(q, k, v, out, dout, lse, is_causal: bool = False, scale: float | None = None, *,

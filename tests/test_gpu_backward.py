@@ -100,3 +100,18 @@ def test_backward_errors():
         m.attention_backward(q.cpu().pin_memory(), k, v, out, do, lse, is_causal=True)
     with pytest.raises(m.CqsaError, match="INVALID"):
         m.attention_backward(q, k, v, out, do.to(torch.bfloat16), lse, is_causal=True)
+
+
+def test_autograd_through_attention():
+    """attention() with requires_grad records the backward: loss = sum(out * dO) gives the oracle's
+    gradients for dO."""
+    B, Hq, Hkv, N, D = 1, 4, 2, 513, 64
+    q, k, v, do = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=91)
+    rq, rk, rv = oracle.backward(q, k, v, do, causal=True, scale=1.0 / math.sqrt(D))
+    qd, kd, vd = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    out = cqsa().attention(qd, kd, vd, is_causal=True)
+    (out.float() * do.to(DEV).float()).sum().backward()
+    torch.cuda.synchronize()
+    for g, r in ((qd.grad, rq), (kd.grad, rk), (vd.grad, rv)):
+        assert g.dtype == torch.float16
+        assert rel_err(g.float(), r) <= 8 * U[torch.float16] + 2 ** -11   # + the fp16 rounding of the gradient
