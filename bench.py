@@ -42,6 +42,8 @@ def parse():
                     help="also time the backward (dQ, dK, dV) on the resident workload")
     ap.add_argument("--split-p", action="store_true",
                     help="also time the split-P precision mode on the resident workload and check it on sampled rows")
+    ap.add_argument("--wave-tokens", type=int, default=None,
+                    help="packed-row budget of a wave of the quorum-set schedule (default: the library's)")
     ap.add_argument("--cqs", type=int, default=0,
                     help="also time the cyclic quorum-set schedule with this many parts (resident workload, "
                          "and the streamed case with --streamed)")
@@ -218,18 +220,21 @@ def main():
     cqs_resident = None
     if args.cqs:
         for _ in range(2):
-            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs)
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, wave_tokens=args.wave_tokens)
         torch.cuda.synchronize()
         c0 = time.perf_counter()
         n_cqs = max(3, args.steps // 4)
         for _ in range(n_cqs):
-            cinfo = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, return_info=True)[1]
+            cinfo = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, wave_tokens=args.wave_tokens,
+                                   return_info=True)[1]
         torch.cuda.synchronize()
         cms = (time.perf_counter() - c0) * 1e3 / n_cqs
         cqs_resident = {"c": args.cqs, "ms_per_call": round(cms, 4), "tflops": round(flops / (cms / 1e3) / 1e12, 2),
                         "pairs": cinfo["chunk_pairs"], "subproblems": cinfo["cqs_subproblems"],
+                        "waves": cinfo["cqs_waves"], "wave_tokens": cinfo["wave_tokens"],
                         "kernel_launches": cinfo["kernel_launches"]}
-        print(f"[bench] cqs c={args.cqs}: {cms:.3f} ms per call", file=sys.stderr, flush=True)
+        print(f"[bench] cqs c={args.cqs}: {cms:.3f} ms per call ({cinfo['cqs_waves']} waves, "
+              f"{cinfo['kernel_launches']} launches)", file=sys.stderr, flush=True)
     split_p = None
     if args.split_p:
         import numpy as np

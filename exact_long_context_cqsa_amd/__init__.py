@@ -40,7 +40,8 @@ class CqsaOptions(ctypes.Structure):
     _fields_ = [("q_chunk", ctypes.c_int64), ("kv_chunk", ctypes.c_int64), ("kv_splits", ctypes.c_int32),
                 ("merge_mode", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("cqs_c", ctypes.c_int32),
-                ("cqs_l", ctypes.c_int32), ("precision", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32))]
+                ("cqs_l", ctypes.c_int32), ("precision", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32)),
+                ("wave_tokens", ctypes.c_int64)]
 
 
 class CqsaPlanInfo(ctypes.Structure):
@@ -51,7 +52,8 @@ class CqsaPlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_uint64), ("budget_bytes", ctypes.c_uint64),
                 ("h2d_bytes", ctypes.c_uint64), ("d2h_bytes", ctypes.c_uint64), ("h2d_ms", ctypes.c_double),
                 ("d2h_ms", ctypes.c_double), ("wall_ms", ctypes.c_double), ("cqs_c", ctypes.c_int32),
-                ("cqs_subproblems", ctypes.c_int32)]
+                ("cqs_subproblems", ctypes.c_int32), ("cqs_waves", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("wave_tokens", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -175,11 +177,13 @@ def cqs_assign(c: int, interest_set) -> list:
 
 
 def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=None, workspace=None,
-             num_cus=None, cqs=None, precision=0) -> CqsaOptions:
+             num_cus=None, cqs=None, precision=0, wave_tokens=None) -> CqsaOptions:
     """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set).
-    precision: 0 (P rounded to the input dtype) or 1 (split P, hi + lo)."""
+    precision: 0 (P rounded to the input dtype) or 1 (split P, hi + lo).
+    wave_tokens: packed-row budget of a wave of the quorum-set schedule (None: the default)."""
     o = CqsaOptions()
     o.precision = int(precision or 0)
+    o.wave_tokens = int(wave_tokens or 0)
     if cqs is not None:
         if isinstance(cqs, int):
             o.cqs_c = cqs
@@ -203,7 +207,7 @@ def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=Non
 
 
 def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
-         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0) -> dict:
+         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0, wave_tokens=None) -> dict:
     """The plan ``attention`` would run (nothing is allocated or computed).
 
     ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
@@ -232,7 +236,8 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
         out = (qshape, qdt)
     do = mk("out", out, None)
     info = CqsaPlanInfo()
-    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision)
+    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision,
+                   wave_tokens=wave_tokens)
     _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
                           int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
                           ctypes.byref(info)))
@@ -243,7 +248,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
               mem_budget: int | None = None, *, q_chunk: int | None = None, kv_chunk: int | None = None,
               kv_splits: int | None = None, merge: int | None = None, out: torch.Tensor | None = None,
               out_dtype: torch.dtype | None = None, return_lse: bool = False, return_info: bool = False,
-              stream: torch.cuda.Stream | None = None, cqs=None, precision: int = 0):
+              stream: torch.cuda.Stream | None = None, cqs=None, precision: int = 0, wave_tokens: int | None = None):
     """Exact ``softmax(scale * q k^T [+ causal mask]) v`` (SDPA semantics; causal is bottom-right
     aligned when Nq < Nk; GQA when k/v have fewer heads).
 
@@ -251,7 +256,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     pinned host memory (then streamed in chunks).  ``mem_budget`` caps the device bytes the call
     uses (0/None: the free memory).  ``kv_chunk``/``q_chunk`` force a decomposition; ``merge``
     picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  ``cqs`` runs the cyclic quorum-set
-    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set).
+    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set); its subproblems
+    run in waves of at most ``wave_tokens`` staged rows (one batched launch per wave).
     ``precision=1`` feeds P to the PV product as a hi part plus a lo residual (two accumulator
     chains), for results near fp32 accuracy at about twice the PV work.  Returns out
     (on q's device; pinned host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the
@@ -262,7 +268,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
             raise ValueError("out= and return_info are not available on the autograd path")
         res = _AttentionFn.apply(q, k, v, bool(is_causal), scale, dict(
             mem_budget=mem_budget, q_chunk=q_chunk, kv_chunk=kv_chunk, kv_splits=kv_splits, merge=merge,
-            out_dtype=out_dtype, stream=stream, cqs=cqs, precision=precision))
+            out_dtype=out_dtype, stream=stream, cqs=cqs, precision=precision, wave_tokens=wave_tokens))
         return res if return_lse else res[0]
     dev = _device_of(q, k, v, out)
     if dev is None:
@@ -281,7 +287,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)
         dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
-        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs, precision=precision)
+        opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs, precision=precision,
+                       wave_tokens=wave_tokens)
         budget = int(mem_budget or 0)
         # size the workspace first so that device-resident calls take it from PyTorch's allocator
         # (stream-ordered, no hipMalloc, no synchronisation)

@@ -218,6 +218,17 @@ struct Plan {
     std::vector<int> cqs_owner;            // owner[a * c + b]
     uint64_t off_stage[2] = {0, 0}, stage_bytes = 0;
     int64_t out_rows = 0;                  // query rows per finalize chunk (host output)
+    struct CqsLaunch {
+        std::vector<std::pair<int, int>> pairs;   // (query part, key part), sorted
+    };
+    struct CqsWave {
+        std::vector<int> subs;                     // subproblems of the wave
+        std::vector<char> qp, kp;                  // query / key parts it stages and reads
+        uint64_t stage = 0;                        // staging bytes (host operands)
+        std::vector<CqsLaunch> launches;           // at most kWaveCap query and key parts each
+    };
+    std::vector<CqsWave> cqs_waves;
+    int64_t wave_tokens = 0;                       // the packed-row budget the waves were cut to
 };
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
@@ -374,46 +385,85 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     pl->cqs_c = c;
     pl->merge = CQSA_MERGE_FUSED;
     pl->kv_splits = 1;
-    // staging per subproblem (host operands only) and the traffic of the whole schedule
+    // subproblems that own at least one non-empty pair, in index order
     const uint64_t qrow = (uint64_t)P.B * P.Hq * P.D * 2, kvrow = (uint64_t)P.B * P.Hkv * P.D * 2;
-    uint64_t stage = 0, h2d = 0;
-    int64_t pairs = 0, subs = 0, max_q = 0, max_k = 0;
-    for (int i = 0; i < c; ++i) {
-        std::vector<char> qp(c, 0), kp(c, 0);
-        bool any = false;
+    auto qlen = [&](int a) { return part_lo(P.Nq, c, a + 1) - part_lo(P.Nq, c, a); };
+    auto klen = [&](int b) { return part_lo(P.Nk, c, b + 1) - part_lo(P.Nk, c, b); };
+    std::vector<std::pair<int, std::vector<std::pair<int, int>>>> subs;
+    int64_t pairs = 0, max_q = 0, max_k = 0;
+    for (int a = 0; a < c; ++a) max_q = std::max(max_q, qlen(a));
+    for (int b = 0; b < c; ++b) max_k = std::max(max_k, klen(b));
+    {
+        std::vector<std::vector<std::pair<int, int>>> by(c);
         for (int a = 0; a < c; ++a)
             for (int b = 0; b < c; ++b)
-                if (pl->cqs_owner[(size_t)a * c + b] == i && pair_visible(P, c, a, b)) {
-                    qp[a] = kp[b] = 1;
-                    any = true;
-                    ++pairs;
-                }
-        if (!any) continue;
-        ++subs;
-        uint64_t bytes = 0;
-        for (int a = 0; a < c; ++a) {
-            const int64_t n = part_lo(P.Nq, c, a + 1) - part_lo(P.Nq, c, a);
-            max_q = std::max(max_q, n);
-            if (qp[a] && P.q.host) {
-                bytes = align_up(bytes + (uint64_t)n * qrow, 256);
-                h2d += (uint64_t)n * qrow;
+                if (pair_visible(P, c, a, b)) by[pl->cqs_owner[(size_t)a * c + b]].emplace_back(a, b);
+        for (int i = 0; i < c; ++i)
+            if (!by[i].empty()) {
+                pairs += (int64_t)by[i].size();
+                subs.emplace_back(i, std::move(by[i]));
             }
-        }
-        for (int b = 0; b < c; ++b) {
-            const int64_t n = part_lo(P.Nk, c, b + 1) - part_lo(P.Nk, c, b);
-            max_k = std::max(max_k, n);
-            if (kp[b] && P.k.host) {
-                bytes = align_up(bytes + (uint64_t)n * kvrow, 256);
-                h2d += (uint64_t)n * kvrow;
-            }
-            if (kp[b] && P.v.host) {
-                bytes = align_up(bytes + (uint64_t)n * kvrow, 256);
-                h2d += (uint64_t)n * kvrow;
-            }
-        }
-        stage = std::max(stage, bytes);
     }
+    // Waves: consecutive subproblems whose staged rows (query rows of the union of their query parts
+    // plus key rows of the union of their key parts) stay within the packed-row budget W; a wave runs
+    // as one launch per kWaveCap query and key parts.
+    auto cut = [&](int64_t W) {
+        std::vector<Plan::CqsWave> ws;
+        Plan::CqsWave cur;
+        int64_t tok = 0;
+        auto fresh = [&]() {
+            cur = Plan::CqsWave();
+            cur.qp.assign(c, 0);
+            cur.kp.assign(c, 0);
+            tok = 0;
+        };
+        fresh();
+        std::vector<char> nq(c), nk(c);
+        auto added = [&](const std::vector<std::pair<int, int>>& prs) {   // rows the subproblem adds to cur
+            std::fill(nq.begin(), nq.end(), 0);
+            std::fill(nk.begin(), nk.end(), 0);
+            int64_t add = 0;
+            for (const auto& pr : prs) {
+                if (!cur.qp[pr.first] && !nq[pr.first]) {
+                    nq[pr.first] = 1;
+                    add += qlen(pr.first);
+                }
+                if (!cur.kp[pr.second] && !nk[pr.second]) {
+                    nk[pr.second] = 1;
+                    add += klen(pr.second);
+                }
+            }
+            return add;
+        };
+        for (const auto& sp : subs) {
+            int64_t add = added(sp.second);
+            if (!cur.subs.empty() && tok + add > W) {
+                ws.push_back(std::move(cur));
+                fresh();
+                add = added(sp.second);
+            }
+            cur.subs.push_back(sp.first);
+            for (int p = 0; p < c; ++p) {
+                cur.qp[p] |= nq[p];
+                cur.kp[p] |= nk[p];
+            }
+            tok += add;
+        }
+        if (!cur.subs.empty()) ws.push_back(std::move(cur));
+        for (auto& wv : ws) {
+            uint64_t bytes = 0;
+            for (int a = 0; a < c; ++a)
+                if (wv.qp[a] && P.q.host) bytes = align_up(bytes + (uint64_t)qlen(a) * qrow, 256);
+            for (int b = 0; b < c; ++b) {
+                if (wv.kp[b] && P.k.host) bytes = align_up(bytes + (uint64_t)klen(b) * kvrow, 256);
+                if (wv.kp[b] && P.v.host) bytes = align_up(bytes + (uint64_t)klen(b) * kvrow, 256);
+            }
+            wv.stage = bytes;
+        }
+        return ws;
+    };
     const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
+    const uint64_t orows = (uint64_t)P.B * P.Hq * max_q;
     uint64_t off = 0;
     auto take = [&](uint64_t b) {
         const uint64_t at = off;
@@ -423,13 +473,59 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     pl->off_acc_o = take(rows * P.D * 4);
     pl->off_acc_ml = take(rows * 8);
     pl->out_rows = max_q;
-    const uint64_t orows = (uint64_t)P.B * P.Hq * max_q;
     pl->off_out = P.out.host ? take(orows * P.D * P.out.es) : 0;
     pl->off_lse = (P.want_lse && P.lse_host) ? take(orows * 4) : 0;
     const uint64_t base = off;
+    int64_t W = opt.wave_tokens > 0 ? opt.wave_tokens
+                                    : std::min<int64_t>(int64_t(1) << 22, std::max<int64_t>(int64_t(1) << 20, P.Nq + P.Nk));
+    std::vector<Plan::CqsWave> waves;
+    uint64_t stage = 0;
+    int nbuf = 0;
+    for (;;) {
+        waves = cut(W);
+        stage = 0;
+        for (const auto& wv : waves) stage = std::max(stage, wv.stage);
+        nbuf = stage == 0 ? 0 : 2;
+        if (nbuf == 2 && base + 2 * align_up(stage, 256) > budget) nbuf = 1;
+        if (base + (uint64_t)nbuf * align_up(stage, 256) <= budget || waves.size() == subs.size() || W <= 1) break;
+        W = std::max<int64_t>(1, W / 2);   // smaller waves until the staging fits the budget
+    }
+    pl->wave_tokens = W;
+    uint64_t h2d = 0;
+    int64_t launches = 0, folds = 0;
+    for (auto& wv : waves) {
+        for (int a = 0; a < c; ++a)
+            if (wv.qp[a] && P.q.host) h2d += (uint64_t)qlen(a) * qrow;
+        for (int b = 0; b < c; ++b)
+            if (wv.kp[b]) h2d += (uint64_t)klen(b) * kvrow * ((P.k.host ? 1 : 0) + (P.v.host ? 1 : 0));
+        std::vector<std::pair<int, int>> prs;
+        for (int i : wv.subs)
+            for (const auto& sp : subs)
+                if (sp.first == i) prs.insert(prs.end(), sp.second.begin(), sp.second.end());
+        std::sort(prs.begin(), prs.end());
+        // launches: blocks of kWaveCap query parts x kWaveCap key parts of the wave's parts (in order)
+        std::vector<int> qrank(c, -1), krank(c, -1);
+        int nqw = 0, nkw = 0;
+        for (int a = 0; a < c; ++a)
+            if (wv.qp[a]) qrank[a] = nqw++;
+        for (int b = 0; b < c; ++b)
+            if (wv.kp[b]) krank[b] = nkw++;
+        const int nkb = (nkw + kWaveCap - 1) / kWaveCap;
+        std::vector<Plan::CqsLaunch> blocks((size_t)((nqw + kWaveCap - 1) / kWaveCap) * nkb);
+        for (const auto& pr : prs)
+            blocks[(size_t)(qrank[pr.first] / kWaveCap) * nkb + krank[pr.second] / kWaveCap].pairs.push_back(pr);
+        for (auto& L : blocks)
+            if (!L.pairs.empty()) wv.launches.push_back(std::move(L));
+        launches += (int64_t)wv.launches.size();
+        for (const auto& L : wv.launches) {
+            std::vector<int> qd;
+            for (const auto& pr : L.pairs)
+                if (qd.empty() || qd.back() != pr.first) qd.push_back(pr.first);
+            folds += (int64_t)qd.size();
+        }
+    }
+    pl->cqs_waves = std::move(waves);
     pl->stage_bytes = stage;
-    int nbuf = stage == 0 ? 0 : 2;
-    if (nbuf == 2 && base + 2 * align_up(stage, 256) > budget) nbuf = 1;
     pl->cqs_nbuf = nbuf;
     for (int i = 0; i < nbuf; ++i) pl->off_stage[i] = take(stage);
     pl->total = off;
@@ -446,13 +542,15 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     in.n_kv_chunks = c;
     in.kv_splits = 1;
     in.chunk_pairs = pairs;
-    in.merges = pairs;
-    in.kernel_launches = pairs + 1 + (P.out.host ? c : 1);   // pairs, accumulator fill, finalize
+    in.merges = folds;
+    in.kernel_launches = launches + 1 + (P.out.host ? c : 1);   // wave launches, accumulator fill, finalize
     in.workspace_bytes = pl->total;
     in.h2d_bytes = h2d;
     in.d2h_bytes = P.out.host ? rows * P.D * P.out.es + ((P.want_lse && P.lse_host) ? rows * 4 : 0) : 0;
     in.cqs_c = c;
-    in.cqs_subproblems = (int32_t)subs;
+    in.cqs_subproblems = (int32_t)subs.size();
+    in.cqs_waves = (int32_t)pl->cqs_waves.size();
+    in.wave_tokens = pl->wave_tokens;
     return CQSA_OK;
 }
 
@@ -467,6 +565,9 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
         return CQSA_OK;
     }
     if (opt.cqs_c < 0) return fail(CQSA_ERR_INVALID, "cqs_c %d is negative", opt.cqs_c);
+    if (opt.wave_tokens < 0) return fail(CQSA_ERR_INVALID, "wave_tokens %lld is negative", (long long)opt.wave_tokens);
+    if (opt.wave_tokens > 0 && opt.cqs_c <= 0)
+        return fail(CQSA_ERR_INVALID, "wave_tokens applies to the quorum-set schedule only (cqs_c > 0)");
     if (opt.cqs_c > 0) return make_plan_cqs(P, budget, opt, pl);
     const int req_merge = opt.merge_mode;
     if (req_merge < 0 || req_merge > 2) return fail(CQSA_ERR_INVALID, "merge_mode %d is not 0, 1 or 2", req_merge);
@@ -1122,19 +1223,12 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
         CQSA_TRY(run_merge(m, st));
     }
     const uint64_t qrow = (uint64_t)P.B * P.Hq * P.D * 2, kvrow = (uint64_t)P.B * P.Hkv * P.D * 2;
+    const int bm = wave_block_m((int)P.D, P.p_split);
+    const int dt = P.dtype == CQSA_F16 ? ET_F16 : ET_BF16;
     bool comp_recorded[2] = {false, false};
     int run = 0;
     std::vector<uint64_t> qoff(c), koff(c), voff(c);
-    for (int i = 0; i < c; ++i) {
-        std::vector<std::pair<int, int>> prs;
-        std::vector<char> qp(c, 0), kp(c, 0);
-        for (int a = 0; a < c; ++a)
-            for (int b = 0; b < c; ++b)
-                if (pl.cqs_owner[(size_t)a * c + b] == i && pair_visible(P, c, a, b)) {
-                    prs.emplace_back(a, b);
-                    qp[a] = kp[b] = 1;
-                }
-        if (prs.empty()) continue;
+    for (const Plan::CqsWave& wv : pl.cqs_waves) {
         const int buf = pl.cqs_nbuf == 2 ? (run & 1) : 0;
         char* stg = ws + pl.off_stage[buf];
         if (host_in) {
@@ -1144,14 +1238,14 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
             CQSA_HIP(hipEventRecord(tc.start, h2d));
             uint64_t o = 0;
             for (int a = 0; a < c; ++a)
-                if (qp[a] && P.q.host) {
+                if (wv.qp[a] && P.q.host) {
                     const int64_t lo = part_lo(P.Nq, c, a), n = part_lo(P.Nq, c, a + 1) - lo;
                     qoff[a] = o;
                     CQSA_TRY(copy_rows(P.q, lo, n, stg + o, true, h2d));
                     o = align_up(o + (uint64_t)n * qrow, 256);
                 }
             for (int b = 0; b < c; ++b)
-                if (kp[b]) {
+                if (wv.kp[b]) {
                     const int64_t lo = part_lo(P.Nk, c, b), n = part_lo(P.Nk, c, b + 1) - lo;
                     if (P.k.host) {
                         koff[b] = o;
@@ -1168,41 +1262,73 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
             CQSA_HIP(hipEventRecord(ev_copy[buf], h2d));
             CQSA_HIP(hipStreamWaitEvent(st, ev_copy[buf], 0));
         }
-        for (const auto& pr : prs) {
-            const int a = pr.first, b = pr.second;
-            const int64_t qa = part_lo(P.Nq, c, a), qn = part_lo(P.Nq, c, a + 1) - qa;
-            const int64_t ka = part_lo(P.Nk, c, b), kn = part_lo(P.Nk, c, b + 1) - ka;
+        for (const Plan::CqsLaunch& L : wv.launches) {
+            // the launch's key parts (ascending) and query parts with their key masks
+            std::vector<int> ks, qs;
+            for (const auto& pr : L.pairs) {
+                if (std::find(ks.begin(), ks.end(), pr.second) == ks.end()) ks.push_back(pr.second);
+                if (qs.empty() || qs.back() != pr.first) qs.push_back(pr.first);
+            }
+            std::sort(ks.begin(), ks.end());
+            WaveTable t;
+            std::memset(&t, 0, sizeof t);
+            t.n_k = (int32_t)ks.size();
+            t.n_q = (int32_t)qs.size();
+            t.q_layout = P.q.host ? (P.q.H > 1 && P.q.sh < P.q.sn ? WAVE_COMPACT_TOKEN : WAVE_COMPACT_HEAD) : WAVE_STRIDED;
+            t.k_layout = P.k.host ? (P.k.H > 1 && P.k.sh < P.k.sn ? WAVE_COMPACT_TOKEN : WAVE_COMPACT_HEAD) : WAVE_STRIDED;
+            t.v_layout = P.v.host ? (P.v.H > 1 && P.v.sh < P.v.sn ? WAVE_COMPACT_TOKEN : WAVE_COMPACT_HEAD) : WAVE_STRIDED;
+            t.H_q = (int32_t)P.Hq;
+            t.H_kv = (int32_t)P.Hkv;
+            for (int u = 0; u < t.n_k; ++u) {
+                const int b = ks[u];
+                const int64_t lo = part_lo(P.Nk, c, b);
+                WaveK& K = t.ki[u];
+                K.k = reinterpret_cast<const uint16_t*>(P.k.host ? stg + koff[b] : P.k.data + (size_t)(lo * P.k.sn) * 2);
+                K.v = reinterpret_cast<const uint16_t*>(P.v.host ? stg + voff[b] : P.v.data + (size_t)(lo * P.v.sn) * 2);
+                K.lo = lo;
+                K.n = (int32_t)(part_lo(P.Nk, c, b + 1) - lo);
+            }
+            // query parts, the ones with the most key rows first (they finish last)
+            std::vector<std::pair<int64_t, int>> order;
+            std::vector<uint32_t> mask(c, 0u);
+            for (const auto& pr : L.pairs) {
+                const int u = (int)(std::find(ks.begin(), ks.end(), pr.second) - ks.begin());
+                mask[pr.first] |= 1u << u;
+            }
+            for (int a : qs) {
+                int64_t keys = 0;
+                for (int u = 0; u < t.n_k; ++u)
+                    if ((mask[a] >> u) & 1u) keys += t.ki[u].n;
+                order.emplace_back(-keys, a);
+            }
+            std::sort(order.begin(), order.end());
+            int64_t tiles = 0;
+            for (int u = 0; u < t.n_q; ++u) {
+                const int a = order[u].second;
+                const int64_t lo = part_lo(P.Nq, c, a), n = part_lo(P.Nq, c, a + 1) - lo;
+                WaveQ& Q = t.qi[u];
+                Q.q = reinterpret_cast<const uint16_t*>(P.q.host ? stg + qoff[a] : P.q.data + (size_t)(lo * P.q.sn) * 2);
+                Q.lo = lo;
+                Q.n = (int32_t)n;
+                Q.kmask = mask[a];
+                Q.n_qt = (int32_t)ceil_div(n, bm);
+                Q.t0 = (int32_t)tiles;
+                tiles += Q.n_qt;
+            }
+            const int64_t blocks = (int64_t)P.B * P.Hq * tiles;
+            if (blocks > 0x7FFFFFFF) return fail(CQSA_ERR_UNSUPPORTED, "too many workgroups in one wave launch");
+            t.n_tiles = (int32_t)tiles;
             FwdArgs fa = base_args(P);
-            if (P.q.host) {
-                const Compact cq = compact_for(P.q, qn);
-                set_q(fa, stg + qoff[a], cq.sb, cq.sh, cq.sn);
-            } else {
-                set_q(fa, P.q.data + (size_t)(qa * P.q.sn) * 2, P.q.sb, P.q.sh, P.q.sn);
-            }
-            if (P.k.host) {
-                const Compact ck = compact_for(P.k, kn);
-                set_k(fa, stg + koff[b], ck.sb, ck.sh, ck.sn);
-            } else {
-                set_k(fa, P.k.data + (size_t)(ka * P.k.sn) * 2, P.k.sb, P.k.sh, P.k.sn);
-            }
-            if (P.v.host) {
-                const Compact cv = compact_for(P.v, kn);
-                set_v(fa, stg + voff[b], cv.sb, cv.sh, cv.sn);
-            } else {
-                set_v(fa, P.v.data + (size_t)(ka * P.v.sn) * 2, P.v.sb, P.v.sh, P.v.sn);
-            }
-            const int64_t pos0 = P.Nk - P.Nq + qa;  // key position of the part's first query row
-            fa.k_lo = 0;
-            fa.k_hi = kn;
-            fa.split_len = kn;
-            fa.causal_delta = pos0 - ka;
-            fa.r0 = P.causal ? std::max<int64_t>(0, ka - pos0) : 0;
-            fa.r1 = qn;
+            if (!P.q.host) set_q(fa, P.q.data, P.q.sb, P.q.sh, P.q.sn);
+            if (!P.k.host) set_k(fa, P.k.data, P.k.sb, P.k.sh, P.k.sn);
+            if (!P.v.host) set_v(fa, P.v.data, P.v.sb, P.v.sh, P.v.sn);
+            fa.causal_delta = P.Nk - P.Nq;
             fa.mode = FWD_ACCUM;
-            fa.acc_o = acc_o + qa * P.D;
-            fa.acc_ml = acc_ml + qa * 2;
+            fa.acc_o = acc_o;
+            fa.acc_ml = acc_ml;
             fa.acc_rows = P.Nq;
-            CQSA_TRY(run_fwd(P, fa, st));
+            const hipError_t e = launch_wave(fa, t, (int)blocks, (int)P.D, dt, st);
+            if (e != hipSuccess) return fail(CQSA_ERR_HIP, "wave launch: %s", hipGetErrorString(e));
         }
         CQSA_HIP(hipEventRecord(ev_comp[buf], st));
         comp_recorded[buf] = true;

@@ -49,6 +49,41 @@ struct FwdArgs {
     int32_t p_split;           // 1: P enters the PV product as an fp16/bf16 hi part plus a lo residual
 };
 
+// One launch of the wave engine (the quorum-set schedule): several query parts, each against the
+// union of its key parts that the launch's subproblems own, in one online-softmax pass per query row
+// that folds into the running accumulator (FWD_ACCUM).  Parts are contiguous row ranges of the whole
+// problem; a part's rows sit either in the caller's tensor (layout STRIDED: the FwdArgs strides) or in a
+// compact staging copy of just that part (COMPACT_HEAD: [B][H][n][D], COMPACT_TOKEN: [B][n][H][D]).
+enum WaveLayout : int32_t { WAVE_STRIDED = 0, WAVE_COMPACT_HEAD = 1, WAVE_COMPACT_TOKEN = 2 };
+
+constexpr int kWaveCap = 32;   // query parts and key parts per launch
+
+struct WaveQ {
+    const uint16_t* q;   // element (b, h, 0, 0) of the part at q + b * sb + h * sh
+    int64_t lo;          // first query row of the part (accumulator row)
+    int32_t n;           // rows of the part
+    uint32_t kmask;      // key parts (bits over WaveTable::ki) this part attends to in the launch
+    int32_t t0;          // first query tile of the part in a head's tile list
+    int32_t n_qt;        // query tiles of the part
+};
+
+struct WaveK {
+    const uint16_t* k;   // element (b, h, 0, 0) of the part (layout k_layout / v_layout)
+    const uint16_t* v;
+    int64_t lo;          // first key of the part
+    int32_t n;           // keys of the part
+    int32_t pad;
+};
+
+struct WaveTable {
+    WaveQ qi[kWaveCap];
+    WaveK ki[kWaveCap];
+    int32_t n_q, n_k;
+    int32_t q_layout, k_layout, v_layout;
+    int32_t H_q, H_kv;   // heads of the compact layouts (Hq for q, Hkv for k and v)
+    int32_t n_tiles;     // query tiles of all parts per (b, query head); workgroups = B * Hq * n_tiles
+};
+
 constexpr int kMaxMergeParts = 64;
 
 // Log-sum-exp merge of n_parts triples for rows (b, h, i), i in [i_lo, i_hi), laid out
@@ -117,5 +152,13 @@ const char* fwd_kernel_name(int D, int p_split);
 // Launchers (return the launch status).
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+// The wave engine's launch: a carries the problem-wide fields (strides of STRIDED views, B, Hq, Hkv,
+// group, causal with causal_delta = Nk - Nq, scale, p_split, FWD_ACCUM with the accumulator base and
+// acc_rows = Nq); blocks = B * Hq * t.n_tiles.
+hipError_t launch_wave(const FwdArgs& a, const WaveTable& t, int blocks, int D, int dtype, hipStream_t stream);
+
+// Query rows per workgroup of the wave kernel.
+int wave_block_m(int D, int p_split);
 
 }  // namespace cqsa

@@ -933,6 +933,254 @@ fwd_dma_kernel(const FwdArgs a) {
     fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
+// The wave engine's kernel: the DMA kernel's tile loop walked over a list of key parts (segments).
+// A workgroup takes BM rows of one query part of the table and one (b, query head); its key loop
+// runs over the key parts in the part's mask in ascending order, each cut at the causal limit of the
+// workgroup's last row, with one online softmax across all of them, and the epilogue folds the result
+// into the accumulator rows of the part (FWD_ACCUM).  Tiles are counted across segments, so the LDS
+// double buffer and the DMA of tile it + 1 run on without a break at a segment boundary.
+__device__ __forceinline__ void wave_strides(int layout, int64_t n, int H, int D, int64_t sb, int64_t sh, int64_t sn,
+                                             int64_t& osb, int64_t& osh, int64_t& osn) {
+    if (layout == WAVE_COMPACT_HEAD) {
+        osb = (int64_t)H * n * D;
+        osh = n * D;
+        osn = D;
+    } else if (layout == WAVE_COMPACT_TOKEN) {
+        osb = n * H * D;
+        osh = D;
+        osn = (int64_t)H * D;
+    } else {
+        osb = sb;
+        osh = sh;
+        osn = sn;
+    }
+}
+
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
+    constexpr int BM = NW * 32;
+    constexpr int TILE = KT * D;
+    constexpr int STAGE = 2 * TILE;
+    constexpr int GPR = D / 8;
+    constexpr int RPI = 64 / GPR;
+    constexpr int NBLK = KT / RPI;
+    constexpr int BPW = (NBLK + NW - 1) / NW;
+    constexpr int NKB = KT / 32;
+    constexpr int NPK = KT / 16;
+    constexpr int NDB = D / 32;
+    constexpr int NDK = D / 16;
+    static_assert(NBLK % NW == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // Workgroups are ordered (b, kv head, head in group, query part, query tile): every (b, head) holds
+    // the same work, so the contiguous ranges the XCD remap hands each XCD stay balanced, and a
+    // head's K/V stays in one XCD's L2.  Within a head the parts come longest-first.
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int r = w % t.n_tiles;
+    w /= t.n_tiles;
+    int item = 0;
+    while (item + 1 < t.n_q && r >= t.qi[item + 1].t0) ++item;
+    const WaveQ& Q = t.qi[item];
+    const int qt_idx = r - Q.t0;
+    const int gi = w % a.group;
+    w /= a.group;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int hq = hkv * a.group + gi;
+    const int qt = Q.n_qt - 1 - qt_idx;
+
+    const int64_t i0 = (int64_t)qt * BM;               // rows local to the query part
+    const int64_t i_end = min(i0 + (int64_t)BM, (int64_t)Q.n);
+    const int64_t iw0 = i0 + (int64_t)wave * 32;
+    const int64_t iw_end = min(iw0 + 32, i_end);
+    const int64_t pos0 = Q.lo + a.causal_delta;        // key position of the part's row 0
+
+    int64_t sb, sh, sn;
+    wave_strides(t.q_layout, Q.n, t.H_q, D, a.q_sb, a.q_sh, a.q_sn, sb, sh, sn);
+    u32x4 qf[NDK];
+    {
+        const uint16_t* qp = Q.q + (int64_t)b * sb + (int64_t)hq * sh;
+        const int64_t row = iw0 + l32;
+        const bool ok = row < i_end;
+        const uint16_t* p = qp + (ok ? row : 0) * sn + 8 * hi;
+#pragma unroll
+        for (int u = 0; u < NDK; ++u) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * u);
+            qf[u] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // keys of segment s this workgroup visits (causal: up to the position of its last row)
+    auto seg_len = [&](int s) -> int {
+        int64_t n = t.ki[s].n;
+        if (a.causal) n = min(n, pos0 + i_end - t.ki[s].lo);
+        return (int)max(n, (int64_t)0);
+    };
+    auto next_seg = [&](int s) -> int {   // next segment after s with keys to visit, or -1
+        for (++s; s < t.n_k; ++s)
+            if (((Q.kmask >> s) & 1u) && seg_len(s) > 0) return s;
+        return -1;
+    };
+
+    // The row strides of K and V do not depend on a part's length in any layout, so the lane offsets
+    // of the DMA are fixed for the whole loop; a segment changes only the base pointers.
+    int64_t ksb, ksh, ksn, vsb, vsh, vsn;
+    wave_strides(t.k_layout, 1, t.H_kv, D, a.k_sb, a.k_sh, a.k_sn, ksb, ksh, ksn);
+    wave_strides(t.v_layout, 1, t.H_kv, D, a.v_sb, a.v_sh, a.v_sn, vsb, vsh, vsn);
+    int koff[BPW], voff[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int n = wave + i * NW;
+        const int r = n * RPI + lane / GPR;
+        const int pg = lane % GPR;
+        koff[i] = (int)((r * ksn + ((pg ^ kswz<D>(r)) * 8)) * 2);
+        voff[i] = (int)((r * vsn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+    }
+    // the (b, kv head) rows of segment s
+    auto seg_k = [&](int s) -> const uint16_t* {
+        int64_t sb_, sh_, sn_;
+        wave_strides(t.k_layout, t.ki[s].n, t.H_kv, D, a.k_sb, a.k_sh, a.k_sn, sb_, sh_, sn_);
+        return t.ki[s].k + (int64_t)b * sb_ + (int64_t)hkv * sh_;
+    };
+    auto seg_v = [&](int s) -> const uint16_t* {
+        int64_t sb_, sh_, sn_;
+        wave_strides(t.v_layout, t.ki[s].n, t.H_kv, D, a.v_sb, a.v_sh, a.v_sn, sb_, sh_, sn_);
+        return t.ki[s].v + (int64_t)b * sb_ + (int64_t)hkv * sh_;
+    };
+
+    // LDS read offsets (relative to a stage) of the matrix operands, as in the DMA kernel
+    int kread[NDK];
+#pragma unroll
+    for (int u = 0; u < NDK; ++u) kread[u] = l32 * D + (((2 * u + hi) ^ kswz<D>(l32)) * 8);
+    int vread[NDB];
+    {
+        const int src = lane & 15;
+        const int row = 4 * hi + src / 4;
+        const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vread[db] = TILE + row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
+    }
+
+    f32x16 oacc[NDB], olo[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        oacc[db] = f32x16{};
+        if constexpr (SPLIT) olo[db] = f32x16{};
+    }
+    float mrun = -INFINITY, lrun = 0.f;
+
+    // fetch cursor (tile fj of segment fs) and compute cursor (tile cj of segment cs), each with the
+    // state of its segment; the fetch cursor runs one tile ahead
+    int fs = next_seg(-1);
+    if (fs < 0) {
+        const int64_t row = iw0 + l32;
+        fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, 0, Q.lo + row, row < i_end, hi);
+        return;
+    }
+    int fj0 = 0, flen = seg_len(fs);
+    const uint16_t* fk = seg_k(fs);
+    const uint16_t* fv = seg_v(fs);
+    int cj0 = 0, clen = flen;
+    int64_t cdelta = pos0 - t.ki[fs].lo;
+    int cs = fs;
+    dma_rows<NW, BPW, D>(lds, fk, ksn, 0, min(flen, KT), koff, wave);
+    dma_rows<NW, BPW, D>(lds + TILE, fv, vsn, 0, min(flen, KT), voff, wave);
+    for (int it = 0;; ++it) {
+        __syncthreads();   // tile it is in LDS; every wave is done with tile it - 1
+        if (fs >= 0) {
+            fj0 += KT;
+            if (fj0 >= flen) {
+                fs = next_seg(fs);
+                if (fs >= 0) {
+                    fj0 = 0;
+                    flen = seg_len(fs);
+                    fk = seg_k(fs);
+                    fv = seg_v(fs);
+                }
+            }
+            if (fs >= 0) {
+                uint16_t* st = lds + ((it + 1) & 1) * STAGE;
+                const int nv = min(flen - fj0, KT);
+                dma_rows<NW, BPW, D>(st, fk, ksn, fj0, nv, koff, wave);
+                dma_rows<NW, BPW, D>(st + TILE, fv, vsn, fj0, nv, voff, wave);
+            }
+        }
+
+        const int j0 = cj0;   // first key of the tile, local to the segment
+        const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + cdelta);
+        if (active) {
+            const uint16_t* st = lds + (it & 1) * STAGE;
+            f32x16 sacc[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+            for (int u = 0; u < NDK; ++u)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(st + kread[u] + kb * 32 * D);
+                    sacc[kb] = mfma32<DT>(af, qf[u], sacc[kb]);
+                }
+            const bool need_mask = (j0 + KT > clen) || (a.causal && (j0 + KT - 1 > iw0 + cdelta));
+            if (need_mask) {
+                int lim = min(clen - j0, KT);
+                if (a.causal) {
+                    const int64_t c = iw0 + l32 + cdelta - j0 + 1;
+                    lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
+                }
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int tt = kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2);
+                        if (tt >= lim) sacc[kb][r] = -INFINITY;
+                    }
+            }
+            u32x4 pf[NPK], plo[NPK];
+            softmax_tile<NKB, NDB, DT, SPLIT>(sacc, pf, plo, mrun, lrun, oacc, olo, a.scale_log2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int u = 0; u < NPK; ++u) {
+                    typedef short s16x4 __attribute__((ext_vector_type(4)));
+                    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * u) * D));
+                    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * u + 8) * D));
+                    u32x4 vf;
+                    vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
+                    vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
+                    vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
+                    vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
+                    oacc[db] = mfma32<DT>(vf, pf[u], oacc[db]);
+                    if constexpr (SPLIT) olo[db] = mfma32<DT>(vf, plo[u], olo[db]);
+                }
+        }
+        // advance the compute cursor
+        cj0 += KT;
+        if (cj0 >= clen) {
+            cs = next_seg(cs);
+            if (cs < 0) break;
+            cj0 = 0;
+            clen = seg_len(cs);
+            cdelta = pos0 - t.ki[cs].lo;
+        }
+    }
+
+    if constexpr (SPLIT) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[db] += olo[db];
+    }
+    const int64_t row = iw0 + l32;
+    fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, 0, Q.lo + row, row < i_end, hi);
+}
+
 // =============================================================================================
 // Backward.  Three launches: bwd_stats_kernel (Delta_i = dO_i . O_i and the base-2 lse per row),
 // bwd_dq_kernel (per query tile, over key tiles: dQ^T += K^T dS^T) and bwd_dkdv_kernel (per key
@@ -1471,6 +1719,53 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
     if (D == 64 && dtype == ET_BF16) return launch_d<64, ET_BF16>(a, stream);
     if (D == 128 && dtype == ET_F16) return launch_d<128, ET_F16>(a, stream);
     if (D == 128 && dtype == ET_BF16) return launch_d<128, ET_BF16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+namespace {
+
+// The wave kernel runs in the default DMA shape of each head dim (the split-P shape with p_split).
+constexpr Shape kWave64 = kShapes64[0];
+constexpr Shape kWave128 = kShapes128[0];
+static_assert(kWave64.kind == 2 && kWave128.kind == 2, "the wave kernel is the DMA kernel's loop");
+static_assert(sizeof(FwdArgs) + sizeof(WaveTable) <= 4096, "the wave kernel's arguments fit the 4 KiB kernel-argument segment");
+
+Shape wave_shape(int D, int p_split) {
+    if (p_split) return D == 64 ? kSplit64 : kSplit128;
+    return D == 64 ? kWave64 : kWave128;
+}
+
+template <int D, int DT>
+hipError_t launch_wave_d(const FwdArgs& a, const WaveTable& t, int blocks, hipStream_t st) {
+    if (a.p_split) {
+        if constexpr (D == 64)
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true>), dim3((unsigned)blocks),
+                               dim3(kSplit64.nw * 64), 0, st, a, t);
+        else
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true>),
+                               dim3((unsigned)blocks), dim3(kSplit128.nw * 64), 0, st, a, t);
+    } else {
+        if constexpr (D == 64)
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave64.kt, kWave64.nw, kWave64.wpe, false>), dim3((unsigned)blocks),
+                               dim3(kWave64.nw * 64), 0, st, a, t);
+        else
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave128.kt, kWave128.nw, kWave128.wpe, false>),
+                               dim3((unsigned)blocks), dim3(kWave128.nw * 64), 0, st, a, t);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int wave_block_m(int D, int p_split) { return wave_shape(D, p_split).nw * 32; }
+
+hipError_t launch_wave(const FwdArgs& a, const WaveTable& t, int blocks, int D, int dtype, hipStream_t stream) {
+    if (blocks <= 0) return hipSuccess;
+    if (t.n_q < 1 || t.n_q > kWaveCap || t.n_k < 0 || t.n_k > kWaveCap || t.n_tiles < 1) return hipErrorInvalidValue;
+    if (D == 64 && dtype == ET_F16) return launch_wave_d<64, ET_F16>(a, t, blocks, stream);
+    if (D == 64 && dtype == ET_BF16) return launch_wave_d<64, ET_BF16>(a, t, blocks, stream);
+    if (D == 128 && dtype == ET_F16) return launch_wave_d<128, ET_F16>(a, t, blocks, stream);
+    if (D == 128 && dtype == ET_BF16) return launch_wave_d<128, ET_BF16>(a, t, blocks, stream);
     return hipErrorInvalidValue;
 }
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define CQSA_ABI_VERSION 2
+#define CQSA_ABI_VERSION 3
 
 typedef enum {
     CQSA_OK = 0,
@@ -99,6 +99,11 @@ typedef struct {
                                  request #800); about twice the PV work, error near the fp32 class */
     const int32_t* cqs_set;   /* the interest set: cqs_l distinct part offsets in [0, cqs_c);
                                  NULL = the built-in set for cqs_c (see cqsa_cqs_default_set) */
+    int64_t wave_tokens;      /* quorum-set schedule: packed-row budget of a wave, the consecutive
+                                 subproblems that share one launch (query rows of the wave's query
+                                 parts plus key rows of its key parts); 0 = min(2^22, max(2^20,
+                                 Nq + Nk)); 1 = one subproblem per wave.  The planner halves it
+                                 until the staging of host operands fits the memory budget. */
 } cqsa_options;
 
 /* What a plan does (filled by cqsa_plan and cqsa_attention_ex). */
@@ -123,6 +128,9 @@ typedef struct {
     double wall_ms;            /* host wall time of a synchronising call */
     int32_t cqs_c;             /* parts of a quorum-set schedule (0 = grid schedule) */
     int32_t cqs_subproblems;   /* subproblems that run (those owning at least one non-empty part pair) */
+    int32_t cqs_waves;         /* waves of the quorum-set schedule */
+    int32_t reserved0;
+    int64_t wave_tokens;       /* the packed-row budget the waves were cut to */
 } cqsa_plan_info;
 
 /*
@@ -251,11 +259,18 @@ uint64_t cqsa_struct_size(int32_t which);
  * set.  The set must be a cyclic quorum set: every pair of parts meets in some subproblem, i.e. every
  * d in 1..c-1 is a difference of two set elements mod c.  The pair (query part a, key part b) is
  * computed by exactly one subproblem, its owner: the smallest i whose parts contain both a and b.
- * Each subproblem stages its parts (from pinned host memory when the inputs live there), runs one
- * forward launch per owned non-empty pair, and folds the partial into a device accumulator for all
- * query rows by the log-sum-exp rule; the accumulator is normalised at the end.  Causal pairs with
- * no visible key are skipped.  Needs budget for the fp32 accumulator (B Hq Nq (D + 2) 4 bytes) plus
- * one subproblem's staging; CQSA_ERR_BUDGET otherwise.
+ * Subproblems run in waves (the wave engine of the same pages: README.md, the paragraph on peak
+ * memory and the wave budget; stream_cqsa/api.py, _pick_wave): consecutive subproblems are packed
+ * into one wave while the rows it stages (query rows of its query parts plus key rows of its key
+ * parts, each part counted once) stay within cqsa_options.wave_tokens.  A wave stages the union of
+ * its parts once (from pinned host memory when the inputs live there) and runs as one batched launch
+ * per 32 query and 32 key parts: every query part of the launch attends, in one online-softmax pass,
+ * to all the key parts it owns pairs with in the wave, and the launch folds the result into a device
+ * accumulator for all query rows by the log-sum-exp rule (on the device, in the kernel epilogue).
+ * Waves run one after another, the staging of wave w + 1 overlapping the compute of wave w; the
+ * accumulator is normalised at the end.  Causal pairs with no visible key are skipped.  Needs budget
+ * for the fp32 accumulator (B Hq Nq (D + 2) 4 bytes) plus one subproblem's staging (two waves'
+ * staging when it fits, for the overlap); CQSA_ERR_BUDGET otherwise.
  */
 
 /* owner[a * c + b] = the subproblem that computes the pair (query part a, key part b), for a valid

@@ -71,7 +71,9 @@ def test_plan_pairs_and_subproblems():
     assert p["n_q_chunks"] == 7 and p["q_chunk"] == 1000
     p = _plan(7000, True, 7)
     assert p["chunk_pairs"] == 28          # causal: key part <= query part
-    assert p["merges"] == 28
+    # the default wave budget holds every subproblem: one launch folds each query part once
+    assert p["cqs_waves"] == 1 and p["merges"] == 7 and p["kernel_launches"] == 3
+    assert p["wave_tokens"] == 1 << 20
     # accumulator for every query row: fp32 O plus (m, l)
     assert p["workspace_bytes"] >= 8 * 7000 * (64 + 2) * 4
     # ragged parts: 7001 rows over 7 parts of 1000 or 1001
@@ -96,3 +98,74 @@ def test_plan_too_small_budget_and_conflicting_options():
         _plan(7000, True, 7, kv_chunk=1024)
     with pytest.raises(m().CqsaError):
         _plan(7000, True, 5)               # no built-in set for c = 5
+
+
+def _waves_model(N, causal, c, iset, W):
+    """The wave cut from its definition: subproblems in index order, each owning the pairs (a, b) whose
+    smallest common subproblem it is; a wave takes the next subproblem while the query rows of the
+    union of its query parts plus the key rows of the union of its key parts stay <= W (a wave always
+    takes at least one).  Returns (waves, launches, folds) for parts of <= 32 per launch."""
+    lo = [N * p // c for p in range(c + 1)]
+    ln = [lo[p + 1] - lo[p] for p in range(c)]
+    members = [{(i + s) % c for s in iset} for i in range(c)]
+    subs = []
+    for i in range(c):
+        prs = []
+        for a in range(c):
+            for b in range(c):
+                if min(j for j in range(c) if a in members[j] and b in members[j]) != i:
+                    continue
+                if ln[a] == 0 or ln[b] == 0 or (causal and lo[b] > lo[a + 1] - 1):
+                    continue
+                prs.append((a, b))
+        if prs:
+            subs.append(prs)
+    waves, cur, qs, ks = [], [], set(), set()
+    for prs in subs:
+        nq, nk = qs | {a for a, _ in prs}, ks | {b for _, b in prs}
+        if cur and sum(ln[a] for a in nq) + sum(ln[b] for b in nk) > W:
+            waves.append(cur)
+            cur, qs, ks = [], set(), set()
+            nq, nk = {a for a, _ in prs}, {b for _, b in prs}
+        cur = cur + prs
+        qs, ks = nq, nk
+    if cur:
+        waves.append(cur)
+    return waves, len(subs)
+
+
+@pytest.mark.parametrize("W", [1, 3000, 5000, 9000, 14000, 1 << 20])
+def test_wave_cut_follows_the_budget(W):
+    N, c, iset = 7000, 7, (0, 1, 3)
+    waves, nsub = _waves_model(N, True, c, iset, W)
+    p = _plan(N, True, c, wave_tokens=W)
+    assert p["cqs_waves"] == len(waves) and p["cqs_subproblems"] == nsub
+    assert p["merges"] == sum(len({a for a, _ in wv}) for wv in waves)   # one fold per query part and wave
+    assert p["kernel_launches"] == len(waves) + 2
+    if W == 1:
+        assert p["cqs_waves"] == nsub
+
+
+def test_wave_launches_split_at_32_parts():
+    # c = 57 (a perfect difference set of size 8 mod 57): one wave holds all 57 query parts, so its
+    # pairs run as launches of at most 32 query parts and 32 key parts each
+    iset = (0, 1, 3, 13, 32, 36, 43, 52)
+    assert sorted({(x - y) % 57 for x in iset for y in iset if x != y}) == list(range(1, 57))
+    p = _plan(57 * 64, False, 57, iset=iset)
+    assert p["cqs_waves"] == 1 and p["chunk_pairs"] == 57 * 57
+    assert p["kernel_launches"] - 2 >= 4      # 57 query parts x 57 key parts in 32 x 32 blocks
+    assert p["merges"] >= 57
+
+
+def test_wave_budget_shrinks_to_fit_memory():
+    # 4M tokens from host memory over 31 parts: the default budget (4M rows) would stage too much for
+    # 16 GB beside the 8.9 GB accumulator, so the planner halves it until the staging fits
+    N = 4_194_304
+    p = _plan(N, True, 31, where="host", budget=16 * GB)
+    assert p["wave_tokens"] < 1 << 22 and p["workspace_bytes"] <= 0.85 * 16 * GB
+    assert 1 <= p["cqs_waves"] <= p["cqs_subproblems"]
+    with pytest.raises(m().CqsaError):
+        _plan(7000, True, 7, wave_tokens=-1)
+    with pytest.raises(m().CqsaError):
+        m().plan(((1, 8, 7000, 64), torch.float16), ((1, 8, 7000, 64), torch.float16),
+                 ((1, 8, 7000, 64), torch.float16), True, 64 * GB, num_cus=256, wave_tokens=5000)
