@@ -77,9 +77,24 @@ def cpu_baseline(w, q, k, v, seconds: float) -> dict:
             pairs += batch * w.Nk
     dt = time.perf_counter() - t0
     flops = 4.0 * w.D * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    rate = flops / dt
+    # the same reference on one thread, over a short sample of the same kind of rows
+    t1 = time.perf_counter()
+    pairs1 = rows1 = 0
+    while time.perf_counter() - t1 < min(2.0, seconds / 4):
+        i = rng.integers(0, w.Nq, 1)
+        rows = np.array([[rng.integers(0, w.B), rng.integers(0, w.Hq), i[0]]], dtype=np.int64)
+        oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=1)
+        rows1 += 1
+        pairs1 += int(i[0] + (w.Nk - w.Nq) + 1) if w.causal else w.Nk
+    dt1 = time.perf_counter() - t1
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done_rows} seeded random query rows of the same workload (all their visible keys), "
                       f"{dt:.1f} s, FP64 C reference on {threads} threads; rows/s = {done_rows / dt:.1f}",
+            "single_thread_value": round(4.0 * w.D * pairs1 / dt1 / 1e12, 6),
+            "single_thread_sample": f"{rows1} rows, {dt1:.1f} s",
+            "extrapolated_full_workload_s": round(w.flops() / rate, 1),
+            "extrapolation_note": "the whole workload at the sampled rate (an extrapolation, not a measurement)",
             "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
 
 

@@ -236,6 +236,16 @@ __device__ __forceinline__ void dma_rows(uint16_t* st, const uint16_t* base, int
 #endif
 }
 
+// One wave's DMA of nbytes (<= 256) of fp32 data from base into LDS at st, 4 bytes per lane; bytes at
+// or past nbytes read as zero.  Device pass only, like dma_rows.
+__device__ __forceinline__ void dma_words(float* st, const float* base, int nbytes, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nbytes > 0 ? nbytes : 0, kRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)st, 4, lane * 4, 0, 0, 0);
+#endif
+}
+
 // Epilogue shared by the forward kernels: the lane pair (l32, l32 + 32) holds one query row's
 // unnormalised O^T column (NDB x 16 dims each), its base-2 shift m and half of its sum l.
 //   FWD_FINAL:   O / l in the output dtype, lse = (m + log2 l) ln 2 (natural log of the scaled logits)
@@ -1424,7 +1434,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     static_assert(NBLK % NW == 0, "tile split");
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) float stl[2][2][QT];   // [stage][lse2 | Delta][row]
+    __shared__ __attribute__((aligned(16))) float stl[2][2 * QT];  // [stage][row][lse2, Delta]
+    static_assert(2 * QT * 4 == 256, "one wave DMA (64 lanes x 4 bytes) carries a tile of row statistics");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -1488,12 +1499,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         dma_rows<NW, BPW, D>(st_, a.q + (int64_t)b * a.q_sb + (int64_t)h_ * a.q_sh, a.q_sn, q0_, nv_, qoff, wave); \
         dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_,   \
                              nv_, doff, wave);                                                            \
-        if (tid < QT) {                                                                                   \
-            const bool ok_ = tid < nv_;                                                                   \
-            const float* sp_ = a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + (ok_ ? q0_ + tid : 0));   \
-            stl[(T) & 1][0][tid] = ok_ ? sp_[0] : INFINITY;                                               \
-            stl[(T) & 1][1][tid] = ok_ ? sp_[1] : 0.f;                                                    \
-        }                                                                                                 \
+        if (wave == NW - 1)   /* the rows' (lse2, Delta) by DMA too; rows past Nq read as zero */          \
+            dma_words(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + q0_), (int)(nv_ * 8), lane); \
     } while (0)
 
     if (total > 0) CQSA_BWD_KV_TILE(0);
@@ -1505,8 +1512,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         const bool active = jw0 < a.Nk && (!a.causal || q0 + QT - 1 + delta_c >= jw0);
         if (!active) continue;
         const uint16_t* st = lds + (it & 1) * STAGE;
-        const float* sl = stl[it & 1][0];
-        const float* sd = stl[it & 1][1];
+        const float* sl = stl[it & 1];
         const bool need_mask = (q0 + QT > a.Nq) || (jw0 + 32 > a.Nk) || (a.causal && q0 + delta_c < jw0 + 31);
 
         u32x4 pp[NPQ], ps[NPQ];
@@ -1527,8 +1533,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
                     const int rr = qb * 32 + 8 * (2 * u + g) + 4 * hi;    // rows rr .. rr + 3
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(sl + rr);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + rr);
+                    const f32x4 s01 = *reinterpret_cast<const f32x4*>(sl + 2 * rr);
+                    const f32x4 s23 = *reinterpret_cast<const f32x4*>(sl + 2 * rr + 4);
+                    const f32x4 l4 = {s01[0], s01[2], s23[0], s23[2]};
+                    const f32x4 d4 = {s01[1], s01[3], s23[1], s23[3]};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 8 * u + 4 * g + e;
