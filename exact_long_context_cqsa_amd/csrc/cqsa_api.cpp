@@ -222,7 +222,8 @@ struct Plan {
         std::vector<std::pair<int, int>> pairs;   // (query part, key part), sorted
     };
     struct CqsWave {
-        std::vector<int> subs;                     // subproblems of the wave
+        std::vector<int> subs;                     // subproblems with pairs in the wave
+        std::vector<std::pair<int, int>> pairs;    // (query part, key part) pairs the wave computes
         std::vector<char> qp, kp;                  // query / key parts it stages and reads
         uint64_t stage = 0;                        // staging bytes (host operands)
         std::vector<CqsLaunch> launches;           // at most kWaveCap query and key parts each
@@ -404,10 +405,22 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
                 subs.emplace_back(i, std::move(by[i]));
             }
     }
-    // Waves: consecutive subproblems whose staged rows (query rows of the union of their query parts
-    // plus key rows of the union of their key parts) stay within the packed-row budget W; a wave runs
-    // as one launch per kWaveCap query and key parts.
-    auto cut = [&](int64_t W) {
+    // Waves: consecutive units (whole subproblems, or a subproblem's pairs of one query part when whole
+    // subproblems stage too much for two staging sets) whose staged rows (query rows of the union of
+    // their query parts plus key rows of the union of their key parts) stay within the packed-row
+    // budget W; a wave runs as one launch per kWaveCap query and key parts.
+    using Units = std::vector<std::pair<int, std::vector<std::pair<int, int>>>>;
+    Units by_part;
+    for (const auto& sp : subs) {
+        size_t i = 0;
+        while (i < sp.second.size()) {   // the pairs are in query-part order
+            size_t j = i;
+            while (j < sp.second.size() && sp.second[j].first == sp.second[i].first) ++j;
+            by_part.emplace_back(sp.first, std::vector<std::pair<int, int>>(sp.second.begin() + i, sp.second.begin() + j));
+            i = j;
+        }
+    }
+    auto cut = [&](int64_t W, const Units& units) {
         std::vector<Plan::CqsWave> ws;
         Plan::CqsWave cur;
         int64_t tok = 0;
@@ -435,21 +448,22 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
             }
             return add;
         };
-        for (const auto& sp : subs) {
+        for (const auto& sp : units) {
             int64_t add = added(sp.second);
-            if (!cur.subs.empty() && tok + add > W) {
+            if (!cur.pairs.empty() && tok + add > W) {
                 ws.push_back(std::move(cur));
                 fresh();
                 add = added(sp.second);
             }
-            cur.subs.push_back(sp.first);
+            if (cur.subs.empty() || cur.subs.back() != sp.first) cur.subs.push_back(sp.first);
+            cur.pairs.insert(cur.pairs.end(), sp.second.begin(), sp.second.end());
             for (int p = 0; p < c; ++p) {
                 cur.qp[p] |= nq[p];
                 cur.kp[p] |= nk[p];
             }
             tok += add;
         }
-        if (!cur.subs.empty()) ws.push_back(std::move(cur));
+        if (!cur.pairs.empty()) ws.push_back(std::move(cur));
         for (auto& wv : ws) {
             uint64_t bytes = 0;
             for (int a = 0; a < c; ++a)
@@ -478,17 +492,47 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     const uint64_t base = off;
     int64_t W = opt.wave_tokens > 0 ? opt.wave_tokens
                                     : std::min<int64_t>(int64_t(1) << 22, std::max<int64_t>(int64_t(1) << 20, P.Nq + P.Nk));
+    // The largest budget (halving from W) whose waves fit two staging sets, so that the copy of a wave
+    // overlaps the compute of the one before; whole subproblems are tried before per-query-part units
+    // (smaller units copy a key part once per unit instead of once per subproblem).  When no budget
+    // gives two sets, the largest one that fits one set.
     std::vector<Plan::CqsWave> waves;
     uint64_t stage = 0;
     int nbuf = 0;
-    for (;;) {
-        waves = cut(W);
-        stage = 0;
-        for (const auto& wv : waves) stage = std::max(stage, wv.stage);
-        nbuf = stage == 0 ? 0 : 2;
-        if (nbuf == 2 && base + 2 * align_up(stage, 256) > budget) nbuf = 1;
-        if (base + (uint64_t)nbuf * align_up(stage, 256) <= budget || waves.size() == subs.size() || W <= 1) break;
-        W = std::max<int64_t>(1, W / 2);   // smaller waves until the staging fits the budget
+    auto stage_of = [](const std::vector<Plan::CqsWave>& ws) {
+        uint64_t m = 0;
+        for (const auto& wv : ws) m = std::max(m, wv.stage);
+        return m;
+    };
+    bool found = false;
+    for (int64_t w2 = W;; w2 = std::max<int64_t>(1, w2 / 2)) {
+        for (const Units* u : {&subs, &by_part}) {
+            std::vector<Plan::CqsWave> ws = cut(w2, *u);
+            const uint64_t st = stage_of(ws);
+            if (st == 0 || base + 2 * align_up(st, 256) <= budget) {
+                waves = std::move(ws);
+                stage = st;
+                nbuf = st == 0 ? 0 : 2;
+                W = w2;
+                found = true;
+                break;
+            }
+        }
+        if (found || w2 <= 1) break;
+    }
+    for (int64_t w1 = W; !found; w1 = std::max<int64_t>(1, w1 / 2)) {
+        for (const Units* u : {&subs, &by_part}) {
+            std::vector<Plan::CqsWave> ws = cut(w1, *u);
+            const uint64_t st = stage_of(ws);
+            if (base + align_up(st, 256) <= budget || (w1 <= 1 && u == &by_part)) {
+                waves = std::move(ws);
+                stage = st;
+                nbuf = 1;
+                W = w1;
+                found = true;
+                break;
+            }
+        }
     }
     pl->wave_tokens = W;
     uint64_t h2d = 0;
@@ -498,10 +542,7 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
             if (wv.qp[a] && P.q.host) h2d += (uint64_t)qlen(a) * qrow;
         for (int b = 0; b < c; ++b)
             if (wv.kp[b]) h2d += (uint64_t)klen(b) * kvrow * ((P.k.host ? 1 : 0) + (P.v.host ? 1 : 0));
-        std::vector<std::pair<int, int>> prs;
-        for (int i : wv.subs)
-            for (const auto& sp : subs)
-                if (sp.first == i) prs.insert(prs.end(), sp.second.begin(), sp.second.end());
+        std::vector<std::pair<int, int>> prs = wv.pairs;
         std::sort(prs.begin(), prs.end());
         // launches: blocks of kWaveCap query parts x kWaveCap key parts of the wave's parts (in order)
         std::vector<int> qrank(c, -1), krank(c, -1);

@@ -102,8 +102,12 @@ typedef struct {
     int64_t wave_tokens;      /* quorum-set schedule: packed-row budget of a wave, the consecutive
                                  subproblems that share one launch (query rows of the wave's query
                                  parts plus key rows of its key parts); 0 = min(2^22, max(2^20,
-                                 Nq + Nk)); 1 = one subproblem per wave.  The planner halves it
-                                 until the staging of host operands fits the memory budget. */
+                                 Nq + Nk)); 1 = one subproblem (or one query part's pairs of a
+                                 subproblem, see below) per wave.  With host operands the
+                                 planner halves it until two waves' staging fits the memory budget
+                                 (copy of one wave under the compute of the other), cutting waves
+                                 per query part of a subproblem when whole subproblems are too large;
+                                 failing that, until one wave's staging fits. */
 } cqsa_options;
 
 /* What a plan does (filled by cqsa_plan and cqsa_attention_ex). */
@@ -269,8 +273,8 @@ uint64_t cqsa_struct_size(int32_t which);
  * accumulator for all query rows by the log-sum-exp rule (on the device, in the kernel epilogue).
  * Waves run one after another, the staging of wave w + 1 overlapping the compute of wave w; the
  * accumulator is normalised at the end.  Causal pairs with no visible key are skipped.  Needs budget
- * for the fp32 accumulator (B Hq Nq (D + 2) 4 bytes) plus one subproblem's staging (two waves'
- * staging when it fits, for the overlap); CQSA_ERR_BUDGET otherwise.
+ * for the fp32 accumulator (B Hq Nq (D + 2) 4 bytes) plus the staging of one query part's pairs of a
+ * subproblem (two waves' staging when it fits, for the overlap); CQSA_ERR_BUDGET otherwise.
  */
 
 /* owner[a * c + b] = the subproblem that computes the pair (query part a, key part b), for a valid

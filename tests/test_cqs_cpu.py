@@ -163,7 +163,12 @@ def test_wave_budget_shrinks_to_fit_memory():
     N = 4_194_304
     p = _plan(N, True, 31, where="host", budget=16 * GB)
     assert p["wave_tokens"] < 1 << 22 and p["workspace_bytes"] <= 0.85 * 16 * GB
-    assert 1 <= p["cqs_waves"] <= p["cqs_subproblems"]
+    # one subproblem's staging (2.6 GB) fits once beside the accumulator but not twice, so the waves
+    # are cut per query part of a subproblem: more copies (a key part once per unit), all double-buffered
+    big = _plan(N, True, 31, where="host", budget=20 * GB)   # room for two subproblem-sized sets
+    assert big["cqs_waves"] <= big["cqs_subproblems"] == 31
+    assert p["cqs_waves"] > p["cqs_subproblems"] == 31
+    assert p["h2d_bytes"] > big["h2d_bytes"]
     with pytest.raises(m().CqsaError):
         _plan(7000, True, 7, wave_tokens=-1)
     with pytest.raises(m().CqsaError):

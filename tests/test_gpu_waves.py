@@ -147,3 +147,19 @@ def test_wave_bench_shape_one_launch_matches_monolithic():
     assert info["cqs_waves"] == 1 and info["kernel_launches"] == 3
     compare(out, lse, ref, w.dtype, rows=rows, label="waves c=31 32K")
     assert (out - mono).abs().max().item() <= 1e-3
+
+
+def test_wave_units_per_query_part_streamed():
+    """131072 host-resident tokens under c = 31 with a 0.48 GB budget: whole subproblems do not fit two
+    staging sets but a subproblem's pairs of one query part do, so the waves are cut per query part
+    (more waves than subproblems), double-buffered; sampled rows against the oracle."""
+    w = synth.workload(3)
+    say("waves per query part, streamed 131072")
+    q, k, v, _ = synth.make_inputs(w, nq=131072, nk=131072, pin=True)
+    out, lse, info = cqsa().attention(q, k, v, is_causal=True, mem_budget=480_000_000, return_lse=True,
+                                      return_info=True, cqs=31)
+    assert info["streamed"] == 1 and info["cqs_waves"] > info["cqs_subproblems"] == 31
+    rows = sample_rows(1, w.Hq, 131072, seed=19, n_random=48, edge=8,
+                       boundaries=[131072 * p // 31 for p in range(32)], heads=range(0, w.Hq, 3))
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    compare(out, lse, ref, w.dtype, rows=rows, label="waves per query part, streamed 131072")
