@@ -236,13 +236,18 @@ __device__ __forceinline__ void dma_rows(uint16_t* st, const uint16_t* base, int
 #endif
 }
 
-// One wave's DMA of nbytes (<= 256) of fp32 data from base into LDS at st, 4 bytes per lane; bytes at
-// or past nbytes read as zero.  Device pass only, like dma_rows.
+// One wave's DMA of NB bytes (a multiple of 256) of fp32 data from base into LDS at st, 4 bytes per
+// lane and instruction; bytes at or past nbytes read as zero.  Device pass only, like dma_rows.
+template <int NB>
 __device__ __forceinline__ void dma_words(float* st, const float* base, int nbytes, int lane) {
+    static_assert(NB % 256 == 0, "whole instructions");
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nbytes > 0 ? nbytes : 0, kRsrcWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)st, 4, lane * 4, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NB / 256; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(st + 64 * i), 4,
+                                                 lane * 4 + 256 * i, 0, 0, 0);
 #endif
 }
 
@@ -1424,7 +1429,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 
 // dK and dV for BN = 32 NW keys of one (b, key/value head), summed over the group's query heads:
 // each wave keeps 32 keys (and their values) as B operands and streams query tiles of QT rows.
-template <int D, int DT, int QT, int NW, int WPE>
+// PART 0 computes both; PART 1 only dV (S -> P -> dV, no dP) and PART 2 only dK (S, dP -> dS -> dK):
+// at D = 128 the two accumulators and both operand sets of PART 0 need more than the 256 VGPRs of
+// two waves per SIMD, so dV and dK run as two launches that each recompute S (10 D FLOP per visible
+// pair instead of 8) at twice the occupancy.
+template <int D, int DT, int QT, int NW, int WPE, int PART>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(const BwdArgs a, int n_kt) {
     constexpr int BN = NW * 32;
     constexpr int TILE = QT * D;
@@ -1435,7 +1444,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
     __shared__ __attribute__((aligned(16))) float stl[2][2 * QT];  // [stage][row][lse2, Delta]
-    static_assert(2 * QT * 4 == 256, "one wave DMA (64 lanes x 4 bytes) carries a tile of row statistics");
+    static_assert(2 * QT * 4 % 256 == 0, "the row statistics of a tile are whole 256-byte DMA instructions");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -1450,6 +1459,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int64_t jw0 = (int64_t)kt * BN + (int64_t)wave * 32;
     const int64_t key = jw0 + l32;
     const bool key_ok = key < a.Nk;
+    constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
     u32x4 kf[NDK], vf[NDK];
     {
         const uint16_t* kr = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh + (key_ok ? key : 0) * a.k_sn + 8 * hi;
@@ -1457,9 +1467,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int t = 0; t < NDK; ++t) {
             const u32x4 x = *reinterpret_cast<const u32x4*>(kr + 16 * t);
-            const u32x4 y = *reinterpret_cast<const u32x4*>(vr + 16 * t);
             kf[t] = key_ok ? x : u32x4{0u, 0u, 0u, 0u};
-            vf[t] = key_ok ? y : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (WANT_DK) {
+                const u32x4 y = *reinterpret_cast<const u32x4*>(vr + 16 * t);
+                vf[t] = key_ok ? y : u32x4{0u, 0u, 0u, 0u};
+            }
         }
     }
     // query rows that see a key of this workgroup: i >= first key - delta (causal)
@@ -1500,7 +1512,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_,   \
                              nv_, doff, wave);                                                            \
         if (wave == NW - 1)   /* the rows' (lse2, Delta) by DMA too; rows past Nq read as zero */          \
-            dma_words(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + q0_), (int)(nv_ * 8), lane); \
+            dma_words<2 * QT * 4>(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + q0_), (int)(nv_ * 8), lane); \
     } while (0)
 
     if (total > 0) CQSA_BWD_KV_TILE(0);
@@ -1522,9 +1534,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
             for (int t = 0; t < NDK; ++t) {
                 const u32x4 qa = *reinterpret_cast<const u32x4*>(st + rread[t] + qb * 32 * D);
-                const u32x4 da = *reinterpret_cast<const u32x4*>(st + TILE + rread[t] + qb * 32 * D);
                 sacc = mfma32<DT>(qa, kf[t], sacc);
-                dpacc = mfma32<DT>(da, vf[t], dpacc);
+                if constexpr (WANT_DK) {
+                    const u32x4 da = *reinterpret_cast<const u32x4*>(st + TILE + rread[t] + qb * 32 * D);
+                    dpacc = mfma32<DT>(da, vf[t], dpacc);
+                }
             }
             // register r of the lane holds query row qb 32 + 8 (r / 4) + 4 hi + r % 4 of the tile
 #pragma unroll
@@ -1548,19 +1562,21 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
                         }
                         const float p = __builtin_amdgcn_exp2f(fmaf(s, a.scale_log2, -l4[e]));
                         xp[4 * g + e] = p;
-                        xs[4 * g + e] = p * (dpacc[r] - d4[e]);
+                        if constexpr (WANT_DK) xs[4 * g + e] = p * (dpacc[r] - d4[e]);
                     }
                 }
-                pp[2 * qb + u] = pack8<DT>(xp);
-                ps[2 * qb + u] = pack8<DT>(xs);
+                if constexpr (WANT_DV) pp[2 * qb + u] = pack8<DT>(xp);
+                if constexpr (WANT_DK) ps[2 * qb + u] = pack8<DT>(xs);
             }
         }
 #pragma unroll
         for (int t = 0; t < NPQ; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                dvacc[db] = mfma32<DT>(tr_operand<D>(st + TILE + tread[db] + 16 * t * D), pp[t], dvacc[db]);
-                dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), ps[t], dkacc[db]);
+                if constexpr (WANT_DV)
+                    dvacc[db] = mfma32<DT>(tr_operand<D>(st + TILE + tread[db] + 16 * t * D), pp[t], dvacc[db]);
+                if constexpr (WANT_DK)
+                    dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), ps[t], dkacc[db]);
             }
     }
 #undef CQSA_BWD_KV_TILE
@@ -1574,8 +1590,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         for (int g = 0; g < 4; ++g) {
             const f32x4 x = {dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
             const f32x4 y = {dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
-            store4(a.dk, kbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
-            store4(a.dv, vbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, y);
+            if constexpr (WANT_DK) store4(a.dk, kbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
+            if constexpr (WANT_DV) store4(a.dv, vbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, y);
         }
 }
 
@@ -1791,8 +1807,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int DQ_NW = 4, DQ_KT = D == 64 ? 64 : 32, DQ_WPE = 2;
-    constexpr int KV_NW = 4, KV_QT = 32, KV_WPE = D == 64 ? 2 : 1;   // D=128 holds 256 accumulator and operand registers
+    constexpr int DQ_NW = D == 64 ? 8 : 4, DQ_KT = D == 64 ? 64 : 32, DQ_WPE = 2;
+    // D=64: dK and dV in one pass; D=128: a dV pass, then a dK pass, each at two waves per SIMD
+    constexpr int KV_NW = 4, KV_QT = 32, KV_WPE = 2;
     {
         const int64_t n_qt = (a.Nq + DQ_NW * 32 - 1) / (DQ_NW * 32);
         const int64_t blocks = (int64_t)a.B * a.Hq * n_qt;
@@ -1807,9 +1824,19 @@ hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
         const int64_t n_kt = (a.Nk + KV_NW * 32 - 1) / (KV_NW * 32);
         const int64_t blocks = (int64_t)a.B * a.Hkv * n_kt;
         if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        if (blocks > 0)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0, st,
-                               a, (int)n_kt);
+        if (blocks > 0) {
+            if constexpr (D == 64) {
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                                   st, a, (int)n_kt);
+            } else {
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                                   st, a, (int)n_kt);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 2>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                                   st, a, (int)n_kt);
+            }
+        }
         return hipGetLastError();
     }
 }
