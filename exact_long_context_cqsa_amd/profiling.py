@@ -5,7 +5,8 @@
         --trace <kernel_trace.csv> --fetch <fetch counter_collection.csv> --write <write counter_collection.csv> \
         --command "<the rocprofv3 command lines that produced the CSVs>"
 
-The kernel trace gives the per-launch duration of the kernel whose name contains --kernel.  FETCH_SIZE and
+The kernel trace gives the per-launch duration of the kernel whose name contains --kernel.  With
+--copy-trace it summarises the host-to-device streaming of a --memory-copy-trace run instead.  FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) are scaled by what the same counters read for the plain 1 GiB device copy in
 the same run (bench.py --copy-calibration), giving HBM bytes per launch.  The summary records the SHA-256 of
 the kernel source it measured; bench.py reports the traffic only while the source is unchanged.
@@ -107,6 +108,51 @@ def summarise(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarise_copies(args) -> str:
+    """Host-to-device streaming from a rocprofv3 --memory-copy-trace run.  The trace gives each copy's
+    stream and duration but not its size, so the bytes are the plan's (cqsa_plan_info.h2d_bytes, as the
+    run reported them); the achieved rate is those bytes over the summed durations of the copies on the
+    library's H2D stream."""
+    per = {}
+    for r in _rows(args.copy_trace):
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        per.setdefault((r["Direction"], r["Stream_Id"]), []).append(d)
+    key = [k for k in per if k[1] == str(args.h2d_stream)]
+    if len(key) != 1:
+        raise SystemExit(f"expected one direction on stream {args.h2d_stream}: {sorted(per)}")
+    durs = per[key[0]]
+    total_ns = sum(durs)
+    gbs = args.h2d_bytes / total_ns
+    lines = [
+        f"# {args.name}",
+        "",
+        "## Commands",
+        "",
+        "```",
+        args.command.strip(),
+        "```",
+        "",
+        "## Copies (rocprofv3 --memory-copy-trace)",
+        "",
+    ]
+    for (direction, stream), v in sorted(per.items()):
+        lines.append(f"- stream {stream}, {direction}: {len(v)} copies, {sum(v) / 1e6:.1f} ms in total, "
+                     f"longest {max(v) / 1e6:.2f} ms")
+    lines += [
+        "",
+        f"h2d_stream: {args.h2d_stream}",
+        f"h2d_copies: {len(durs)}",
+        f"h2d_bytes: {args.h2d_bytes}",
+        f"h2d_busy_ns: {total_ns}",
+        f"h2d_gbs: {gbs:.2f}",
+        f"link_peak_gbs: {args.link_gbs:.2f}",
+        f"h2d_frac_of_link: {gbs / args.link_gbs:.3f}",
+    ]
+    if args.note:
+        lines += ["", "## Notes", "", args.note.strip()]
+    return "\n".join(lines) + "\n"
+
+
 def read_profile(path: str) -> dict:
     """Key: value pairs of a summary written by this module."""
     out = {}
@@ -122,15 +168,26 @@ def read_profile(path: str) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--name", required=True)
-    ap.add_argument("--kernel", required=True)
-    ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel")
+    ap.add_argument("--trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-trace", help="memory_copy_trace.csv: summarise the H2D streaming instead")
+    ap.add_argument("--h2d-stream", type=int, default=1)
+    ap.add_argument("--h2d-bytes", type=int, default=0)
+    ap.add_argument("--link-gbs", type=float, default=0.0)
     ap.add_argument("--command", required=True)
     ap.add_argument("--note", default="")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
-    text = summarise(args)
+    if args.copy_trace:
+        if args.h2d_bytes <= 0 or args.link_gbs <= 0:
+            ap.error("--copy-trace needs --h2d-bytes and --link-gbs")
+        text = summarise_copies(args)
+    else:
+        if not (args.kernel and args.trace and args.fetch and args.write):
+            ap.error("--kernel, --trace, --fetch and --write are required")
+        text = summarise(args)
     out = args.out or os.path.join(ROOT, "profiles", args.name + ".md")
     os.makedirs(os.path.dirname(out), exist_ok=True)
     with open(out, "w") as f:

@@ -1,0 +1,61 @@
+"""The rocprofv3 summary writer (host logic): per-launch durations, traffic scaled by the 1 GiB copy's
+counters, the H2D streaming summary, and the key: value reader that bench.py uses."""
+import argparse
+import csv
+
+import pytest
+
+from exact_long_context_cqsa_amd import profiling
+
+
+def _csv(path, header, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+    return str(path)
+
+
+def test_kernel_summary_scales_counters_by_the_copy(tmp_path):
+    trace = _csv(tmp_path / "kt.csv", ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+                 [["void k_attn<64>(Args)", 100, 1100], ["void k_attn<64>(Args)", 2000, 4000],
+                  ["other_kernel", 0, 50]])
+    hdr = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    # the copy of 1 GiB reports half its bytes on FETCH_SIZE (KiB) and all of them on WRITE_SIZE
+    fetch = _csv(tmp_path / "f.csv", hdr, [["void k_attn<64>(Args)", 256, "FETCH_SIZE", 1000.0],
+                                           ["void k_attn<64>(Args)", 256, "FETCH_SIZE", 3000.0],
+                                           ["__amd_rocclr_copyBuffer", 1024, "FETCH_SIZE", 524288.0]])
+    write = _csv(tmp_path / "w.csv", hdr, [["void k_attn<64>(Args)", 256, "WRITE_SIZE", 500.0],
+                                           ["__amd_rocclr_copyBuffer", 1024, "WRITE_SIZE", 1048576.0]])
+    args = argparse.Namespace(name="k_attn_case", kernel="k_attn<", trace=trace, fetch=fetch, write=write,
+                              command="rocprofv3 ...", note="a note")
+    text = profiling.summarise(args)
+    out = tmp_path / "s.md"
+    out.write_text(text)
+    p = profiling.read_profile(str(out))
+    assert p["calls"] == "2" and float(p["avg_ns"]) == 1500.0 and p["min_ns"] == "1000"
+    assert float(p["fetch_bytes_per_launch"]) == 2000.0 * 1024 * 2     # mean KiB x 1024 x scale 2
+    assert float(p["write_bytes_per_launch"]) == 500.0 * 1024
+    assert float(p["traffic_bytes_per_launch"]) == 2000.0 * 2048 + 500.0 * 1024
+    assert p["kernel_source_sha256"] == profiling.kernel_source_sha256()
+    assert "## Notes" in text and "a note" in text
+
+
+def test_copy_summary(tmp_path):
+    hdr = ["Kind", "Direction", "Stream_Id", "Source_Agent_Id", "Destination_Agent_Id", "Correlation_Id",
+           "Start_Timestamp", "End_Timestamp"]
+    rows = [["MEMORY_COPY", "MEMORY_COPY_DEVICE_TO_DEVICE", 1, "Agent 0", "Agent 1", i, 1000 * i, 1000 * i + 400]
+            for i in range(5)]
+    rows += [["MEMORY_COPY", "MEMORY_COPY_HOST_TO_DEVICE", 0, "Agent 0", "Agent 1", 9, 0, 7000]]
+    trace = _csv(tmp_path / "mc.csv", hdr, rows)
+    args = argparse.Namespace(name="h2d_case", copy_trace=trace, h2d_stream=1, h2d_bytes=100_000, link_gbs=60.0,
+                              command="rocprofv3 --memory-copy-trace ...", note="")
+    text = profiling.summarise_copies(args)
+    out = tmp_path / "c.md"
+    out.write_text(text)
+    p = profiling.read_profile(str(out))
+    assert p["h2d_copies"] == "5" and p["h2d_busy_ns"] == "2000"
+    assert float(p["h2d_gbs"]) == pytest.approx(50.0) and float(p["h2d_frac_of_link"]) == pytest.approx(0.833, abs=1e-3)
+    args.h2d_stream = 3
+    with pytest.raises(SystemExit):
+        profiling.summarise_copies(args)
