@@ -146,9 +146,14 @@ def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
     link = 3 * (1 << 30) / (time.perf_counter() - t1) / 1e9
     del src, dst
     torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base_alloc = torch.cuda.memory_allocated()
     t2 = time.perf_counter()
     _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True, cqs=cqs)
     wall = time.perf_counter() - t2
+    # the call's device memory: its workspace comes from PyTorch's allocator (the library then allocates
+    # nothing itself), so the allocator's high-water mark over the call is the call's peak
+    peak = torch.cuda.max_memory_allocated() - base_alloc
     print(f"[bench] streamed {'grid' if not cqs else f'cqs c={cqs}'}: {wall:.2f} s", file=sys.stderr, flush=True)
     tok = w.B * w.Nq / wall
     h2d_gbs = info["h2d_bytes"] / (info["h2d_ms"] / 1e3) / 1e9 if info["h2d_ms"] > 0 else None
@@ -175,6 +180,7 @@ def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
             "q_chunk": info["q_chunk"], "kv_chunk": info["kv_chunk"], "chunk_pairs": info["chunk_pairs"],
             "cqs_subproblems": info["cqs_subproblems"],
             "workspace_bytes": info["workspace_bytes"], "budget_bytes": info["budget_bytes"],
+            "peak_device_bytes": int(peak), "mem_budget": w.mem_budget,
             "parity_rows": int(len(rows)), "parity_max_abs_fp16_out": max_abs,
             "note": "wall time includes PCIe transfers from/to pinned host memory; not the headline value"}
 
