@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
-           "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward",
+           "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward", "schedule_trace",
            "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -89,6 +89,9 @@ def _load_library():
     lib.cqsa_attention_ex.restype = ctypes.c_int
     lib.cqsa_plan.argtypes = [T, T, T, ctypes.c_int, ctypes.c_uint64, T, ctypes.c_int, O, I]
     lib.cqsa_plan.restype = ctypes.c_int
+    lib.cqsa_schedule_trace.argtypes = [T, T, T, ctypes.c_int, ctypes.c_uint64, T, ctypes.c_int, O, ctypes.c_char_p,
+                                        ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+    lib.cqsa_schedule_trace.restype = ctypes.c_int
     lib.cqsa_fwd_partial.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_int64, fp, fp,
                                      ctypes.c_void_p]
     lib.cqsa_fwd_partial.restype = ctypes.c_int
@@ -242,6 +245,36 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
                           int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
                           ctypes.byref(info)))
     return info.as_dict()
+
+
+def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chunk=None, kv_chunk=None,
+                   kv_splits=None, merge=None, num_cus=256, cqs=None, precision=0, wave_tokens=None) -> str:
+    """The operations ``attention`` would issue, recorded instead of run (no GPU needed); see
+    ``cqsa_schedule_trace`` in cqsa.h for the line format.  q, k, v and out are
+    ``(shape, dtype, where, address)`` tuples ("host" or "device"; the address is a stand-in that is
+    never dereferenced), optionally with element strides as a fifth item (default: contiguous)."""
+    def mk(t):
+        shape, dtype, where, addr = t[:4]
+        stride = t[4] if len(t) > 4 else [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+        d = CqsaTensor()
+        d.data = int(addr)
+        d.dtype = _DT[dtype]
+        d.where = {"host": WHERE_HOST, "device": WHERE_DEVICE}.get(where, WHERE_DETECT)
+        for i in range(4):
+            d.shape[i] = shape[i]
+            d.stride[i] = stride[i]
+        return d
+
+    dq, dk, dv, do = mk(q), mk(k), mk(v), mk(out)
+    opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision,
+                   wave_tokens=wave_tokens)
+    need = ctypes.c_uint64(0)
+    args = (ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0, int(mem_budget),
+            ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt))
+    _check(_lib.cqsa_schedule_trace(*args, None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(int(need.value))
+    _check(_lib.cqsa_schedule_trace(*args, buf, int(need.value), None))
+    return buf.value.decode()
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False, scale: float | None = None,

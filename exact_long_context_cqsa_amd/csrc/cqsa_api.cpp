@@ -771,6 +771,90 @@ cqsa_status side_streams(DeviceRes* r) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Schedule recording (cqsa_schedule_trace): the executors issue every copy, launch, event record and
+// event wait through the x_* wrappers below.  With a recorder installed on the calling thread they
+// append one line per operation instead of calling HIP (no GPU is touched):
+//   copy <stream> R:<lo>:<hi> | W:<lo>:<hi>        a device range the copy reads (D2H) or writes (H2D)
+//   kernel <stream> <name> R:<lo>:<hi> ... W:<lo>:<hi> ...   byte ranges (hulls) a launch reads / writes
+//   record <stream> <event>,  wait <stream> <event>,  sync <stream>
+// Streams and events are numbered in order of first use.
+
+struct Recorder {
+    std::string text;
+    std::vector<const void*> streams, events;
+    uintptr_t next_event = 0x1000;
+    int id(std::vector<const void*>& v, const void* p) {
+        for (size_t i = 0; i < v.size(); ++i)
+            if (v[i] == p) return (int)i;
+        v.push_back(p);
+        return (int)v.size() - 1;
+    }
+    void line(const std::string& l) { text += l + "\n"; }
+    std::string st(hipStream_t s) { return "s" + std::to_string(id(streams, s)); }
+    std::string ev(hipEvent_t e) { return "e" + std::to_string(id(events, e)); }
+};
+thread_local Recorder* g_rec = nullptr;
+
+std::string rng(char kind, const void* lo, const void* hi) {
+    return std::string(1, kind) + ":" + std::to_string((unsigned long long)(uintptr_t)lo) + ":" +
+           std::to_string((unsigned long long)(uintptr_t)hi);
+}
+
+hipError_t x_record(hipEvent_t e, hipStream_t s) {
+    if (g_rec) {
+        g_rec->line("record " + g_rec->st(s) + " " + g_rec->ev(e));
+        return hipSuccess;
+    }
+    return hipEventRecord(e, s);
+}
+hipError_t x_wait(hipStream_t s, hipEvent_t e) {
+    if (g_rec) {
+        g_rec->line("wait " + g_rec->st(s) + " " + g_rec->ev(e));
+        return hipSuccess;
+    }
+    return hipStreamWaitEvent(s, e, 0);
+}
+hipError_t x_sync(hipStream_t s) {
+    if (g_rec) {
+        g_rec->line("sync " + g_rec->st(s));
+        return hipSuccess;
+    }
+    return hipStreamSynchronize(s);
+}
+hipError_t x_elapsed(float* ms, hipEvent_t a, hipEvent_t b) {
+    if (g_rec) {
+        *ms = 0.f;
+        return hipSuccess;
+    }
+    return hipEventElapsedTime(ms, a, b);
+}
+// a 2D copy of height rows of width bytes; the device side's rows are pitch bytes apart
+hipError_t x_copy2d(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
+                    hipMemcpyKind kind, hipStream_t s) {
+    if (g_rec) {
+        const bool h2d = kind == hipMemcpyHostToDevice;
+        const char* dev = static_cast<const char*>(h2d ? dst : src);
+        const size_t pitch = h2d ? dpitch : spitch;
+        const size_t extent = height == 0 ? 0 : (height - 1) * pitch + width;
+        g_rec->line("copy " + g_rec->st(s) + " " + rng(h2d ? 'W' : 'R', dev, dev + extent));
+        return hipSuccess;
+    }
+    return hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, kind, s);
+}
+hipError_t x_copy(void* dst, const void* src, size_t bytes, hipMemcpyKind kind, hipStream_t s) {
+    if (g_rec) return x_copy2d(dst, bytes, src, bytes, bytes, 1, kind, s);
+    return hipMemcpyAsync(dst, src, bytes, kind, s);
+}
+
+// the byte hull of rows [r0, r1) of a [B, H, *, D] view with element strides (sb, sh, sn)
+std::string view_hull(char kind, const void* base, int64_t es, int64_t B, int64_t H, int64_t sb, int64_t sh,
+                      int64_t sn, int64_t r0, int64_t r1, int64_t D) {
+    const char* p = static_cast<const char*>(base);
+    if (r1 <= r0 || B <= 0 || H <= 0) return "";
+    return rng(kind, p + r0 * sn * es, p + ((B - 1) * sb + (H - 1) * sh + (r1 - 1) * sn + D) * es);
+}
+
+// ---------------------------------------------------------------------------------------------
 // chunk copies between a [B, H, N, D] tensor (any strides) and a compact device buffer
 
 struct Compact {
@@ -798,25 +882,25 @@ cqsa_status copy_rows(const View& t, int64_t ra, int64_t rn, char* dev, bool to_
         if (token_major && t.sh == t.D && t.sn == t.H * t.D) {
             const size_t bytes = (size_t)rn * t.H * t.D * es;
             if (to_device)
-                CQSA_HIP(hipMemcpyAsync(db, hb, bytes, kind, st));
+                CQSA_HIP(x_copy(db, hb, bytes, kind, st));
             else
-                CQSA_HIP(hipMemcpyAsync(hb, db, bytes, kind, st));
+                CQSA_HIP(x_copy(hb, db, bytes, kind, st));
         } else if (!token_major && t.sn == t.D && t.sh >= rn * t.D) {
             // each head: rn * D contiguous elements; heads at stride sh
             const size_t width = (size_t)rn * t.D * es;
             if (to_device)
-                CQSA_HIP(hipMemcpy2DAsync(db, (size_t)c.sh * es, hb, (size_t)t.sh * es, width, (size_t)t.H, kind, st));
+                CQSA_HIP(x_copy2d(db, (size_t)c.sh * es, hb, (size_t)t.sh * es, width, (size_t)t.H, kind, st));
             else
-                CQSA_HIP(hipMemcpy2DAsync(hb, (size_t)t.sh * es, db, (size_t)c.sh * es, width, (size_t)t.H, kind, st));
+                CQSA_HIP(x_copy2d(hb, (size_t)t.sh * es, db, (size_t)c.sh * es, width, (size_t)t.H, kind, st));
         } else {
             for (int64_t h = 0; h < t.H; ++h) {
                 char* hh = hb + (size_t)(h * t.sh) * es;
                 char* dh = db + (size_t)(h * c.sh) * es;
                 const size_t width = (size_t)t.D * es;
                 if (to_device)
-                    CQSA_HIP(hipMemcpy2DAsync(dh, (size_t)c.sn * es, hh, (size_t)t.sn * es, width, (size_t)rn, kind, st));
+                    CQSA_HIP(x_copy2d(dh, (size_t)c.sn * es, hh, (size_t)t.sn * es, width, (size_t)rn, kind, st));
                 else
-                    CQSA_HIP(hipMemcpy2DAsync(hh, (size_t)t.sn * es, dh, (size_t)c.sn * es, width, (size_t)rn, kind, st));
+                    CQSA_HIP(x_copy2d(hh, (size_t)t.sn * es, dh, (size_t)c.sn * es, width, (size_t)rn, kind, st));
             }
         }
     }
@@ -827,8 +911,8 @@ cqsa_status copy_rows(const View& t, int64_t ra, int64_t rn, char* dev, bool to_
 cqsa_status copy_lse_rows(float* host, const float* dev, int64_t B, int64_t Hq, int64_t Nq, int64_t ra, int64_t rn,
                           hipStream_t st) {
     if (rn <= 0) return CQSA_OK;
-    CQSA_HIP(hipMemcpy2DAsync(host + ra, (size_t)Nq * 4, dev, (size_t)rn * 4, (size_t)rn * 4, (size_t)(B * Hq),
-                              hipMemcpyDeviceToHost, st));
+    CQSA_HIP(x_copy2d(host + ra, (size_t)Nq * 4, dev, (size_t)rn * 4, (size_t)rn * 4, (size_t)(B * Hq),
+                      hipMemcpyDeviceToHost, st));
     return CQSA_OK;
 }
 
@@ -875,12 +959,51 @@ cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
     const int64_t n_qt = ceil_div(rows, bm);
     if (n_qt > 0x7FFFFFFF) return fail(CQSA_ERR_UNSUPPORTED, "too many query tiles");
     a.n_qt = (int32_t)n_qt;
+    if (g_rec) {
+        const int64_t D = P.D;
+        std::string l = "kernel " + g_rec->st(st) + " fwd";
+        l += " " + view_hull('R', a.q, 2, a.B, a.Hq, a.q_sb, a.q_sh, a.q_sn, a.r0, a.r1, D);
+        l += " " + view_hull('R', a.k, 2, a.B, a.Hkv, a.k_sb, a.k_sh, a.k_sn, a.k_lo, a.k_hi, D);
+        l += " " + view_hull('R', a.v, 2, a.B, a.Hkv, a.v_sb, a.v_sh, a.v_sn, a.k_lo, a.k_hi, D);
+        if (a.mode == FWD_FINAL) {
+            const int64_t es = a.out_dtype == ET_F32 ? 4 : 2;
+            l += " " + view_hull('W', a.out, es, a.B, a.Hq, a.o_sb, a.o_sh, a.o_sn, a.r0, a.r1, D);
+            if (a.lse) l += " " + view_hull('W', a.lse, 4, a.B, a.Hq, a.l_sb, a.l_sh, 1, a.r0, a.r1, 1);
+        } else {
+            // accumulator rows ((split B + b) Hq + h) acc_rows + i, i in [r0, r1)
+            const int64_t heads = (int64_t)a.n_splits * a.B * a.Hq;
+            const std::string o = view_hull('W', a.acc_o, 4, 1, heads, 0, a.acc_rows * D, D, a.r0, a.r1, D);
+            const std::string ml = view_hull('W', a.acc_ml, 4, 1, heads, 0, a.acc_rows * 2, 2, a.r0, a.r1, 2);
+            l += " " + o + " " + ml;
+            if (a.mode == FWD_ACCUM) l += " R" + o.substr(1) + " R" + ml.substr(1);
+        }
+        g_rec->line(l);
+        return CQSA_OK;
+    }
     const hipError_t e = launch_fwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
     if (e != hipSuccess) return fail(CQSA_ERR_HIP, "forward kernel launch failed: %s", hipGetErrorString(e));
     return CQSA_OK;
 }
 
 cqsa_status run_merge(MergeArgs& m, hipStream_t st) {
+    if (g_rec) {
+        const int64_t D = m.D, heads = (int64_t)m.B * m.Hq;
+        std::string l = "kernel " + g_rec->st(st) + " merge";
+        for (int p = 0; p < m.n_parts; ++p) {
+            l += " " + view_hull('R', m.part_o[p], 4, 1, heads, 0, m.rows_per_head * D, D, m.i_lo, m.i_hi, D);
+            l += " " + view_hull('R', m.part_ml[p], 4, 1, heads, 0, m.rows_per_head * 2, 2, m.i_lo, m.i_hi, 2);
+        }
+        if (m.final_out) {
+            const int64_t es = m.out_dtype == ET_F32 ? 4 : 2;
+            l += " " + view_hull('W', m.out, es, m.B, m.Hq, m.o_sb, m.o_sh, m.o_sn, 0, m.i_hi - m.i_lo, D);
+            if (m.lse) l += " " + view_hull('W', m.lse, 4, m.B, m.Hq, m.l_sb, m.l_sh, 1, 0, m.i_hi - m.i_lo, 1);
+        } else {
+            l += " " + view_hull('W', m.o_out, 4, 1, heads, 0, m.rows_per_head * D, D, m.i_lo, m.i_hi, D);
+            l += " " + view_hull('W', m.ml_out, 4, 1, heads, 0, m.rows_per_head * 2, 2, m.i_lo, m.i_hi, 2);
+        }
+        g_rec->line(l);
+        return CQSA_OK;
+    }
     const hipError_t e = launch_merge(m, st);
     if (e != hipSuccess) return fail(CQSA_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
     return CQSA_OK;
@@ -957,6 +1080,10 @@ struct EventSet {
         for (hipEvent_t e : evs) (void)hipEventDestroy(e);
     }
     cqsa_status make(hipEvent_t* e, bool timing) {
+        if (g_rec) {   // a distinct handle that no HIP call ever sees
+            *e = reinterpret_cast<hipEvent_t>(g_rec->next_event += 0x10);
+            return CQSA_OK;
+        }
         hipError_t r = hipEventCreateWithFlags(e, timing ? hipEventDefault : hipEventDisableTiming);
         if (r != hipSuccess) return fail(CQSA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(r));
         evs.push_back(*e);
@@ -998,10 +1125,10 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
         return CQSA_OK;
     };
     // side streams start after the work already queued on the compute stream
-    CQSA_HIP(hipEventRecord(ev_start, st));
+    CQSA_HIP(x_record(ev_start, st));
     if (need_side) {
-        CQSA_HIP(hipStreamWaitEvent(h2d, ev_start, 0));
-        CQSA_HIP(hipStreamWaitEvent(d2h, ev_start, 0));
+        CQSA_HIP(x_wait(h2d, ev_start));
+        CQSA_HIP(x_wait(d2h, ev_start));
     }
     bool qfree_recorded = false, d2h_recorded = false;
     bool comp_recorded[2] = {false, false};
@@ -1017,14 +1144,14 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
         FwdArgs a = base_args(P);
         // ---- Q view
         if (P.q.host) {
-            if (qfree_recorded) CQSA_HIP(hipStreamWaitEvent(h2d, ev_qfree, 0));
+            if (qfree_recorded) CQSA_HIP(x_wait(h2d, ev_qfree));
             TimedCopy tc;
             CQSA_TRY(timed(h2d_t, &tc));
-            CQSA_HIP(hipEventRecord(tc.start, h2d));
+            CQSA_HIP(x_record(tc.start, h2d));
             CQSA_TRY(copy_rows(P.q, qa, qn, ws + pl.off_q, true, h2d));
-            CQSA_HIP(hipEventRecord(tc.stop, h2d));
-            CQSA_HIP(hipEventRecord(ev_qcopy, h2d));
-            CQSA_HIP(hipStreamWaitEvent(st, ev_qcopy, 0));
+            CQSA_HIP(x_record(tc.stop, h2d));
+            CQSA_HIP(x_record(ev_qcopy, h2d));
+            CQSA_HIP(x_wait(st, ev_qcopy));
             const Compact c = compact_for(P.q, qn);
             set_q(a, ws + pl.off_q, c.sb, c.sh, c.sn);
         } else {
@@ -1069,15 +1196,15 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
             const int buf = (int)(pair & 1);
             // ---- K/V views (copy into buffer `buf` after the compute that last read it)
             if (P.k.host || P.v.host) {
-                if (comp_recorded[buf]) CQSA_HIP(hipStreamWaitEvent(h2d, ev_comp[buf], 0));
+                if (comp_recorded[buf]) CQSA_HIP(x_wait(h2d, ev_comp[buf]));
                 TimedCopy tc;
                 CQSA_TRY(timed(h2d_t, &tc));
-                CQSA_HIP(hipEventRecord(tc.start, h2d));
+                CQSA_HIP(x_record(tc.start, h2d));
                 if (P.k.host) CQSA_TRY(copy_rows(P.k, ka, kn, ws + pl.off_k[buf], true, h2d));
                 if (P.v.host) CQSA_TRY(copy_rows(P.v, ka, kn, ws + pl.off_v[buf], true, h2d));
-                CQSA_HIP(hipEventRecord(tc.stop, h2d));
-                CQSA_HIP(hipEventRecord(ev_copy[buf], h2d));
-                CQSA_HIP(hipStreamWaitEvent(st, ev_copy[buf], 0));
+                CQSA_HIP(x_record(tc.stop, h2d));
+                CQSA_HIP(x_record(ev_copy[buf], h2d));
+                CQSA_HIP(x_wait(st, ev_copy[buf]));
             }
             if (P.k.host) {
                 const Compact c = compact_for(P.k, kn);
@@ -1099,7 +1226,7 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
             a.r1 = qn;
             a.acc_rows = qn;
             if (single) {
-                if (P.out.host && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+                if (P.out.host && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
                 a.mode = FWD_FINAL;
                 a.out = out_base;
                 a.out_dtype = elem_type(P.out.dtype);
@@ -1137,12 +1264,12 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
                 m.ml_out = acc_ml;
                 CQSA_TRY(run_merge(m, st));
             }
-            CQSA_HIP(hipEventRecord(ev_comp[buf], st));
+            CQSA_HIP(x_record(ev_comp[buf], st));
             comp_recorded[buf] = true;
             ++pair;
         }
         if (!single) {
-            if (P.out.host && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+            if (P.out.host && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
             MergeArgs m;
             std::memset(&m, 0, sizeof m);
             m.part_o[0] = acc_o;
@@ -1165,19 +1292,19 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
             m.l_sh = l_sh;
             CQSA_TRY(run_merge(m, st));
         }
-        CQSA_HIP(hipEventRecord(ev_qfree, st));
+        CQSA_HIP(x_record(ev_qfree, st));
         qfree_recorded = true;
         if (P.out.host || (P.want_lse && P.lse_host)) {
-            CQSA_HIP(hipEventRecord(ev_fin, st));
-            CQSA_HIP(hipStreamWaitEvent(d2h, ev_fin, 0));
+            CQSA_HIP(x_record(ev_fin, st));
+            CQSA_HIP(x_wait(d2h, ev_fin));
             TimedCopy tc;
             CQSA_TRY(timed(d2h_t, &tc));
-            CQSA_HIP(hipEventRecord(tc.start, d2h));
+            CQSA_HIP(x_record(tc.start, d2h));
             if (P.out.host) CQSA_TRY(copy_rows(P.out, qa, qn, ws + pl.off_out, false, d2h));
             if (P.want_lse && P.lse_host)
                 CQSA_TRY(copy_lse_rows(P.lse, reinterpret_cast<float*>(ws + pl.off_lse), P.B, P.Hq, P.Nq, qa, qn, d2h));
-            CQSA_HIP(hipEventRecord(tc.stop, d2h));
-            CQSA_HIP(hipEventRecord(ev_d2h, d2h));
+            CQSA_HIP(x_record(tc.stop, d2h));
+            CQSA_HIP(x_record(ev_d2h, d2h));
             d2h_recorded = true;
         }
     }
@@ -1186,20 +1313,20 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
         hipEvent_t j1, j2;
         CQSA_TRY(es.make(&j1, false));
         CQSA_TRY(es.make(&j2, false));
-        CQSA_HIP(hipEventRecord(j1, h2d));
-        CQSA_HIP(hipEventRecord(j2, d2h));
-        CQSA_HIP(hipStreamWaitEvent(st, j1, 0));
-        CQSA_HIP(hipStreamWaitEvent(st, j2, 0));
-        CQSA_HIP(hipStreamSynchronize(st));
+        CQSA_HIP(x_record(j1, h2d));
+        CQSA_HIP(x_record(j2, d2h));
+        CQSA_HIP(x_wait(st, j1));
+        CQSA_HIP(x_wait(st, j2));
+        CQSA_HIP(x_sync(st));
         double h = 0, d = 0;
         for (auto& t : h2d_t) {
             float ms = 0;
-            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
             h += ms;
         }
         for (auto& t : d2h_t) {
             float ms = 0;
-            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
             d += ms;
         }
         if (info) {
@@ -1242,10 +1369,10 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
         v.push_back(*tc);
         return CQSA_OK;
     };
-    CQSA_HIP(hipEventRecord(ev_start, st));
+    CQSA_HIP(x_record(ev_start, st));
     if (host_in || host_out) {
-        CQSA_HIP(hipStreamWaitEvent(h2d, ev_start, 0));
-        CQSA_HIP(hipStreamWaitEvent(d2h, ev_start, 0));
+        CQSA_HIP(x_wait(h2d, ev_start));
+        CQSA_HIP(x_wait(d2h, ev_start));
     }
     float* acc_o = reinterpret_cast<float*>(ws + pl.off_acc_o);
     float* acc_ml = reinterpret_cast<float*>(ws + pl.off_acc_ml);
@@ -1273,10 +1400,10 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
         const int buf = pl.cqs_nbuf == 2 ? (run & 1) : 0;
         char* stg = ws + pl.off_stage[buf];
         if (host_in) {
-            if (comp_recorded[buf]) CQSA_HIP(hipStreamWaitEvent(h2d, ev_comp[buf], 0));
+            if (comp_recorded[buf]) CQSA_HIP(x_wait(h2d, ev_comp[buf]));
             TimedCopy tc;
             CQSA_TRY(timed(h2d_t, &tc));
-            CQSA_HIP(hipEventRecord(tc.start, h2d));
+            CQSA_HIP(x_record(tc.start, h2d));
             uint64_t o = 0;
             for (int a = 0; a < c; ++a)
                 if (wv.qp[a] && P.q.host) {
@@ -1299,9 +1426,9 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
                         o = align_up(o + (uint64_t)n * kvrow, 256);
                     }
                 }
-            CQSA_HIP(hipEventRecord(tc.stop, h2d));
-            CQSA_HIP(hipEventRecord(ev_copy[buf], h2d));
-            CQSA_HIP(hipStreamWaitEvent(st, ev_copy[buf], 0));
+            CQSA_HIP(x_record(tc.stop, h2d));
+            CQSA_HIP(x_record(ev_copy[buf], h2d));
+            CQSA_HIP(x_wait(st, ev_copy[buf]));
         }
         for (const Plan::CqsLaunch& L : wv.launches) {
             // the launch's key parts (ascending) and query parts with their key masks
@@ -1368,10 +1495,35 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
             fa.acc_o = acc_o;
             fa.acc_ml = acc_ml;
             fa.acc_rows = P.Nq;
-            const hipError_t e = launch_wave(fa, t, (int)blocks, (int)P.D, dt, st);
-            if (e != hipSuccess) return fail(CQSA_ERR_HIP, "wave launch: %s", hipGetErrorString(e));
+            if (g_rec) {
+                const int64_t D = P.D;
+                std::string l = "kernel " + g_rec->st(st) + " wave";
+                auto part = [&](char kind, const uint16_t* p0, int layout, int64_t n, int64_t H, int64_t sb, int64_t sh,
+                                int64_t sn) {
+                    const Compact cc = layout == WAVE_COMPACT_TOKEN ? Compact{n * H * D, D, H * D}
+                                       : layout == WAVE_COMPACT_HEAD ? Compact{H * n * D, n * D, D}
+                                                                     : Compact{sb, sh, sn};
+                    return view_hull(kind, p0, 2, P.B, H, cc.sb, cc.sh, cc.sn, 0, n, D);
+                };
+                for (int u = 0; u < t.n_q; ++u) {
+                    const WaveQ& Q = t.qi[u];
+                    l += " " + part('R', Q.q, t.q_layout, Q.n, P.Hq, P.q.sb, P.q.sh, P.q.sn);
+                    const std::string o = view_hull('W', fa.acc_o, 4, 1, P.B * P.Hq, 0, P.Nq * D, D, Q.lo, Q.lo + Q.n, D);
+                    const std::string ml = view_hull('W', fa.acc_ml, 4, 1, P.B * P.Hq, 0, P.Nq * 2, 2, Q.lo, Q.lo + Q.n, 2);
+                    l += " " + o + " " + ml + " R" + o.substr(1) + " R" + ml.substr(1);
+                }
+                for (int u = 0; u < t.n_k; ++u) {
+                    const WaveK& K = t.ki[u];
+                    l += " " + part('R', K.k, t.k_layout, K.n, P.Hkv, P.k.sb, P.k.sh, P.k.sn);
+                    l += " " + part('R', K.v, t.v_layout, K.n, P.Hkv, P.v.sb, P.v.sh, P.v.sn);
+                }
+                g_rec->line(l);
+            } else {
+                const hipError_t e = launch_wave(fa, t, (int)blocks, (int)P.D, dt, st);
+                if (e != hipSuccess) return fail(CQSA_ERR_HIP, "wave launch: %s", hipGetErrorString(e));
+            }
         }
-        CQSA_HIP(hipEventRecord(ev_comp[buf], st));
+        CQSA_HIP(x_record(ev_comp[buf], st));
         comp_recorded[buf] = true;
         ++run;
     }
@@ -1418,19 +1570,19 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
                 m.l_sh = P.Nq;
             }
         }
-        if (host_out && d2h_recorded) CQSA_HIP(hipStreamWaitEvent(st, ev_d2h, 0));
+        if (host_out && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
         CQSA_TRY(run_merge(m, st));
         if (host_out) {
-            CQSA_HIP(hipEventRecord(ev_fin, st));
-            CQSA_HIP(hipStreamWaitEvent(d2h, ev_fin, 0));
+            CQSA_HIP(x_record(ev_fin, st));
+            CQSA_HIP(x_wait(d2h, ev_fin));
             TimedCopy tc;
             CQSA_TRY(timed(d2h_t, &tc));
-            CQSA_HIP(hipEventRecord(tc.start, d2h));
+            CQSA_HIP(x_record(tc.start, d2h));
             if (P.out.host) CQSA_TRY(copy_rows(P.out, qa, qn, ws + pl.off_out, false, d2h));
             if (lse_host)
                 CQSA_TRY(copy_lse_rows(P.lse, reinterpret_cast<float*>(ws + pl.off_lse), P.B, P.Hq, P.Nq, qa, qn, d2h));
-            CQSA_HIP(hipEventRecord(tc.stop, d2h));
-            CQSA_HIP(hipEventRecord(ev_d2h, d2h));
+            CQSA_HIP(x_record(tc.stop, d2h));
+            CQSA_HIP(x_record(ev_d2h, d2h));
             d2h_recorded = true;
         }
     }
@@ -1438,20 +1590,20 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
         hipEvent_t j1, j2;
         CQSA_TRY(es.make(&j1, false));
         CQSA_TRY(es.make(&j2, false));
-        CQSA_HIP(hipEventRecord(j1, h2d));
-        CQSA_HIP(hipEventRecord(j2, d2h));
-        CQSA_HIP(hipStreamWaitEvent(st, j1, 0));
-        CQSA_HIP(hipStreamWaitEvent(st, j2, 0));
-        CQSA_HIP(hipStreamSynchronize(st));
+        CQSA_HIP(x_record(j1, h2d));
+        CQSA_HIP(x_record(j2, d2h));
+        CQSA_HIP(x_wait(st, j1));
+        CQSA_HIP(x_wait(st, j2));
+        CQSA_HIP(x_sync(st));
         double h = 0, d = 0;
         for (auto& t : h2d_t) {
             float ms = 0;
-            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
             h += ms;
         }
         for (auto& t : d2h_t) {
             float ms = 0;
-            CQSA_HIP(hipEventElapsedTime(&ms, t.start, t.stop));
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
             d += ms;
         }
         if (info) {
@@ -1582,6 +1734,65 @@ cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_ten
     Plan pl;
     CQSA_TRY(make_plan(P, budget, o, cus, &pl));
     if (info) *info = pl.info;
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                                uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
+                                char* buf, uint64_t buf_len, uint64_t* needed) {
+    g_err.clear();
+    if (!q || !k || !v || !out) return fail(CQSA_ERR_INVALID, "schedule trace: q, k, v and out are required");
+    for (const cqsa_tensor* t : {q, k, v, out})
+        if (t->where != CQSA_WHERE_HOST && t->where != CQSA_WHERE_DEVICE)
+            return fail(CQSA_ERR_INVALID, "schedule trace: every tensor needs where = HOST or DEVICE");
+    if (mem_budget == 0) return fail(CQSA_ERR_INVALID, "schedule trace: mem_budget must be given");
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    if (opt) o = *opt;
+    Problem P;
+    CQSA_TRY(build_problem(q, k, v, is_causal, 0.f, out, nullptr, want_lse, false, true, &P));
+    CQSA_TRY(set_precision(o, &P));
+    P.lse_host = want_lse && P.out.host;
+    P.streamed = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
+    Recorder rec;
+    if (P.want_lse) {   // the lse array: a distinct fake range after out (host with out, else device)
+        P.lse = reinterpret_cast<float*>(out->data ? static_cast<char*>(out->data) + ((uint64_t)1 << 40) : nullptr);
+    }
+    if (!P.empty) {
+        uint64_t budget = 0;
+        CQSA_TRY(resolve_budget(mem_budget, &budget));
+        Plan pl;
+        CQSA_TRY(make_plan(P, budget, o, o.num_cus > 0 ? o.num_cus : 256, &pl));
+        // stand-ins that no HIP call sees: the workspace base and the three streams
+        char* ws = static_cast<char*>(o.workspace ? o.workspace : reinterpret_cast<void*>((uintptr_t)1 << 46));
+        hipStream_t st = o.stream ? static_cast<hipStream_t>(o.stream) : reinterpret_cast<hipStream_t>((uintptr_t)0x10);
+        DeviceRes res;
+        res.init = true;
+        res.num_cus = 256;
+        res.h2d = reinterpret_cast<hipStream_t>((uintptr_t)0x20);
+        res.d2h = reinterpret_cast<hipStream_t>((uintptr_t)0x30);
+        rec.id(rec.streams, st);
+        rec.line("workspace " + rng('W', ws, ws + pl.total));
+        g_rec = &rec;
+        cqsa_status s;
+        if (pl.cqs)
+            s = exec_cqs(P, pl, ws, st, &res, &pl.info);
+        else if (!pl.chunked)
+            s = exec_single(P, pl, ws, st);
+        else
+            s = exec_chunked(P, pl, ws, st, &res, &pl.info);
+        g_rec = nullptr;
+        CQSA_TRY(s);
+        if (P.streamed) rec.line("sync " + rec.st(st));
+    }
+    if (needed) *needed = rec.text.size() + 1;
+    if (buf && buf_len > 0) {
+        const size_t n = std::min<size_t>(rec.text.size(), buf_len - 1);
+        std::memcpy(buf, rec.text.data(), n);
+        buf[n] = 0;
+        if (n < rec.text.size()) return fail(CQSA_ERR_INVALID, "schedule trace: buffer of %llu bytes is too small",
+                                             (unsigned long long)buf_len);
+    }
     return CQSA_OK;
 }
 

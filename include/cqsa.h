@@ -181,6 +181,27 @@ cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_ten
                       cqsa_plan_info* info);
 
 /*
+ * cqsa_schedule_trace: the operations cqsa_attention_ex would issue for this problem, recorded instead
+ * of issued (no HIP call is made, no memory is allocated or touched): one line per copy, kernel
+ * launch, event record, event wait and stream synchronisation, in host issue order, with the device
+ * byte ranges each copy and kernel reads (R:lo:hi) and writes (W:lo:hi):
+ *     workspace W:lo:hi | copy sN R|W:lo:hi | kernel sN fwd|merge|wave R:..|W:.. ... |
+ *     record sN eM | wait sN eM | sync sN
+ * Streams (sN) and events (eM) are numbered by first use; s0 is the caller's stream.  It exists to
+ * check the executors' stream and event ordering on a machine without a GPU (any two operations that
+ * touch one device byte, one of them writing, must be ordered by their streams and events).
+ * The tensors' data pointers are used as given (stand-in addresses are fine; they are never
+ * dereferenced); every `where` must be DEVICE or HOST and mem_budget must be > 0; opt->workspace and
+ * opt->stream, when set, stand in for the workspace base and the caller's stream.  want_lse records
+ * the lse writes at a stand-in address 2^40 bytes past out.  The text (NUL-terminated) goes to buf;
+ * *needed (may be NULL) receives the size it needs.  CQSA_ERR_INVALID when buf_len is too small (buf
+ * then holds the truncated text), or an argument error of cqsa_plan.
+ */
+cqsa_status cqsa_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                                uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
+                                char* buf, uint64_t buf_len, uint64_t* needed);
+
+/*
  * cqsa_fwd_partial: the partial triple of one KV chunk, for every query row.
  *   q, k, v            device tensors as above.
  *   kv_begin, kv_end   the key range [kv_begin, kv_end) of the chunk (0 <= begin <= end <= Nk).
