@@ -18,7 +18,7 @@ import os
 import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
-           "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward", "schedule_trace",
+           "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward", "schedule_trace", "backward_schedule_trace",
            "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +92,10 @@ def _load_library():
     lib.cqsa_schedule_trace.argtypes = [T, T, T, ctypes.c_int, ctypes.c_uint64, T, ctypes.c_int, O, ctypes.c_char_p,
                                         ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
     lib.cqsa_schedule_trace.restype = ctypes.c_int
+    lib.cqsa_backward_schedule_trace.argtypes = [T, T, T, T, T, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int,
+                                                 ctypes.c_uint64, T, T, T, O, ctypes.c_char_p, ctypes.c_uint64,
+                                                 ctypes.POINTER(ctypes.c_uint64)]
+    lib.cqsa_backward_schedule_trace.restype = ctypes.c_int
     lib.cqsa_fwd_partial.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_int64, fp, fp,
                                      ctypes.c_void_p]
     lib.cqsa_fwd_partial.restype = ctypes.c_int
@@ -111,6 +115,9 @@ def _load_library():
     lib.cqsa_attention_backward.argtypes = [T, T, T, T, T, fp, ctypes.c_int, ctypes.c_float, T, T, T, fp,
                                             ctypes.c_void_p]
     lib.cqsa_attention_backward.restype = ctypes.c_int
+    lib.cqsa_attention_backward_ex.argtypes = [T, T, T, T, T, fp, ctypes.c_int, ctypes.c_float, ctypes.c_uint64, T, T,
+                                               T, O, I]
+    lib.cqsa_attention_backward_ex.restype = ctypes.c_int
     lib.cqsa_cqs_assign.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]
     lib.cqsa_cqs_assign.restype = ctypes.c_int
@@ -247,6 +254,36 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
     return info.as_dict()
 
 
+def _trace_desc(t) -> CqsaTensor:
+    shape, dtype, where, addr = t[:4]
+    stride = t[4] if len(t) > 4 else [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+    d = CqsaTensor()
+    d.data = int(addr)
+    d.dtype = _DT[dtype]
+    d.where = {"host": WHERE_HOST, "device": WHERE_DEVICE}.get(where, WHERE_DETECT)
+    for i in range(4):
+        d.shape[i] = shape[i]
+        d.stride[i] = stride[i]
+    return d
+
+
+def backward_schedule_trace(q, k, v, out, dout, lse, dq, dk, dv, is_causal, mem_budget, *, q_chunk=None,
+                            kv_chunk=None) -> str:
+    """The chunked backward's operations, recorded (see ``cqsa_backward_schedule_trace``).  Tensors are
+    ``(shape, dtype, where, address[, strides])`` tuples; lse is ``(where, address)``."""
+    ds = [_trace_desc(t) for t in (q, k, v, out, dout)]
+    gs = [_trace_desc(t) for t in (dq, dk, dv)]
+    opt = _options(q_chunk, kv_chunk, None, None)
+    lwhere = WHERE_HOST if lse[0] == "host" else WHERE_DEVICE
+    need = ctypes.c_uint64(0)
+    args = (*[ctypes.byref(d) for d in ds], ctypes.c_void_p(int(lse[1])), lwhere, 1 if is_causal else 0,
+            int(mem_budget), *[ctypes.byref(g) for g in gs], ctypes.byref(opt))
+    _check(_lib.cqsa_backward_schedule_trace(*args, None, 0, ctypes.byref(need)))
+    buf = ctypes.create_string_buffer(int(need.value))
+    _check(_lib.cqsa_backward_schedule_trace(*args, buf, int(need.value), None))
+    return buf.value.decode()
+
+
 def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chunk=None, kv_chunk=None,
                    kv_splits=None, merge=None, num_cus=256, cqs=None, precision=0, wave_tokens=None) -> str:
     """The operations ``attention`` would issue, recorded instead of run (no GPU needed); see
@@ -368,19 +405,38 @@ class _AttentionFn(torch.autograd.Function):
 
 
 def attention_backward(q, k, v, out, dout, lse, is_causal: bool = False, scale: float | None = None, *,
-                       grad_dtype: torch.dtype | None = None, stream: torch.cuda.Stream | None = None):
+                       grad_dtype: torch.dtype | None = None, stream: torch.cuda.Stream | None = None,
+                       mem_budget: int | None = None, q_chunk: int | None = None, kv_chunk: int | None = None,
+                       return_info: bool = False):
     """Gradients (dq, dk, dv) of ``attention`` for the upstream gradient ``dout``, from the forward's
-    ``out`` and ``lse`` (all on the GPU).  dk/dv have k's shape (GQA heads summed)."""
+    ``out`` and ``lse``.  dk/dv have k's shape (GQA heads summed).  Every tensor may be on the GPU or
+    in pinned host memory; host operands (or a forced ``q_chunk``/``kv_chunk``, or ``mem_budget``) run
+    the chunked backward, which streams them under the device-memory budget.  dq is allocated where q
+    lives, dk and dv where k lives (pinned when on the host)."""
     gd = grad_dtype or q.dtype
     dev = _device_of(q, k, v, out, dout) or torch.device("cuda", torch.cuda.current_device())
-    dq = torch.empty(q.shape, dtype=gd, device=dev)
-    dk = torch.empty(k.shape, dtype=gd, device=dev)
-    dv = torch.empty(v.shape, dtype=gd, device=dev)
+
+    def like(t, shape):
+        return (torch.empty(shape, dtype=gd, device=dev) if t.is_cuda
+                else torch.empty(shape, dtype=gd, pin_memory=True))
+
+    dq, dk, dv = like(q, q.shape), like(k, k.shape), like(k, v.shape)
     B, Hq, Nq, _ = q.shape
+    chunked = (not all(t.is_cuda for t in (q, k, v, out, dout, lse)) or q_chunk or kv_chunk or mem_budget
+               or return_info)
     with torch.cuda.device(dev):
         st = stream if stream is not None else torch.cuda.current_stream(dev)
-        stats = torch.empty(max(1, 2 * B * Hq * Nq), dtype=torch.float32, device=dev)
         sc = float(scale) if scale is not None else 0.0
+        if chunked:
+            opt = _options(q_chunk, kv_chunk, None, None, stream=st.cuda_stream)
+            info = CqsaPlanInfo()
+            _check(_lib.cqsa_attention_backward_ex(
+                ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)), ctypes.byref(_desc(out)),
+                ctypes.byref(_desc(dout)), _fptr(lse), 1 if is_causal else 0, sc, int(mem_budget or 0),
+                ctypes.byref(_desc(dq)), ctypes.byref(_desc(dk)), ctypes.byref(_desc(dv)), ctypes.byref(opt),
+                ctypes.byref(info)))
+            return (dq, dk, dv, info.as_dict()) if return_info else (dq, dk, dv)
+        stats = torch.empty(max(1, 2 * B * Hq * Nq), dtype=torch.float32, device=dev)
         _check(_lib.cqsa_attention_backward(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)),
                                             ctypes.byref(_desc(out)), ctypes.byref(_desc(dout)), _fptr(lse),
                                             1 if is_causal else 0, sc, ctypes.byref(_desc(dq)),

@@ -1872,18 +1872,26 @@ cqsa_status cqsa_attention(const cqsa_tensor* q, const cqsa_tensor* k, const cqs
     return cqsa_attention_ex(q, k, v, is_causal, scale, mem_budget, out, lse, nullptr, nullptr);
 }
 
-cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
-                                    const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
-                                    float scale, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv, float* stats_ws,
-                                    void* stream) {
-    g_err.clear();
+// The backward's operands, validated: q, k, v, out (Problem), dout, the gradients and lse.
+struct BwdProblem {
     Problem P;
-    CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, nullptr, 0, true, false, &P));
-    View vdo, vdq, vdk, vdv;
-    CQSA_TRY(make_view(dout, "dout", false, true, &vdo));
-    CQSA_TRY(make_view(dq, "dq", false, true, &vdq));
-    CQSA_TRY(make_view(dk, "dk", false, true, &vdk));
-    CQSA_TRY(make_view(dv, "dv", false, true, &vdv));
+    View dout, dq, dk, dv;
+    const float* lse = nullptr;
+    bool lse_host = false;
+};
+
+// detect: find each operand's placement with HIP; otherwise take it from `where` (lse_where for lse).
+cqsa_status bwd_problem(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, const cqsa_tensor* out,
+                        const cqsa_tensor* dout, const float* lse, int is_causal, float scale, cqsa_tensor* dq,
+                        cqsa_tensor* dk, cqsa_tensor* dv, BwdProblem* bp, bool detect = true,
+                        int lse_where = CQSA_WHERE_DETECT) {
+    Problem& P = bp->P;
+    CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, nullptr, 0, detect, false, &P));
+    View &vdo = bp->dout, &vdq = bp->dq, &vdk = bp->dk, &vdv = bp->dv;
+    CQSA_TRY(make_view(dout, "dout", false, detect, &vdo));
+    CQSA_TRY(make_view(dq, "dq", false, detect, &vdq));
+    CQSA_TRY(make_view(dk, "dk", false, detect, &vdk));
+    CQSA_TRY(make_view(dv, "dv", false, detect, &vdv));
     if (vdo.dtype != P.dtype) return fail(CQSA_ERR_INVALID, "dout must have q's dtype");
     if (vdo.B != P.B || vdo.H != P.Hq || vdo.N != P.Nq || vdo.D != P.D) return fail(CQSA_ERR_INVALID, "dout must have q's shape");
     if (vdq.B != P.B || vdq.H != P.Hq || vdq.N != P.Nq || vdq.D != P.D) return fail(CQSA_ERR_INVALID, "dq must have q's shape");
@@ -1892,19 +1900,18 @@ cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, 
             return fail(CQSA_ERR_INVALID, "dk and dv must have k's shape");
     if (vdk.dtype != vdq.dtype || vdv.dtype != vdq.dtype) return fail(CQSA_ERR_INVALID, "dq, dk, dv must share one dtype");
     if (P.empty || P.Nk == 0) return CQSA_OK;
-    if (P.streamed || vdo.host || vdq.host || vdk.host || vdv.host)
-        return fail(CQSA_ERR_UNSUPPORTED, "the backward needs q, k, v, out, dout and the gradients in device memory");
     if (!lse) return fail(CQSA_ERR_INVALID, "lse is NULL");
-    {
+    bp->lse = lse;
+    if (!detect) {
+        bp->lse_host = lse_where == CQSA_WHERE_HOST;
+    } else {
         cqsa_tensor lt;
         std::memset(&lt, 0, sizeof lt);
         lt.data = const_cast<float*>(lse);
         lt.dtype = CQSA_F32;
         lt.shape[0] = 1; lt.shape[1] = 1; lt.shape[2] = 1; lt.shape[3] = 1;
         lt.stride[3] = 1;
-        bool host = false;
-        CQSA_TRY(locate(&lt, "lse", false, &host));
-        if (host) return fail(CQSA_ERR_UNSUPPORTED, "lse must be in device memory");
+        CQSA_TRY(locate(&lt, "lse", false, &bp->lse_host));
     }
     if (!aligned16(vdo.data) || vdo.sn % 8 || vdo.sh % 8 || vdo.sb % 8)
         return fail(CQSA_ERR_UNSUPPORTED, "dout data and strides must be 16-byte aligned");
@@ -1914,6 +1921,430 @@ cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, 
     if (P.out.dtype == CQSA_F32 ? (!aligned16(P.out.data) || P.out.sn % 4 || P.out.sh % 4 || P.out.sb % 4)
                                 : (!aligned16(P.out.data) || P.out.sn % 8 || P.out.sh % 8 || P.out.sb % 8))
         return fail(CQSA_ERR_UNSUPPORTED, "out data and strides must be 16-byte aligned for the backward");
+    return CQSA_OK;
+}
+
+// Arguments common to every backward launch of a problem (pointers and extents are set per launch).
+BwdArgs bwd_base(const BwdProblem& bp) {
+    const Problem& P = bp.P;
+    BwdArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.B = (int32_t)P.B;
+    a.Hq = (int32_t)P.Hq;
+    a.Hkv = (int32_t)P.Hkv;
+    a.group = (int32_t)(P.Hq / P.Hkv);
+    a.causal = P.causal ? 1 : 0;
+    a.out_dtype = elem_type(P.out.dtype);
+    a.grad_dtype = elem_type(bp.dq.dtype);
+    a.scale = P.scale;
+    a.scale_log2 = P.scale * 1.44269504088896340736f;
+    return a;
+}
+
+cqsa_status run_bwd_pass(const Problem& P, const BwdArgs& a, int pass, hipStream_t st) {
+    if (g_rec) {
+        const int64_t D = P.D, oes = a.out_dtype == ET_F32 ? 4 : 2, ges = a.grad_dtype == ET_F32 ? 4 : 2;
+        std::string l = "kernel " + g_rec->st(st) + (pass == BWD_STATS ? " bwd_stats" : pass == BWD_DQ ? " bwd_dq" : " bwd_dkdv");
+        const std::string stats_rows =
+            view_hull('X', a.stats, 4, 1, a.B * a.Hq, 0, a.stats_rows * 2, 2, 0, a.Nq, 2).substr(1);
+        if (pass == BWD_STATS) {
+            l += " " + view_hull('R', a.out, oes, a.B, a.Hq, a.o_sb, a.o_sh, a.o_sn, 0, a.Nq, D);
+            l += " " + view_hull('R', a.dout, 2, a.B, a.Hq, a.do_sb, a.do_sh, a.do_sn, 0, a.Nq, D);
+            l += " " + view_hull('R', a.lse, 4, a.B, a.Hq, a.l_sb, a.l_sh, 1, 0, a.Nq, 1);
+            l += " W" + stats_rows;
+        } else {
+            l += " " + view_hull('R', a.q, 2, a.B, a.Hq, a.q_sb, a.q_sh, a.q_sn, 0, a.Nq, D);
+            l += " " + view_hull('R', a.dout, 2, a.B, a.Hq, a.do_sb, a.do_sh, a.do_sn, 0, a.Nq, D);
+            l += " " + view_hull('R', a.k, 2, a.B, a.Hkv, a.k_sb, a.k_sh, a.k_sn, 0, a.Nk, D);
+            l += " " + view_hull('R', a.v, 2, a.B, a.Hkv, a.v_sb, a.v_sh, a.v_sn, 0, a.Nk, D);
+            l += " R" + stats_rows;
+            auto grad = [&](const void* g, int64_t H, int64_t sb, int64_t sh, int64_t sn, int64_t n) {
+                const std::string w = view_hull('W', g, ges, a.B, H, sb, sh, sn, 0, n, D);
+                return a.accumulate ? w + " R" + w.substr(1) : w;
+            };
+            if (pass == BWD_DQ) l += " " + grad(a.dq, a.Hq, a.dq_sb, a.dq_sh, a.dq_sn, a.Nq);
+            else l += " " + grad(a.dk, a.Hkv, a.dk_sb, a.dk_sh, a.dk_sn, a.Nk) + " " + grad(a.dv, a.Hkv, a.dv_sb, a.dv_sh, a.dv_sn, a.Nk);
+        }
+        g_rec->line(l);
+        return CQSA_OK;
+    }
+    const hipError_t e = launch_bwd_pass(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, pass, st);
+    if (e != hipSuccess) return fail(CQSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return CQSA_OK;
+}
+
+cqsa_status run_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_t D, void* dst, int dtype, int64_t sb,
+                     int64_t sh, int64_t sn, hipStream_t st) {
+    if (g_rec) {
+        const int64_t es = dtype == ET_F32 ? 4 : 2;
+        g_rec->line("kernel " + g_rec->st(st) + " cast " + view_hull('R', src, 4, B, H, H * n * D, n * D, D, 0, n, D) + " " +
+                    view_hull('W', dst, es, B, H, sb, sh, sn, 0, n, D));
+        return CQSA_OK;
+    }
+    const hipError_t e = launch_cast(src, B, H, n, D, dst, dtype, sb, sh, sn, st);
+    if (e != hipSuccess) return fail(CQSA_ERR_HIP, "cast launch failed: %s", hipGetErrorString(e));
+    return CQSA_OK;
+}
+
+// lse rows [ra, ra + rn) of a [B, Hq, Nq] fp32 host array -> compact device [B, Hq, rn]
+cqsa_status copy_lse_rows_in(float* dev, const float* host, int64_t B, int64_t Hq, int64_t Nq, int64_t ra, int64_t rn,
+                             hipStream_t st) {
+    if (rn <= 0) return CQSA_OK;
+    CQSA_HIP(x_copy2d(dev, (size_t)rn * 4, host + ra, (size_t)Nq * 4, (size_t)rn * 4, (size_t)(B * Hq),
+                      hipMemcpyHostToDevice, st));
+    return CQSA_OK;
+}
+
+// The chunked backward plan: query chunks of qc rows, key chunks of kc keys, and the workspace layout.
+struct BwdPlan {
+    int64_t qc = 0, kc = 0;
+    uint64_t off_stats = 0, off_dq = 0, off_dk = 0, off_dv = 0;
+    uint64_t off_q[2] = {0, 0}, off_do[2] = {0, 0}, off_lse[2] = {0, 0}, off_o = 0;
+    uint64_t off_k[2] = {0, 0}, off_v[2] = {0, 0};
+    uint64_t off_gq = 0, off_gk = 0, off_gv = 0;   // gradient staging for host gradients
+    uint64_t total = 0;
+};
+
+uint64_t bwd_layout(const BwdProblem& bp, int64_t qc, int64_t kc, BwdPlan* pl) {
+    const Problem& P = bp.P;
+    uint64_t off = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const uint64_t qrow = (uint64_t)P.B * P.Hq * P.D, krow = (uint64_t)P.B * P.Hkv * P.D;
+    const uint64_t ges = (uint64_t)bp.dq.es;
+    pl->qc = qc;
+    pl->kc = kc;
+    pl->off_stats = take((uint64_t)P.B * P.Hq * P.Nq * 8);
+    pl->off_dq = take(qrow * P.Nq * 4);
+    pl->off_dk = take(krow * kc * 4);
+    pl->off_dv = take(krow * kc * 4);
+    for (int i = 0; i < 2; ++i) {
+        pl->off_q[i] = P.q.host ? take(qrow * qc * 2) : 0;
+        pl->off_do[i] = bp.dout.host ? take(qrow * qc * 2) : 0;
+        pl->off_lse[i] = bp.lse_host ? take((uint64_t)P.B * P.Hq * qc * 4) : 0;
+        pl->off_k[i] = P.k.host ? take(krow * kc * 2) : 0;
+        pl->off_v[i] = P.v.host ? take(krow * kc * 2) : 0;
+    }
+    pl->off_o = P.out.host ? take(qrow * qc * P.out.es) : 0;
+    pl->off_gq = bp.dq.host ? take(qrow * qc * ges) : 0;
+    pl->off_gk = bp.dk.host ? take(krow * kc * ges) : 0;
+    pl->off_gv = bp.dv.host ? take(krow * kc * ges) : 0;
+    pl->total = off;
+    return off;
+}
+
+cqsa_status bwd_plan(const BwdProblem& bp, uint64_t budget, const cqsa_options& o, BwdPlan* pl) {
+    const Problem& P = bp.P;
+    int64_t qc = o.q_chunk > 0 ? std::min(o.q_chunk, P.Nq) : std::min<int64_t>(P.Nq, kKvCap);
+    int64_t kc = o.kv_chunk > 0 ? std::min(o.kv_chunk, P.Nk) : std::min<int64_t>(P.Nk, kKvCap);
+    for (;;) {
+        if (bwd_layout(bp, qc, kc, pl) <= budget) return CQSA_OK;
+        const bool can_q = o.q_chunk <= 0 && qc > kRowGrain, can_k = o.kv_chunk <= 0 && kc > kRowGrain;
+        if (!can_q && !can_k) break;
+        if (can_k && (kc >= qc || !can_q)) kc = std::max<int64_t>(kRowGrain, (kc / 2 + kRowGrain - 1) / kRowGrain * kRowGrain);
+        else qc = std::max<int64_t>(kRowGrain, (qc / 2 + kRowGrain - 1) / kRowGrain * kRowGrain);
+    }
+    return fail(CQSA_ERR_BUDGET,
+                "mem_budget too small for the chunked backward: needs %llu bytes at %lld-row query chunks and "
+                "%lld-key chunks (the fp32 dq accumulator alone is %llu bytes)",
+                (unsigned long long)pl->total, (long long)qc, (long long)kc,
+                (unsigned long long)((uint64_t)P.B * P.Hq * P.Nq * P.D * 4));
+}
+
+// Key chunks outermost.  Pass 1: the row statistics of every query chunk (out, dout and lse staged when
+// on the host).  Pass 2: for each key chunk (K, V staged), every query chunk that sees it (Q, dout
+// staged): dQ accumulates in an fp32 array for all query rows, dK and dV in fp32 arrays for the key
+// chunk, which are rounded into the caller's gradients (through staging and a D2H copy when those live
+// on the host) when the chunk is done.  dQ is rounded last.  Staging alternates between two buffers
+// per operand, ordered by events like the forward's chunked schedule.
+cqsa_status exec_bwd_chunked(const BwdProblem& bp, const BwdPlan& pl, char* ws, hipStream_t st, DeviceRes* res,
+                             cqsa_plan_info* info) {
+    const Problem& P = bp.P;
+    const bool any_in = P.q.host || P.k.host || P.v.host || P.out.host || bp.dout.host || bp.lse_host;
+    const bool any_out = bp.dq.host || bp.dk.host || bp.dv.host;
+    hipStream_t h2d = st, d2h = st;
+    if (any_in || any_out) {
+        CQSA_TRY(side_streams(res));
+        h2d = res->h2d;
+        d2h = res->d2h;
+    }
+    EventSet es;
+    hipEvent_t ev_start, ev_qcopy[2], ev_qcomp[2], ev_kvcopy[2], ev_kvcomp[2], ev_ocopy, ev_ocomp, ev_cast, ev_d2h;
+    CQSA_TRY(es.make(&ev_start, false));
+    CQSA_TRY(es.make(&ev_ocopy, false));
+    CQSA_TRY(es.make(&ev_ocomp, false));
+    CQSA_TRY(es.make(&ev_cast, false));
+    CQSA_TRY(es.make(&ev_d2h, false));
+    for (int i = 0; i < 2; ++i) {
+        CQSA_TRY(es.make(&ev_qcopy[i], false));
+        CQSA_TRY(es.make(&ev_qcomp[i], false));
+        CQSA_TRY(es.make(&ev_kvcopy[i], false));
+        CQSA_TRY(es.make(&ev_kvcomp[i], false));
+    }
+    bool qcomp_rec[2] = {false, false}, kvcomp_rec[2] = {false, false}, ocomp_rec = false, d2h_rec = false;
+    std::vector<TimedCopy> h2d_t, d2h_t;
+    auto timed = [&](std::vector<TimedCopy>& v, TimedCopy* tc) -> cqsa_status {
+        CQSA_TRY(es.make(&tc->start, true));
+        CQSA_TRY(es.make(&tc->stop, true));
+        v.push_back(*tc);
+        return CQSA_OK;
+    };
+    CQSA_HIP(x_record(ev_start, st));
+    if (any_in || any_out) {
+        CQSA_HIP(x_wait(h2d, ev_start));
+        CQSA_HIP(x_wait(d2h, ev_start));
+    }
+    const int64_t D = P.D, Nq = P.Nq, Nk = P.Nk, qc = pl.qc, kc = pl.kc;
+    const int64_t n_q = ceil_div(Nq, qc), n_k = ceil_div(Nk, kc);
+    float* stats = reinterpret_cast<float*>(ws + pl.off_stats);
+    float* dq_acc = reinterpret_cast<float*>(ws + pl.off_dq);
+    float* dk_acc = reinterpret_cast<float*>(ws + pl.off_dk);
+    float* dv_acc = reinterpret_cast<float*>(ws + pl.off_dv);
+    const BwdArgs base = bwd_base(bp);
+    int64_t pairs = 0, launches = 0;
+    int qturn = 0;   // alternates the query-side staging buffers across both passes
+
+    // stage (or point at) rows [qa, qa + qn) of a query-side operand
+    auto qside = [&](const View& t, int64_t qa, int64_t qn, uint64_t off, bool host, const char** p, int64_t* sb,
+                     int64_t* sh, int64_t* sn) -> cqsa_status {
+        if (host) {
+            CQSA_TRY(copy_rows(t, qa, qn, ws + off, true, h2d));
+            const Compact c = compact_for(t, qn);
+            *p = ws + off;
+            *sb = c.sb;
+            *sh = c.sh;
+            *sn = c.sn;
+        } else {
+            *p = t.data + (size_t)(qa * t.sn) * t.es;
+            *sb = t.sb;
+            *sh = t.sh;
+            *sn = t.sn;
+        }
+        return CQSA_OK;
+    };
+
+    // pass 1: row statistics
+    for (int64_t r = 0; r < n_q; ++r) {
+        const int64_t qa = r * qc, qn = std::min(qc, Nq - qa);
+        const int qb = qturn++ & 1;
+        BwdArgs a = base;
+        const char *po = nullptr, *pd = nullptr;
+        if (P.out.host || bp.dout.host || bp.lse_host) {
+            if (qcomp_rec[qb]) CQSA_HIP(x_wait(h2d, ev_qcomp[qb]));
+            if (P.out.host && ocomp_rec) CQSA_HIP(x_wait(h2d, ev_ocomp));
+            TimedCopy tc;
+            CQSA_TRY(timed(h2d_t, &tc));
+            CQSA_HIP(x_record(tc.start, h2d));
+        }
+        CQSA_TRY(qside(P.out, qa, qn, pl.off_o, P.out.host, &po, &a.o_sb, &a.o_sh, &a.o_sn));
+        CQSA_TRY(qside(bp.dout, qa, qn, pl.off_do[qb], bp.dout.host, &pd, &a.do_sb, &a.do_sh, &a.do_sn));
+        if (bp.lse_host) {
+            float* dl = reinterpret_cast<float*>(ws + pl.off_lse[qb]);
+            CQSA_TRY(copy_lse_rows_in(dl, bp.lse, P.B, P.Hq, Nq, qa, qn, h2d));
+            a.lse = dl;
+            a.l_sb = P.Hq * qn;
+            a.l_sh = qn;
+        } else {
+            a.lse = bp.lse + qa;
+            a.l_sb = P.Hq * Nq;
+            a.l_sh = Nq;
+        }
+        if (P.out.host || bp.dout.host || bp.lse_host) {
+            CQSA_HIP(x_record(h2d_t.back().stop, h2d));
+            CQSA_HIP(x_record(ev_qcopy[qb], h2d));
+            CQSA_HIP(x_wait(st, ev_qcopy[qb]));
+        }
+        a.out = po;
+        a.dout = reinterpret_cast<const uint16_t*>(pd);
+        a.stats = stats + 2 * qa;
+        a.stats_rows = Nq;
+        a.Nq = qn;
+        a.Nk = Nk;
+        CQSA_TRY(run_bwd_pass(P, a, BWD_STATS, st));
+        ++launches;
+        CQSA_HIP(x_record(ev_qcomp[qb], st));
+        qcomp_rec[qb] = true;
+        if (P.out.host) {
+            CQSA_HIP(x_record(ev_ocomp, st));
+            ocomp_rec = true;
+        }
+    }
+
+    // pass 2: key chunks outermost
+    for (int64_t c = 0; c < n_k; ++c) {
+        const int64_t ka = c * kc, kn = std::min(kc, Nk - ka);
+        const int kb = (int)(c & 1);
+        const char *pk = nullptr, *pv = nullptr;
+        int64_t k_sb, k_sh, k_sn, v_sb, v_sh, v_sn;
+        if (P.k.host || P.v.host) {
+            if (kvcomp_rec[kb]) CQSA_HIP(x_wait(h2d, ev_kvcomp[kb]));
+            TimedCopy tc;
+            CQSA_TRY(timed(h2d_t, &tc));
+            CQSA_HIP(x_record(tc.start, h2d));
+        }
+        CQSA_TRY(qside(P.k, ka, kn, pl.off_k[kb], P.k.host, &pk, &k_sb, &k_sh, &k_sn));
+        CQSA_TRY(qside(P.v, ka, kn, pl.off_v[kb], P.v.host, &pv, &v_sb, &v_sh, &v_sn));
+        if (P.k.host || P.v.host) {
+            CQSA_HIP(x_record(h2d_t.back().stop, h2d));
+            CQSA_HIP(x_record(ev_kvcopy[kb], h2d));
+            CQSA_HIP(x_wait(st, ev_kvcopy[kb]));
+        }
+        bool first = true;
+        for (int64_t r = 0; r < n_q; ++r) {
+            const int64_t qa = r * qc, qn = std::min(qc, Nq - qa);
+            if (P.causal && ka > qa + qn - 1 + (Nk - Nq)) continue;   // no row of the chunk sees these keys
+            const int qb = qturn++ & 1;
+            BwdArgs a = base;
+            const char *pq = nullptr, *pd = nullptr;
+            if (P.q.host || bp.dout.host) {
+                if (qcomp_rec[qb]) CQSA_HIP(x_wait(h2d, ev_qcomp[qb]));
+                TimedCopy tc;
+                CQSA_TRY(timed(h2d_t, &tc));
+                CQSA_HIP(x_record(tc.start, h2d));
+            }
+            CQSA_TRY(qside(P.q, qa, qn, pl.off_q[qb], P.q.host, &pq, &a.q_sb, &a.q_sh, &a.q_sn));
+            CQSA_TRY(qside(bp.dout, qa, qn, pl.off_do[qb], bp.dout.host, &pd, &a.do_sb, &a.do_sh, &a.do_sn));
+            if (P.q.host || bp.dout.host) {
+                CQSA_HIP(x_record(h2d_t.back().stop, h2d));
+                CQSA_HIP(x_record(ev_qcopy[qb], h2d));
+                CQSA_HIP(x_wait(st, ev_qcopy[qb]));
+            }
+            a.q = reinterpret_cast<const uint16_t*>(pq);
+            a.dout = reinterpret_cast<const uint16_t*>(pd);
+            a.k = reinterpret_cast<const uint16_t*>(pk);
+            a.v = reinterpret_cast<const uint16_t*>(pv);
+            a.k_sb = k_sb; a.k_sh = k_sh; a.k_sn = k_sn;
+            a.v_sb = v_sb; a.v_sh = v_sh; a.v_sn = v_sn;
+            a.stats = stats + 2 * qa;
+            a.stats_rows = Nq;
+            a.Nq = qn;
+            a.Nk = kn;
+            a.causal_delta = qa - ka + (Nk - Nq);
+            a.grad_dtype = ET_F32;
+            // dQ rows of the chunk in the all-rows accumulator; key chunk 0 is seen by every row, so it
+            // starts each row's sum
+            a.dq = dq_acc + qa * D;
+            a.dq_sb = P.Hq * Nq * D; a.dq_sh = Nq * D; a.dq_sn = D;
+            a.accumulate = c > 0 ? 1 : 0;
+            CQSA_TRY(run_bwd_pass(P, a, BWD_DQ, st));
+            a.dk = dk_acc;
+            a.dv = dv_acc;
+            a.dk_sb = a.dv_sb = P.Hkv * kn * D; a.dk_sh = a.dv_sh = kn * D; a.dk_sn = a.dv_sn = D;
+            a.accumulate = first ? 0 : 1;
+            CQSA_TRY(run_bwd_pass(P, a, BWD_DKDV, st));
+            launches += P.D == 128 ? 3 : 2;   // the dK/dV pass is two launches at D = 128
+            ++pairs;
+            first = false;
+            CQSA_HIP(x_record(ev_qcomp[qb], st));
+            qcomp_rec[qb] = true;
+        }
+        CQSA_HIP(x_record(ev_kvcomp[kb], st));
+        kvcomp_rec[kb] = true;
+        // deliver dK and dV of the chunk
+        const int gdt = elem_type(bp.dq.dtype);
+        for (int g = 0; g < 2; ++g) {
+            const View& t = g == 0 ? bp.dk : bp.dv;
+            const float* acc = g == 0 ? dk_acc : dv_acc;
+            if (!t.host) {
+                CQSA_TRY(run_cast(acc, P.B, P.Hkv, kn, D, t.data + (size_t)(ka * t.sn) * t.es, gdt, t.sb, t.sh, t.sn, st));
+            } else {
+                if (d2h_rec) CQSA_HIP(x_wait(st, ev_d2h));
+                char* stg = ws + (g == 0 ? pl.off_gk : pl.off_gv);
+                const Compact cc = compact_for(t, kn);
+                CQSA_TRY(run_cast(acc, P.B, P.Hkv, kn, D, stg, gdt, cc.sb, cc.sh, cc.sn, st));
+                CQSA_HIP(x_record(ev_cast, st));
+                CQSA_HIP(x_wait(d2h, ev_cast));
+                TimedCopy tc;
+                CQSA_TRY(timed(d2h_t, &tc));
+                CQSA_HIP(x_record(tc.start, d2h));
+                CQSA_TRY(copy_rows(t, ka, kn, stg, false, d2h));
+                CQSA_HIP(x_record(tc.stop, d2h));
+                CQSA_HIP(x_record(ev_d2h, d2h));
+                d2h_rec = true;
+            }
+            ++launches;
+        }
+    }
+    // deliver dQ
+    {
+        const View& t = bp.dq;
+        const int gdt = elem_type(t.dtype);
+        if (!t.host) {
+            CQSA_TRY(run_cast(dq_acc, P.B, P.Hq, Nq, D, t.data, gdt, t.sb, t.sh, t.sn, st));
+            ++launches;
+        } else {
+            for (int64_t r = 0; r < n_q; ++r) {
+                const int64_t qa = r * qc, qn = std::min(qc, Nq - qa);
+                if (d2h_rec) CQSA_HIP(x_wait(st, ev_d2h));
+                const Compact cc = compact_for(t, qn);
+                // rows [qa, qa + qn) of every head: a [B Hq][qn] slice of the accumulator with head
+                // stride Nq D, rounded into the compact staging
+                for (int64_t bh = 0; bh < P.B * P.Hq; ++bh) {
+                    const int64_t b = bh / P.Hq, h = bh % P.Hq;
+                    CQSA_TRY(run_cast(dq_acc + (bh * Nq + qa) * D, 1, 1, qn, D,
+                                      ws + pl.off_gq + (size_t)(b * cc.sb + h * cc.sh) * t.es, gdt, 0, 0, cc.sn, st));
+                    ++launches;
+                }
+                CQSA_HIP(x_record(ev_cast, st));
+                CQSA_HIP(x_wait(d2h, ev_cast));
+                TimedCopy tc;
+                CQSA_TRY(timed(d2h_t, &tc));
+                CQSA_HIP(x_record(tc.start, d2h));
+                CQSA_TRY(copy_rows(t, qa, qn, ws + pl.off_gq, false, d2h));
+                CQSA_HIP(x_record(tc.stop, d2h));
+                CQSA_HIP(x_record(ev_d2h, d2h));
+                d2h_rec = true;
+            }
+        }
+    }
+    if (any_in || any_out) {
+        hipEvent_t j1, j2;
+        CQSA_TRY(es.make(&j1, false));
+        CQSA_TRY(es.make(&j2, false));
+        CQSA_HIP(x_record(j1, h2d));
+        CQSA_HIP(x_record(j2, d2h));
+        CQSA_HIP(x_wait(st, j1));
+        CQSA_HIP(x_wait(st, j2));
+        CQSA_HIP(x_sync(st));
+        double h = 0, d = 0;
+        for (auto& t : h2d_t) {
+            float ms = 0;
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
+            h += ms;
+        }
+        for (auto& t : d2h_t) {
+            float ms = 0;
+            CQSA_HIP(x_elapsed(&ms, t.start, t.stop));
+            d += ms;
+        }
+        if (info) {
+            info->h2d_ms = h;
+            info->d2h_ms = d;
+        }
+    }
+    if (info) {
+        info->chunk_pairs = pairs;
+        info->kernel_launches = launches;
+    }
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                    const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
+                                    float scale, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv, float* stats_ws,
+                                    void* stream) {
+    g_err.clear();
+    BwdProblem bp;
+    CQSA_TRY(bwd_problem(q, k, v, out, dout, lse, is_causal, scale, dq, dk, dv, &bp));
+    const Problem& P = bp.P;
+    if (P.empty || P.Nk == 0) return CQSA_OK;
+    if (P.streamed || bp.dout.host || bp.dq.host || bp.dk.host || bp.dv.host || bp.lse_host)
+        return fail(CQSA_ERR_UNSUPPORTED,
+                    "cqsa_attention_backward needs every operand in device memory (cqsa_attention_backward_ex "
+                    "streams host operands)");
     hipStream_t st = static_cast<hipStream_t>(stream);
     float* stats = stats_ws;
     bool owned = false;
@@ -1927,37 +2358,30 @@ cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, 
         }
         owned = true;
     }
-    BwdArgs a;
-    std::memset(&a, 0, sizeof a);
+    BwdArgs a = bwd_base(bp);
     a.q = reinterpret_cast<const uint16_t*>(P.q.data);
     a.k = reinterpret_cast<const uint16_t*>(P.k.data);
     a.v = reinterpret_cast<const uint16_t*>(P.v.data);
-    a.dout = reinterpret_cast<const uint16_t*>(vdo.data);
+    a.dout = reinterpret_cast<const uint16_t*>(bp.dout.data);
     a.out = P.out.data;
-    a.lse = lse;
+    a.lse = bp.lse;
     a.q_sb = P.q.sb; a.q_sh = P.q.sh; a.q_sn = P.q.sn;
     a.k_sb = P.k.sb; a.k_sh = P.k.sh; a.k_sn = P.k.sn;
     a.v_sb = P.v.sb; a.v_sh = P.v.sh; a.v_sn = P.v.sn;
-    a.do_sb = vdo.sb; a.do_sh = vdo.sh; a.do_sn = vdo.sn;
+    a.do_sb = bp.dout.sb; a.do_sh = bp.dout.sh; a.do_sn = bp.dout.sn;
     a.o_sb = P.out.sb; a.o_sh = P.out.sh; a.o_sn = P.out.sn;
     a.l_sb = P.Hq * P.Nq;
     a.l_sh = P.Nq;
     a.stats = stats;
-    a.dq = vdq.data; a.dk = vdk.data; a.dv = vdv.data;
-    a.dq_sb = vdq.sb; a.dq_sh = vdq.sh; a.dq_sn = vdq.sn;
-    a.dk_sb = vdk.sb; a.dk_sh = vdk.sh; a.dk_sn = vdk.sn;
-    a.dv_sb = vdv.sb; a.dv_sh = vdv.sh; a.dv_sn = vdv.sn;
+    a.dq = bp.dq.data; a.dk = bp.dk.data; a.dv = bp.dv.data;
+    a.dq_sb = bp.dq.sb; a.dq_sh = bp.dq.sh; a.dq_sn = bp.dq.sn;
+    a.dk_sb = bp.dk.sb; a.dk_sh = bp.dk.sh; a.dk_sn = bp.dk.sn;
+    a.dv_sb = bp.dv.sb; a.dv_sh = bp.dv.sh; a.dv_sn = bp.dv.sn;
     a.Nq = P.Nq;
     a.Nk = P.Nk;
-    a.B = (int32_t)P.B;
-    a.Hq = (int32_t)P.Hq;
-    a.Hkv = (int32_t)P.Hkv;
-    a.group = (int32_t)(P.Hq / P.Hkv);
-    a.causal = P.causal ? 1 : 0;
-    a.out_dtype = elem_type(P.out.dtype);
-    a.grad_dtype = elem_type(vdq.dtype);
-    a.scale = P.scale;
-    a.scale_log2 = P.scale * 1.44269504088896340736f;
+    a.causal_delta = P.Nk - P.Nq;
+    a.stats_rows = P.Nq;
+    a.accumulate = 0;
     hipError_t e = launch_bwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
     cqsa_status s = CQSA_OK;
     if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
@@ -1966,6 +2390,147 @@ cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, 
         (void)hipFree(stats);
     }
     return s;
+}
+
+cqsa_status cqsa_backward_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                         const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse,
+                                         int32_t lse_where, int is_causal, uint64_t mem_budget, const cqsa_tensor* dq,
+                                         const cqsa_tensor* dk, const cqsa_tensor* dv, const cqsa_options* opt,
+                                         char* buf, uint64_t buf_len, uint64_t* needed) {
+    g_err.clear();
+    for (const cqsa_tensor* t : {q, k, v, out, dout, dq, dk, dv})
+        if (!t || (t->where != CQSA_WHERE_HOST && t->where != CQSA_WHERE_DEVICE))
+            return fail(CQSA_ERR_INVALID, "schedule trace: every tensor needs where = HOST or DEVICE");
+    if (lse_where != CQSA_WHERE_HOST && lse_where != CQSA_WHERE_DEVICE)
+        return fail(CQSA_ERR_INVALID, "schedule trace: lse_where must be HOST or DEVICE");
+    if (mem_budget == 0) return fail(CQSA_ERR_INVALID, "schedule trace: mem_budget must be given");
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    if (opt) o = *opt;
+    BwdProblem bp;
+    CQSA_TRY(bwd_problem(q, k, v, out, dout, lse, is_causal, 0.f, const_cast<cqsa_tensor*>(dq),
+                         const_cast<cqsa_tensor*>(dk), const_cast<cqsa_tensor*>(dv), &bp, false, lse_where));
+    Recorder rec;
+    if (!bp.P.empty && bp.P.Nk > 0) {
+        uint64_t budget = 0;
+        CQSA_TRY(resolve_budget(mem_budget, &budget));
+        BwdPlan pl;
+        CQSA_TRY(bwd_plan(bp, budget, o, &pl));
+        char* ws = static_cast<char*>(o.workspace ? o.workspace : reinterpret_cast<void*>((uintptr_t)1 << 46));
+        hipStream_t st = o.stream ? static_cast<hipStream_t>(o.stream) : reinterpret_cast<hipStream_t>((uintptr_t)0x10);
+        DeviceRes res;
+        res.init = true;
+        res.num_cus = 256;
+        res.h2d = reinterpret_cast<hipStream_t>((uintptr_t)0x20);
+        res.d2h = reinterpret_cast<hipStream_t>((uintptr_t)0x30);
+        rec.id(rec.streams, st);
+        rec.line("workspace " + rng('W', ws, ws + pl.total));
+        g_rec = &rec;
+        const cqsa_status s = exec_bwd_chunked(bp, pl, ws, st, &res, nullptr);
+        g_rec = nullptr;
+        CQSA_TRY(s);
+        rec.line("sync " + rec.st(st));
+    }
+    if (needed) *needed = rec.text.size() + 1;
+    if (buf && buf_len > 0) {
+        const size_t n = std::min<size_t>(rec.text.size(), buf_len - 1);
+        std::memcpy(buf, rec.text.data(), n);
+        buf[n] = 0;
+        if (n < rec.text.size())
+            return fail(CQSA_ERR_INVALID, "schedule trace: buffer of %llu bytes is too small", (unsigned long long)buf_len);
+    }
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_attention_backward_ex(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                       const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
+                                       float scale, uint64_t mem_budget, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv,
+                                       const cqsa_options* opt, cqsa_plan_info* info) {
+    g_err.clear();
+    const auto t0 = std::chrono::steady_clock::now();
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    if (opt) o = *opt;
+    if (info) std::memset(info, 0, sizeof *info);
+    if (o.q_chunk < 0 || o.kv_chunk < 0) return fail(CQSA_ERR_INVALID, "negative chunk option");
+    BwdProblem bp;
+    CQSA_TRY(bwd_problem(q, k, v, out, dout, lse, is_causal, scale, dq, dk, dv, &bp));
+    const Problem& P = bp.P;
+    if (P.empty || P.Nk == 0) return CQSA_OK;
+    const bool host = P.streamed || bp.dout.host || bp.dq.host || bp.dk.host || bp.dv.host || bp.lse_host;
+    if (!host && o.q_chunk == 0 && o.kv_chunk == 0) {
+        float* stats = nullptr;
+        const uint64_t bytes = (uint64_t)P.B * P.Hq * P.Nq * 8;
+        if (o.workspace && o.workspace_bytes >= bytes) stats = static_cast<float*>(o.workspace);
+        CQSA_TRY(cqsa_attention_backward(q, k, v, out, dout, lse, is_causal, scale, dq, dk, dv, stats, o.stream));
+        if (info) {
+            info->workspace_bytes = bytes;
+            info->chunk_pairs = 1;
+            info->kernel_launches = P.D == 128 ? 4 : 3;
+        }
+        return CQSA_OK;
+    }
+    DeviceRes* res = nullptr;
+    CQSA_TRY(device_res(&res));
+    uint64_t budget = 0;
+    CQSA_TRY(resolve_budget(mem_budget, &budget));
+    BwdPlan pl;
+    CQSA_TRY(bwd_plan(bp, budget, o, &pl));
+    hipStream_t st = static_cast<hipStream_t>(o.stream);
+    char* ws = nullptr;
+    bool owned = false;
+    if (o.workspace && o.workspace_bytes >= pl.total) {
+        ws = static_cast<char*>(o.workspace);
+    } else {
+        hipError_t e = hipMalloc(reinterpret_cast<void**>(&ws), pl.total);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(CQSA_ERR_OOM, "hipMalloc of %llu workspace bytes failed: %s", (unsigned long long)pl.total,
+                        hipGetErrorString(e));
+        }
+        owned = true;
+    }
+    cqsa_plan_info in;
+    std::memset(&in, 0, sizeof in);
+    cqsa_status s = exec_bwd_chunked(bp, pl, ws, st, res, &in);
+    if (s == CQSA_OK && (owned || host)) {
+        const hipError_t e = hipStreamSynchronize(st);
+        if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    }
+    if (owned) {
+        if (s != CQSA_OK) (void)hipStreamSynchronize(st);
+        (void)hipFree(ws);
+    }
+    if (s != CQSA_OK) return s;
+    if (info) {
+        *info = in;
+        info->streamed = host ? 1 : 0;
+        info->q_chunk = pl.qc;
+        info->kv_chunk = pl.kc;
+        info->n_q_chunks = ceil_div(P.Nq, pl.qc);
+        info->n_kv_chunks = ceil_div(P.Nk, pl.kc);
+        info->workspace_bytes = pl.total;
+        info->budget_bytes = budget;
+        const uint64_t qb = (uint64_t)P.B * P.Hq * P.D, kb = (uint64_t)P.B * P.Hkv * P.D;
+        uint64_t h2d_b = 0;
+        if (P.out.host) h2d_b += qb * P.Nq * P.out.es;
+        if (bp.lse_host) h2d_b += (uint64_t)P.B * P.Hq * P.Nq * 4;
+        if (P.k.host) h2d_b += kb * P.Nk * 2;
+        if (P.v.host) h2d_b += kb * P.Nk * 2;
+        // Q and dout travel once per (query chunk, key chunk) pair, dout once more for the statistics
+        if (bp.dout.host) h2d_b += qb * P.Nq * 2;
+        for (int64_t c = 0; c < info->n_kv_chunks; ++c)
+            for (int64_t r = 0; r < info->n_q_chunks; ++r) {
+                const int64_t qa = r * pl.qc, qn = std::min(pl.qc, P.Nq - qa), ka = c * pl.kc;
+                if (P.causal && ka > qa + qn - 1 + (P.Nk - P.Nq)) continue;
+                h2d_b += qb * qn * 2 * ((P.q.host ? 1 : 0) + (bp.dout.host ? 1 : 0));
+            }
+        info->h2d_bytes = h2d_b;
+        info->d2h_bytes = (uint64_t)bp.dq.es * (qb * P.Nq * (bp.dq.host ? 1 : 0) + kb * P.Nk * ((bp.dk.host ? 1 : 0) + (bp.dv.host ? 1 : 0)));
+        if (owned || host)
+            info->wall_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    }
+    return CQSA_OK;
 }
 
 cqsa_status cqsa_fwd_partial(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,

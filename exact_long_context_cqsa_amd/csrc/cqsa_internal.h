@@ -107,11 +107,13 @@ struct MergeArgs {
     int64_t l_sb, l_sh;
 };
 
-// Backward: gradients of out = softmax(scale q k^T [+ causal]) v for an upstream gradient dout.
-// stats is a compact fp32 [B][Hq][Nq][2] array of (lse * log2 e, Delta = rowsum(dout * out)),
-// written by the first pass and read by the two gradient kernels.  Causal is bottom-right aligned
-// (key j visible to row i iff j <= i + Nk - Nq).  dq is [B, Hq, Nq, D]; dk, dv are [B, Hkv, Nk, D]
-// and sum over the query heads of their group.
+// Backward: gradients of out = softmax(scale q k^T [+ causal]) v for an upstream gradient dout, over
+// Nq query rows and Nk keys (the whole problem, or one query chunk against one key chunk).  stats is
+// an fp32 array of (lse * log2 e, Delta = rowsum(dout * out)) pairs: row i of head (b, h) at
+// 2 ((b Hq + h) stats_rows + i), written by the first pass and read by the two gradient kernels.  The
+// causal rule is key j visible to row i iff j <= i + causal_delta (Nk - Nq for a whole, bottom-right
+// aligned problem).  dq is [B, Hq, Nq, D]; dk, dv are [B, Hkv, Nk, D] and sum over the query heads of
+// their group.  With accumulate set the gradients are fp32 and each kernel adds to what they hold.
 struct BwdArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -139,9 +141,22 @@ struct BwdArgs {
     int32_t grad_dtype;  // ElemType of dq, dk, dv
     float scale;
     float scale_log2;
+    int64_t causal_delta;
+    int64_t stats_rows;
+    int32_t accumulate;
+    int32_t pad;
 };
 
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
+
+// One pass of the backward: BWD_STATS (the row statistics), BWD_DQ or BWD_DKDV.
+enum BwdPass : int32_t { BWD_STATS = 0, BWD_DQ = 1, BWD_DKDV = 2 };
+hipError_t launch_bwd_pass(const BwdArgs& a, int D, int dtype, int pass, hipStream_t stream);
+
+// fp32 rows of a compact [B][H][n][D] buffer, rounded (RNE) into element (b, h, i) of a strided
+// [B, H, n, D] tensor of ElemType dtype.
+hipError_t launch_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_t D, void* dst, int dtype,
+                       int64_t sb, int64_t sh, int64_t sn, hipStream_t stream);
 
 // Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
 int fwd_block_m(int D, int p_split);

@@ -1246,6 +1246,31 @@ __device__ __forceinline__ f32x8 load8(const void* base, int64_t off, int dt) {
 }
 
 // stats[row] = (lse * log2 e, sum_d dO O); D / 8 threads per row, 8 dims each.
+// A gradient store: four values at element off of base, in dtype dt; with accumulate (fp32 only)
+// added to what the four elements hold.
+__device__ __forceinline__ void store_grad(void* base, int64_t off, int dt, int accumulate, f32x4 v) {
+    if (accumulate) {
+        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(base) + off);
+        *p = *p + v;
+    } else {
+        store4(base, off, dt, v);
+    }
+}
+
+// Rounds fp32 rows of a compact [B][H][n][D] buffer into a strided tensor (4 values per thread).
+__global__ void __launch_bounds__(256) cast_kernel(const float* src, int64_t B, int64_t H, int64_t n, int64_t D,
+                                                   void* dst, int dtype, int64_t sb, int64_t sh, int64_t sn) {
+    const int64_t per_row = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= B * H * n * per_row) return;
+    const int64_t d0 = (idx % per_row) * 4;
+    const int64_t r = idx / per_row;             // (b H + h) n + i
+    const int64_t i = r % n, bh = r / n;
+    const int64_t b = bh / H, h = bh % H;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * D + d0);
+    store4(dst, b * sb + h * sh + i * sn + d0, dtype, v);
+}
+
 template <int D, int DT>
 __global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
     constexpr int TPR = D / 8;
@@ -1268,8 +1293,9 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
     for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (r < total && d0 == 0) {
         const float l = a.lse[b * a.l_sb + h * a.l_sh + i];
-        a.stats[2 * r] = l == -INFINITY ? INFINITY : l * kLog2e;   // no visible key: P = 0
-        a.stats[2 * r + 1] = acc;
+        const int64_t sr = (b * a.Hq + h) * a.stats_rows + i;
+        a.stats[2 * sr] = l == -INFINITY ? INFINITY : l * kLog2e;   // no visible key: P = 0
+        a.stats[2 * sr + 1] = acc;
     }
 }
 
@@ -1295,7 +1321,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int b = w / a.Hq;
     const int hkv = hq / a.group;
     const int qt = n_qt - 1 - qt_idx;
-    const int64_t delta_c = a.Nk - a.Nq;
+    const int64_t delta_c = a.causal_delta;
 
     const int64_t i0 = (int64_t)qt * BM;
     const int64_t i_end = min(i0 + (int64_t)BM, a.Nq);
@@ -1325,7 +1351,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     }
     float lse2 = INFINITY, dlt = 0.f;
     if (row_ok) {
-        const float* sp = a.stats + 2 * (((int64_t)b * a.Hq + hq) * a.Nq + row);
+        const float* sp = a.stats + 2 * (((int64_t)b * a.Hq + hq) * a.stats_rows + row);
         lse2 = sp[0];
         dlt = sp[1];
     }
@@ -1423,7 +1449,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 x = {dqacc[db][4 * g], dqacc[db][4 * g + 1], dqacc[db][4 * g + 2], dqacc[db][4 * g + 3]};
-            store4(a.dq, ob + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
+            store_grad(a.dq, ob + db * 32 + 8 * g + 4 * hi, a.grad_dtype, a.accumulate, x * a.scale);
         }
 }
 
@@ -1454,7 +1480,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     w /= n_kt;
     const int hkv = w % a.Hkv;
     const int b = w / a.Hkv;
-    const int64_t delta_c = a.Nk - a.Nq;
+    const int64_t delta_c = a.causal_delta;
 
     const int64_t jw0 = (int64_t)kt * BN + (int64_t)wave * 32;
     const int64_t key = jw0 + l32;
@@ -1512,7 +1538,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_,   \
                              nv_, doff, wave);                                                            \
         if (wave == NW - 1)   /* the rows' (lse2, Delta) by DMA too; rows past Nq read as zero */          \
-            dma_words<2 * QT * 4>(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.Nq + q0_), (int)(nv_ * 8), lane); \
+            dma_words<2 * QT * 4>(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.stats_rows + q0_), (int)(nv_ * 8), lane); \
     } while (0)
 
     if (total > 0) CQSA_BWD_KV_TILE(0);
@@ -1590,8 +1616,8 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         for (int g = 0; g < 4; ++g) {
             const f32x4 x = {dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
             const f32x4 y = {dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
-            if constexpr (WANT_DK) store4(a.dk, kbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, x * a.scale);
-            if constexpr (WANT_DV) store4(a.dv, vbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, y);
+            if constexpr (WANT_DK) store_grad(a.dk, kbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, a.accumulate, x * a.scale);
+            if constexpr (WANT_DV) store_grad(a.dv, vbase + db * 32 + 8 * g + 4 * hi, a.grad_dtype, a.accumulate, y);
         }
 }
 
@@ -1796,59 +1822,74 @@ hipError_t launch_wave(const FwdArgs& a, const WaveTable& t, int blocks, int D, 
 namespace {
 
 template <int D, int DT>
-hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd_d(const BwdArgs& a, int pass, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
     if (rows <= 0) return hipSuccess;
-    {
+    if (pass == BWD_STATS) {
         constexpr int RPB = 256 / (D / 8);
         const int64_t blocks = (rows + RPB - 1) / RPB;
         if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((bwd_stats_kernel<D, DT>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        return hipGetLastError();
     }
     constexpr int DQ_NW = D == 64 ? 8 : 4, DQ_KT = D == 64 ? 64 : 32, DQ_WPE = 2;
     // D=64: dK and dV in one pass; D=128: a dV pass, then a dK pass, each at two waves per SIMD
     constexpr int KV_NW = 4, KV_QT = 32, KV_WPE = 2;
-    {
+    if (pass == BWD_DQ) {
         const int64_t n_qt = (a.Nq + DQ_NW * 32 - 1) / (DQ_NW * 32);
         const int64_t blocks = (int64_t)a.B * a.Hq * n_qt;
         if (blocks > 0x7FFFFFFF || n_qt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
         if (blocks > 0)
             hipLaunchKernelGGL((bwd_dq_kernel<D, DT, DQ_KT, DQ_NW, DQ_WPE>), dim3((unsigned)blocks), dim3(DQ_NW * 64), 0, st, a,
                                (int)n_qt);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    {
-        const int64_t n_kt = (a.Nk + KV_NW * 32 - 1) / (KV_NW * 32);
-        const int64_t blocks = (int64_t)a.B * a.Hkv * n_kt;
-        if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        if (blocks > 0) {
-            if constexpr (D == 64) {
-                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
-                                   st, a, (int)n_kt);
-            } else {
-                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
-                                   st, a, (int)n_kt);
-                const hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-                hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 2>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
-                                   st, a, (int)n_kt);
-            }
-        }
         return hipGetLastError();
     }
+    if (pass != BWD_DKDV) return hipErrorInvalidValue;
+    const int64_t n_kt = (a.Nk + KV_NW * 32 - 1) / (KV_NW * 32);
+    const int64_t blocks = (int64_t)a.B * a.Hkv * n_kt;
+    if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (blocks > 0) {
+        if constexpr (D == 64) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                               st, a, (int)n_kt);
+        } else {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                               st, a, (int)n_kt);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 2>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+                               st, a, (int)n_kt);
+        }
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
-    if (D == 64 && dtype == ET_F16) return launch_bwd_d<64, ET_F16>(a, stream);
-    if (D == 64 && dtype == ET_BF16) return launch_bwd_d<64, ET_BF16>(a, stream);
-    if (D == 128 && dtype == ET_F16) return launch_bwd_d<128, ET_F16>(a, stream);
-    if (D == 128 && dtype == ET_BF16) return launch_bwd_d<128, ET_BF16>(a, stream);
+hipError_t launch_bwd_pass(const BwdArgs& a, int D, int dtype, int pass, hipStream_t stream) {
+    if (D == 64 && dtype == ET_F16) return launch_bwd_d<64, ET_F16>(a, pass, stream);
+    if (D == 64 && dtype == ET_BF16) return launch_bwd_d<64, ET_BF16>(a, pass, stream);
+    if (D == 128 && dtype == ET_F16) return launch_bwd_d<128, ET_F16>(a, pass, stream);
+    if (D == 128 && dtype == ET_BF16) return launch_bwd_d<128, ET_BF16>(a, pass, stream);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
+    for (int pass : {BWD_STATS, BWD_DQ, BWD_DKDV}) {
+        const hipError_t e = launch_bwd_pass(a, D, dtype, pass, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_t D, void* dst, int dtype,
+                       int64_t sb, int64_t sh, int64_t sn, hipStream_t stream) {
+    const int64_t threads = B * H * n * (D / 4);
+    if (threads <= 0) return hipSuccess;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7FFFFFFF || D % 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cast_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, B, H, n, D, dst, dtype, sb, sh, sn);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {

@@ -201,6 +201,16 @@ cqsa_status cqsa_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, cons
                                 uint64_t mem_budget, const cqsa_tensor* out, int want_lse, const cqsa_options* opt,
                                 char* buf, uint64_t buf_len, uint64_t* needed);
 
+/* The chunked backward's operations (cqsa_attention_backward_ex with host operands or forced chunks),
+ * recorded the same way: every tensor's `where` must be HOST or DEVICE, lse_where says where lse
+ * lives, and the stand-in addresses are never dereferenced.  Kernel lines name bwd_stats, bwd_dq,
+ * bwd_dkdv and cast. */
+cqsa_status cqsa_backward_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                         const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse,
+                                         int32_t lse_where, int is_causal, uint64_t mem_budget, const cqsa_tensor* dq,
+                                         const cqsa_tensor* dk, const cqsa_tensor* dv, const cqsa_options* opt,
+                                         char* buf, uint64_t buf_len, uint64_t* needed);
+
 /*
  * cqsa_fwd_partial: the partial triple of one KV chunk, for every query row.
  *   q, k, v            device tensors as above.
@@ -263,6 +273,26 @@ cqsa_status cqsa_attention_backward(const cqsa_tensor* q, const cqsa_tensor* k, 
                                     const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
                                     float scale, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv, float* stats_ws,
                                     void* stream);
+
+/*
+ * cqsa_attention_backward_ex: the same gradients, with every operand (q, k, v, out, dout, lse and the
+ * gradients) in device memory or in pinned host memory, under a device-memory budget.  When every
+ * operand is on the device and opt forces no chunking it is cqsa_attention_backward (opt->workspace,
+ * when large enough, holds the statistics).  Otherwise the problem runs in query chunks x key chunks,
+ * key chunks outermost: the row statistics of every query chunk first, then for each key chunk (K, V
+ * staged) every query chunk that sees it (Q, dout staged); dQ accumulates in fp32 for all query rows
+ * and dK, dV in fp32 for the key chunk, rounded into the caller's gradients when complete.  Host
+ * operands move on two side streams with double-buffered staging; the call then returns after
+ * completion.  Device bytes: the fp32 dQ accumulator (B Hq Nq D 4) and statistics (B Hq Nq 8) plus
+ * the chunks' accumulators and staging; the chunks are halved until that fits mem_budget x 0.85
+ * (0 = free memory x 0.85), else CQSA_ERR_BUDGET.  opt: q_chunk, kv_chunk (> 0 forces the size),
+ * workspace (used when large enough, else hipMalloc), stream.  info (may be NULL): chunk sizes and
+ * counts, pairs, launches, workspace, H2D/D2H bytes and times.
+ */
+cqsa_status cqsa_attention_backward_ex(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v,
+                                       const cqsa_tensor* out, const cqsa_tensor* dout, const float* lse, int is_causal,
+                                       float scale, uint64_t mem_budget, cqsa_tensor* dq, cqsa_tensor* dk, cqsa_tensor* dv,
+                                       const cqsa_options* opt, cqsa_plan_info* info);
 
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* cqsa_last_error(void);

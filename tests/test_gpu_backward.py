@@ -96,8 +96,11 @@ def test_backward_errors():
     m = cqsa()
     q, k, v, do = (t.to(DEV) for t in gen(1, 2, 2, 64, 64, 64, torch.float16, seed=1))
     out, lse = m.attention(q, k, v, is_causal=True, return_lse=True)
-    with pytest.raises(m.CqsaError, match="UNSUPPORTED"):
-        m.attention_backward(q.cpu().pin_memory(), k, v, out, do, lse, is_causal=True)
+    # a pinned host operand takes the chunked path (dq then lives on the host); pageable memory is refused
+    dq, dk, dv = m.attention_backward(q.cpu().pin_memory(), k, v, out, do, lse, is_causal=True)
+    assert not dq.is_cuda and dk.is_cuda
+    with pytest.raises(m.CqsaError, match="INVALID.*pinned"):
+        m.attention_backward(q.cpu(), k, v, out, do, lse, is_causal=True)
     with pytest.raises(m.CqsaError, match="INVALID"):
         m.attention_backward(q, k, v, out, do.to(torch.bfloat16), lse, is_causal=True)
 
@@ -115,3 +118,67 @@ def test_autograd_through_attention():
     for g, r in ((qd.grad, rq), (kd.grad, rk), (vd.grad, rv)):
         assert g.dtype == torch.float16
         assert rel_err(g.float(), r) <= 8 * U[torch.float16] + 2 ** -11   # + the fp16 rounding of the gradient
+
+
+# The chunked backward (cqsa_attention_backward_ex): host-resident operands streamed in query chunks x
+# key chunks (key chunks outermost, fp32 dQ/dK/dV accumulation), or forced chunks on the device.
+STREAM_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, q_chunk, kv_chunk, placement
+    (1, 2, 2, 1300, 1300, 64, torch.float16, True, 512, 256, "host"),
+    (1, 4, 1, 700, 2100, 128, torch.bfloat16, True, 256, 768, "host"),     # GQA 4:1, bottom-right causal
+    (2, 2, 2, 900, 1100, 64, torch.float16, False, 384, 512, "host"),      # non-causal, ragged chunks
+    (1, 4, 2, 1024, 1024, 128, torch.float16, True, 256, 256, "mixed"),    # device inputs, host gradients
+    (1, 2, 2, 1536, 1536, 64, torch.bfloat16, True, 512, 512, "device"),   # forced chunks, resident
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}-{c[10]}")
+def test_chunked_backward_parity(case):
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, qc, kc, place = case
+    say("chunked backward", case)
+    q, k, v, do = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=6000 + Nq + Nk + D)
+    scale = 1.0 / math.sqrt(D)
+    rq, rk, rv = oracle.backward(q, k, v, do, causal=causal, scale=scale)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, return_lse=True)
+    if place == "host":
+        args = [t.cpu().pin_memory() for t in (qd, kd, vd, out, dod, lse)]
+    elif place == "mixed":
+        args = [qd.cpu().pin_memory(), kd.cpu().pin_memory(), vd, out, dod, lse]   # grads follow q and k
+    else:
+        args = [qd, kd, vd, out, dod, lse]
+    dq, dk, dv, info = cqsa().attention_backward(*args, is_causal=causal, grad_dtype=torch.float32, q_chunk=qc,
+                                                 kv_chunk=kc, return_info=True)
+    torch.cuda.synchronize()
+    assert info["q_chunk"] == qc and info["kv_chunk"] == kc and info["chunk_pairs"] >= 2
+    assert info["streamed"] == (0 if place == "device" else 1)
+    if place != "device":
+        assert not dq.is_cuda
+    errs = {n: rel_err(g, r) for n, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))}
+    say("errors", errs)
+    for n, e in errs.items():
+        assert e <= 8 * U[dtype], (n, e)
+    # against the single-pass backward on the same device inputs: equal up to the fp32 summation order
+    g1 = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=causal, grad_dtype=torch.float32)
+    for n, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), g1):
+        diff = float((a.cpu() - b.cpu()).abs().max()) / max(1.0, float(b.abs().max()))
+        assert diff <= 1e-5, (n, diff)
+
+
+def test_chunked_backward_budget_and_dtypes():
+    """A budget that forces the planner's own chunking, fp16 gradients on the host, and the budget
+    error when even the smallest chunks do not fit."""
+    B, H, N, D = 1, 4, 4096, 64
+    q, k, v, do = gen(B, H, H, N, N, D, torch.float16, seed=6100)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=True, return_lse=True)
+    host = [t.cpu().pin_memory() for t in (qd, kd, vd, out, dod, lse)]
+    # dq accumulator 4 MiB + statistics 128 KiB; 12 MB leaves room only for chunks below the full length
+    dq, dk, dv, info = cqsa().attention_backward(*host, is_causal=True, mem_budget=12_000_000, return_info=True)
+    assert dq.dtype == torch.float16 and not dq.is_cuda
+    assert info["n_q_chunks"] * info["n_kv_chunks"] > 1 and info["workspace_bytes"] <= 0.85 * 12_000_000
+    g1 = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=True)
+    for a, b in zip((dq, dk, dv), g1):
+        assert float((a.float() - b.float().cpu()).abs().max()) <= 2 * 2.0 ** -11 * max(1.0, float(b.float().abs().max()))
+    with pytest.raises(cqsa().CqsaError, match="BUDGET"):
+        cqsa().attention_backward(*host, is_causal=True, mem_budget=1_000_000)

@@ -3,14 +3,16 @@ records and waits a call would issue (nothing runs), and a happens-before analys
 and events checks that every two operations touching one device byte, one of them writing, are
 ordered; that every workspace read follows a write of it; and that everything is finished before the
 call returns.  Run over the grid schedule (forced Q and KV chunks, both merge modes, host and device
-operands, token-major host layouts, lse), single-pass KV splits and the quorum-set waves."""
+operands, token-major host layouts, lse), single-pass KV splits, the quorum-set waves and the
+chunked backward."""
 import re
 
 import pytest
 import torch
 
 GB = 1 << 30
-ADDR = {"q": 1 << 36, "k": 2 << 36, "v": 3 << 36, "out": 4 << 36}   # stand-in addresses, far apart
+ADDR = {"q": 1 << 36, "k": 2 << 36, "v": 3 << 36, "out": 4 << 36,   # stand-in addresses, far apart
+        "dout": 5 << 36, "lse": 6 << 36, "dq": 7 << 36, "dk": 8 << 36, "dv": 9 << 36}
 
 
 def m():
@@ -175,3 +177,31 @@ def test_trace_needs_explicit_placement_and_budget():
     with pytest.raises(m().CqsaError):
         m().schedule_trace((s, torch.float16, "host", 1 << 36), (s, torch.float16, "host", 2 << 36),
                            (s, torch.float16, "host", 3 << 36), True, 0, out=(s, torch.float16, "host", 4 << 36))
+
+
+BWD = [
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=1024),                       # all on the host
+    dict(Nq=4096, Nk=10240, q_chunk=1024, kv_chunk=4096, H=8, Hkv=2, D=128),     # GQA, bottom-right causal
+    dict(Nq=6000, Nk=6000, q_chunk=1536, kv_chunk=2560, causal=False),           # ragged chunks
+    dict(Nq=8192, Nk=8192, kv_chunk=2048, place="mixed"),                       # device q/k/v/out, host grads
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=2048, place="device"),        # resident, forced chunks
+    dict(Nq=1 << 20, Nk=1 << 20, H=8, budget=6 * 10**9),                          # the planner's own chunks
+]
+
+
+@pytest.mark.parametrize("kw", BWD, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items()))
+def test_chunked_backward_schedule_is_race_free(kw):
+    kw = dict(kw)
+    Nq, Nk, H = kw.pop("Nq"), kw.pop("Nk"), kw.pop("H", 4)
+    Hkv, D, causal = kw.pop("Hkv", H), kw.pop("D", 64), kw.pop("causal", True)
+    place, budget = kw.pop("place", "host"), kw.pop("budget", 4 * GB)
+    qside = "device" if place in ("mixed", "device") else "host"
+    grads = "device" if place == "device" else "host"
+    t = lambda name, shape, where: spec(name, shape, where)
+    qs, ks = (1, H, Nq, D), (1, Hkv, Nk, D)
+    text = m().backward_schedule_trace(
+        t("q", qs, qside), t("k", ks, qside), t("v", ks, qside), t("out", qs, qside), t("dout", qs, qside),
+        (qside, ADDR["lse"]), t("dq", qs, grads), t("dk", ks, grads), t("dv", ks, grads), causal, budget, **kw)
+    ops = check(text, streamed=True)
+    kinds = [o.kind for o in ops]
+    assert "bwd_stats" in kinds and "bwd_dq" in kinds and "bwd_dkdv" in kinds and "cast" in kinds
