@@ -43,6 +43,8 @@ def parse():
                     help="skip the 4M-token host-streamed case")
     ap.add_argument("--backward", action="store_true",
                     help="also time the backward (dQ, dK, dV) on the resident workload")
+    ap.add_argument("--streamed-backward", action="store_true",
+                    help="also run the 4M-token backward from pinned host memory (about two minutes)")
     ap.add_argument("--split-p", action="store_true",
                     help="also time the split-P precision mode on the resident workload and check it on sampled rows")
     ap.add_argument("--wave-tokens", type=int, default=None,
@@ -131,6 +133,34 @@ def run_streamed(cqsa, torch, synth, cqs=None) -> dict:
     if cqs:
         res["cqs"] = streamed_run(cqsa, torch, w, q, k, v, out, cqs)
     return res
+
+
+def run_streamed_backward(cqsa, torch, synth) -> dict:
+    """dQ, dK, dV of the 4M-token causal case from pinned host memory under the 16e9-byte budget (fp32
+    gradients on the host).  At this size the FP64 reference is out of reach, so the check is two
+    identities that hold at any size: sum_j dV_j = sum_i dO_i (each row of P sums to one) and
+    sum_j dK_j = 0 (each row of dS sums to zero)."""
+    w = synth.workload(3)
+    q, k, v, _ = synth.make_inputs(w, pin=True)
+    do = torch.empty(q.shape, dtype=q.dtype, pin_memory=True)
+    synth.fill_(do, seed=w.seed, tensor_id=synth.TENSOR_DO)
+    out, lse = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, return_lse=True)
+    t0 = time.perf_counter()
+    dq, dk, dv, info = cqsa.attention_backward(q, k, v, out, do, lse, is_causal=True, mem_budget=w.mem_budget,
+                                               grad_dtype=torch.float32, return_info=True)
+    wall = time.perf_counter() - t0
+    sdo = do.sum(2, dtype=torch.float64)
+    e_v = float((dv.sum(2, dtype=torch.float64) - sdo).abs().max() / sdo.abs().max())
+    e_k = float(dk.sum(2, dtype=torch.float64).abs().max() / dk.abs().sum(2, dtype=torch.float64).max())
+    print(f"[bench] streamed backward: {wall:.1f} s; sum dV vs sum dO {e_v:.1e}, sum dK {e_k:.1e}",
+          file=sys.stderr, flush=True)
+    return {"workload": w.name, "seconds": round(wall, 2), "tokens_per_s": round(w.B * w.Nq / wall, 1),
+            "tflops": round(2.5 * w.flops() / wall / 1e12, 2),
+            "note": "10 D FLOP per visible pair (2.5x the forward); fp32 gradients streamed back to pinned host memory",
+            "q_chunk": info["q_chunk"], "kv_chunk": info["kv_chunk"], "chunk_pairs": info["chunk_pairs"],
+            "h2d_bytes": info["h2d_bytes"], "h2d_seconds_busy": round(info["h2d_ms"] / 1e3, 3),
+            "d2h_bytes": info["d2h_bytes"], "workspace_bytes": info["workspace_bytes"],
+            "identity_sum_dv_rel": e_v, "identity_sum_dk_rel": e_k}
 
 
 def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
@@ -343,6 +373,8 @@ def main():
         line["backward"] = backward
     if args.streamed:
         line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
+    if args.streamed_backward:
+        line["streamed_backward_4m"] = run_streamed_backward(cqsa, torch, synth)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(line), flush=True)
