@@ -163,3 +163,18 @@ def test_plan_budget_monotone():
             if p["n_q_chunks"] == prev["n_q_chunks"]:
                 assert p["kv_chunk"] >= prev["kv_chunk"]
         prev = p
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/cqsa.h is a C header: it compiles as C99 with warnings as errors, with no HIP header."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    src.write_text('#include "cqsa.h"\nint main(void) { cqsa_options o; cqsa_plan_info i; (void)o; (void)i; '
+                   'return (int)cqsa_struct_size(0) * 0; }\n')
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
