@@ -485,3 +485,39 @@ def test_config5_softmax_stress_full_size():
     rows = sample_rows(2, 16, w.Nq, seed=7, n_random=2, edge=1, heads=(0, 9, 15))
     ref = reference(q, k, v, causal=False, scale=w.scale, rows=rows)
     say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 full"))
+
+
+def test_allocation_failure_is_reported_and_leaves_nothing_behind():
+    """With no caller workspace the library allocates its own; when the device cannot hold it the call
+    returns CQSA_ERR_OOM (no retry) and the free memory afterwards is what it was.  The device is
+    filled by a PyTorch allocation first, leaving 1 GiB, and the plan needs more than that."""
+    import ctypes
+    m = cqsa()
+    B, H, N, D = 1, 8, 1 << 20, 64
+    q = torch.zeros((B, H, N, D), dtype=torch.float16, pin_memory=True)
+    k = torch.zeros_like(q).pin_memory()
+    v = torch.zeros_like(q).pin_memory()
+    out = torch.empty_like(q).pin_memory()
+    opt = m._options()                                   # no workspace: the library calls hipMalloc
+    budget = 16 * 10**9
+    plan = m.plan(q, k, v, True, budget)
+    assert plan["workspace_bytes"] > 2 * (1 << 30)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    free0, _ = torch.cuda.mem_get_info()
+    hog = torch.empty(free0 - (1 << 30), dtype=torch.uint8, device=DEV)
+    try:
+        st = m._lib.cqsa_attention_ex(ctypes.byref(m._desc(q)), ctypes.byref(m._desc(k)), ctypes.byref(m._desc(v)),
+                                      1, ctypes.c_float(0.0), budget, ctypes.byref(m._desc(out)), None,
+                                      ctypes.byref(opt), None)
+        msg = m._lib.cqsa_last_error().decode()
+    finally:
+        del hog
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    assert st == -4 and "hipMalloc" in msg, (st, msg)
+    free1, _ = torch.cuda.mem_get_info()
+    assert abs(free1 - free0) <= 64 << 20, (free0, free1)
+    # and the same call succeeds once the memory is back
+    o2 = m.attention(q[:, :, :4096], k[:, :, :4096], v[:, :, :4096], is_causal=True, mem_budget=budget)
+    assert torch.isfinite(o2.float()).all()
