@@ -182,3 +182,26 @@ def test_chunked_backward_budget_and_dtypes():
         assert float((a.float() - b.float().cpu()).abs().max()) <= 2 * 2.0 ** -11 * max(1.0, float(b.float().abs().max()))
     with pytest.raises(cqsa().CqsaError, match="BUDGET"):
         cqsa().attention_backward(*host, is_causal=True, mem_budget=1_000_000)
+
+
+def test_chunked_backward_token_major_host_tensors():
+    """Pinned host inputs stored token-major ([B, N, H, D]) move as one block per batch entry and chunk
+    (the gradients are head-major pinned tensors here: each operand keeps its own layout)."""
+    B, Hq, Hkv, N, D = 2, 4, 2, 1100, 64
+    say("chunked backward, token-major host")
+    q, k, v, do = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=6200)
+    rq, rk, rv = oracle.backward(q, k, v, do, causal=True, scale=1.0 / math.sqrt(D))
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=True, return_lse=True)
+
+    def tm(t):   # [B, N, H, D] storage in pinned memory, viewed as [B, H, N, D]
+        x = torch.empty((t.shape[0], t.shape[2], t.shape[1], t.shape[3]), dtype=t.dtype, pin_memory=True)
+        x.copy_(t.transpose(1, 2))
+        return x.transpose(1, 2)
+
+    args = [tm(t.cpu()) for t in (qd, kd, vd, out, dod)] + [lse.cpu().pin_memory()]
+    dq, dk, dv = cqsa().attention_backward(*args, is_causal=True, grad_dtype=torch.float32, q_chunk=256, kv_chunk=512)
+    for n, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        assert not g.is_cuda
+        e = rel_err(g, r)
+        assert e <= 8 * U[torch.float16], (n, e)
