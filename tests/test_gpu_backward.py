@@ -166,8 +166,8 @@ def test_chunked_backward_parity(case):
 
 
 def test_chunked_backward_budget_and_dtypes():
-    """A budget that forces the planner's own chunking, fp16 gradients on the host, and the budget
-    error when even the smallest chunks do not fit."""
+    """A budget that forces the planner's own chunking, fp16 gradients on the host (bitwise the same on
+    a second call), and the budget error when even the smallest chunks do not fit."""
     B, H, N, D = 1, 4, 4096, 64
     q, k, v, do = gen(B, H, H, N, N, D, torch.float16, seed=6100)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
@@ -177,6 +177,8 @@ def test_chunked_backward_budget_and_dtypes():
     dq, dk, dv, info = cqsa().attention_backward(*host, is_causal=True, mem_budget=12_000_000, return_info=True)
     assert dq.dtype == torch.float16 and not dq.is_cuda
     assert info["n_q_chunks"] * info["n_kv_chunks"] > 1 and info["workspace_bytes"] <= 0.85 * 12_000_000
+    again = cqsa().attention_backward(*host, is_causal=True, mem_budget=12_000_000)
+    assert all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip((dq, dk, dv), again))  # bitwise
     g1 = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=True)
     for a, b in zip((dq, dk, dv), g1):
         assert float((a.float() - b.float().cpu()).abs().max()) <= 2 * 2.0 ** -11 * max(1.0, float(b.float().abs().max()))
