@@ -6,7 +6,8 @@ in one call: validate, plan, forward kernel with the in-kernel finalise).  Print
 
   value         algorithmic TFLOP/s = 4 * D * (visible (query, key) pairs) * B * H / step time
   roofline      the forward kernel against the dense fp16 matrix-core peak (2.5 PFLOP/s), timed
-                per launch with HIP events on the stream the kernel runs on
+                per launch with HIP events on the stream the kernel runs on; with the rates this
+                device measures (matrix cores, LDS, HBM copy) and the clock they ran at beside it
   cpu_baseline  the FP64 reference on this host's cores over a time-bounded sample of rows
   streamed_4m   4,194,304-token causal attention from pinned host memory under a 16e9-byte device
                 budget: tokens/s and H2D GB/s (the metric's second figure; --no-streamed skips it)
@@ -54,6 +55,8 @@ def parse():
                          "and the streamed case with --streamed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
+    ap.add_argument("--no-probe", dest="probe", action="store_false", default=True,
+                    help="skip the device probe (matrix-core, LDS and HBM rates with the clock they ran at)")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
                     "(default profiles/<forward kernel>_<workload>.md)")
     return ap.parse_args()
@@ -289,6 +292,27 @@ def main():
     print(f"[bench] step {ms_step:.3f} ms (events {ms_kernel:.3f} ms, min {min(per):.3f}) -> {value:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
+    measured = None
+    if args.probe:
+        # the rates this device delivers, measured after the timed steps so that they do not warm it
+        # first: the fraction of the measured matrix-core rate is the kernel's efficiency at the clock
+        # the chip holds, which the datasheet peak (2.4 GHz) does not reflect
+        pr = cqsa.probe_device(copy_bytes=1 << 30, repeats=5)
+        measured = {"mfma_f16_tflops": round(pr["mfma_f16_tflops"], 1),
+                    "mfma_clock_ghz": round(pr["mfma_clock_ghz"], 3),
+                    "mfma_flop_per_clk_per_cu": round(pr["mfma_flop_per_clk_per_cu"] or 0.0, 1),
+                    "frac_of_measured_mfma": round(achieved / pr["mfma_f16_tflops"], 4),
+                    "lds_read_tbs": round(pr["lds_read_tbs"], 2),
+                    "lds_bytes_per_clk_per_cu": round(pr["lds_bytes_per_clk_per_cu"] or 0.0, 1),
+                    "hbm_copy_gbs": round(pr["hbm_copy_gbs"], 1),
+                    "compute_units": pr["compute_units"],
+                    "source": "cqsa_probe_device: back-to-back v_mfma_f32_32x32x16_f16, ds_read_b128 and a "
+                              "1 GiB copy on this device, fastest of 5 launches each"}
+        print(f"[bench] probe: MFMA {measured['mfma_f16_tflops']} TFLOP/s at {measured['mfma_clock_ghz']} GHz "
+              f"({measured['mfma_flop_per_clk_per_cu']} FLOP/clk/CU), LDS {measured['lds_read_tbs']} TB/s "
+              f"({measured['lds_bytes_per_clk_per_cu']} B/clk/CU), HBM copy {measured['hbm_copy_gbs']} GB/s",
+              file=sys.stderr, flush=True)
+
     cqs_resident = None
     if args.cqs:
         for _ in range(2):
@@ -383,6 +407,8 @@ def main():
                      "kernel_ms": round(ms_kernel, 4),
                      "launches_per_step": info["kernel_launches"]},
     }
+    if measured:
+        line["roofline"]["measured_on_this_device"] = measured
     if cqs_resident:
         line["cqs_resident"] = cqs_resident
     if split_p:

@@ -59,6 +59,14 @@ class CqsaPlanInfo(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class CqsaProbeResult(ctypes.Structure):
+    _fields_ = [("mfma_f16_flop_per_s", ctypes.c_double), ("mfma_clock_hz", ctypes.c_double),
+                ("lds_read_bytes_per_s", ctypes.c_double), ("lds_clock_hz", ctypes.c_double),
+                ("hbm_copy_bytes_per_s", ctypes.c_double), ("mfma_seconds", ctypes.c_double),
+                ("lds_seconds", ctypes.c_double), ("copy_seconds", ctypes.c_double),
+                ("compute_units", ctypes.c_int32), ("wall_clock_khz", ctypes.c_int32)]
+
+
 class CqsaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"cqsa {_STATUS.get(status, status)}: {message}")
@@ -68,6 +76,23 @@ class CqsaError(RuntimeError):
 def fwd_kernel_name(head_dim: int, precision: int = 0) -> str:
     """The forward kernel (name and shape) a call with this head dim and precision launches."""
     return _lib.cqsa_fwd_kernel_name(int(head_dim), int(precision)).decode()
+
+
+def probe_device(copy_bytes: int = 1 << 30, repeats: int = 5) -> dict:
+    """Rates of the current device measured by cqsa_probe_device: dense fp16 matrix-core FLOP/s,
+    LDS read bytes/s and HBM copy bytes/s, with the shader clock of the matrix and LDS runs and the
+    per-clock, per-compute-unit figures derived from them."""
+    r = CqsaProbeResult()
+    _check(_lib.cqsa_probe_device(int(copy_bytes), int(repeats), ctypes.byref(r)))
+    d = {name: getattr(r, name) for name, _ in r._fields_}
+    cu = max(1, r.compute_units)
+    d["mfma_f16_tflops"] = r.mfma_f16_flop_per_s / 1e12
+    d["mfma_clock_ghz"] = r.mfma_clock_hz / 1e9
+    d["mfma_flop_per_clk_per_cu"] = r.mfma_f16_flop_per_s / (r.mfma_clock_hz * cu) if r.mfma_clock_hz else None
+    d["lds_read_tbs"] = r.lds_read_bytes_per_s / 1e12
+    d["lds_bytes_per_clk_per_cu"] = r.lds_read_bytes_per_s / (r.lds_clock_hz * cu) if r.lds_clock_hz else None
+    d["hbm_copy_gbs"] = r.hbm_copy_bytes_per_s / 1e9
+    return d
 
 
 def library_path() -> str:
@@ -123,7 +148,9 @@ def _load_library():
     lib.cqsa_cqs_assign.restype = ctypes.c_int
     lib.cqsa_cqs_default_set.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.cqsa_cqs_default_set.restype = ctypes.c_int32
-    for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo)):
+    lib.cqsa_probe_device.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(CqsaProbeResult)]
+    lib.cqsa_probe_device.restype = ctypes.c_int
+    for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo, CqsaProbeResult)):
         if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"{cls.__name__} layout differs from the built library")
     return lib

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcqsa.so")
-SOURCES = [os.path.join(CSRC, "cqsa_kernels.hip"), os.path.join(CSRC, "cqsa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "cqsa_kernels.hip"), os.path.join(CSRC, "cqsa_probe.hip"), os.path.join(CSRC, "cqsa_api.cpp")]
 
 # Packed fp32 instructions are disabled for all device code; hipcc's host pass warns that it does
 # not know the feature, which is harmless.

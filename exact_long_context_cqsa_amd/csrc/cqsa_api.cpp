@@ -1682,6 +1682,7 @@ uint64_t cqsa_struct_size(int32_t which) {
         case 0: return sizeof(cqsa_tensor);
         case 1: return sizeof(cqsa_options);
         case 2: return sizeof(cqsa_plan_info);
+        case 3: return sizeof(cqsa_probe_result);
         default: return 0;
     }
 }
@@ -2622,6 +2623,101 @@ cqsa_status cqsa_finalize(const float* o, const float* ml, cqsa_tensor* out, flo
     m.l_sb = ov.H * ov.N;
     m.l_sh = ov.N;
     return run_merge(m, static_cast<hipStream_t>(stream));
+}
+
+cqsa_status cqsa_probe_device(uint64_t copy_bytes, int32_t repeats, cqsa_probe_result* out) {
+    g_err.clear();
+    if (!out) return fail(CQSA_ERR_INVALID, "out is NULL");
+    if (repeats < 1 || repeats > 100) return fail(CQSA_ERR_INVALID, "repeats (%d) must be in [1, 100]", repeats);
+    if (copy_bytes < (1ull << 20) || copy_bytes > (1ull << 34) || copy_bytes % 16)
+        return fail(CQSA_ERR_INVALID, "copy_bytes (%llu) must be a multiple of 16 in [2^20, 2^34]",
+                    (unsigned long long)copy_bytes);
+    *out = cqsa_probe_result{};
+    int dev = 0, cus = 0, wall_khz = 0;
+    CQSA_HIP(hipGetDevice(&dev));
+    CQSA_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    CQSA_HIP(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev));
+    if (cus < 1 || wall_khz < 1) return fail(CQSA_ERR_HIP, "device reports %d compute units, wall clock %d kHz", cus, wall_khz);
+    // 4-wave workgroups: eight per compute unit for the matrix cores (not all resident at once; the
+    // rate is taken over the whole launch), two for LDS (32 KiB each)
+    const int mfma_blocks = 8 * cus, lds_blocks = 2 * cus;
+    const int waves = 4 * mfma_blocks;             // the larger of the two launches
+    constexpr int kMfmaIters = 4096, kLdsIters = 32768;
+
+    struct Res {   // everything the probe holds, released on every return
+        void *sink = nullptr, *src = nullptr, *dst = nullptr;
+        uint64_t* clk = nullptr;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        ~Res() {
+            if (e0) (void)hipEventDestroy(e0);
+            if (e1) (void)hipEventDestroy(e1);
+            for (void* p : {sink, src, dst, static_cast<void*>(clk)})
+                if (p) (void)hipFree(p);
+        }
+    } r;
+    auto alloc = [](void** p, size_t bytes) -> cqsa_status {
+        const hipError_t e = hipMalloc(p, bytes);
+        if (e == hipSuccess) return CQSA_OK;
+        (void)hipGetLastError();
+        *p = nullptr;
+        return fail(e == hipErrorOutOfMemory ? CQSA_ERR_OOM : CQSA_ERR_HIP, "hipMalloc of %zu bytes failed: %s", bytes,
+                    hipGetErrorString(e));
+    };
+    CQSA_TRY(alloc(&r.sink, (size_t)mfma_blocks * 256 * 4));
+    CQSA_TRY(alloc(reinterpret_cast<void**>(&r.clk), (size_t)waves * 2 * sizeof(uint64_t)));
+    CQSA_TRY(alloc(&r.src, copy_bytes));
+    CQSA_TRY(alloc(&r.dst, copy_bytes));
+    CQSA_HIP(hipMemset(r.src, 0x3c, copy_bytes));
+    CQSA_HIP(hipEventCreate(&r.e0));
+    CQSA_HIP(hipEventCreate(&r.e1));
+    std::vector<uint64_t> clk((size_t)waves * 2);
+
+    // launch(0) untimed, then `repeats` timed launches; returns the fastest time and the clock of that
+    // launch (0 when the kernel records none)
+    auto run = [&](auto&& launch, int clocked_waves, double* secs, double* hz) -> cqsa_status {
+        CQSA_HIP(launch());
+        CQSA_HIP(hipDeviceSynchronize());
+        double best = 0.0, best_hz = 0.0;
+        for (int i = 0; i < repeats; ++i) {
+            CQSA_HIP(hipEventRecord(r.e0, nullptr));
+            CQSA_HIP(launch());
+            CQSA_HIP(hipEventRecord(r.e1, nullptr));
+            CQSA_HIP(hipEventSynchronize(r.e1));
+            float ms = 0.f;
+            CQSA_HIP(hipEventElapsedTime(&ms, r.e0, r.e1));
+            double f = 0.0;
+            if (clocked_waves > 0) {
+                CQSA_HIP(hipMemcpy(clk.data(), r.clk, (size_t)clocked_waves * 2 * sizeof(uint64_t),
+                                   hipMemcpyDeviceToHost));
+                int n = 0;
+                for (int w = 0; w < clocked_waves; ++w)
+                    if (clk[2 * w + 1] > 0) {
+                        f += (double)clk[2 * w] / (double)clk[2 * w + 1];
+                        ++n;
+                    }
+                f = n ? f / n * wall_khz * 1e3 : 0.0;
+            }
+            if (i == 0 || ms * 1e-3 < best) {
+                best = ms * 1e-3;
+                best_hz = f;
+            }
+        }
+        *secs = best;
+        if (hz) *hz = best_hz;
+        return CQSA_OK;
+    };
+    CQSA_TRY(run([&] { return launch_probe_mfma(mfma_blocks, static_cast<float*>(r.sink), r.clk, kMfmaIters, nullptr); },
+                 4 * mfma_blocks, &out->mfma_seconds, &out->mfma_clock_hz));
+    CQSA_TRY(run([&] { return launch_probe_lds(lds_blocks, static_cast<uint32_t*>(r.sink), r.clk, kLdsIters, nullptr); },
+                 4 * lds_blocks, &out->lds_seconds, &out->lds_clock_hz));
+    CQSA_TRY(run([&] { return launch_probe_copy(16 * cus, r.src, r.dst, (int64_t)copy_bytes, nullptr); }, 0,
+                 &out->copy_seconds, nullptr));
+    out->mfma_f16_flop_per_s = 4.0 * mfma_blocks * kMfmaIters * 4 * 32768.0 / out->mfma_seconds;
+    out->lds_read_bytes_per_s = 4.0 * lds_blocks * kLdsIters * 8 * 1024.0 / out->lds_seconds;
+    out->hbm_copy_bytes_per_s = 2.0 * (double)copy_bytes / out->copy_seconds;
+    out->compute_units = cus;
+    out->wall_clock_khz = wall_khz;
+    return CQSA_OK;
 }
 
 }  // extern "C"

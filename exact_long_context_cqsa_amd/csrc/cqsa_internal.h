@@ -176,4 +176,12 @@ hipError_t launch_wave(const FwdArgs& a, const WaveTable& t, int blocks, int D, 
 // Query rows per workgroup of the wave kernel.
 int wave_block_m(int D, int p_split);
 
+// Rate probes (cqsa_probe.hip), 256-thread workgroups of four waves.  The matrix and LDS probes
+// write one float / uint32 per thread to sink (blocks * 256 of them) and, per wave w, the shader
+// cycles and wall-clock ticks of its loop to clk[2 w], clk[2 w + 1] (blocks * 8 uint64 in all).
+hipError_t launch_probe_mfma(int blocks, float* sink, uint64_t* clk, int iters, hipStream_t stream);
+hipError_t launch_probe_lds(int blocks, uint32_t* sink, uint64_t* clk, int iters, hipStream_t stream);
+// dst = src over bytes (a multiple of 16; both 16-byte aligned).
+hipError_t launch_probe_copy(int blocks, const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
 }  // namespace cqsa

@@ -301,7 +301,7 @@ const char* cqsa_last_error(void);
 int32_t cqsa_version(void);
 
 /* sizeof of the ABI structs, for bindings to check their layout:
- * 0 = cqsa_tensor, 1 = cqsa_options, 2 = cqsa_plan_info; 0 for other values. */
+ * 0 = cqsa_tensor, 1 = cqsa_options, 2 = cqsa_plan_info, 3 = cqsa_probe_result; 0 for other values. */
 uint64_t cqsa_struct_size(int32_t which);
 
 /*
@@ -343,6 +343,36 @@ int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l);
  * (0 or unset = the default kernel), read at every launch.  The string is static; no HIP call is
  * made. */
 const char* cqsa_fwd_kernel_name(int64_t head_dim, int32_t precision);
+
+/*
+ * Device probe: the rates the kernels are measured against, measured on the current device, each with
+ * the shader clock it ran at.  Three kernels, each launched once untimed and then `repeats` times
+ * between hip events on the null stream (the fastest launch is reported):
+ *  - matrix cores: back-to-back v_mfma_f32_32x32x16_f16 with operands in registers, four independent
+ *    accumulator chains per wave, eight 4-wave workgroups per compute unit;
+ *  - LDS: ds_read_b128 at bank-conflict-free addresses (consecutive lanes on consecutive 16-byte
+ *    granules), two 4-wave workgroups per compute unit;
+ *  - HBM: a copy kernel over copy_bytes (the rate counts the bytes read plus the bytes written).
+ * The clock is the mean over the waves of the launch of (shader cycles / wall-clock ticks) across
+ * the wave's loop, times the wall-clock rate (hipDeviceAttributeWallClockRate).
+ * copy_bytes: a multiple of 16 in [2^20, 2^34]; repeats in [1, 100].  Allocates 2 copy_bytes plus a
+ * few KiB of device memory and frees them before returning (CQSA_ERR_OOM if that fails); synchronous.
+ * CQSA_ERR_INVALID for bad arguments or a NULL result (checked before any HIP call), CQSA_ERR_HIP for
+ * a failing HIP call.  Not part of the attention path: bench and profile tooling use it to state the
+ * peak each figure is a fraction of.
+ */
+typedef struct {
+    double mfma_f16_flop_per_s;    /* dense fp16 matrix-core FLOP/s */
+    double mfma_clock_hz;          /* shader clock during that launch */
+    double lds_read_bytes_per_s;   /* LDS bytes read per second, all compute units */
+    double lds_clock_hz;
+    double hbm_copy_bytes_per_s;   /* (read + written) bytes per second */
+    double mfma_seconds, lds_seconds, copy_seconds;   /* the timed launches (fastest of `repeats`) */
+    int32_t compute_units;
+    int32_t wall_clock_khz;
+} cqsa_probe_result;
+
+cqsa_status cqsa_probe_device(uint64_t copy_bytes, int32_t repeats, cqsa_probe_result* out);
 
 #ifdef __cplusplus
 }

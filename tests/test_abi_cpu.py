@@ -60,7 +60,19 @@ def test_struct_layout_and_version():
     assert [f for f, _ in m.CqsaOptions._fields_][-3:] == ["precision", "cqs_set", "wave_tokens"]
     assert [f for f, _ in m.CqsaPlanInfo._fields_][-3:] == ["cqs_waves", "reserved0", "wave_tokens"]
     assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo) == 152
+    assert lib.cqsa_struct_size(3) == ctypes.sizeof(m.CqsaProbeResult) == 72
     assert lib.cqsa_struct_size(7) == 0
+
+
+def test_probe_rejects_bad_arguments_before_any_hip_call():
+    """cqsa_probe_device validates its arguments first, so these fail the same way with or without a
+    GPU (a HIP call here, with no device, would give CQSA_ERR_HIP instead)."""
+    import exact_long_context_cqsa_amd as m
+    lib, r = m._lib, m.CqsaProbeResult()
+    for copy_bytes, repeats in [(1 << 30, 0), (1 << 30, 101), (1000, 5), ((1 << 20) + 8, 5), ((1 << 34) + 16, 5)]:
+        assert lib.cqsa_probe_device(copy_bytes, repeats, ctypes.byref(r)) == -1, (copy_bytes, repeats)
+        assert lib.cqsa_last_error()
+    assert lib.cqsa_probe_device(1 << 30, 5, None) == -1
 
 
 def test_missing_library_fails_loudly(tmp_path):
