@@ -55,6 +55,8 @@ def parse():
                          "and the streamed case with --streamed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
+    ap.add_argument("--merge", action="store_true",
+                    help="also time the exact merge and the finalize (HBM-bound steps) at 8.4M rows")
     ap.add_argument("--no-probe", dest="probe", action="store_false", default=True,
                     help="skip the device probe (matrix-core, LDS and HBM rates with the clock they ran at)")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
@@ -135,6 +137,64 @@ def run_streamed(cqsa, torch, synth, cqs=None) -> dict:
     res = streamed_run(cqsa, torch, w, q, k, v, out, None)
     if cqs:
         res["cqs"] = streamed_run(cqsa, torch, w, q, k, v, out, cqs)
+    return res
+
+
+def run_merge(cqsa, torch, steps: int) -> dict:
+    """The exact log-sum-exp merge (step a5) and the finalize (step a6) at the softmax-stress workload's
+    row count (B=2, Hq=16, Nq=262144, D=128: 8.4M rows), the unit its 16 KV chunks repeat: one two-way
+    fold of fp32 partial triples, then the normalisation into bf16 with lse.  Both are HBM-bound.
+    Algorithmic bytes: a J-way merge reads J (D + 2) 4 and writes (D + 2) 4 bytes per row; the finalize
+    reads (D + 2) 4 and writes 2 D + 4.  Also a 16-way merge at 1/8 of the rows.  Partials are seeded
+    random (O ~ N(0, 1), m ~ N(0, 16), l ~ U[1, 101]); times are HIP events on the current stream."""
+    dev = "cuda:0"
+    B, Hq, N, D = 2, 16, 262144, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(0xC05A0005)
+
+    def part(n):
+        o = torch.randn(B, Hq, n, D, device=dev, generator=g)
+        ml = torch.empty(B, Hq, n, 2, device=dev)
+        ml[..., 0] = torch.randn(B, Hq, n, device=dev, generator=g) * 4.0
+        ml[..., 1] = torch.rand(B, Hq, n, device=dev, generator=g) * 100.0 + 1.0
+        return o, ml
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        st = torch.cuda.current_stream()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            e[2 * i].record(st)
+            fn()
+            e[2 * i + 1].record(st)
+        torch.cuda.synchronize()
+        return sum(e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(reps)) / reps
+
+    reps = max(3, steps // 2)
+    res = {"workload": f"merge_b{B}_h{Hq}_n{N}_d{D}_f32", "rows": B * Hq * N, "peak_gbs": PEAK_HBM_GBS}
+    parts = [part(N), part(N)]
+    out = (torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1]))
+    ms = timed(lambda: cqsa.lse_merge(parts, out=out), reps)
+    nbytes = 3 * B * Hq * N * (D + 2) * 4
+    res["merge2"] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(nbytes / ms / 1e6, 1),
+                     "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    ms = timed(lambda: cqsa.finalize(out[0], out[1], out_dtype=torch.bfloat16), reps)
+    nbytes = B * Hq * N * ((D + 2) * 4 + 2 * D + 4)
+    res["finalize_bf16"] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(nbytes / ms / 1e6, 1),
+                            "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del parts, out
+    n16 = N // 8
+    parts = [part(n16) for _ in range(16)]
+    out = (torch.empty_like(parts[0][0]), torch.empty_like(parts[0][1]))
+    ms = timed(lambda: cqsa.lse_merge(parts, out=out), reps)
+    nbytes = 17 * B * Hq * n16 * (D + 2) * 4
+    res["merge16_rows_div8"] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(nbytes / ms / 1e6, 1),
+                                "frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    del parts, out
+    torch.cuda.empty_cache()
+    print(f"[bench] merge: 2-way {res['merge2']['gbs']} GB/s, finalize {res['finalize_bf16']['gbs']} GB/s, "
+          f"16-way {res['merge16_rows_div8']['gbs']} GB/s", file=sys.stderr, flush=True)
     return res
 
 
@@ -417,6 +477,8 @@ def main():
         line["backward"] = backward
     if args.streamed:
         line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
+    if args.merge:
+        line["merge"] = run_merge(cqsa, torch, args.steps)
     if args.streamed_backward:
         line["streamed_backward_4m"] = run_streamed_backward(cqsa, torch, synth)
     if not args.no_cpu_baseline:

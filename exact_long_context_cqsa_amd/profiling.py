@@ -36,49 +36,72 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def trace_stats(path: str, kernel: str) -> dict:
+def _grid(r: dict) -> int:
+    if r.get("Grid_Size"):
+        return int(r["Grid_Size"])
+    return int(r.get("Grid_Size_X") or 1) * int(r.get("Grid_Size_Y") or 1) * int(r.get("Grid_Size_Z") or 1)
+
+
+def _pick(rows: list, kernel: str, grid: int | None, select: str | None) -> list:
+    """Dispatches of the kernel (name contains `kernel`; grid size `grid` if given), in dispatch order,
+    then the python slice `select` ("a:b") of them if given: a way to single out one phase of a run
+    whose phases launch the same kernel."""
+    got = [r for r in rows if kernel in r.get("Kernel_Name", "") and (grid is None or _grid(r) == grid)]
+    got.sort(key=lambda r: int(r.get("Dispatch_Id") or 0))
+    if select:
+        a, _, b = select.partition(":")
+        got = got[int(a) if a else None:int(b) if b else None]
+    return got
+
+
+def trace_stats(path: str, kernel: str, grid: int | None = None, select: str | None = None) -> dict:
     durs = []
     name = None
-    for r in _rows(path):
-        kn = r.get("Kernel_Name", "")
-        if kernel in kn:
-            durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-            name = kn
+    for r in _pick(_rows(path), kernel, grid, select):
+        durs.append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        name = r["Kernel_Name"]
     if not durs:
         raise SystemExit(f"no dispatch of a kernel matching {kernel!r} in {path}")
     return {"kernel_name": name, "calls": len(durs), "avg_ns": statistics.mean(durs), "min_ns": min(durs),
             "max_ns": max(durs), "median_ns": statistics.median(durs)}
 
 
-def counter_per_dispatch(path: str, counter: str, kernel: str) -> tuple[float, float]:
-    """(mean value for the attention kernel's dispatches, value for the 1 GiB copy dispatch)."""
-    kvals, cvals = [], []
-    for r in _rows(path):
-        if r["Counter_Name"] != counter:
-            continue
-        kn = r.get("Kernel_Name", "")
-        v = float(r["Counter_Value"])
-        if kernel in kn:
-            kvals.append(v)
-        elif int(r.get("Grid_Size", "0") or 0) > 0 and ("copy" in kn.lower() or "elementwise" in kn.lower()):
-            cvals.append(v)
+def counter_per_dispatch(path: str, counter: str, kernel: str, grid: int | None = None,
+                         select: str | None = None) -> tuple[float, float]:
+    """(mean value for the measured kernel's dispatches, value for the 1 GiB copy dispatch)."""
+    rows = [r for r in _rows(path) if r["Counter_Name"] == counter]
+    kvals = [float(r["Counter_Value"]) for r in _pick(rows, kernel, grid, select)]
+    # the calibration copy: the runtime's device-to-device copy kernel; a run without one (a copy that
+    # torch ran as an elementwise kernel) falls back to the largest elementwise dispatch
+    def copies(words):
+        return [float(r["Counter_Value"]) for r in rows
+                if kernel not in r.get("Kernel_Name", "") and int(r.get("Grid_Size", "0") or 0) > 0
+                and any(w in r.get("Kernel_Name", "").lower() for w in words)]
+    cvals = copies(("copybuffer",)) or copies(("copy", "elementwise"))
     if not kvals or not cvals:
         raise SystemExit(f"{counter}: kernel or copy dispatch missing in {path}")
     return statistics.mean(kvals), max(cvals)
 
 
 def summarise(args) -> str:
-    ts = trace_stats(args.trace, args.kernel)
-    fk, fc = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel)
-    wk, wc = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel)
+    grid, select = getattr(args, "grid", None), getattr(args, "select", None)
+    ts = trace_stats(args.trace, args.kernel, grid, select)
+    fk, fc = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel, grid, select)
+    wk, wc = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel, grid, select)
     f_scale = COPY_BYTES / (fc * 1024.0)     # the copy reads 1 GiB
     w_scale = COPY_BYTES / (wc * 1024.0)     # and writes 1 GiB
     fetch_b = fk * 1024.0 * f_scale
     write_b = wk * 1024.0 * w_scale
+    sel = []
+    if grid or select:
+        sel.append(f"dispatches: grid size {grid}" if grid else "dispatches: every grid size")
+        if select:
+            sel.append(f"selected: [{select}] of the matching dispatches, in dispatch order")
     lines = [
         f"# {args.name}",
         "",
         f"kernel: `{ts['kernel_name']}`",
+        *sel,
         f"kernel_source_sha256: {kernel_source_sha256()}",
         "",
         "## Commands",
@@ -176,6 +199,8 @@ def main():
     ap.add_argument("--h2d-stream", type=int, default=1)
     ap.add_argument("--h2d-bytes", type=int, default=0)
     ap.add_argument("--link-gbs", type=float, default=0.0)
+    ap.add_argument("--grid", type=int, default=None, help="only dispatches of this grid size (threads)")
+    ap.add_argument("--select", default=None, help="python slice a:b of the matching dispatches")
     ap.add_argument("--command", required=True)
     ap.add_argument("--note", default="")
     ap.add_argument("--out", default=None)

@@ -41,6 +41,26 @@ def test_kernel_summary_scales_counters_by_the_copy(tmp_path):
     assert "## Notes" in text and "a note" in text
 
 
+def test_dispatch_selection_by_grid_and_slice(tmp_path):
+    """Several phases launch one kernel: --grid keeps one launch shape, --select a slice of the matching
+    dispatches in dispatch order (the trace and the counter files alike)."""
+    hdr_t = ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+             "End_Timestamp"]
+    rows_t = [[1, "merge_kernel<128>", 4096, 1, 1, 0, 100], [2, "merge_kernel<128>", 4096, 1, 1, 200, 400],
+              [3, "merge_kernel<128>", 4096, 1, 1, 500, 1100], [4, "merge_kernel<128>", 512, 1, 1, 2000, 2010]]
+    trace = _csv(tmp_path / "kt.csv", hdr_t, list(reversed(rows_t)))
+    hdr_c = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    cnt = [[i, "merge_kernel<128>", g, "FETCH_SIZE", float(10 * i)] for i, g in ((1, 4096), (2, 4096), (3, 4096), (4, 512))]
+    cnt.append([5, "__amd_rocclr_copyBuffer", 1024, "FETCH_SIZE", 524288.0])
+    fetch = _csv(tmp_path / "f.csv", hdr_c, cnt)
+    assert profiling.trace_stats(trace, "merge_kernel", grid=4096)["calls"] == 3
+    st = profiling.trace_stats(trace, "merge_kernel", grid=4096, select="1:3")
+    assert st["calls"] == 2 and st["avg_ns"] == 400 and st["min_ns"] == 200
+    assert profiling.trace_stats(trace, "merge_kernel", grid=512)["avg_ns"] == 10
+    assert profiling.counter_per_dispatch(fetch, "FETCH_SIZE", "merge_kernel", 4096, "1:3") == (25.0, 524288.0)
+    assert profiling.counter_per_dispatch(fetch, "FETCH_SIZE", "merge_kernel", 512) == (40.0, 524288.0)
+
+
 def test_copy_summary(tmp_path):
     hdr = ["Kind", "Direction", "Stream_Id", "Source_Agent_Id", "Destination_Agent_Id", "Correlation_Id",
            "Start_Timestamp", "End_Timestamp"]
