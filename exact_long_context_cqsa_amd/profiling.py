@@ -131,6 +131,58 @@ def summarise(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+def summarise_mfma(args) -> str:
+    """Matrix-core counters of one kernel from a run with --kernel-trace and
+    --pmc MfmaFlopsF16 MfmaFlopsBF16 MfmaUtil GRBM_GUI_ACTIVE: the FLOPs the MFMA instructions executed
+    per launch (against the algorithmic count), the share of SIMD cycles the matrix cores were busy,
+    and the clock the launch ran at (GRBM_GUI_ACTIVE summed over the XCDs, per XCD, over the launch's
+    duration in the same run)."""
+    grid, select = getattr(args, "grid", None), getattr(args, "select", None)
+    durs = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in _pick(_rows(args.trace), args.kernel, grid, select)}
+    per = {}
+    for r in _pick(_rows(args.counters), args.kernel, grid, None):
+        d = int(r["Dispatch_Id"])
+        if d in durs:
+            per.setdefault(d, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no counter rows for the selected dispatches of {args.kernel!r}")
+    mean = lambda key: statistics.mean(v.get(key, 0.0) for v in per.values())
+    flop = mean("MfmaFlopsF16") + mean("MfmaFlopsBF16")
+    util = mean("MfmaUtil")
+    cyc = mean("GRBM_GUI_ACTIVE") / args.xcds
+    avg_ns = statistics.mean(durs[d] for d in per)
+    name = next(r["Kernel_Name"] for r in _pick(_rows(args.trace), args.kernel, grid, select))
+    lines = [
+        f"# {args.name}",
+        "",
+        f"kernel: `{name}`",
+        f"kernel_source_sha256: {kernel_source_sha256()}",
+        "",
+        "## Commands",
+        "",
+        "```",
+        args.command.strip(),
+        "```",
+        "",
+        "## Matrix-core counters (rocprofv3 --kernel-trace --pmc MfmaFlopsF16 MfmaFlopsBF16 MfmaUtil GRBM_GUI_ACTIVE)",
+        "",
+        f"calls: {len(per)}",
+        f"avg_ns: {avg_ns:.0f}",
+        f"mfma_flop_per_launch: {flop:.4e}",
+        f"algorithmic_flop_per_launch: {args.algorithmic_flop:.4e}",
+        f"executed_over_algorithmic: {flop / args.algorithmic_flop:.4f}",
+        f"mfma_util_pct: {util:.1f}",
+        f"gui_active_cycles_per_xcd: {cyc:.0f}",
+        f"clock_ghz: {cyc / avg_ns:.3f}",
+        f"algorithmic_tflops_in_this_run: {args.algorithmic_flop / avg_ns / 1e3:.1f}",
+        f"executed_tflops_in_this_run: {flop / avg_ns / 1e3:.1f}",
+    ]
+    if args.note:
+        lines += ["", "## Notes", "", args.note.strip()]
+    return "\n".join(lines) + "\n"
+
+
 def summarise_copies(args) -> str:
     """Host-to-device streaming from a rocprofv3 --memory-copy-trace run.  The trace gives each copy's
     stream and duration but not its size, so the bytes are the plan's (cqsa_plan_info.h2d_bytes, as the
@@ -195,6 +247,9 @@ def main():
     ap.add_argument("--trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
+    ap.add_argument("--counters", help="counter_collection.csv with the matrix-core counters: summarise those")
+    ap.add_argument("--algorithmic-flop", type=float, default=0.0, help="algorithmic FLOP per launch (--counters)")
+    ap.add_argument("--xcds", type=int, default=8, help="XCDs GRBM_GUI_ACTIVE is summed over (--counters)")
     ap.add_argument("--copy-trace", help="memory_copy_trace.csv: summarise the H2D streaming instead")
     ap.add_argument("--h2d-stream", type=int, default=1)
     ap.add_argument("--h2d-bytes", type=int, default=0)
@@ -205,7 +260,11 @@ def main():
     ap.add_argument("--note", default="")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
-    if args.copy_trace:
+    if args.counters:
+        if not (args.kernel and args.trace and args.algorithmic_flop > 0):
+            ap.error("--counters needs --kernel, --trace and --algorithmic-flop")
+        text = summarise_mfma(args)
+    elif args.copy_trace:
         if args.h2d_bytes <= 0 or args.link_gbs <= 0:
             ap.error("--copy-trace needs --h2d-bytes and --link-gbs")
         text = summarise_copies(args)

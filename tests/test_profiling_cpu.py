@@ -61,6 +61,32 @@ def test_dispatch_selection_by_grid_and_slice(tmp_path):
     assert profiling.counter_per_dispatch(fetch, "FETCH_SIZE", "merge_kernel", 512) == (40.0, 524288.0)
 
 
+def test_mfma_counter_summary(tmp_path):
+    """Executed MFMA FLOPs per launch against the algorithmic count, utilisation, and the clock from
+    GRBM_GUI_ACTIVE (summed over 8 XCDs) over the launch's own duration in the same run."""
+    hdr_t = ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+             "End_Timestamp"]
+    trace = _csv(tmp_path / "kt.csv", hdr_t, [[1, "void fwd_k<64>()", 256, 1, 1, 0, 1000],
+                                              [2, "void fwd_k<64>()", 256, 1, 1, 5000, 7000],
+                                              [3, "other", 64, 1, 1, 8000, 8100]])
+    hdr_c = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    rows = []
+    for d, flop, util, gui in ((1, 3.0e9, 40.0, 8 * 2000.0), (2, 5.0e9, 50.0, 8 * 4000.0)):
+        rows += [[d, "void fwd_k<64>()", 256, "MfmaFlopsF16", flop], [d, "void fwd_k<64>()", 256, "MfmaFlopsBF16", 0.0],
+                 [d, "void fwd_k<64>()", 256, "MfmaUtil", util], [d, "void fwd_k<64>()", 256, "GRBM_GUI_ACTIVE", gui]]
+    rows.append([3, "other", 64, "MfmaFlopsF16", 1e12])
+    counters = _csv(tmp_path / "c.csv", hdr_c, rows)
+    args = argparse.Namespace(name="fwd_k_counters", kernel="fwd_k<", trace=trace, counters=counters,
+                              algorithmic_flop=3.2e9, xcds=8, grid=None, select=None, command="rocprofv3 ...",
+                              note="")
+    out = tmp_path / "m.md"
+    out.write_text(profiling.summarise_mfma(args))
+    p = profiling.read_profile(str(out))
+    assert p["calls"] == "2" and float(p["avg_ns"]) == 1500.0
+    assert float(p["mfma_flop_per_launch"]) == 4.0e9 and float(p["executed_over_algorithmic"]) == 1.25
+    assert float(p["mfma_util_pct"]) == 45.0 and float(p["clock_ghz"]) == 2.0
+
+
 def test_copy_summary(tmp_path):
     hdr = ["Kind", "Direction", "Stream_Id", "Source_Agent_Id", "Destination_Agent_Id", "Correlation_Id",
            "Start_Timestamp", "End_Timestamp"]
