@@ -2672,8 +2672,8 @@ cqsa_status cqsa_probe_device(uint64_t copy_bytes, int32_t repeats, cqsa_probe_r
     CQSA_HIP(hipEventCreate(&r.e1));
     std::vector<uint64_t> clk((size_t)waves * 2);
 
-    // launch(0) untimed, then `repeats` timed launches; returns the fastest time and the clock of that
-    // launch (0 when the kernel records none)
+    // one untimed launch, then `repeats` timed ones: the fastest time, and the clock of that launch
+    // averaged over its first clocked_waves waves (0 when the kernel records no clock)
     auto run = [&](auto&& launch, int clocked_waves, double* secs, double* hz) -> cqsa_status {
         CQSA_HIP(launch());
         CQSA_HIP(hipDeviceSynchronize());
