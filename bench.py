@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cqs", type=int, default=0,
                     help="also time the cyclic quorum-set schedule with this many parts (resident workload, "
                          "and the streamed case with --streamed)")
+    ap.add_argument("--cqs-itr", type=int, default=1,
+                    help="depth of the quorum-set schedule of --cqs (c**itr parts; default 1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device to device once (scales HBM byte counters)")
     ap.add_argument("--merge", action="store_true",
@@ -127,7 +129,7 @@ def measured_traffic(path: str):
     return int(float(prof["traffic_bytes_per_launch"])), os.path.relpath(path, ROOT)
 
 
-def run_streamed(cqsa, torch, synth, cqs=None) -> dict:
+def run_streamed(cqsa, torch, synth, cqs=None, cqs_itr=1) -> dict:
     w = synth.workload(3)
     t0 = time.perf_counter()
     q, k, v, _ = synth.make_inputs(w, pin=True)
@@ -136,7 +138,7 @@ def run_streamed(cqsa, torch, synth, cqs=None) -> dict:
     print(f"[bench] streamed inputs ready ({gen_s:.1f} s)", file=sys.stderr, flush=True)
     res = streamed_run(cqsa, torch, w, q, k, v, out, None)
     if cqs:
-        res["cqs"] = streamed_run(cqsa, torch, w, q, k, v, out, cqs)
+        res["cqs"] = streamed_run(cqsa, torch, w, q, k, v, out, cqs, cqs_itr)
     return res
 
 
@@ -226,7 +228,7 @@ def run_streamed_backward(cqsa, torch, synth) -> dict:
             "identity_sum_dv_rel": e_v, "identity_sum_dk_rel": e_k}
 
 
-def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
+def streamed_run(cqsa, torch, w, q, k, v, out, cqs, cqs_itr=1) -> dict:
     # link peak: one pinned 1 GiB H2D copy timed by the host clock between two synchronisations
     src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -242,12 +244,14 @@ def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
     torch.cuda.reset_peak_memory_stats()
     base_alloc = torch.cuda.memory_allocated()
     t2 = time.perf_counter()
-    _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True, cqs=cqs)
+    _, info = cqsa.attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_info=True, cqs=cqs,
+                             cqs_itr=cqs_itr if cqs else None)
     wall = time.perf_counter() - t2
     # the call's device memory: its workspace comes from PyTorch's allocator (the library then allocates
     # nothing itself), so the allocator's high-water mark over the call is the call's peak
     peak = torch.cuda.max_memory_allocated() - base_alloc
-    print(f"[bench] streamed {'grid' if not cqs else f'cqs c={cqs}'}: {wall:.2f} s", file=sys.stderr, flush=True)
+    print(f"[bench] streamed {'grid' if not cqs else f'cqs c={cqs} itr={cqs_itr}'}: {wall:.2f} s", file=sys.stderr,
+          flush=True)
     tok = w.B * w.Nq / wall
     h2d_gbs = info["h2d_bytes"] / (info["h2d_ms"] / 1e3) / 1e9 if info["h2d_ms"] > 0 else None
     # parity on sampled rows against the FP64 reference (first/last rows, Q-chunk edges, seeded rows)
@@ -255,7 +259,7 @@ def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
     import oracle
     rng = np.random.default_rng(4)
     qc = info["q_chunk"]
-    edges = [w.Nq * p // cqs for p in range(1, cqs)][:6] if cqs else [qc - 1, qc]
+    edges = [w.Nq * p // cqs ** cqs_itr for p in range(1, cqs ** cqs_itr)][:6] if cqs else [qc - 1, qc]
     idx = sorted({0, 1, w.Nq - 1, w.Nq - 2, *edges, *[e - 1 for e in edges], *rng.integers(0, w.Nq, 10).tolist()})
     rows = np.array([(0, h, i) for h in (0, 5) for i in idx if 0 <= i < w.Nq], dtype=np.int64)
     t3 = time.perf_counter()
@@ -280,7 +284,7 @@ def streamed_run(cqsa, torch, w, q, k, v, out, cqs) -> dict:
         torch.cuda.empty_cache()
         print(f"[bench] same call with the tensors in HBM: {resident:.2f} s; overlap score {overlap:.3f}",
               file=sys.stderr, flush=True)
-    return {"workload": w.name, "schedule": "grid" if not cqs else f"cyclic quorum sets, c={cqs}",
+    return {"workload": w.name, "schedule": "grid" if not cqs else f"cyclic quorum sets, c={cqs}, itr={cqs_itr}",
             "seconds": round(wall, 3), "tokens_per_s": round(tok, 1),
             "tflops": round(w.flops() / wall / 1e12, 2), "h2d_bytes": info["h2d_bytes"],
             "h2d_gbs_during_copies": round(h2d_gbs, 2) if h2d_gbs else None,
@@ -376,16 +380,17 @@ def main():
     cqs_resident = None
     if args.cqs:
         for _ in range(2):
-            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, wave_tokens=args.wave_tokens)
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, wave_tokens=args.wave_tokens,
+                           cqs_itr=args.cqs_itr)
         torch.cuda.synchronize()
         c0 = time.perf_counter()
         n_cqs = max(3, args.steps // 4)
         for _ in range(n_cqs):
             cinfo = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, cqs=args.cqs, wave_tokens=args.wave_tokens,
-                                   return_info=True)[1]
+                                   cqs_itr=args.cqs_itr, return_info=True)[1]
         torch.cuda.synchronize()
         cms = (time.perf_counter() - c0) * 1e3 / n_cqs
-        cqs_resident = {"c": args.cqs, "ms_per_call": round(cms, 4), "tflops": round(flops / (cms / 1e3) / 1e12, 2),
+        cqs_resident = {"c": args.cqs, "itr": args.cqs_itr, "ms_per_call": round(cms, 4), "tflops": round(flops / (cms / 1e3) / 1e12, 2),
                         "pairs": cinfo["chunk_pairs"], "subproblems": cinfo["cqs_subproblems"],
                         "waves": cinfo["cqs_waves"], "wave_tokens": cinfo["wave_tokens"],
                         "kernel_launches": cinfo["kernel_launches"]}
@@ -476,7 +481,7 @@ def main():
     if backward:
         line["backward"] = backward
     if args.streamed:
-        line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None)
+        line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None, cqs_itr=args.cqs_itr)
     if args.merge:
         line["merge"] = run_merge(cqsa, torch, args.steps)
     if args.streamed_backward:

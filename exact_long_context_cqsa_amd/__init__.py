@@ -41,7 +41,7 @@ class CqsaOptions(ctypes.Structure):
                 ("merge_mode", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_uint64),
                 ("stream", ctypes.c_void_p), ("num_cus", ctypes.c_int32), ("cqs_c", ctypes.c_int32),
                 ("cqs_l", ctypes.c_int32), ("precision", ctypes.c_int32), ("cqs_set", ctypes.POINTER(ctypes.c_int32)),
-                ("wave_tokens", ctypes.c_int64)]
+                ("wave_tokens", ctypes.c_int64), ("cqs_itr", ctypes.c_int32)]
 
 
 class CqsaPlanInfo(ctypes.Structure):
@@ -146,6 +146,9 @@ def _load_library():
     lib.cqsa_cqs_assign.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]
     lib.cqsa_cqs_assign.restype = ctypes.c_int
+    lib.cqsa_cqs_assign_itr.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_int32)]
+    lib.cqsa_cqs_assign_itr.restype = ctypes.c_int
     lib.cqsa_cqs_default_set.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.cqsa_cqs_default_set.restype = ctypes.c_int32
     lib.cqsa_probe_device.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(CqsaProbeResult)]
@@ -205,22 +208,29 @@ def cqs_default_set(c: int) -> tuple:
     return tuple(buf[i] for i in range(n))
 
 
-def cqs_assign(c: int, interest_set) -> list:
-    """owner[a][b]: the subproblem of the quorum-set schedule that computes (query part a, key part b)."""
+def cqs_assign(c: int, interest_set, itr: int = 1) -> list:
+    """owner[a][b]: the subproblem of the quorum-set schedule that computes (query part a, key part b);
+    with itr > 1, over the c**itr parts of the depth-itr schedule."""
     arr = _int_array(interest_set)
-    own = (ctypes.c_int32 * (int(c) * int(c)))()
-    _check(_lib.cqsa_cqs_assign(int(c), arr, len(arr), own))
-    return [[own[a * c + b] for b in range(c)] for a in range(c)]
+    n = int(c) ** int(itr) if itr >= 1 and c >= 1 else 0
+    own = (ctypes.c_int32 * max(1, n * n))()
+    if itr == 1:
+        _check(_lib.cqsa_cqs_assign(int(c), arr, len(arr), own))
+    else:
+        _check(_lib.cqsa_cqs_assign_itr(int(c), arr, len(arr), int(itr), own))
+    return [[own[a * n + b] for b in range(n)] for a in range(n)]
 
 
 def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=None, workspace=None,
-             num_cus=None, cqs=None, precision=0, wave_tokens=None) -> CqsaOptions:
-    """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set).
+             num_cus=None, cqs=None, precision=0, wave_tokens=None, cqs_itr=None) -> CqsaOptions:
+    """cqs: None (grid schedule), c (quorum-set schedule with the built-in set) or (c, interest_set);
+    cqs_itr: its depth (None or 1: one level; itr > 1: c**itr parts).
     precision: 0 (P rounded to the input dtype) or 1 (split P, hi + lo).
     wave_tokens: packed-row budget of a wave of the quorum-set schedule (None: the default)."""
     o = CqsaOptions()
     o.precision = int(precision or 0)
     o.wave_tokens = int(wave_tokens or 0)
+    o.cqs_itr = int(cqs_itr or 0)
     if cqs is not None:
         if isinstance(cqs, int):
             o.cqs_c = cqs
@@ -244,7 +254,8 @@ def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=Non
 
 
 def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
-         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0, wave_tokens=None) -> dict:
+         kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0, wave_tokens=None,
+         cqs_itr=None) -> dict:
     """The plan ``attention`` would run (nothing is allocated or computed).
 
     ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
@@ -274,7 +285,7 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
     do = mk("out", out, None)
     info = CqsaPlanInfo()
     opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision,
-                   wave_tokens=wave_tokens)
+                   wave_tokens=wave_tokens, cqs_itr=cqs_itr)
     _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
                           int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
                           ctypes.byref(info)))
@@ -312,7 +323,8 @@ def backward_schedule_trace(q, k, v, out, dout, lse, dq, dk, dv, is_causal, mem_
 
 
 def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chunk=None, kv_chunk=None,
-                   kv_splits=None, merge=None, num_cus=256, cqs=None, precision=0, wave_tokens=None) -> str:
+                   kv_splits=None, merge=None, num_cus=256, cqs=None, precision=0, wave_tokens=None,
+                   cqs_itr=None) -> str:
     """The operations ``attention`` would issue, recorded instead of run (no GPU needed); see
     ``cqsa_schedule_trace`` in cqsa.h for the line format.  q, k, v and out are
     ``(shape, dtype, where, address)`` tuples ("host" or "device"; the address is a stand-in that is
@@ -331,7 +343,7 @@ def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chu
 
     dq, dk, dv, do = mk(q), mk(k), mk(v), mk(out)
     opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision,
-                   wave_tokens=wave_tokens)
+                   wave_tokens=wave_tokens, cqs_itr=cqs_itr)
     need = ctypes.c_uint64(0)
     args = (ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0, int(mem_budget),
             ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt))
@@ -345,7 +357,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
               mem_budget: int | None = None, *, q_chunk: int | None = None, kv_chunk: int | None = None,
               kv_splits: int | None = None, merge: int | None = None, out: torch.Tensor | None = None,
               out_dtype: torch.dtype | None = None, return_lse: bool = False, return_info: bool = False,
-              stream: torch.cuda.Stream | None = None, cqs=None, precision: int = 0, wave_tokens: int | None = None):
+              stream: torch.cuda.Stream | None = None, cqs=None, precision: int = 0, wave_tokens: int | None = None,
+              cqs_itr: int | None = None):
     """Exact ``softmax(scale * q k^T [+ causal mask]) v`` (SDPA semantics; causal is bottom-right
     aligned when Nq < Nk; GQA when k/v have fewer heads).
 
@@ -353,8 +366,9 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
     pinned host memory (then streamed in chunks).  ``mem_budget`` caps the device bytes the call
     uses (0/None: the free memory).  ``kv_chunk``/``q_chunk`` force a decomposition; ``merge``
     picks how partials merge (MERGE_KERNEL or MERGE_FUSED).  ``cqs`` runs the cyclic quorum-set
-    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set); its subproblems
-    run in waves of at most ``wave_tokens`` staged rows (one batched launch per wave).
+    schedule instead of the chunk grid: c (built-in interest set) or (c, interest_set), ``cqs_itr``
+    levels deep (c**cqs_itr parts; default one level); its subproblems run in waves of at most
+    ``wave_tokens`` staged rows (one batched launch per wave).
     ``precision=1`` feeds P to the PV product as a hi part plus a lo residual (two accumulator
     chains), for results near fp32 accuracy at about twice the PV work.  Returns out
     (on q's device; pinned host memory when q is on the host), plus lse [B, Hq, Nq] fp32 and the
@@ -365,7 +379,8 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
             raise ValueError("out= and return_info are not available on the autograd path")
         res = _AttentionFn.apply(q, k, v, bool(is_causal), scale, dict(
             mem_budget=mem_budget, q_chunk=q_chunk, kv_chunk=kv_chunk, kv_splits=kv_splits, merge=merge,
-            out_dtype=out_dtype, stream=stream, cqs=cqs, precision=precision, wave_tokens=wave_tokens))
+            out_dtype=out_dtype, stream=stream, cqs=cqs, precision=precision, wave_tokens=wave_tokens,
+            cqs_itr=cqs_itr))
         return res if return_lse else res[0]
     dev = _device_of(q, k, v, out)
     if dev is None:
@@ -385,7 +400,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
         st = stream if stream is not None else torch.cuda.current_stream(dev)
         dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
         opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs, precision=precision,
-                       wave_tokens=wave_tokens)
+                       wave_tokens=wave_tokens, cqs_itr=cqs_itr)
         budget = int(mem_budget or 0)
         # size the workspace first so that device-resident calls take it from PyTorch's allocator
         # (stream-ordered, no hipMalloc, no synchronisation)

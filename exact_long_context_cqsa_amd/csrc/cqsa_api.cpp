@@ -357,6 +357,35 @@ cqsa_status quorum_owner(int c, const int* set, int l, std::vector<int>* owner) 
     return CQSA_OK;
 }
 
+// Depth itr: the sequence is cut into C = c^itr parts, part p having base-c digits p_1 .. p_itr (p_1 the
+// most significant, so that the parts with one p_1 form part p_1 of the depth-1 cut).  Subproblem
+// I = (i_1 .. i_itr), also read base c, holds the parts whose every digit p_k is in {(i_k + s) mod c}:
+// the cyclic quorum set applied again inside each part of the level above.  Two parts a and b meet in
+// subproblem I exactly when a_k and b_k meet in i_k at every level, so the lexicographically smallest
+// such I, the owner, takes the depth-1 owner of (a_k, b_k) digit by digit.  Fills owner[a * C + b].
+cqsa_status quorum_owner_itr(int c, const int* set, int l, int itr, std::vector<int>* owner) {
+    std::vector<int> own1;
+    CQSA_TRY(quorum_owner(c, set, l, &own1));
+    int64_t C = 1;
+    for (int k = 0; k < itr; ++k) {
+        C *= c;
+        if (C > 4096) return fail(CQSA_ERR_INVALID, "cqs: c^itr = %d^%d parts exceed 4096", c, itr);
+    }
+    owner->assign((size_t)(C * C), 0);
+    for (int64_t a = 0; a < C; ++a)
+        for (int64_t b = 0; b < C; ++b) {
+            int64_t o = 0, x = a, y = b, w = 1;
+            for (int k = 0; k < itr; ++k) {   // least significant digit first
+                o += own1[(size_t)(x % c) * c + (size_t)(y % c)] * w;
+                x /= c;
+                y /= c;
+                w *= c;
+            }
+            (*owner)[(size_t)(a * C + b)] = (int)o;
+        }
+    return CQSA_OK;
+}
+
 int64_t part_lo(int64_t n, int c, int p) { return n * p / c; }
 
 // Does any key of key part b lie at or before the last row of query part a (causal)?
@@ -369,16 +398,18 @@ bool pair_visible(const Problem& P, int c, int a, int b) {
 }
 
 cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options& opt, Plan* pl) {
-    const int c = opt.cqs_c;
+    const int c0 = opt.cqs_c, itr = std::max(1, opt.cqs_itr);
     int dflt[8];
     const int* set = opt.cqs_set;
     int l = opt.cqs_l;
     if (!set) {
-        l = default_quorum_set(c, dflt, 8);
-        if (l == 0) return fail(CQSA_ERR_INVALID, "cqs: no built-in interest set for c = %d; pass cqs_set", c);
+        l = default_quorum_set(c0, dflt, 8);
+        if (l == 0) return fail(CQSA_ERR_INVALID, "cqs: no built-in interest set for c = %d; pass cqs_set", c0);
         set = dflt;
     }
-    CQSA_TRY(quorum_owner(c, set, l, &pl->cqs_owner));
+    CQSA_TRY(quorum_owner_itr(c0, set, l, itr, &pl->cqs_owner));
+    int c = 1;   // from here on: the number of parts (and of subproblems), c0^itr
+    for (int k = 0; k < itr; ++k) c *= c0;
     if (opt.q_chunk > 0 || opt.kv_chunk > 0 || opt.kv_splits > 1)
         return fail(CQSA_ERR_INVALID, "cqs: q_chunk, kv_chunk and kv_splits do not apply to the quorum-set schedule");
     pl->cqs = true;
@@ -572,7 +603,7 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     pl->total = off;
     if (pl->total > budget)
         return fail(CQSA_ERR_BUDGET,
-                    "mem_budget too small for the quorum-set schedule over c = %d parts: needs %llu bytes "
+                    "mem_budget too small for the quorum-set schedule over %d parts: needs %llu bytes "
                     "(x 1/0.85 = %llu)", c, (unsigned long long)pl->total,
                     (unsigned long long)(pl->total / kSafety) + 1);
     cqsa_plan_info& in = pl->info;
@@ -588,7 +619,7 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     in.workspace_bytes = pl->total;
     in.h2d_bytes = h2d;
     in.d2h_bytes = P.out.host ? rows * P.D * P.out.es + ((P.want_lse && P.lse_host) ? rows * 4 : 0) : 0;
-    in.cqs_c = c;
+    in.cqs_c = c0;
     in.cqs_subproblems = (int32_t)subs.size();
     in.cqs_waves = (int32_t)pl->cqs_waves.size();
     in.wave_tokens = pl->wave_tokens;
@@ -606,6 +637,9 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
         return CQSA_OK;
     }
     if (opt.cqs_c < 0) return fail(CQSA_ERR_INVALID, "cqs_c %d is negative", opt.cqs_c);
+    if (opt.cqs_itr < 0) return fail(CQSA_ERR_INVALID, "cqs_itr %d is negative", opt.cqs_itr);
+    if (opt.cqs_itr > 1 && opt.cqs_c <= 0)
+        return fail(CQSA_ERR_INVALID, "cqs_itr applies to the quorum-set schedule only (cqs_c > 0)");
     if (opt.wave_tokens < 0) return fail(CQSA_ERR_INVALID, "wave_tokens %lld is negative", (long long)opt.wave_tokens);
     if (opt.wave_tokens > 0 && opt.cqs_c <= 0)
         return fail(CQSA_ERR_INVALID, "wave_tokens applies to the quorum-set schedule only (cqs_c > 0)");
@@ -1438,6 +1472,9 @@ cqsa_status exec_cqs(const Problem& P, const Plan& pl, char* ws, hipStream_t st,
                 if (qs.empty() || qs.back() != pr.first) qs.push_back(pr.first);
             }
             std::sort(ks.begin(), ks.end());
+            if (ks.size() > 32 || qs.size() > 32)   // the planner's blocks hold at most 32 of each
+                return fail(CQSA_ERR_INVALID, "internal: a wave launch with %zu query and %zu key parts", qs.size(),
+                            ks.size());
             WaveTable t;
             std::memset(&t, 0, sizeof t);
             t.n_k = (int32_t)ks.size();
@@ -1693,6 +1730,17 @@ cqsa_status cqsa_cqs_assign(int32_t c, const int32_t* interest_set, int32_t l, i
     std::vector<int> set(interest_set ? interest_set : nullptr, interest_set ? interest_set + std::max(l, 0) : nullptr);
     std::vector<int> own;
     CQSA_TRY(quorum_owner(c, interest_set ? set.data() : nullptr, l, &own));
+    for (size_t i = 0; i < own.size(); ++i) owner[i] = own[i];
+    return CQSA_OK;
+}
+
+cqsa_status cqsa_cqs_assign_itr(int32_t c, const int32_t* interest_set, int32_t l, int32_t itr, int32_t* owner) {
+    g_err.clear();
+    if (!owner) return fail(CQSA_ERR_INVALID, "owner is NULL");
+    if (itr < 1) return fail(CQSA_ERR_INVALID, "cqs: itr = %d is below 1", itr);
+    std::vector<int> set(interest_set ? interest_set : nullptr, interest_set ? interest_set + std::max(l, 0) : nullptr);
+    std::vector<int> own;
+    CQSA_TRY(quorum_owner_itr(c, interest_set ? set.data() : nullptr, l, itr, &own));
     for (size_t i = 0; i < own.size(); ++i) owner[i] = own[i];
     return CQSA_OK;
 }

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define CQSA_ABI_VERSION 3
+#define CQSA_ABI_VERSION 4
 
 typedef enum {
     CQSA_OK = 0,
@@ -108,6 +108,9 @@ typedef struct {
                                  (copy of one wave under the compute of the other), cutting waves
                                  per query part of a subproblem when whole subproblems are too large;
                                  failing that, until one wave's staging fits. */
+    int32_t cqs_itr;          /* depth of the quorum-set decomposition: 0 or 1 = one level (c parts);
+                                 itr > 1 = the set applied again inside each part, itr levels deep
+                                 (c^itr parts and subproblems, at most 4096; see below) */
 } cqsa_options;
 
 /* What a plan does (filled by cqsa_plan and cqsa_attention_ex). */
@@ -308,12 +311,17 @@ uint64_t cqsa_struct_size(int32_t which);
  * Cyclic quorum-set (CQS) schedule.  The method decomposes one attention call into c^itr
  * subproblems over c parts of the sequence, each subproblem holding an interest set of l parts,
  * with work factor (l^2/c)^itr (stream-cqsa 2.2.0 -> 2.2.2 diff, stream_cqsa/autoconfig.py, plan()
- * docstring; the default set (0, 1, 3) for c = 7 in stream_cqsa/api.py).  This library runs depth
- * itr = 1: the query rows and the keys are each split into c contiguous parts (part p covers
- * [floor(p n / c), floor((p + 1) n / c))), and subproblem i holds the parts (i + s) mod c for s in the
- * set.  The set must be a cyclic quorum set: every pair of parts meets in some subproblem, i.e. every
- * d in 1..c-1 is a difference of two set elements mod c.  The pair (query part a, key part b) is
- * computed by exactly one subproblem, its owner: the smallest i whose parts contain both a and b.
+ * docstring; the default set (0, 1, 3) for c = 7 in stream_cqsa/api.py).  At depth itr = 1 the query
+ * rows and the keys are each split into c contiguous parts (part p covers [floor(p n / c),
+ * floor((p + 1) n / c))), and subproblem i holds the parts (i + s) mod c for s in the set.  The set
+ * must be a cyclic quorum set: every pair of parts meets in some subproblem, i.e. every d in 1..c-1 is
+ * a difference of two set elements mod c.  The pair (query part a, key part b) is computed by exactly
+ * one subproblem, its owner: the smallest i whose parts contain both a and b.  At depth itr > 1
+ * (cqsa_options.cqs_itr) the same set is applied inside each part of the level above: there are
+ * C = c^itr contiguous parts, part p with base-c digits p_1 .. p_itr (p_1 the most significant, the
+ * depth-1 part it lies in); subproblem I = (i_1 .. i_itr) holds the parts whose digit p_k is in
+ * {(i_k + s) mod c} at every level k, i.e. l^itr of the C parts, and the owner of a pair is the
+ * smallest such I (digit by digit the depth-1 owner).  Every pair of parts is still computed once.
  * Subproblems run in waves (the wave engine of the same pages: README.md, the paragraph on peak
  * memory and the wave budget; stream_cqsa/api.py, _pick_wave): consecutive subproblems are packed
  * into one wave while the rows it stages (query rows of its query parts plus key rows of its key
@@ -332,6 +340,11 @@ uint64_t cqsa_struct_size(int32_t which);
  * cyclic quorum set; CQSA_ERR_INVALID (with a message) when c < 1, l < 1, l > c, an element is
  * outside [0, c) or repeated, or some pair of parts shares no subproblem.  Host-only. */
 cqsa_status cqsa_cqs_assign(int32_t c, const int32_t* interest_set, int32_t l, int32_t* owner);
+
+/* The owner table of the depth-itr schedule (itr >= 1; itr = 1 is cqsa_cqs_assign): owner[a * C + b]
+ * for the C = c^itr parts, C at most 4096.  Errors as cqsa_cqs_assign, and CQSA_ERR_INVALID for
+ * itr < 1 or C > 4096.  Host-only. */
+cqsa_status cqsa_cqs_assign_itr(int32_t c, const int32_t* interest_set, int32_t l, int32_t itr, int32_t* owner);
 
 /* The built-in interest set for c parts (perfect difference sets: c = 3, 7, 13, 21, 31): writes up to
  * max_l elements to set and returns its size, or 0 when there is none for c. */

@@ -54,10 +54,10 @@ def test_forward_kernel_name(monkeypatch):
 def test_struct_layout_and_version():
     import exact_long_context_cqsa_amd as m
     lib = m._lib
-    assert lib.cqsa_version() == 3
+    assert lib.cqsa_version() == 4
     assert lib.cqsa_struct_size(0) == ctypes.sizeof(m.CqsaTensor) == 80
-    assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions) == 80
-    assert [f for f, _ in m.CqsaOptions._fields_][-3:] == ["precision", "cqs_set", "wave_tokens"]
+    assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions) == 88
+    assert [f for f, _ in m.CqsaOptions._fields_][-3:] == ["cqs_set", "wave_tokens", "cqs_itr"]
     assert [f for f, _ in m.CqsaPlanInfo._fields_][-3:] == ["cqs_waves", "reserved0", "wave_tokens"]
     assert lib.cqsa_struct_size(2) == ctypes.sizeof(m.CqsaPlanInfo) == 152
     assert lib.cqsa_struct_size(3) == ctypes.sizeof(m.CqsaProbeResult) == 72

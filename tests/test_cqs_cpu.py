@@ -174,3 +174,59 @@ def test_wave_budget_shrinks_to_fit_memory():
     with pytest.raises(m().CqsaError):
         m().plan(((1, 8, 7000, 64), torch.float16), ((1, 8, 7000, 64), torch.float16),
                  ((1, 8, 7000, 64), torch.float16), True, 64 * GB, num_cus=256, wave_tokens=5000)
+
+
+# ---------------------------------------------------------------- depth itr > 1
+
+def _digits(p, c, itr):
+    """Base-c digits of part p, most significant (the depth-1 part) first."""
+    return [(p // c ** (itr - 1 - k)) % c for k in range(itr)]
+
+
+def _holds(c, iset, itr, sub, part):
+    """Subproblem `sub` holds `part` when every digit of the part is in the cyclic shift of the set by
+    the subproblem's digit at the same level (the set applied again inside each part)."""
+    return all(pd in parts_of(c, iset, sd) for pd, sd in zip(_digits(part, c, itr), _digits(sub, c, itr)))
+
+
+@pytest.mark.parametrize("c,iset,itr", [(3, (0, 1), 2), (7, (0, 1, 3), 2), (3, (0, 1), 3), (4, (0, 1, 2), 2),
+                                        (5, (0, 1, 2, 3, 4), 2)])
+def test_depth_owner_is_the_first_subproblem_holding_both_parts(c, iset, itr):
+    """Brute force over the definition: C = c^itr parts and subproblems; each subproblem holds l^itr
+    parts; every pair of parts has a holder, and the owner is the smallest one, so each pair is
+    computed exactly once."""
+    C = c ** itr
+    own = m().cqs_assign(c, iset, itr)
+    assert len(own) == C
+    held = {i: {p for p in range(C) if _holds(c, iset, itr, i, p)} for i in range(C)}
+    assert all(len(h) == len(iset) ** itr for h in held.values())
+    per_sub = [0] * C
+    for a, b in itertools.product(range(C), repeat=2):
+        holders = [i for i in range(C) if a in held[i] and b in held[i]]
+        assert holders, (a, b)
+        assert own[a][b] == holders[0]
+        per_sub[own[a][b]] += 1
+    assert sum(per_sub) == C * C and max(per_sub) <= len(iset) ** (2 * itr)
+
+
+def test_depth_one_is_the_single_level_schedule():
+    assert m().cqs_assign(7, (0, 1, 3), 1) == m().cqs_assign(7, (0, 1, 3))
+
+
+def test_depth_plan_counts_and_errors():
+    """c = 7 at depth 2: 49 parts; the plan's pairs are the visible pairs of the 49-part cut; the
+    user's c is reported as such."""
+    p = _plan(4900, False, 7, cqs_itr=2)
+    assert p["n_q_chunks"] == 49 and p["cqs_c"] == 7 and p["chunk_pairs"] == 49 * 49
+    assert p["cqs_subproblems"] == 49 and p["q_chunk"] == 100
+    p = _plan(4900, True, 7, cqs_itr=2)
+    assert p["chunk_pairs"] == 49 * 50 // 2                                  # key part <= query part
+    p1 = _plan(4900, True, 7)
+    assert p["workspace_bytes"] == p1["workspace_bytes"]                      # the same accumulator
+    with pytest.raises(m().CqsaError, match="exceed 4096"):
+        _plan(4900, True, 31, cqs_itr=3)
+    with pytest.raises(m().CqsaError, match="cqs_itr applies"):
+        m().plan(((1, 2, 64, 64), torch.float16), ((1, 2, 64, 64), torch.float16), ((1, 2, 64, 64), torch.float16),
+                 True, GB, where={n: "device" for n in ("q", "k", "v", "out")}, num_cus=256, cqs_itr=2)
+    with pytest.raises(m().CqsaError, match="negative"):
+        _plan(4900, True, 7, cqs_itr=-1)

@@ -2,7 +2,8 @@
 launch per wave (per 32 query and 32 key parts), each query part attending to the union of its key
 parts in one pass, folded into the accumulator on the device.  Compared with the FP64 oracle at
 several wave budgets, from one subproblem per wave to a single wave, with device-resident and
-pinned-host inputs (head-major and token-major host layouts)."""
+pinned-host inputs (head-major and token-major host layouts); and the schedule at depth 2 and 3
+(c^itr parts)."""
 import math
 import sys
 
@@ -163,3 +164,38 @@ def test_wave_units_per_query_part_streamed():
                        boundaries=[131072 * p // 31 for p in range(32)], heads=range(0, w.Hq, 3))
     ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
     compare(out, lse, ref, w.dtype, rows=rows, label="waves per query part, streamed 131072")
+
+
+DEPTH_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, c, itr
+    (1, 2, 2, 1500, 1500, 64, torch.float16, True, 3, 2),       # 9 parts
+    (1, 4, 1, 700, 2100, 128, torch.bfloat16, True, 7, 2),      # 49 parts, GQA 4:1, bottom-right causal
+    (2, 2, 2, 900, 900, 64, torch.float16, False, 3, 3),        # 27 parts, non-causal
+    (1, 2, 2, 1201, 1201, 128, torch.float16, True, 13, 2),     # 169 parts of 7-8 rows: several launches per wave
+]
+
+
+@pytest.mark.parametrize("case", DEPTH_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}-cqs{c[8]}^{c[9]}")
+def test_depth_against_oracle(case):
+    """The quorum-set schedule itr levels deep (c^itr parts): against the oracle with device-resident
+    inputs at the default wave budget and one subproblem per wave, and with pinned host inputs; and
+    against the single-level schedule and the monolithic pass."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, c, itr = case
+    say("depth", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=5400 + Nq + Nk + c + itr)
+    ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D))
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    agree = 2e-3 if dtype == torch.float16 else 1.6e-2
+    mono = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32)
+    for wt in (None, 1):
+        out, lse, info = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
+                                          return_info=True, cqs=c, cqs_itr=itr, wave_tokens=wt)
+        torch.cuda.synchronize()
+        assert info["n_q_chunks"] == c ** itr and info["cqs_c"] == c
+        compare(out, lse, ref, dtype, label=f"depth wave_tokens={wt} {case}")
+        assert (out - mono).abs().max().item() <= agree
+    out_h, lse_h, info_h = cqsa().attention(q.pin_memory(), k.pin_memory(), v.pin_memory(), is_causal=causal,
+                                            out_dtype=torch.float32, return_lse=True, return_info=True, cqs=c,
+                                            cqs_itr=itr)
+    assert info_h["streamed"] == 1 and not out_h.is_cuda
+    compare(out_h, lse_h, ref, dtype, label=f"depth host {case}")

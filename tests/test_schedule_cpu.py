@@ -152,6 +152,13 @@ def test_quorum_set_waves_are_race_free(c, wt, budget):
     assert sum(o.kind == "wave" for o in resident) >= 1
 
 
+@pytest.mark.parametrize("c,itr,wt", [(7, 2, None), (3, 3, 20000), (13, 2, None)])
+def test_quorum_set_waves_of_depth_are_race_free(c, itr, wt):
+    ops = check(trace(131072, 131072, H=8, cqs=c, cqs_itr=itr, wave_tokens=wt, want_lse=True), streamed=True)
+    assert sum(o.kind == "wave" for o in ops) >= 1
+    check(trace(30000, 30000, where=("device",) * 4, cqs=c, cqs_itr=itr), streamed=False)
+
+
 def test_checker_catches_a_missing_wait():
     """Plant the mistake in the trace, not in the library: drop the compute stream's wait for a staged
     K/V copy (or the copy stream's wait for the compute that last used a buffer)."""
