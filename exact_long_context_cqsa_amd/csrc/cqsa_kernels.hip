@@ -207,6 +207,69 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[NKB], u32x4 (&pf)
     softmax_tile<NKB, NDB, DT, false>(s, pf, unused_lo, m, l, o, o, c);
 }
 
+// Transposed scores of one key tile, S^T = K Q^T: NKB blocks of 32 keys, each accumulated over the
+// NDK 16-dim steps of the head.  The NKB accumulation chains alternate, so no MFMA waits on the one
+// before it.
+template <int D, int NKB, int NDK, int DT>
+__device__ __forceinline__ void scores(const uint16_t* st, const int (&kread)[NDK], const u32x4 (&qf)[NDK],
+                                       f32x16 (&sacc)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NDK; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            sacc[kb] = mfma32<DT>(*reinterpret_cast<const u32x4*>(st + kread[t] + kb * 32 * D), qf[t], sacc[kb]);
+}
+
+// PV product of the 16-key group t of the tile in stage st: O^T += V^T P^T for every 32-dim block.
+// The V^T operand comes from the row-major V tile by two transposing reads whose lane addresses
+// pick the key order of the packed probabilities (vslot).
+template <int D, int NDB, int DT, bool SPLIT>
+__device__ __forceinline__ void pv_group(const uint16_t* st, const int (&vread)[NDB], int t, u32x4 pf, u32x4 plo,
+                                         f32x16 (&o)[NDB], f32x16 (&olo)[NDB]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t) * D));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t + 8) * D));
+        u32x4 vf;
+        vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
+        vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
+        vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
+        vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
+        o[db] = mfma32<DT>(vf, pf, o[db]);
+        if constexpr (SPLIT) olo[db] = mfma32<DT>(vf, plo, olo[db]);
+    }
+}
+
+// Online softmax and PV products of one key tile (scores s: NKB blocks of 32 keys).  Without PIPE
+// the softmax of the whole tile (and its lazy-shift check) runs first, then every PV product.  With
+// PIPE the softmax runs per 32-key block and the block's PV products are issued before the softmax
+// of the next block, so inside one wave the matrix core works on block kb while the VALU computes
+// block kb + 1.  Each accumulator still sums the key groups in ascending order; only the points at
+// which the shift may move differ (any shift gives the same exact result).
+template <int D, int NKB, int NDB, int DT, bool SPLIT, bool PIPE>
+__device__ __forceinline__ void softmax_pv(const f32x16 (&s)[NKB], const uint16_t* st, const int (&vread)[NDB],
+                                           float& m, float& l, f32x16 (&o)[NDB], f32x16 (&olo)[NDB], float c) {
+    if constexpr (PIPE) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            u32x4 pf[2], plo[2];
+            softmax_tile<1, NDB, DT, SPLIT>(reinterpret_cast<const f32x16(&)[1]>(s[kb]), pf, plo, m, l, o, olo, c);
+            pv_group<D, NDB, DT, SPLIT>(st, vread, 2 * kb, pf[0], plo[0], o, olo);
+            pv_group<D, NDB, DT, SPLIT>(st, vread, 2 * kb + 1, pf[1], plo[1], o, olo);
+        }
+    } else {
+        u32x4 pf[2 * NKB], plo[2 * NKB];
+        softmax_tile<NKB, NDB, DT, SPLIT>(s, pf, plo, m, l, o, olo, c);
+#pragma unroll
+        for (int t = 0; t < 2 * NKB; ++t) pv_group<D, NDB, DT, SPLIT>(st, vread, t, pf[t], plo[t], o, olo);
+    }
+}
+
 // Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts: 32-bit data format,
 // no swizzle.  Loads at or past num_records bytes return zero.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -776,7 +839,7 @@ __device__ __forceinline__ int vswz(int r) {
 // NW waves per workgroup (32 query rows each); WPE asks the compiler for registers that leave room for
 // WPE waves per SIMD (several small workgroups per CU drift out of phase, so one's softmax overlaps
 // another's matrix products).
-template <int D, int DT, int KT, int NW, int WPE, bool SPLIT>
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT, bool PIPE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd_dma_kernel(const FwdArgs a) {
     constexpr int BM = NW * 32;
@@ -787,7 +850,6 @@ fwd_dma_kernel(const FwdArgs a) {
     constexpr int NBLK = KT / RPI;                         // DMA instructions per tensor and tile
     constexpr int BPW = (NBLK + NW - 1) / NW;              // per wave
     constexpr int NKB = KT / 32;
-    constexpr int NPK = KT / 16;
     constexpr int NDB = D / 32;
     constexpr int NDK = D / 16;
     static_assert(NBLK % NW == 0, "tile split");
@@ -889,15 +951,7 @@ fwd_dma_kernel(const FwdArgs a) {
         const uint16_t* st = lds + (it & 1) * STAGE;
 
         f32x16 sacc[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NDK; ++t)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const u32x4 af = *reinterpret_cast<const u32x4*>(st + kread[t] + kb * 32 * D);
-                sacc[kb] = mfma32<DT>(af, qf[t], sacc[kb]);
-            }
+        scores<D, NKB, NDK, DT>(st, kread, qf, sacc);
 
         const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + a.causal_delta));
         if (need_mask) {
@@ -915,26 +969,7 @@ fwd_dma_kernel(const FwdArgs a) {
                 }
         }
 
-        u32x4 pf[NPK], plo[NPK];
-        softmax_tile<NKB, NDB, DT, SPLIT>(sacc, pf, plo, mrun, lrun, oacc, olo, a.scale_log2);
-
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int t = 0; t < NPK; ++t) {
-                typedef short s16x4 __attribute__((ext_vector_type(4)));
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t) * D));
-                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * t + 8) * D));
-                u32x4 vf;
-                vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
-                vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
-                vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
-                vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
-                oacc[db] = mfma32<DT>(vf, pf[t], oacc[db]);
-                if constexpr (SPLIT) olo[db] = mfma32<DT>(vf, plo[t], olo[db]);
-            }
+        softmax_pv<D, NKB, NDB, DT, SPLIT, PIPE>(sacc, st, vread, mrun, lrun, oacc, olo, a.scale_log2);
     }
 
 #undef CQSA_ISSUE_TILE
@@ -971,7 +1006,7 @@ __device__ __forceinline__ void wave_strides(int layout, int64_t n, int H, int D
     }
 }
 
-template <int D, int DT, int KT, int NW, int WPE, bool SPLIT>
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT, bool PIPE>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
     constexpr int BM = NW * 32;
@@ -982,7 +1017,6 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
     constexpr int NBLK = KT / RPI;
     constexpr int BPW = (NBLK + NW - 1) / NW;
     constexpr int NKB = KT / 32;
-    constexpr int NPK = KT / 16;
     constexpr int NDB = D / 32;
     constexpr int NDK = D / 16;
     static_assert(NBLK % NW == 0, "tile split");
@@ -1133,15 +1167,7 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
         if (active) {
             const uint16_t* st = lds + (it & 1) * STAGE;
             f32x16 sacc[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
-#pragma unroll
-            for (int u = 0; u < NDK; ++u)
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const u32x4 af = *reinterpret_cast<const u32x4*>(st + kread[u] + kb * 32 * D);
-                    sacc[kb] = mfma32<DT>(af, qf[u], sacc[kb]);
-                }
+            scores<D, NKB, NDK, DT>(st, kread, qf, sacc);
             const bool need_mask = (j0 + KT > clen) || (a.causal && (j0 + KT - 1 > iw0 + cdelta));
             if (need_mask) {
                 int lim = min(clen - j0, KT);
@@ -1157,25 +1183,7 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
                         if (tt >= lim) sacc[kb][r] = -INFINITY;
                     }
             }
-            u32x4 pf[NPK], plo[NPK];
-            softmax_tile<NKB, NDB, DT, SPLIT>(sacc, pf, plo, mrun, lrun, oacc, olo, a.scale_log2);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int u = 0; u < NPK; ++u) {
-                    typedef short s16x4 __attribute__((ext_vector_type(4)));
-                    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * u) * D));
-                    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(st + vread[db] + (16 * u + 8) * D));
-                    u32x4 vf;
-                    vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
-                    vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
-                    vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 0, 1));
-                    vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v1, v1, 2, 3));
-                    oacc[db] = mfma32<DT>(vf, pf[u], oacc[db]);
-                    if constexpr (SPLIT) olo[db] = mfma32<DT>(vf, plo[u], olo[db]);
-                }
+            softmax_pv<D, NKB, NDB, DT, SPLIT, PIPE>(sacc, st, vread, mrun, lrun, oacc, olo, a.scale_log2);
         }
         // advance the compute cursor
         cj0 += KT;
@@ -1660,13 +1668,13 @@ __global__ void __launch_bounds__(256) merge_kernel(const MergeArgs a) {
     }
 }
 
-template <int D, int DT, int KT, int NW, int WPE, bool SPLIT = false>
+template <int D, int DT, int KT, int NW, int WPE, bool SPLIT = false, bool PIPE = false>
 hipError_t launch_dma_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT, NW, WPE, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
-                       a);
+    hipLaunchKernelGGL((fwd_dma_kernel<D, DT, KT, NW, WPE, SPLIT, PIPE>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       stream, a);
     return hipGetLastError();
 }
 
@@ -1689,15 +1697,20 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 }
 
 // Kernel choice per head dim: kind 2 the DMA kernel (nw waves, kt keys per tile, wpe waves per SIMD
-// asked of the register allocator), kind 1 the register-staged kernel, kind 0 the ping-pong kernel.
-// Entry 0 is the default; the environment variable CQSA_FWD_VARIANT (read at every launch) selects
-// another entry, for measurement and for the tests that cover every kernel.
+// asked of the register allocator, pipe: softmax and PV products interleaved per 32-key block), kind 1
+// the register-staged kernel, kind 0 the ping-pong kernel.
+// Entry 0 is the default (pipelined at D=64, where it measured faster; not at D=128, where it did
+// not); entry 4 is the default shape with the other choice.  The environment variable
+// CQSA_FWD_VARIANT (read at every launch) selects another entry, for measurement and for the tests
+// that cover every kernel.
 struct Shape {
-    int kind, nw, kt, wpe;
+    int kind, nw, kt, wpe, pipe;
 };
-constexpr Shape kShapes64[] = {{2, 4, 64, 3}, {2, 8, 128, 2}, {1, 8, 128, 2}, {0, 8, 128, 2}};
-constexpr Shape kShapes128[] = {{2, 8, 64, 2}, {2, 8, 32, 2}, {1, 8, 64, 2}, {0, 8, 64, 2}};
-constexpr int kNumShapes = 4;
+constexpr Shape kShapes64[] = {{2, 4, 64, 3, 1}, {2, 8, 128, 2, 0}, {1, 8, 128, 2, 0}, {0, 8, 128, 2, 0},
+                               {2, 4, 64, 3, 0}};
+constexpr Shape kShapes128[] = {{2, 8, 64, 2, 0}, {2, 8, 32, 2, 0}, {1, 8, 64, 2, 0}, {0, 8, 64, 2, 0},
+                                {2, 8, 64, 2, 1}};
+constexpr int kNumShapes = 5;
 
 int variant() {
     const char* e = getenv("CQSA_FWD_VARIANT");
@@ -1706,8 +1719,8 @@ int variant() {
 }
 
 // The split-P product (two PV chains) runs on the DMA kernel in one shape per head dim.
-constexpr Shape kSplit64 = {2, 8, 64, 2};
-constexpr Shape kSplit128 = {2, 8, 32, 2};
+constexpr Shape kSplit64 = {2, 8, 64, 2, 0};
+constexpr Shape kSplit128 = {2, 8, 32, 2, 0};
 
 Shape shape_of(int D, int p_split) {
     if (p_split) return D == 64 ? kSplit64 : kSplit128;
@@ -1724,14 +1737,17 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     }
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
     if (sh.kind == 2) {
-#define CQSA_DMA_CASE(NW_, KT_, WPE_) \
-    if (sh.nw == NW_ && sh.kt == KT_ && sh.wpe == WPE_) return launch_dma_t<D, DT, KT_, NW_, WPE_>(a, st);
+#define CQSA_DMA_CASE(NW_, KT_, WPE_, PIPE_)                                          \
+    if (sh.nw == NW_ && sh.kt == KT_ && sh.wpe == WPE_ && sh.pipe == PIPE_) \
+        return launch_dma_t<D, DT, KT_, NW_, WPE_, false, (PIPE_ != 0)>(a, st);
         if constexpr (D == 64) {
-            CQSA_DMA_CASE(4, 64, 3)
-            CQSA_DMA_CASE(8, 128, 2)
+            CQSA_DMA_CASE(4, 64, 3, 1)
+            CQSA_DMA_CASE(4, 64, 3, 0)
+            CQSA_DMA_CASE(8, 128, 2, 0)
         } else {
-            CQSA_DMA_CASE(8, 64, 2)
-            CQSA_DMA_CASE(8, 32, 2)
+            CQSA_DMA_CASE(8, 64, 2, 0)
+            CQSA_DMA_CASE(8, 32, 2, 0)
+            CQSA_DMA_CASE(8, 64, 2, 1)
         }
 #undef CQSA_DMA_CASE
         return hipErrorInvalidValue;
@@ -1759,8 +1775,8 @@ const char* fwd_kernel_name(int D, int p_split) {
     const Shape sh = shape_of(D, p_split);
     static const char* const kind[3] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel"};
     char* out = names[D == 64 ? 0 : 1][v];
-    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s", kind[sh.kind], sh.nw, sh.kt,
-             p_split ? " split_p" : "");
+    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s%s", kind[sh.kind], sh.nw, sh.kt,
+             sh.pipe ? " pipelined" : "", p_split ? " split_p" : "");
     return out;
 }
 
@@ -1789,17 +1805,17 @@ template <int D, int DT>
 hipError_t launch_wave_d(const FwdArgs& a, const WaveTable& t, int blocks, hipStream_t st) {
     if (a.p_split) {
         if constexpr (D == 64)
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true, false>), dim3((unsigned)blocks),
                                dim3(kSplit64.nw * 64), 0, st, a, t);
         else
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true>),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true, false>),
                                dim3((unsigned)blocks), dim3(kSplit128.nw * 64), 0, st, a, t);
     } else {
         if constexpr (D == 64)
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave64.kt, kWave64.nw, kWave64.wpe, false>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave64.kt, kWave64.nw, kWave64.wpe, false, (kWave64.pipe != 0)>), dim3((unsigned)blocks),
                                dim3(kWave64.nw * 64), 0, st, a, t);
         else
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave128.kt, kWave128.nw, kWave128.wpe, false>),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kWave128.kt, kWave128.nw, kWave128.wpe, false, (kWave128.pipe != 0)>),
                                dim3((unsigned)blocks), dim3(kWave128.nw * 64), 0, st, a, t);
     }
     return hipGetLastError();

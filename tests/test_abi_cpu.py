@@ -41,8 +41,13 @@ def test_forward_kernel_name(monkeypatch):
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
     assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ")
     assert m.fwd_kernel_name(96) == ""
+    # the default shape is pipelined at D=64 and not at D=128; variant 4 is the other choice
+    assert "pipelined" in m.fwd_kernel_name(64) and "pipelined" not in m.fwd_kernel_name(128)
     monkeypatch.setenv("CQSA_FWD_VARIANT", "2")
     assert m.fwd_kernel_name(64).startswith("fwd_kernel ")
+    monkeypatch.setenv("CQSA_FWD_VARIANT", "4")
+    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ") and "pipelined" not in m.fwd_kernel_name(64)
+    assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ") and "pipelined" in m.fwd_kernel_name(128)
     monkeypatch.setenv("CQSA_FWD_VARIANT", "99")   # out of range: the default
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
     # split-P runs the DMA kernel in its own shape whatever the variant

@@ -70,7 +70,7 @@ def test_small_full_parity(case):
 VARIANT_CASES = [SMALL[1], SMALL[2], SMALL[3], SMALL[4], SMALL[7]]
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
 def test_every_forward_kernel_variant(variant, monkeypatch):
     """The non-default forward kernels (selected per launch by CQSA_FWD_VARIANT) on ragged, GQA,
     non-causal and long-key cases, monolithic and with a forced KV split."""
