@@ -354,6 +354,45 @@ def test_config5_softmax_stress_reduced():
     say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 reduced"))
 
 
+SHIFT_CASES = [
+    # D, dtype, causal
+    (64, torch.float16, True),
+    (64, torch.bfloat16, False),
+    (128, torch.float16, False),
+    (128, torch.bfloat16, True),
+]
+
+
+@pytest.mark.parametrize("variant", [0, 4])
+@pytest.mark.parametrize("case", SHIFT_CASES, ids=lambda c: f"d{c[0]}{'f16' if c[1] == torch.float16 else 'bf16'}"
+                         f"{'c' if c[2] else 'n'}")
+def test_shift_moves_inside_a_tile(case, variant, monkeypatch):
+    """The running maximum jumps at the start of the second 32-key block of many 64-key tiles (and at
+    the start of other tiles), by growing amounts, so the exact path of the online softmax runs in the
+    middle of a tile, after the first block's probabilities were formed (and, in the pipelined kernel,
+    after its PV products were issued).  Every query gets q[..., 0] = 3; the chosen keys get
+    k[..., 0] raised so that their logit rises by 8 + 1.5 t (natural log) in tile t.  Both choices of
+    the pipelined order (the default and CQSA_FWD_VARIANT=4) are compared with the FP64 reference."""
+    D, dtype, causal = case
+    monkeypatch.setenv("CQSA_FWD_VARIANT", str(variant))
+    B, H, N = 1, 2, 1100
+    say("shift", case, "variant", variant)
+    q, k, v = gen(B, H, H, N, N, D, dtype, seed=4100 + D + variant)
+    scale = 1.0 / math.sqrt(D)
+    q[..., 0] = 3.0
+    for t in range(N // 64 + 1):
+        j = 64 * t + (32 + t % 5 if t % 3 else t % 7)     # second block in two tiles of three, else the first
+        if j < N:
+            k[:, :, j, 0] = (k[:, :, j, 0].float() + (8.0 + 1.5 * t) / (3.0 * scale)).to(dtype)
+    ref = reference(q, k, v, causal=causal, scale=scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True)
+    torch.cuda.synchronize()
+    say("shift", compare(out, lse, ref, dtype, label=f"shift {case} variant {variant}"))
+    # the spike keys dominate the rows that see them: the output is far from the plain average
+    assert float((out.float().cpu() - v.float().mean(2, keepdim=True)).abs().max()) > 0.5
+
+
 @pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
 def test_streamed_from_pinned_host(layout):
     """Host-resident q/k/v/out under a small budget: the planner must chunk Q and KV."""
