@@ -804,6 +804,23 @@ cqsa_status side_streams(DeviceRes* r) {
     return CQSA_OK;
 }
 
+// After a failed call: wait for every stream the call may have issued work on (the caller's stream and
+// the library's copy streams), so that no copy or kernel of the failed call still reads or writes
+// caller memory (inputs, outputs, workspace) once the error is returned.  Errors met while waiting are
+// cleared; the call's first error is the one reported.
+void drain_after_failure(hipStream_t st, DeviceRes* r) {
+    hipStream_t side[2] = {nullptr, nullptr};
+    if (r) {
+        std::lock_guard<std::mutex> lk(g_res_mu);
+        side[0] = r->h2d;
+        side[1] = r->d2h;
+    }
+    (void)hipStreamSynchronize(st);
+    for (hipStream_t s : side)
+        if (s) (void)hipStreamSynchronize(s);
+    (void)hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------------------
 // Schedule recording (cqsa_schedule_trace): the executors issue every copy, launch, event record and
 // event wait through the x_* wrappers below.  With a recorder installed on the calling thread they
@@ -986,6 +1003,17 @@ void set_v(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
     a.v_sn = sn;
 }
 
+// Failure injection for the error-path tests: with CQSA_FAIL_AFTER_LAUNCHES=n in the environment, every
+// forward launch of a call after its first n fails as a launch error would, once the call's earlier
+// copies and launches have been issued.  The count restarts at each public call.
+thread_local int64_t g_fwd_launches = 0;
+
+bool injected_launch_failure() {
+    const char* e = std::getenv("CQSA_FAIL_AFTER_LAUNCHES");
+    if (!e || !*e) return false;
+    return g_fwd_launches++ >= std::atoll(e);
+}
+
 cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
     const int bm = fwd_block_m((int)P.D, P.p_split);
     const int64_t rows = a.r1 - a.r0;
@@ -1014,6 +1042,7 @@ cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
         g_rec->line(l);
         return CQSA_OK;
     }
+    if (injected_launch_failure()) return fail(CQSA_ERR_HIP, "forward kernel launch failed: injected (CQSA_FAIL_AFTER_LAUNCHES)");
     const hipError_t e = launch_fwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
     if (e != hipSuccess) return fail(CQSA_ERR_HIP, "forward kernel launch failed: %s", hipGetErrorString(e));
     return CQSA_OK;
@@ -1849,6 +1878,7 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
                               float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse,
                               const cqsa_options* opt, cqsa_plan_info* info) {
     g_err.clear();
+    g_fwd_launches = 0;
     const auto t0 = std::chrono::steady_clock::now();
     cqsa_options o;
     std::memset(&o, 0, sizeof o);
@@ -1895,10 +1925,8 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
         hipError_t e = hipStreamSynchronize(st);
         if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
     }
-    if (owned) {
-        if (s != CQSA_OK) (void)hipStreamSynchronize(st);
-        (void)hipFree(ws);
-    }
+    if (s != CQSA_OK) drain_after_failure(st, res);
+    if (owned) (void)hipFree(ws);
     if (s != CQSA_OK) return s;
     if (sync) pl.info.wall_ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (info) *info = pl.info;
@@ -2546,10 +2574,8 @@ cqsa_status cqsa_attention_backward_ex(const cqsa_tensor* q, const cqsa_tensor* 
         const hipError_t e = hipStreamSynchronize(st);
         if (e != hipSuccess) s = fail(CQSA_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
     }
-    if (owned) {
-        if (s != CQSA_OK) (void)hipStreamSynchronize(st);
-        (void)hipFree(ws);
-    }
+    if (s != CQSA_OK) drain_after_failure(st, res);
+    if (owned) (void)hipFree(ws);
     if (s != CQSA_OK) return s;
     if (info) {
         *info = in;

@@ -37,6 +37,12 @@
  *   - The calls run on the current HIP device.  Errors never throw: every call
  *     returns a cqsa_status, and cqsa_last_error() returns a message for the
  *     calling thread.  Arguments are validated before any device work starts.
+ *     A call that fails after it has issued device work (a failed launch or
+ *     copy) returns only once its stream and the library's copy streams have
+ *     drained: nothing of the failed call still reads or writes caller memory.
+ *     Its outputs are then unspecified.
+ *   - CQSA_FAIL_AFTER_LAUNCHES=n in the environment (for error-path tests) makes
+ *     every forward launch of a call after its first n fail with CQSA_ERR_HIP.
  */
 #ifndef CQSA_H
 #define CQSA_H

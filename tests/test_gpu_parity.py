@@ -526,6 +526,32 @@ def test_config5_softmax_stress_full_size():
     say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 full"))
 
 
+def test_launch_failure_mid_stream_is_reported_and_the_next_call_is_exact(monkeypatch):
+    """A forward launch that fails partway through a host-streamed call is reported as CQSA_ERR_HIP.  The
+    failure is forced from the host (CQSA_FAIL_AFTER_LAUNCHES=3: the call's Q and KV copies and its
+    first three launches are already issued when the fourth launch fails), so no kernel faults.  The
+    call returns only after its streams have drained; nothing of it is left running, and the next
+    call on the same pinned buffers is exact."""
+    m = cqsa()
+    B, Hq, Hkv, N, D = 1, 4, 2, 6000, 64
+    q, k, v = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=45)
+    qh, kh, vh = q.pin_memory(), k.pin_memory(), v.pin_memory()
+    out = torch.full((B, Hq, N, D), 7.0, dtype=torch.float32, pin_memory=True)
+    budget = 2_000_000
+    say("injected launch failure, streamed")
+    monkeypatch.setenv("CQSA_FAIL_AFTER_LAUNCHES", "3")
+    with pytest.raises(m.CqsaError, match="HIP.*injected"):
+        m.attention(qh, kh, vh, is_causal=True, mem_budget=budget, out=out)
+    torch.cuda.synchronize()                      # no GPU error left behind
+    monkeypatch.delenv("CQSA_FAIL_AFTER_LAUNCHES")
+    o, lse, info = m.attention(qh, kh, vh, is_causal=True, mem_budget=budget, out=out, return_lse=True,
+                               return_info=True)
+    assert info["streamed"] == 1 and info["kernel_launches"] > 3
+    rows = sample_rows(B, Hq, N, seed=45, n_random=64, edge=8)
+    ref = reference(q, k, v, causal=True, scale=0.125, rows=rows)
+    compare(o, lse, ref, torch.float16, rows=rows, label="after an injected failure")
+
+
 def test_allocation_failure_is_reported_and_leaves_nothing_behind():
     """With no caller workspace the library allocates its own; when the device cannot hold it the call
     returns CQSA_ERR_OOM (no retry) and the free memory afterwards is what it was.  The device is
