@@ -1718,8 +1718,9 @@ int variant() {
     return (v < 0 || v >= kNumShapes) ? 0 : v;
 }
 
-// The split-P product (two PV chains) runs on the DMA kernel in one shape per head dim.
-constexpr Shape kSplit64 = {2, 8, 64, 2, 0};
+// The split-P product (two PV chains) runs on the DMA kernel in one shape per head dim; pipelined at
+// D=64 (measured 11% faster than 8 waves in the plain order, though it spills three VGPRs).
+constexpr Shape kSplit64 = {2, 4, 64, 3, 1};
 constexpr Shape kSplit128 = {2, 8, 32, 2, 0};
 
 Shape shape_of(int D, int p_split) {
@@ -1731,9 +1732,9 @@ template <int D, int DT>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
     if (a.p_split) {
         if constexpr (D == 64)
-            return launch_dma_t<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true>(a, st);
+            return launch_dma_t<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true, (kSplit64.pipe != 0)>(a, st);
         else
-            return launch_dma_t<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true>(a, st);
+            return launch_dma_t<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true, (kSplit128.pipe != 0)>(a, st);
     }
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
     if (sh.kind == 2) {
@@ -1805,10 +1806,10 @@ template <int D, int DT>
 hipError_t launch_wave_d(const FwdArgs& a, const WaveTable& t, int blocks, hipStream_t st) {
     if (a.p_split) {
         if constexpr (D == 64)
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true, false>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit64.kt, kSplit64.nw, kSplit64.wpe, true, (kSplit64.pipe != 0)>), dim3((unsigned)blocks),
                                dim3(kSplit64.nw * 64), 0, st, a, t);
         else
-            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true, false>),
+            hipLaunchKernelGGL((fwd_wave_kernel<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true, (kSplit128.pipe != 0)>),
                                dim3((unsigned)blocks), dim3(kSplit128.nw * 64), 0, st, a, t);
     } else {
         if constexpr (D == 64)

@@ -160,9 +160,10 @@ def test_plan_errors():
 
 
 def test_plan_split_p_block_m():
-    """The split-P product runs in its own kernel shape (256-row workgroups at both head dims)."""
+    """The split-P product runs in its own kernel shape: 128-row workgroups (4 waves, pipelined) at
+    D=64, 256-row workgroups at D=128."""
     a = plan(shp(1, 2, 1000, 64), shp(1, 2, 1000, 64), shp(1, 2, 1000, 64), True, GB, precision=1)
-    assert a["block_m"] == 256
+    assert a["block_m"] == 128
     b = plan(shp(1, 2, 1000, 128), shp(1, 2, 1000, 128), shp(1, 2, 1000, 128), True, GB, precision=1)
     assert b["block_m"] == 256
 
