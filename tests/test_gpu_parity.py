@@ -582,7 +582,9 @@ def test_allocation_failure_is_reported_and_leaves_nothing_behind():
         torch.cuda.empty_cache()
     assert st == -4 and "hipMalloc" in msg, (st, msg)
     free1, _ = torch.cuda.mem_get_info()
-    assert abs(free1 - free0) <= 64 << 20, (free0, free1)
+    # nothing of the library is left allocated; the runtime may release cached memory of its own when
+    # an allocation fails, so more memory can be free afterwards than before
+    assert free1 >= free0 - (64 << 20), (free0, free1)
     # and the same call succeeds once the memory is back
     o2 = m.attention(q[:, :, :4096], k[:, :, :4096], v[:, :, :4096], is_causal=True, mem_budget=budget)
     assert torch.isfinite(o2.float()).all()
