@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
            "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward", "schedule_trace", "backward_schedule_trace",
-           "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
+           "set_test_controls", "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcqsa.so")
@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(_PKG, "libcqsa.so")
 F16, BF16, F32 = 0, 1, 2
 WHERE_DETECT, WHERE_DEVICE, WHERE_HOST = 0, 1, 2
 MERGE_AUTO, MERGE_KERNEL, MERGE_FUSED = 0, 1, 2
+LSE_NONE, LSE_WITH_OUT, LSE_DEVICE, LSE_HOST = 0, 1, 2, 3
 _STATUS = {0: "OK", -1: "INVALID", -2: "UNSUPPORTED", -3: "BUDGET", -4: "OOM", -5: "HIP"}
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 
@@ -99,6 +100,12 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def set_test_controls(fwd_variant: int = 0, fail_after_launches: int = -1) -> None:
+    """Process-wide test and measurement controls (cqsa_set_test_controls): the forward kernel shape
+    (0 = the default) and forced launch failures after n launches per call (-1 = off)."""
+    _check(_lib.cqsa_set_test_controls(int(fwd_variant), int(fail_after_launches)))
+
+
 def _load_library():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -153,6 +160,8 @@ def _load_library():
     lib.cqsa_cqs_default_set.restype = ctypes.c_int32
     lib.cqsa_probe_device.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(CqsaProbeResult)]
     lib.cqsa_probe_device.restype = ctypes.c_int
+    lib.cqsa_set_test_controls.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    lib.cqsa_set_test_controls.restype = ctypes.c_int
     for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo, CqsaProbeResult)):
         if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"{cls.__name__} layout differs from the built library")
@@ -253,13 +262,23 @@ def _options(q_chunk=None, kv_chunk=None, kv_splits=None, merge=None, stream=Non
     return o
 
 
+def _lse_code(want_lse) -> int:
+    """want_lse: False/None (no lse), True (lse where out lives), "device" or "host"."""
+    if want_lse in (False, None, 0):
+        return LSE_NONE
+    if want_lse is True or want_lse == 1:
+        return LSE_WITH_OUT
+    return {"device": LSE_DEVICE, "host": LSE_HOST}[want_lse]
+
+
 def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False, q_chunk=None, kv_chunk=None,
          kv_splits=None, merge=None, where=None, num_cus=None, cqs=None, precision=0, wave_tokens=None,
          cqs_itr=None) -> dict:
     """The plan ``attention`` would run (nothing is allocated or computed).
 
     ``q``/``k``/``v``/``out`` may be tensors, or ``(shape, dtype)`` pairs with ``where`` = a dict of
-    "device"/"host" per name, for a dry run of shapes that do not exist."""
+    "device"/"host" per name, for a dry run of shapes that do not exist.  ``want_lse``: False, True
+    (lse where out lives), "device" or "host"."""
     where = where or {}
 
     def mk(name, t, default_dtype):
@@ -287,7 +306,7 @@ def plan(q, k, v, is_causal=False, mem_budget=None, *, out=None, want_lse=False,
     opt = _options(q_chunk, kv_chunk, kv_splits, merge, num_cus=num_cus, cqs=cqs, precision=precision,
                    wave_tokens=wave_tokens, cqs_itr=cqs_itr)
     _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0,
-                          int(mem_budget or 0), ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt),
+                          int(mem_budget or 0), ctypes.byref(do), _lse_code(want_lse), ctypes.byref(opt),
                           ctypes.byref(info)))
     return info.as_dict()
 
@@ -328,7 +347,8 @@ def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chu
     """The operations ``attention`` would issue, recorded instead of run (no GPU needed); see
     ``cqsa_schedule_trace`` in cqsa.h for the line format.  q, k, v and out are
     ``(shape, dtype, where, address)`` tuples ("host" or "device"; the address is a stand-in that is
-    never dereferenced), optionally with element strides as a fifth item (default: contiguous)."""
+    never dereferenced), optionally with element strides as a fifth item (default: contiguous).
+    ``want_lse``: False, True (lse where out lives), "device" or "host"."""
     def mk(t):
         shape, dtype, where, addr = t[:4]
         stride = t[4] if len(t) > 4 else [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
@@ -346,7 +366,7 @@ def schedule_trace(q, k, v, is_causal, mem_budget, *, out, want_lse=False, q_chu
                    wave_tokens=wave_tokens, cqs_itr=cqs_itr)
     need = ctypes.c_uint64(0)
     args = (ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0, int(mem_budget),
-            ctypes.byref(do), 1 if want_lse else 0, ctypes.byref(opt))
+            ctypes.byref(do), _lse_code(want_lse), ctypes.byref(opt))
     _check(_lib.cqsa_schedule_trace(*args, None, 0, ctypes.byref(need)))
     buf = ctypes.create_string_buffer(int(need.value))
     _check(_lib.cqsa_schedule_trace(*args, buf, int(need.value), None))
@@ -401,12 +421,15 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool
         dq, dk, dv, do = _desc(q), _desc(k), _desc(v), _desc(out)
         opt = _options(q_chunk, kv_chunk, kv_splits, merge, stream=st.cuda_stream, cqs=cqs, precision=precision,
                        wave_tokens=wave_tokens, cqs_itr=cqs_itr)
-        budget = int(mem_budget or 0)
+        # the budget is resolved here, once: left to the library, the plan below and the call would each
+        # read the free memory, and the workspace allocated in between would change the second reading
+        budget = int(mem_budget or 0) or int(torch.cuda.mem_get_info(dev)[0])
         # size the workspace first so that device-resident calls take it from PyTorch's allocator
         # (stream-ordered, no hipMalloc, no synchronisation)
         pinfo = CqsaPlanInfo()
+        lse_code = LSE_NONE if lse is None else (LSE_DEVICE if lse.is_cuda else LSE_HOST)
         _check(_lib.cqsa_plan(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), 1 if is_causal else 0, budget,
-                              ctypes.byref(do), 1 if return_lse else 0, ctypes.byref(opt), ctypes.byref(pinfo)))
+                              ctypes.byref(do), lse_code, ctypes.byref(opt), ctypes.byref(pinfo)))
         ws = None
         if pinfo.workspace_bytes > 0:
             ws = torch.empty(int(pinfo.workspace_bytes), dtype=torch.uint8, device=dev)

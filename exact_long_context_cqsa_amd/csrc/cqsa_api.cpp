@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -615,10 +616,13 @@ cqsa_status make_plan_cqs(const Problem& P, uint64_t budget, const cqsa_options&
     in.kv_splits = 1;
     in.chunk_pairs = pairs;
     in.merges = folds;
-    in.kernel_launches = launches + 1 + (P.out.host ? c : 1);   // wave launches, accumulator fill, finalize
+    // wave launches, the accumulator fill, and the finalize: one per query part when out or lse is
+    // shipped to the host in query-part pieces, else one
+    const bool host_out = P.out.host || (P.want_lse && P.lse_host);
+    in.kernel_launches = launches + 1 + (host_out ? c : 1);
     in.workspace_bytes = pl->total;
     in.h2d_bytes = h2d;
-    in.d2h_bytes = P.out.host ? rows * P.D * P.out.es + ((P.want_lse && P.lse_host) ? rows * 4 : 0) : 0;
+    in.d2h_bytes = (P.out.host ? rows * P.D * P.out.es : 0) + ((P.want_lse && P.lse_host) ? rows * 4 : 0);
     in.cqs_c = c0;
     in.cqs_subproblems = (int32_t)subs.size();
     in.cqs_waves = (int32_t)pl->cqs_waves.size();
@@ -1003,15 +1007,15 @@ void set_v(FwdArgs& a, const char* data, int64_t sb, int64_t sh, int64_t sn) {
     a.v_sn = sn;
 }
 
-// Failure injection for the error-path tests: with CQSA_FAIL_AFTER_LAUNCHES=n in the environment, every
+// Failure injection for the error-path tests (cqsa_set_test_controls): with a limit n >= 0, every
 // forward launch of a call after its first n fails as a launch error would, once the call's earlier
-// copies and launches have been issued.  The count restarts at each public call.
+// copies and launches have been issued.  The count restarts at each public call; -1 = off.
+std::atomic<int64_t> g_fail_after{-1};
 thread_local int64_t g_fwd_launches = 0;
 
 bool injected_launch_failure() {
-    const char* e = std::getenv("CQSA_FAIL_AFTER_LAUNCHES");
-    if (!e || !*e) return false;
-    return g_fwd_launches++ >= std::atoll(e);
+    const int64_t n = g_fail_after.load(std::memory_order_relaxed);
+    return n >= 0 && g_fwd_launches++ >= n;
 }
 
 cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
@@ -1042,7 +1046,7 @@ cqsa_status run_fwd(const Problem& P, FwdArgs& a, hipStream_t st) {
         g_rec->line(l);
         return CQSA_OK;
     }
-    if (injected_launch_failure()) return fail(CQSA_ERR_HIP, "forward kernel launch failed: injected (CQSA_FAIL_AFTER_LAUNCHES)");
+    if (injected_launch_failure()) return fail(CQSA_ERR_HIP, "forward kernel launch failed: injected (cqsa_set_test_controls)");
     const hipError_t e = launch_fwd(a, (int)P.D, P.dtype == CQSA_F16 ? ET_F16 : ET_BF16, st);
     if (e != hipSuccess) return fail(CQSA_ERR_HIP, "forward kernel launch failed: %s", hipGetErrorString(e));
     return CQSA_OK;
@@ -1162,7 +1166,10 @@ struct TimedCopy {
 // Q chunks x KV chunks; operands may live in pinned host memory.
 cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t st, DeviceRes* res,
                          cqsa_plan_info* info) {
-    const bool need_side = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
+    // out and lse of a Q chunk are staged in the workspace when they live on the host; the next Q chunk
+    // writes the same staging, so it waits for the D2H copy of either one
+    const bool host_out = P.out.host || (P.want_lse && P.lse_host);
+    const bool need_side = P.q.host || P.k.host || P.v.host || host_out;
     hipStream_t h2d = st, d2h = st;
     if (need_side) {
         CQSA_TRY(side_streams(res));
@@ -1289,7 +1296,7 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
             a.r1 = qn;
             a.acc_rows = qn;
             if (single) {
-                if (P.out.host && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
+                if (host_out && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
                 a.mode = FWD_FINAL;
                 a.out = out_base;
                 a.out_dtype = elem_type(P.out.dtype);
@@ -1332,7 +1339,7 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
             ++pair;
         }
         if (!single) {
-            if (P.out.host && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
+            if (host_out && d2h_recorded) CQSA_HIP(x_wait(st, ev_d2h));
             MergeArgs m;
             std::memset(&m, 0, sizeof m);
             m.part_o[0] = acc_o;
@@ -1357,7 +1364,7 @@ cqsa_status exec_chunked(const Problem& P, const Plan& pl, char* ws, hipStream_t
         }
         CQSA_HIP(x_record(ev_qfree, st));
         qfree_recorded = true;
-        if (P.out.host || (P.want_lse && P.lse_host)) {
+        if (host_out) {
             CQSA_HIP(x_record(ev_fin, st));
             CQSA_HIP(x_wait(d2h, ev_fin));
             TimedCopy tc;
@@ -1705,6 +1712,17 @@ cqsa_status build_problem(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa
     return check_problem(P, is_causal, scale);
 }
 
+// want_lse of cqsa_plan and cqsa_schedule_trace: CQSA_LSE_NONE, _WITH_OUT, _DEVICE or _HOST
+cqsa_status check_lse_where(int want_lse) {
+    if (want_lse < CQSA_LSE_NONE || want_lse > CQSA_LSE_HOST)
+        return fail(CQSA_ERR_INVALID, "want_lse %d is not one of CQSA_LSE_NONE/WITH_OUT/DEVICE/HOST", want_lse);
+    return CQSA_OK;
+}
+
+bool lse_on_host(int want_lse, bool out_host) {
+    return want_lse == CQSA_LSE_HOST || (want_lse == CQSA_LSE_WITH_OUT && out_host);
+}
+
 cqsa_status set_precision(const cqsa_options& o, Problem* P) {
     if (o.precision != 0 && o.precision != 1)
         return fail(CQSA_ERR_INVALID, "precision %d is not 0 (operand-rounded P) or 1 (split P)", o.precision);
@@ -1742,6 +1760,17 @@ extern "C" {
 const char* cqsa_last_error(void) { return g_err.c_str(); }
 
 int32_t cqsa_version(void) { return CQSA_ABI_VERSION; }
+
+cqsa_status cqsa_set_test_controls(int32_t fwd_variant, int64_t fail_after_launches) {
+    g_err.clear();
+    if (fwd_variant < 0 || fwd_variant > 4)
+        return fail(CQSA_ERR_INVALID, "fwd_variant %d is not in 0..4", fwd_variant);
+    if (fail_after_launches < -1)
+        return fail(CQSA_ERR_INVALID, "fail_after_launches %lld is below -1", (long long)fail_after_launches);
+    set_fwd_variant(fwd_variant);
+    g_fail_after.store(fail_after_launches, std::memory_order_relaxed);
+    return CQSA_OK;
+}
 
 uint64_t cqsa_struct_size(int32_t which) {
     switch (which) {
@@ -1797,9 +1826,10 @@ cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_ten
     Problem P;
     const bool detect = (q && q->where == CQSA_WHERE_DETECT) || (k && k->where == CQSA_WHERE_DETECT) ||
                         (v && v->where == CQSA_WHERE_DETECT) || (out && out->where == CQSA_WHERE_DETECT);
+    CQSA_TRY(check_lse_where(want_lse));
     CQSA_TRY(build_problem(q, k, v, is_causal, 0.f, out, nullptr, want_lse, detect, true, &P));
     CQSA_TRY(set_precision(o, &P));
-    P.lse_host = want_lse && P.out.host;  // lse travels with out
+    P.lse_host = lse_on_host(want_lse, P.out.host);
     P.streamed = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
     uint64_t budget = 0;
     CQSA_TRY(resolve_budget(mem_budget, &budget));
@@ -1828,12 +1858,13 @@ cqsa_status cqsa_schedule_trace(const cqsa_tensor* q, const cqsa_tensor* k, cons
     std::memset(&o, 0, sizeof o);
     if (opt) o = *opt;
     Problem P;
+    CQSA_TRY(check_lse_where(want_lse));
     CQSA_TRY(build_problem(q, k, v, is_causal, 0.f, out, nullptr, want_lse, false, true, &P));
     CQSA_TRY(set_precision(o, &P));
-    P.lse_host = want_lse && P.out.host;
+    P.lse_host = lse_on_host(want_lse, P.out.host);
     P.streamed = P.q.host || P.k.host || P.v.host || P.out.host || (P.want_lse && P.lse_host);
     Recorder rec;
-    if (P.want_lse) {   // the lse array: a distinct fake range after out (host with out, else device)
+    if (P.want_lse) {   // the lse array: a distinct stand-in range 2^40 bytes past out
         P.lse = reinterpret_cast<float*>(out->data ? static_cast<char*>(out->data) + ((uint64_t)1 << 40) : nullptr);
     }
     if (!P.empty) {

@@ -158,6 +158,9 @@ hipError_t launch_bwd_pass(const BwdArgs& a, int D, int dtype, int pass, hipStre
 hipError_t launch_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_t D, void* dst, int dtype,
                        int64_t sb, int64_t sh, int64_t sn, hipStream_t stream);
 
+// Which forward kernel shape the launches take (0 = the default); set by cqsa_set_test_controls.
+void set_fwd_variant(int v);
+
 // Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
 int fwd_block_m(int D, int p_split);
 

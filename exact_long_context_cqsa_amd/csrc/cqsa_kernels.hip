@@ -23,6 +23,7 @@
 // LDS that way, fwd_dma_kernel assembles it from row-major tiles with transpose loads.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -1709,9 +1710,8 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 // asked of the register allocator, pipe: softmax and PV products interleaved per 32-key block), kind 1
 // the register-staged kernel, kind 0 the ping-pong kernel.
 // Entry 0 is the default (pipelined at D=64, where it measured faster; not at D=128, where it did
-// not); entry 4 is the default shape with the other choice.  The environment variable
-// CQSA_FWD_VARIANT (read at every launch) selects another entry, for measurement and for the tests
-// that cover every kernel.
+// not); entry 4 is the default shape with the other choice.  cqsa_set_test_controls selects another
+// entry for the whole process, for measurement and for the tests that cover every kernel.
 struct Shape {
     int kind, nw, kt, wpe, pipe;
 };
@@ -1721,11 +1721,9 @@ constexpr Shape kShapes128[] = {{2, 8, 64, 2, 0}, {2, 8, 32, 2, 0}, {1, 8, 64, 2
                                 {2, 8, 64, 2, 1}};
 constexpr int kNumShapes = 5;
 
-int variant() {
-    const char* e = getenv("CQSA_FWD_VARIANT");
-    const int v = (e && *e) ? atoi(e) : 0;
-    return (v < 0 || v >= kNumShapes) ? 0 : v;
-}
+std::atomic<int> g_variant{0};
+
+int variant() { return g_variant.load(std::memory_order_relaxed); }
 
 // The split-P product (two PV chains) runs on the DMA kernel in one shape per head dim; pipelined at
 // D=64 (measured 11% faster than 8 waves in the plain order, though it spills three VGPRs).
@@ -1775,6 +1773,8 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+void set_fwd_variant(int v) { g_variant.store((v < 0 || v >= kNumShapes) ? 0 : v, std::memory_order_relaxed); }
 
 int fwd_block_m(int D, int p_split) { return shape_of(D, p_split).nw * 32; }
 

@@ -41,8 +41,6 @@
  *     copy) returns only once its stream and the library's copy streams have
  *     drained: nothing of the failed call still reads or writes caller memory.
  *     Its outputs are then unspecified.
- *   - CQSA_FAIL_AFTER_LAUNCHES=n in the environment (for error-path tests) makes
- *     every forward launch of a call after its first n fail with CQSA_ERR_HIP.
  */
 #ifndef CQSA_H
 #define CQSA_H
@@ -54,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CQSA_ABI_VERSION 4
+#define CQSA_ABI_VERSION 5
 
 typedef enum {
     CQSA_OK = 0,
@@ -178,11 +176,19 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
                               float scale, uint64_t mem_budget, cqsa_tensor* out, float* lse,
                               const cqsa_options* opt, cqsa_plan_info* info);
 
+/* want_lse of cqsa_plan and cqsa_schedule_trace: whether the call returns lse, and where the lse
+ * array lives (host lse is staged in the workspace and copied back, like host out). */
+#define CQSA_LSE_NONE 0      /* no lse */
+#define CQSA_LSE_WITH_OUT 1  /* lse lives where out lives */
+#define CQSA_LSE_DEVICE 2    /* lse in device memory */
+#define CQSA_LSE_HOST 3      /* lse in pinned host memory */
+
 /*
  * cqsa_plan: the plan cqsa_attention_ex would run, without running it or
  * allocating (the dry run of the pages' estimate(): stream-cqsa 2.2.2 -> 2.2.3
  * diff, README.md section "Use").  Tensor data may be NULL; then each tensor's
- * `where` must say DEVICE or HOST.  With mem_budget > 0, explicit `where` values
+ * `where` must say DEVICE or HOST.  want_lse is one of the CQSA_LSE_ values
+ * (CQSA_ERR_INVALID otherwise).  With mem_budget > 0, explicit `where` values
  * and opt->num_cus > 0 the call makes no HIP call at all.
  */
 cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
@@ -201,8 +207,9 @@ cqsa_status cqsa_plan(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_ten
  * touch one device byte, one of them writing, must be ordered by their streams and events).
  * The tensors' data pointers are used as given (stand-in addresses are fine; they are never
  * dereferenced); every `where` must be DEVICE or HOST and mem_budget must be > 0; opt->workspace and
- * opt->stream, when set, stand in for the workspace base and the caller's stream.  want_lse records
- * the lse writes at a stand-in address 2^40 bytes past out.  The text (NUL-terminated) goes to buf;
+ * opt->stream, when set, stand in for the workspace base and the caller's stream.  want_lse (a
+ * CQSA_LSE_ value, which also says where lse lives) records the lse writes at a stand-in address
+ * 2^40 bytes past out.  The text (NUL-terminated) goes to buf;
  * *needed (may be NULL) receives the size it needs.  CQSA_ERR_INVALID when buf_len is too small (buf
  * then holds the truncated text), or an argument error of cqsa_plan.
  */
@@ -221,7 +228,12 @@ cqsa_status cqsa_backward_schedule_trace(const cqsa_tensor* q, const cqsa_tensor
                                          char* buf, uint64_t buf_len, uint64_t* needed);
 
 /*
- * cqsa_fwd_partial: the partial triple of one KV chunk, for every query row.
+ * cqsa_fwd_partial: the partial triple of one KV chunk, for every query row.  This is one
+ * subproblem's forward pass of the method, the FlashAttention-2 online softmax of the pages' CQS
+ * forward kernel (stream-cqsa 2.2.0 -> 2.2.2 diff, README.md, kernel table) run over one key range
+ * and stopped before the normalisation, so that the ranges can be merged afterwards (stream-cqsa
+ * 2.2.2 -> 2.2.3 diff, README.md section "Use": the decomposed call still gives the monolithic
+ * answer).
  *   q, k, v            device tensors as above.
  *   kv_begin, kv_end   the key range [kv_begin, kv_end) of the chunk (0 <= begin <= end <= Nk).
  *   o_part             fp32 [B, Hq, Nq, D] contiguous: sum over visible keys in the range of
@@ -236,7 +248,10 @@ cqsa_status cqsa_fwd_partial(const cqsa_tensor* q, const cqsa_tensor* k, const c
                              void* stream);
 
 /*
- * cqsa_lse_merge: exact log-sum-exp merge of num_parts partial triples, row by row:
+ * cqsa_lse_merge: exact log-sum-exp merge of num_parts partial triples, row by row (the merge of
+ * per-subproblem partial outputs that the pages' wave engine performs on the host, here on the
+ * device: stream-cqsa 2.2.0 -> 2.2.2 diff, README.md, the paragraph on peak memory and the wave
+ * budget, where each packed token keeps one fp32 partial output until its wave is merged):
  *   m = max_p m_p,  w_p = exp(m_p - m) (0 when m_p = -inf),  l = sum_p w_p l_p,
  *   O = sum_p w_p O_p.  Empty partials (m = -inf) are identities and never give NaN.
  *   o_parts[p]   device fp32 [rows, D];  ml_parts[p]  device fp32 [rows, 2] (m, l).
@@ -251,7 +266,11 @@ cqsa_status cqsa_lse_merge(const float* const* o_parts, const float* const* ml_p
 
 /*
  * cqsa_finalize: deliver a merged triple: out = O / l rounded to out's dtype, and
- * lse = m + ln(l).
+ * lse = m + ln(l).  This is the last step of the pages' attention() call, which leaves the fp32
+ * result in the accumulator and then casts it to the input dtype and moves it to the caller
+ * (stream-cqsa 2.2.0 -> 2.2.2 diff, stream_cqsa/api.py, _attention() and _deliver()), with the
+ * softmax normaliser applied once at the end as in the FlashAttention-2 recurrence of the forward
+ * kernel (the same diff, README.md, kernel table).
  *   o     device fp32 [B, Hq, Nq, D] contiguous (B, Hq, Nq, D taken from out's shape).
  *   ml    device fp32 [B, Hq, Nq, 2] contiguous.
  *   out   device tensor, any strides (stride[3] == 1); lse NULL or device fp32 [B, Hq, Nq].
@@ -358,10 +377,23 @@ int32_t cqsa_cqs_default_set(int32_t c, int32_t* set, int32_t max_l);
 
 /* Name and shape of the forward kernel a call with this head dim (64 or 128) and precision (see
  * cqsa_options) launches, e.g. "fwd_dma_kernel waves=4 keys_per_tile=64 rows_per_wave=32"; "" for
- * another head dim.  With precision 0 the choice follows the environment variable CQSA_FWD_VARIANT
- * (0 or unset = the default kernel), read at every launch.  The string is static; no HIP call is
- * made. */
+ * another head dim.  With precision 0 the choice follows cqsa_set_test_controls (fwd_variant 0 =
+ * the default kernel).  The string is static; no HIP call is made. */
 const char* cqsa_fwd_kernel_name(int64_t head_dim, int32_t precision);
+
+/*
+ * Test and measurement controls, process-wide (not part of the attention contract; every call
+ * runs with the defaults, 0 and -1, unless a test or a measurement sets them):
+ *   fwd_variant          0 = the default forward kernel of each head dim; 1..4 = the alternative
+ *                        kernel shapes, so that tests can run every kernel and measurements can
+ *                        compare them (cqsa_fwd_kernel_name names the choice).
+ *   fail_after_launches  -1 = off; n >= 0 makes every forward launch of a call after its first n
+ *                        fail from the host, as a failed launch would (CQSA_ERR_HIP), so that tests
+ *                        can exercise the error path of a streamed call with no kernel fault.
+ * CQSA_ERR_INVALID for values outside these ranges (nothing is changed then).  Host-only; no HIP
+ * call.  Calls in flight on other threads see the change at their next launch.
+ */
+cqsa_status cqsa_set_test_controls(int32_t fwd_variant, int64_t fail_after_launches);
 
 /*
  * Device probe: the rates the kernels are measured against, measured on the current device, each with

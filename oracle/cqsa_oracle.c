@@ -31,7 +31,8 @@
  * product of two such values is exact in double.  Each row is done in two
  * passes (scores and their maximum, then weights), and l and every output
  * coordinate are accumulated with Neumaier's compensated summation
- * (Neumaier, 1974).  Rows are spread over POSIX threads.
+ * (Neumaier, 1974).  Rows are handed out to POSIX threads one small batch at a
+ * time; each row's result depends only on the row.
  */
 #include <math.h>
 #include <pthread.h>
@@ -65,6 +66,18 @@ double oracle_bf16_to_double(uint16_t b) {
     return (double)f;
 }
 
+/* Every 16-bit pattern of each input format, widened once by the two functions above (whose every
+ * output the tests check), so that the inner loops read a table instead of decoding. */
+static double g_decode[2][65536];
+static pthread_once_t g_decode_once = PTHREAD_ONCE_INIT;
+
+static void fill_decode_tables(void) {
+    for (uint32_t u = 0; u < 65536u; ++u) {
+        g_decode[0][u] = oracle_f16_to_double((uint16_t)u);
+        g_decode[1][u] = oracle_bf16_to_double((uint16_t)u);
+    }
+}
+
 typedef struct {
     const uint16_t* q;
     const uint16_t* k;
@@ -81,7 +94,8 @@ typedef struct {
 typedef struct {
     const oracle_problem* p;
     const int64_t* rows; /* triples (b, h, i) */
-    int64_t row_begin, row_end;
+    int64_t nrows;
+    int64_t* next_row;   /* shared by the workers: the next row not yet taken */
     int64_t key_lo, key_hi;
     int32_t partial;
     double* out_o;       /* [nrows][D] */
@@ -92,18 +106,22 @@ typedef struct {
 } oracle_job;
 
 static inline double elem(const oracle_problem* p, const uint16_t* base, uint64_t off) {
-    return p->dtype == ORACLE_BF16 ? oracle_bf16_to_double(base[off]) : oracle_f16_to_double(base[off]);
+    return g_decode[p->dtype == ORACLE_BF16 ? 1 : 0][base[off]];
 }
 
-/* Neumaier: add x to (sum, comp). */
+/* Neumaier: add x to (sum, comp), where comp collects the exact rounding error of every addition.
+ * The error is formed by Knuth's TwoSum, which needs no test of which operand is larger in
+ * magnitude; Neumaier's formulation branches on |sum| >= |x| instead, and both give the same exact
+ * error of a finite sum. */
 static inline void nsum(double* sum, double* comp, double x) {
-    double t = *sum + x;
-    if (fabs(*sum) >= fabs(x))
-        *comp += (*sum - t) + x;
-    else
-        *comp += (x - t) + *sum;
+    const double t = *sum + x;
+    const double z = t - *sum;
+    *comp += (*sum - (t - z)) + (x - z);
     *sum = t;
 }
+
+/* Rows in batches of this many go to the next free worker. */
+enum { ROW_BATCH = 4 };
 
 static void* row_worker(void* arg) {
     oracle_job* job = (oracle_job*)arg;
@@ -120,7 +138,11 @@ static void* row_worker(void* arg) {
         free(s); free(qrow); free(osum); free(ocomp);
         return NULL;
     }
-    for (int64_t r = job->row_begin; r < job->row_end; ++r) {
+    for (;;) {
+      const int64_t r0 = __atomic_fetch_add(job->next_row, (int64_t)ROW_BATCH, __ATOMIC_RELAXED);
+      if (r0 >= job->nrows) break;
+      const int64_t r1 = r0 + ROW_BATCH < job->nrows ? r0 + ROW_BATCH : job->nrows;
+      for (int64_t r = r0; r < r1; ++r) {
         const int64_t b = job->rows[3 * r + 0];
         const int64_t h = job->rows[3 * r + 1];
         const int64_t i = job->rows[3 * r + 2];
@@ -165,6 +187,7 @@ static void* row_worker(void* arg) {
             if (job->out_m) job->out_m[r] = m;
             if (job->out_l) job->out_l[r] = (hi > lo) ? l : 0.0;
         }
+      }
     }
     free(s); free(qrow); free(osum); free(ocomp);
     job->status = 0;
@@ -187,24 +210,24 @@ int oracle_rows(const oracle_problem* p, const int64_t* rows, int64_t nrows, int
         const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
         if (b < 0 || b >= p->B || h < 0 || h >= p->Hq || i < 0 || i >= p->Nq) return -1;
     }
+    pthread_once(&g_decode_once, fill_decode_tables);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > nrows) nthreads = (int32_t)(nrows > 0 ? nrows : 1);
     pthread_t th[256];
     int joinable[256];
     oracle_job jobs[256];
-    const int64_t per = (nrows + nthreads - 1) / nthreads;
+    int64_t next_row = 0;
     int njobs = 0;
     for (int t = 0; t < nthreads; ++t) {
         oracle_job* j = &jobs[t];
         j->p = p; j->rows = rows; j->key_lo = key_lo; j->key_hi = key_hi; j->partial = partial;
         j->out_o = out_o; j->out_m = out_m; j->out_l = out_l; j->out_lse = out_lse; j->status = 0;
-        j->row_begin = (int64_t)t * per;
-        j->row_end = j->row_begin + per < nrows ? j->row_begin + per : nrows;
-        if (j->row_begin >= j->row_end) break;
+        j->nrows = nrows;
+        j->next_row = &next_row;
         njobs = t + 1;
         joinable[t] = pthread_create(&th[t], NULL, row_worker, j) == 0;
-        if (!joinable[t]) row_worker(j); /* no thread available: run it here */
+        if (!joinable[t]) row_worker(j); /* no thread available: take rows here */
     }
     int status = 0;
     for (int t = 0; t < njobs; ++t) {
@@ -404,6 +427,7 @@ int oracle_backward(const oracle_problem* p, const uint16_t* dout, const int64_t
                     double* dv, int32_t nthreads) {
     if (!p || !dout || !do_stride || !dq || !dk || !dv) return -1;
     if (p->Hkv <= 0 || p->Hq % p->Hkv != 0 || p->D <= 0 || (p->causal && p->Nq > p->Nk)) return -1;
+    pthread_once(&g_decode_once, fill_decode_tables);
     const int64_t nq = p->B * p->Hq * p->Nq, nk = p->B * p->Hkv * p->Nk;
     double* stats = (double*)malloc(sizeof(double) * 3 * (size_t)(nq > 0 ? nq : 1));
     if (!stats) return -2;

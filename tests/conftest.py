@@ -20,3 +20,12 @@ def _built_cpu_helpers():
     synth.build(force=False)
     oracle.build(force=False)
     yield
+
+
+@pytest.fixture
+def test_controls():
+    """Sets the library's process-wide test controls (forward kernel shape, forced launch failures)
+    for one test and restores the defaults afterwards."""
+    import exact_long_context_cqsa_amd as m
+    yield m.set_test_controls
+    m.set_test_controls(0, -1)

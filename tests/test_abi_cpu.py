@@ -35,31 +35,35 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
-def test_forward_kernel_name(monkeypatch):
+def test_forward_kernel_name(test_controls):
     import exact_long_context_cqsa_amd as m
-    monkeypatch.delenv("CQSA_FWD_VARIANT", raising=False)
+    test_controls(0, -1)
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
     assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ")
     assert m.fwd_kernel_name(96) == ""
     # the default shape is pipelined at D=64 and not at D=128; variant 4 is the other choice
     assert "pipelined" in m.fwd_kernel_name(64) and "pipelined" not in m.fwd_kernel_name(128)
-    monkeypatch.setenv("CQSA_FWD_VARIANT", "2")
+    test_controls(2, -1)
     assert m.fwd_kernel_name(64).startswith("fwd_kernel ")
-    monkeypatch.setenv("CQSA_FWD_VARIANT", "4")
+    test_controls(4, -1)
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ") and "pipelined" not in m.fwd_kernel_name(64)
     assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ") and "pipelined" in m.fwd_kernel_name(128)
-    monkeypatch.setenv("CQSA_FWD_VARIANT", "99")   # out of range: the default
-    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
+    for bad in ((99, -1), (-1, -1), (0, -2)):   # out of range: rejected, nothing changes
+        with pytest.raises(m.CqsaError, match="INVALID"):
+            test_controls(*bad)
+        assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ") and "pipelined" not in m.fwd_kernel_name(64)
     # split-P runs the DMA kernel in its own shape whatever the variant
-    monkeypatch.setenv("CQSA_FWD_VARIANT", "2")
+    test_controls(2, -1)
     assert m.fwd_kernel_name(64, 1).startswith("fwd_dma_kernel ") and m.fwd_kernel_name(64, 1).endswith("split_p")
     assert m.fwd_kernel_name(128, 1).endswith("split_p")
+    test_controls(0, -1)
+    assert "pipelined" in m.fwd_kernel_name(64)
 
 
 def test_struct_layout_and_version():
     import exact_long_context_cqsa_amd as m
     lib = m._lib
-    assert lib.cqsa_version() == 4
+    assert lib.cqsa_version() == 5
     assert lib.cqsa_struct_size(0) == ctypes.sizeof(m.CqsaTensor) == 80
     assert lib.cqsa_struct_size(1) == ctypes.sizeof(m.CqsaOptions) == 88
     assert [f for f, _ in m.CqsaOptions._fields_][-3:] == ["cqs_set", "wave_tokens", "cqs_itr"]

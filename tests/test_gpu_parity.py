@@ -71,10 +71,10 @@ VARIANT_CASES = [SMALL[1], SMALL[2], SMALL[3], SMALL[4], SMALL[7]]
 
 
 @pytest.mark.parametrize("variant", [1, 2, 3, 4])
-def test_every_forward_kernel_variant(variant, monkeypatch):
-    """The non-default forward kernels (selected per launch by CQSA_FWD_VARIANT) on ragged, GQA,
+def test_every_forward_kernel_variant(variant, test_controls):
+    """The non-default forward kernels (selected by cqsa_set_test_controls) on ragged, GQA,
     non-causal and long-key cases, monolithic and with a forced KV split."""
-    monkeypatch.setenv("CQSA_FWD_VARIANT", str(variant))
+    test_controls(variant, -1)
     for case in VARIANT_CASES:
         B, Hq, Hkv, Nq, Nk, D, dtype, causal = case
         say("variant", variant, case)
@@ -281,60 +281,79 @@ def test_lse_merge_kernel_matches_oracle_merge():
 
 
 def test_finalize():
+    """The finalize kernel against the oracle's normalise (o / l, m + ln l) of the same triples, and the
+    identity triple (l = 0, m = -inf), which the library delivers as out = 0, lse = -inf."""
+    import oracle
     rng = np.random.default_rng(4)
     B, H, N, D = 2, 3, 50, 64
     o = torch.from_numpy(rng.normal(0, 1, (B, H, N, D))).float()
     m = torch.from_numpy(rng.normal(0, 1, (B, H, N))).float()
     l = torch.from_numpy(rng.uniform(0.5, 9, (B, H, N))).float()
+    m[1, 2, 7], l[1, 2, 7], o[1, 2, 7] = -math.inf, 0.0, 0.0
     ml = torch.stack([m, l], -1)
     out, lse = cqsa().finalize(o.to(DEV), ml.to(DEV), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    torch.testing.assert_close(out.cpu(), o / l[..., None], rtol=1e-6, atol=1e-6)
-    torch.testing.assert_close(lse.cpu(), m + torch.log(l), rtol=1e-6, atol=1e-6)
+    want = oracle.normalise({"o": o.double().reshape(-1, D).numpy(), "m": m.double().reshape(-1).numpy(),
+                             "l": l.double().reshape(-1).numpy()})
+    got_o, got_lse = out.cpu().double().reshape(-1, D).numpy(), lse.cpu().double().reshape(-1).numpy()
+    ok = l.reshape(-1).numpy() > 0
+    np.testing.assert_allclose(got_o[ok], want["o"][ok], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(got_lse[ok], want["lse"][ok], rtol=1e-6, atol=1e-6)
+    assert np.all(got_o[~ok] == 0) and np.all(np.isneginf(got_lse[~ok]))
 
 
 def test_config2_monolithic_and_8way_split_agree():
-    """B=1, H=8, N=32768, D=64 causal fp16: one pass, and a forced split into 8 KV chunks."""
+    """B=1, H=8, N=32768, D=64 causal fp16: one pass, and a forced split into 8 KV chunks (merge kernel
+    and fused merges), each checked in full (all 262,144 rows) against the FP64 reference."""
     w = synth.workload(1)
-    say("workload", w.name)
+    say("workload", w.name, "every row")
     q, k, v, _ = synth.make_inputs(w)
-    rows = sample_rows(1, 8, w.Nq, seed=2, n_random=96, edge=32, boundaries=range(0, w.Nq, 4096))
-    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     mono, lse_m = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True)
     split, lse_s, info = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, out_dtype=torch.float32,
                                           return_lse=True, return_info=True)
+    fused, lse_f = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, merge=2, out_dtype=torch.float32,
+                                    return_lse=True)
     torch.cuda.synchronize()
     assert info["n_kv_chunks"] == 8 and info["chunk_pairs"] == 8
-    r1 = compare(mono, lse_m, ref, torch.float16, rows=rows, label="config2 mono")
-    r2 = compare(split, lse_s, ref, torch.float16, rows=rows, label="config2 split")
+    ref = reference(q, k, v, causal=True, scale=w.scale)
+    r1 = compare(mono, lse_m, ref, torch.float16, label="config2 mono")
+    r2 = compare(split, lse_s, ref, torch.float16, label="config2 split")
+    r3 = compare(fused, lse_f, ref, torch.float16, label="config2 fused")
     agree = (mono - split).abs().max().item()
-    say("config2", r1, r2, "max|mono-split|", agree)
+    say("config2", r1, r2, r3, "max|mono-split|", agree)
     assert agree <= 1e-3
-    # fused merges give the same answer
-    fused = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, merge=2, out_dtype=torch.float32)
-    torch.cuda.synchronize()
     assert (fused - split).abs().max().item() <= 1e-3
+
+
+# Rows checked at the sizes the reference cannot finish in full within the test's time: every (b, h),
+# with the first and last EDGE rows, rows +-1 around Q-chunk, KV-chunk and 128-row tile edges, and
+# RANDOM seeded rows.  (edge, random) per workload; the row count per (b, h) is logged.
+C14_SAMPLED = {"prompt_131072": (16, 64), "streamed_4m": (8, 24), "stress_full": (8, 24)}
 
 
 @pytest.mark.parametrize("nk", [8192, 32768, 131072])
 def test_config3_prompt_gqa(nk):
-    """2048 queries at the end of the context, 32 query heads over 8 KV heads, D=128, bf16."""
+    """2048 queries at the end of the context, 32 query heads over 8 KV heads, D=128, bf16: every row
+    at 8K and 32K keys; at 131K, sampled rows in every head."""
     w = synth.workload(2, nk=nk)
     say("workload", w.name)
     q, k, v, _ = synth.make_inputs(w)
-    rows = sample_rows(1, 32, 2048, seed=3, n_random=24, edge=8, boundaries=range(0, 2048, 128),
-                       heads=range(0, 32, 3))
-    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    if nk <= 32768:
+        rows = None
+    else:
+        edge, n_random = C14_SAMPLED["prompt_131072"]
+        rows = sample_rows(1, 32, 2048, seed=3, n_random=n_random, edge=edge, boundaries=range(0, 2048, 128))
+        say("config3", nk, "rows per head", len(rows) // 32)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True,
                                       return_info=True)
-    torch.cuda.synchronize()
-    say("config3", nk, info["kv_splits"], compare(out, lse, ref, torch.bfloat16, rows=rows, label=f"config3 {nk}"))
     # split-KV across the GPU merges to the same answer
     out2, lse2 = cqsa().attention(qd, kd, vd, is_causal=True, kv_splits=4, out_dtype=torch.float32,
                                   return_lse=True)
     torch.cuda.synchronize()
+    ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
+    say("config3", nk, info["kv_splits"], compare(out, lse, ref, torch.bfloat16, rows=rows, label=f"config3 {nk}"))
     compare(out2, lse2, ref, torch.bfloat16, rows=rows, label=f"config3 {nk} splits=4")
 
 
@@ -366,15 +385,15 @@ SHIFT_CASES = [
 @pytest.mark.parametrize("variant", [0, 4])
 @pytest.mark.parametrize("case", SHIFT_CASES, ids=lambda c: f"d{c[0]}{'f16' if c[1] == torch.float16 else 'bf16'}"
                          f"{'c' if c[2] else 'n'}")
-def test_shift_moves_inside_a_tile(case, variant, monkeypatch):
+def test_shift_moves_inside_a_tile(case, variant, test_controls):
     """The running maximum jumps at the start of the second 32-key block of many 64-key tiles (and at
     the start of other tiles), by growing amounts, so the exact path of the online softmax runs in the
     middle of a tile, after the first block's probabilities were formed (and, in the pipelined kernel,
     after its PV products were issued).  Every query gets q[..., 0] = 3; the chosen keys get
     k[..., 0] raised so that their logit rises by 8 + 1.5 t (natural log) in tile t.  Both choices of
-    the pipelined order (the default and CQSA_FWD_VARIANT=4) are compared with the FP64 reference."""
+    the pipelined order (the default and kernel variant 4) are compared with the FP64 reference."""
     D, dtype, causal = case
-    monkeypatch.setenv("CQSA_FWD_VARIANT", str(variant))
+    test_controls(variant, -1)
     B, H, N = 1, 2, 1100
     say("shift", case, "variant", variant)
     q, k, v = gen(B, H, H, N, N, D, dtype, seed=4100 + D + variant)
@@ -491,7 +510,8 @@ def test_errors():
 
 def test_config4_streamed_4m_full_size():
     """4,194,304-token causal attention, H=8, D=64, fp16, q/k/v and out in pinned host memory, device budget
-    16e9 bytes: the planner must cut Q in two and stream KV; sampled rows against the FP64 reference."""
+    16e9 bytes: the planner must cut Q in two and stream KV; sampled rows in every head against the FP64
+    reference."""
     w = synth.workload(3)
     say("workload", w.name, "full size")
     q, k, v, _ = synth.make_inputs(w, pin=True)
@@ -503,15 +523,17 @@ def test_config4_streamed_4m_full_size():
     assert info["streamed"] == 1 and info["n_q_chunks"] == 2
     assert info["workspace_bytes"] <= 16e9 * 0.85
     assert info["h2d_bytes"] == 16 * 2**30
-    rows = sample_rows(1, 8, w.Nq, seed=6, n_random=4, edge=2, boundaries=[info["q_chunk"]] +
-                       list(range(0, w.Nq, info["kv_chunk"])), cap=8, heads=(0, 7))
+    edge, n_random = C14_SAMPLED["streamed_4m"]
+    rows = sample_rows(1, 8, w.Nq, seed=6, n_random=n_random, edge=edge, boundaries=[info["q_chunk"]] +
+                       list(range(0, w.Nq, info["kv_chunk"])), cap=32)
+    say("config4", "rows per head", len(rows) // 8)
     ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
     say("config4", compare(o, lse, ref, torch.float16, rows=rows, label="config4 streamed"))
 
 
 def test_config5_softmax_stress_full_size():
     """B=2, H=16, N=262,144, D=128, bf16, non-causal, logits N(0, 9^2) with +20 spikes on 5% of keys,
-    KV chunk 16,384 (16 LSE merges); sampled rows against the FP64 reference."""
+    KV chunk 16,384 (16 LSE merges); sampled rows in every (b, h) against the FP64 reference."""
     w = synth.workload(4)
     say("workload", w.name, "full size")
     q, k, v, pos = synth.make_inputs(w)
@@ -521,14 +543,16 @@ def test_config5_softmax_stress_full_size():
                                       return_lse=True, return_info=True)
     torch.cuda.synchronize()
     assert info["n_kv_chunks"] == 16 and info["merges"] == 15
-    rows = sample_rows(2, 16, w.Nq, seed=7, n_random=2, edge=1, heads=(0, 9, 15))
+    edge, n_random = C14_SAMPLED["stress_full"]
+    rows = sample_rows(2, 16, w.Nq, seed=7, n_random=n_random, edge=edge, boundaries=range(0, w.Nq, 16384))
+    say("config5", "rows per (b, h)", len(rows) // 32)
     ref = reference(q, k, v, causal=False, scale=w.scale, rows=rows)
     say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 full"))
 
 
-def test_launch_failure_mid_stream_is_reported_and_the_next_call_is_exact(monkeypatch):
+def test_launch_failure_mid_stream_is_reported_and_the_next_call_is_exact(test_controls):
     """A forward launch that fails partway through a host-streamed call is reported as CQSA_ERR_HIP.  The
-    failure is forced from the host (CQSA_FAIL_AFTER_LAUNCHES=3: the call's Q and KV copies and its
+    failure is forced from the host (cqsa_set_test_controls with 3: the call's Q and KV copies and its
     first three launches are already issued when the fourth launch fails), so no kernel faults.  The
     call returns only after its streams have drained; nothing of it is left running, and the next
     call on the same pinned buffers is exact."""
@@ -539,11 +563,11 @@ def test_launch_failure_mid_stream_is_reported_and_the_next_call_is_exact(monkey
     out = torch.full((B, Hq, N, D), 7.0, dtype=torch.float32, pin_memory=True)
     budget = 2_000_000
     say("injected launch failure, streamed")
-    monkeypatch.setenv("CQSA_FAIL_AFTER_LAUNCHES", "3")
+    test_controls(0, 3)
     with pytest.raises(m.CqsaError, match="HIP.*injected"):
         m.attention(qh, kh, vh, is_causal=True, mem_budget=budget, out=out)
     torch.cuda.synchronize()                      # no GPU error left behind
-    monkeypatch.delenv("CQSA_FAIL_AFTER_LAUNCHES")
+    test_controls(0, -1)
     o, lse, info = m.attention(qh, kh, vh, is_causal=True, mem_budget=budget, out=out, return_lse=True,
                                return_info=True)
     assert info["streamed"] == 1 and info["kernel_launches"] > 3

@@ -83,7 +83,7 @@ def test_case_table_covers_the_space():
 def test_random_problem_against_oracle(c):
     print("[gpu-case] random", _name(c), c["opt"], f"scale={c['scale']} sigma={c['sigma']}", file=sys.stderr,
           flush=True)
-    m = pytest.importorskip("exact_long_context_cqsa_amd")
+    import exact_long_context_cqsa_amd as m
     q = synth.normal((c["B"], c["Hq"], c["Nq"], c["D"]), seed=c["seed"], tensor_id=0, sigma=c["sigma"], dtype=c["dtype"])
     k = synth.normal((c["B"], c["Hkv"], c["Nk"], c["D"]), seed=c["seed"], tensor_id=1, sigma=c["sigma"], dtype=c["dtype"])
     v = synth.normal((c["B"], c["Hkv"], c["Nk"], c["D"]), seed=c["seed"], tensor_id=2, dtype=c["dtype"])
@@ -143,7 +143,7 @@ def test_random_backward_against_oracle(c):
     """Gradients within 8 u of the FP64 oracle (max |g - g_ref| / max(1, max |g_ref|)), u the unit
     roundoff of the input format: every product takes operands rounded to it once."""
     print("[gpu-case] random backward", _bname(c), c["opt"], file=sys.stderr, flush=True)
-    m = pytest.importorskip("exact_long_context_cqsa_amd")
+    import exact_long_context_cqsa_amd as m
     import oracle
     shp_q, shp_k = (c["B"], c["Hq"], c["Nq"], c["D"]), (c["B"], c["Hkv"], c["Nk"], c["D"])
     q = synth.normal(shp_q, seed=c["seed"], tensor_id=0, dtype=c["dtype"])

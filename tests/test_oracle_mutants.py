@@ -82,8 +82,7 @@ def _build_mutant(tmp_path, old: str, new: str) -> str:
     path = tmp_path / "mutant.c"
     path.write_text(src.replace(old, new))
     lib = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-fno-fast-math", "-o", str(lib), str(path),
-                           "-lm"])
+    subprocess.check_call(["gcc", *oracle.CFLAGS, "-o", str(lib), str(path), "-lm"])
     return str(lib)
 
 

@@ -124,13 +124,24 @@ GRID = [
     dict(Nq=8192, Nk=8192, kv_chunk=2048, where=("host", "device", "device", "host"), want_lse=True),
     dict(Nq=8192, Nk=8192, kv_chunk=1024, where=("device",) * 4),               # resident, forced split
     dict(Nq=1 << 20, Nk=1 << 20, H=8, budget=3 * 10**9),                         # the planner's own chunks
+    # out on the device, lse in pinned host memory: the lse staging of one Q chunk must not be
+    # rewritten by the next Q chunk while its D2H copy still reads it
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=1024, merge=2, where=("device",) * 4, want_lse="host"),
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=1024, merge=1, where=("device",) * 4, want_lse="host"),
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=8192, where=("device",) * 4, want_lse="host"),  # single pass per Q chunk
+    dict(Nq=8192, Nk=8192, q_chunk=2048, kv_chunk=1024, where=("host",) * 4, want_lse="device"),
 ]
 
 
-@pytest.mark.parametrize("kw", GRID, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items() if k != "where"))
+def _streamed(kw):
+    return "host" in kw.get("where", ("host",)) or kw.get("want_lse") == "host"
+
+
+@pytest.mark.parametrize("kw", GRID, ids=lambda d: ",".join(f"{k}={v}" for k, v in d.items() if k != "where")
+                         + ("," + "".join(w[0] for w in d["where"]) if "where" in d else ""))
 def test_grid_schedule_is_race_free(kw):
     kw = dict(kw)
-    streamed = "host" in kw.get("where", ("host",))
+    streamed = _streamed(kw)
     ops = check(trace(**kw), streamed)
     kinds = {o.kind for o in ops}
     assert "fwd" in kinds
@@ -150,6 +161,9 @@ def test_quorum_set_waves_are_race_free(c, wt, budget):
     assert sum(o.kind == "wave" for o in ops) >= 1
     resident = check(trace(30000, 30000, where=("device",) * 4, cqs=c, wave_tokens=wt), streamed=False)
     assert sum(o.kind == "wave" for o in resident) >= 1
+    lse_host = check(trace(30000, 30000, where=("device",) * 4, cqs=c, wave_tokens=wt, want_lse="host"),
+                     streamed=True)
+    assert sum(o.kind == "copy" for o in lse_host) >= 1
 
 
 @pytest.mark.parametrize("c,itr,wt", [(7, 2, None), (3, 3, 20000), (13, 2, None)])
