@@ -70,8 +70,8 @@ def test_device_resident_prompt_with_kv_splits():
 
 @pytest.mark.parametrize("place", ["all_host", "device_out_host_lse"])
 def test_streamed_under_a_small_budget(place):
-    """Causal fp16, 6000 tokens, 4 query heads over 2, D=64, under a 3 MB budget that forces Q chunks and KV
-    chunks.  all_host: q, k, v, out and lse in pinned host memory.  device_out_host_lse: q, k, v and out
+    """Causal fp16, 6000 tokens, 4 query heads over 2, D=64, under a 3 MB budget that forces Q chunks (and KV
+    chunks, where K and V are on the host).  all_host: q, k, v, out and lse in pinned host memory.  device_out_host_lse: q, k, v and out
     on the device and lse in pinned host memory, so every Q chunk's lse goes through the one staging
     buffer and back to the host while the next Q chunk runs."""
     B, Hq, Hkv, N, D = 1, 4, 2, 6000, 64
@@ -92,7 +92,9 @@ def test_streamed_under_a_small_budget(place):
                   is_causal=True, mem_budget=budget, out=((B, Hq, N, D), torch.float32), want_lse=want_lse,
                   where=where, num_cus=256)
     say("cqsa_attention", place, {x: info[x] for x in ("n_q_chunks", "n_kv_chunks", "workspace_bytes", "d2h_bytes")})
-    assert info["streamed"] == 1 and info["n_q_chunks"] > 1 and info["n_kv_chunks"] > 1
+    assert info["streamed"] == 1 and info["n_q_chunks"] > 1
+    if place == "all_host":          # device K/V is read in place, so only host K/V is cut into chunks
+        assert info["n_kv_chunks"] > 1
     assert info["d2h_bytes"] >= B * Hq * N * 4
     call(qx, kx, vx, True, 0.125, budget, out, lse)
     torch.cuda.synchronize()
