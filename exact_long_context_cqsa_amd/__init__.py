@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["attention", "plan", "fwd_partial", "lse_merge", "finalize", "CqsaError", "library_path",
            "fwd_kernel_name", "cqs_assign", "cqs_default_set", "attention_backward", "schedule_trace", "backward_schedule_trace",
-           "set_test_controls", "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
+           "set_test_controls", "attention_noalloc", "MERGE_AUTO", "MERGE_KERNEL", "MERGE_FUSED"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libcqsa.so")
@@ -162,6 +162,9 @@ def _load_library():
     lib.cqsa_probe_device.restype = ctypes.c_int
     lib.cqsa_set_test_controls.argtypes = [ctypes.c_int32, ctypes.c_int64]
     lib.cqsa_set_test_controls.restype = ctypes.c_int
+    lib.cqsa_attention_noalloc.argtypes = [T, T, T, ctypes.c_int, ctypes.c_float, T, fp, ctypes.c_int32,
+                                           ctypes.c_void_p, I]
+    lib.cqsa_attention_noalloc.restype = ctypes.c_int
     for which, cls in enumerate((CqsaTensor, CqsaOptions, CqsaPlanInfo, CqsaProbeResult)):
         if lib.cqsa_struct_size(which) != ctypes.sizeof(cls):
             raise ImportError(f"{cls.__name__} layout differs from the built library")
@@ -509,6 +512,22 @@ def attention_backward(q, k, v, out, dout, lse, is_causal: bool = False, scale: 
                                             st.cuda_stream))
         stats.record_stream(st)
     return dq, dk, dv
+
+
+def attention_noalloc(q, k, v, out, lse=None, is_causal: bool = False, scale: float | None = None, *,
+                      kv_splits: int = 0, stream: torch.cuda.Stream | None = None) -> dict:
+    """cqsa_attention_noalloc: the same attention with every operand on the device and no allocation at
+    all (the partials of a split key range live in the library's fixed device array); out and lse
+    are the caller's tensors.  Stream-ordered.  Returns the plan that ran."""
+    info = CqsaPlanInfo()
+    dev = _device_of(q, k, v, out) or torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(dev):
+        st = stream if stream is not None else torch.cuda.current_stream(dev)
+        sc = float(scale) if scale is not None else 0.0
+        _check(_lib.cqsa_attention_noalloc(ctypes.byref(_desc(q)), ctypes.byref(_desc(k)), ctypes.byref(_desc(v)),
+                                           1 if is_causal else 0, sc, ctypes.byref(_desc(out)), _fptr(lse),
+                                           int(kv_splits), st.cuda_stream, ctypes.byref(info)))
+    return info.as_dict()
 
 
 def fwd_partial(q, k, v, is_causal=False, scale=None, kv_begin=0, kv_end=None, stream=None):

@@ -1980,6 +1980,61 @@ cqsa_status cqsa_attention(const cqsa_tensor* q, const cqsa_tensor* k, const cqs
     return cqsa_attention_ex(q, k, v, is_causal, scale, mem_budget, out, lse, nullptr, nullptr);
 }
 
+cqsa_status cqsa_attention_noalloc(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                                   float scale, cqsa_tensor* out, float* lse, int32_t kv_splits, void* stream,
+                                   cqsa_plan_info* info) {
+    static_assert(kNoAllocScratchBytes == CQSA_NOALLOC_SCRATCH_BYTES, "one size on both sides of the ABI");
+    g_err.clear();
+    g_fwd_launches = 0;
+    if (kv_splits < 0) return fail(CQSA_ERR_INVALID, "kv_splits %d is negative", kv_splits);
+    Problem P;
+    CQSA_TRY(build_problem(q, k, v, is_causal, scale, out, lse, lse != nullptr, true, false, &P));
+    if (P.streamed)
+        return fail(CQSA_ERR_UNSUPPORTED, "cqsa_attention_noalloc takes device memory only (host operands need "
+                                          "staging): use cqsa_attention_ex");
+    if (P.empty) {
+        if (info) std::memset(info, 0, sizeof *info);
+        return CQSA_OK;
+    }
+    // a forced split: its partial triples must fit the fixed array as asked, not halved to fit
+    const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
+    if (kv_splits > 1) {
+        const int64_t s = std::min<int64_t>({kv_splits, kMaxMergeParts, ceil_div(P.Nk, 64)});
+        const uint64_t need = (uint64_t)s * rows * (P.D + 2) * 4 + 512;
+        if (need > kNoAllocScratchBytes)
+            return fail(CQSA_ERR_BUDGET, "kv_splits=%d needs %llu bytes of partials; the no-allocation entry point "
+                        "holds %llu bytes (CQSA_NOALLOC_SCRATCH_BYTES)", kv_splits, (unsigned long long)need,
+                        (unsigned long long)kNoAllocScratchBytes);
+    }
+    DeviceRes* res = nullptr;
+    CQSA_TRY(device_res(&res));
+    cqsa_options o;
+    std::memset(&o, 0, sizeof o);
+    o.kv_splits = kv_splits;
+    o.stream = stream;
+    Plan pl;
+    CQSA_TRY(make_plan(P, kNoAllocScratchBytes, o, res->num_cus, &pl));
+    if (pl.cqs || pl.chunked || pl.total > kNoAllocScratchBytes)
+        return fail(CQSA_ERR_BUDGET, "the plan needs %llu bytes; the no-allocation entry point holds %llu",
+                    (unsigned long long)pl.total, (unsigned long long)kNoAllocScratchBytes);
+    char* ws = nullptr;
+    if (pl.total > 0) {
+        void* p = nullptr;
+        const hipError_t e = noalloc_scratch(&p);
+        if (e != hipSuccess)
+            return fail(CQSA_ERR_HIP, "address of the no-allocation scratch array: %s", hipGetErrorString(e));
+        ws = static_cast<char*>(p);
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const cqsa_status s = exec_single(P, pl, ws, st);
+    if (s != CQSA_OK) {
+        drain_after_failure(st, res);
+        return s;
+    }
+    if (info) *info = pl.info;
+    return CQSA_OK;
+}
+
 // The backward's operands, validated: q, k, v, out (Problem), dout, the gradients and lse.
 struct BwdProblem {
     Problem P;

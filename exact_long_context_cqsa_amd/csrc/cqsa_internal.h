@@ -161,6 +161,13 @@ hipError_t launch_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_
 // Which forward kernel shape the launches take (0 = the default); set by cqsa_set_test_controls.
 void set_fwd_variant(int v);
 
+// Bytes of the fixed device array behind cqsa_attention_noalloc (CQSA_NOALLOC_SCRATCH_BYTES).
+constexpr uint64_t kNoAllocScratchBytes = 128ull << 20;
+
+// The device address of that array on the current device, resolved once per device
+// (hipGetSymbolAddress) and kept; the error of the first resolution is returned.
+hipError_t noalloc_scratch(void** ptr);
+
 // Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
 int fwd_block_m(int D, int p_split);
 

@@ -25,6 +25,7 @@
 
 #include <atomic>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -1775,6 +1776,36 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 void set_fwd_variant(int v) { g_variant.store((v < 0 || v >= kNumShapes) ? 0 : v, std::memory_order_relaxed); }
+
+namespace {
+
+// The device memory of the no-allocation entry point: one fixed array, which every device holds from
+// the loading of this code object until the process ends.  In host code the name stands in for the
+// array and is not a device address; host code passes kernels the address hipGetSymbolAddress gives
+// for the current device (noalloc_scratch), never the name.
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 int fwd_block_m(int D, int p_split) { return shape_of(D, p_split).nw * 32; }
 

@@ -184,6 +184,32 @@ cqsa_status cqsa_attention_ex(const cqsa_tensor* q, const cqsa_tensor* k, const 
 #define CQSA_LSE_HOST 3      /* lse in pinned host memory */
 
 /*
+ * cqsa_attention_noalloc: cqsa_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  It makes no hipMalloc,
+ * hipFree or other allocating call.  The only buffer its kernels need beyond q, k, v, out and lse,
+ * the partial triples of a key range split across the GPU, lives in a fixed device array inside the
+ * library: CQSA_NOALLOC_SCRATCH_BYTES per device, held by every device the library runs on from the
+ * loading of its code until the process ends.
+ *   q, k, v, out, lse  as for cqsa_attention, all in device memory (host operands: CQSA_ERR_UNSUPPORTED).
+ *   kv_splits          0 = the planner's split (within the array), 1 = one pass, n > 1 = n side-by-side
+ *                      splits merged by log-sum-exp; a split whose partials exceed the array gives
+ *                      CQSA_ERR_BUDGET (with the bytes it needs) before any device work.
+ *   stream             hipStream_t (NULL = the null stream); the call is stream-ordered and returns
+ *                      without waiting.
+ *   info               NULL, or the plan that ran.
+ * Every call on one device uses that device's one array and leaves its last contents there (nothing
+ * in it needs to start at zero): calls that may overlap on one device (on different streams, or from
+ * several threads) race on it and must be ordered by the caller.  The first call on each device looks
+ * up the array's address (hipGetSymbolAddress, no allocation); a caller that captures calls into a
+ * graph makes one call on that device before capturing.
+ */
+#define CQSA_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+cqsa_status cqsa_attention_noalloc(const cqsa_tensor* q, const cqsa_tensor* k, const cqsa_tensor* v, int is_causal,
+                                   float scale, cqsa_tensor* out, float* lse, int32_t kv_splits, void* stream,
+                                   cqsa_plan_info* info);
+
+/*
  * cqsa_plan: the plan cqsa_attention_ex would run, without running it or
  * allocating (the dry run of the pages' estimate(): stream-cqsa 2.2.2 -> 2.2.3
  * diff, README.md section "Use").  Tensor data may be NULL; then each tensor's
