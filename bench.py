@@ -8,7 +8,13 @@ in one call: validate, plan, forward kernel with the in-kernel finalise).  Print
   roofline      the forward kernel against the dense fp16 matrix-core peak (2.5 PFLOP/s), timed
                 per launch with HIP events on the stream the kernel runs on; with the rates this
                 device measures (matrix cores, LDS, HBM copy) and the clock they ran at beside it
-  cpu_baseline  the FP64 reference on this host's cores over a time-bounded sample of rows
+                (roofline.profile: the same kernel's average and matrix-core counters from the committed
+                rocprofv3 summaries under profiles/)
+  configs       the other measured cases, inputs in HBM: the 1,024-token parity case, the 2,048-query
+                GQA prompt at 8K/32K/131K keys, the full-size softmax-stress case (--no-configs skips)
+  cpu_baseline  the FP64 reference on this host's cores: time-bounded samples of every case (the
+                1,024-token case in full; --cpu-full times the bench workload and the prompt at 8K
+                and 32K in full too)
   streamed_4m   4,194,304-token causal attention from pinned host memory under a 16e9-byte device
                 budget: tokens/s and H2D GB/s (the metric's second figure; --no-streamed skips it)
 """
@@ -61,53 +67,71 @@ def parse():
                     help="also time the exact merge and the finalize (HBM-bound steps) at 8.4M rows")
     ap.add_argument("--no-probe", dest="probe", action="store_false", default=True,
                     help="skip the device probe (matrix-core, LDS and HBM rates with the clock they ran at)")
+    ap.add_argument("--no-configs", dest="configs", action="store_false", default=True,
+                    help="skip the other measured configurations (the 1,024-token parity case, the 2,048-query "
+                         "prompt at 8K/32K/131K keys, the full-size softmax-stress case)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="time the FP64 reference in full on the 1,024-token case, the bench workload and the "
+                         "prompt at 8K and 32K keys (several minutes) instead of on bounded samples")
+    ap.add_argument("--fwd-variant", type=int, default=0,
+                    help="forward kernel shape (0 = the default; see cqsa_set_test_controls), for A/B runs")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
                     "(default profiles/<forward kernel>_<workload>.md)")
     return ap.parse_args()
 
 
-def cpu_baseline(w, q, k, v, seconds: float) -> dict:
-    """The FP64 reference on this host, over seeded random rows until `seconds` of CPU time pass."""
+def _oracle_rate(w, q, k, v, seconds: float, threads: int, rng, full: bool = False) -> dict:
+    """The FP64 reference on rows of one workload: every row (full), or seeded random rows until
+    `seconds` pass.  Returns rows, visible pairs, seconds and the algorithmic TFLOP/s."""
+    import numpy as np
+    import oracle
+    t0 = time.perf_counter()
+    if full:
+        oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, threads=threads)
+        n = w.B * w.Hq * w.Nq
+        pairs = w.visible_pairs() * w.B * w.Hq
+    else:
+        n = pairs = 0
+        batch = 2 * threads
+        while time.perf_counter() - t0 < seconds:
+            b = rng.integers(0, w.B, batch)
+            h = rng.integers(0, w.Hq, batch)
+            i = rng.integers(0, w.Nq, batch)
+            rows = np.stack([b, h, i], 1).astype(np.int64)
+            oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
+            n += batch
+            pairs += int(np.sum(np.minimum(i + (w.Nk - w.Nq) + 1, w.Nk))) if w.causal else batch * w.Nk
+    dt = time.perf_counter() - t0
+    rate = 4.0 * w.D * pairs / dt
+    return {"rows": int(n), "seconds": round(dt, 2), "tflops": round(rate / 1e12, 6),
+            "mode": "every row" if full else "seeded random rows",
+            "full_workload_s": round(w.flops() / rate, 1),
+            "full_workload_s_is": "measured" if full else "extrapolated from the sampled rate"}
+
+
+def cpu_baseline(w, q, k, v, seconds: float, others: dict, full: bool = False) -> dict:
+    """The FP64 reference on this host's cores, reported beside the GPU figures (never a target).  The
+    headline is the bench workload, sampled for `seconds` (or in full with --cpu-full); `others` maps the
+    names of the other configurations to (workload, q, k, v), each timed for a few seconds, or in full
+    where the plan times it in full (the 1,024-token case always; the prompt at 8K and 32K with
+    --cpu-full).  A one-thread figure of the headline workload is given too."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
     rng = np.random.default_rng(12345)
-    done_rows = 0
-    pairs = 0
-    t0 = time.perf_counter()
-    batch = 2 * threads
-    while time.perf_counter() - t0 < seconds:
-        b = rng.integers(0, w.B, batch)
-        h = rng.integers(0, w.Hq, batch)
-        i = rng.integers(0, w.Nq, batch)
-        rows = np.stack([b, h, i], 1).astype(np.int64)
-        oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=threads)
-        done_rows += batch
-        if w.causal:
-            pairs += int(np.sum(i + (w.Nk - w.Nq) + 1))
-        else:
-            pairs += batch * w.Nk
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.D * pairs
-    rate = flops / dt
-    # the same reference on one thread, over a short sample of the same kind of rows
-    t1 = time.perf_counter()
-    pairs1 = rows1 = 0
-    while time.perf_counter() - t1 < min(2.0, seconds / 4):
-        i = rng.integers(0, w.Nq, 1)
-        rows = np.array([[rng.integers(0, w.B), rng.integers(0, w.Hq), i[0]]], dtype=np.int64)
-        oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows, threads=1)
-        rows1 += 1
-        pairs1 += int(i[0] + (w.Nk - w.Nq) + 1) if w.causal else w.Nk
-    dt1 = time.perf_counter() - t1
-    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_rows} seeded random query rows of the same workload (all their visible keys), "
-                      f"{dt:.1f} s, FP64 C reference on {threads} threads; rows/s = {done_rows / dt:.1f}",
-            "single_thread_value": round(4.0 * w.D * pairs1 / dt1 / 1e12, 6),
-            "single_thread_sample": f"{rows1} rows, {dt1:.1f} s",
-            "extrapolated_full_workload_s": round(w.flops() / rate, 1),
-            "extrapolation_note": "the whole workload at the sampled rate (an extrapolation, not a measurement)",
-            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+    head = _oracle_rate(w, q, k, v, seconds, threads, rng, full=full)
+    one = _oracle_rate(w, q, k, v, min(2.0, seconds / 4), 1, rng)
+    per = {w.name: head}
+    for name, (w2, q2, k2, v2) in others.items():
+        whole = w2.index == 0 or (full and w2.index == 2 and w2.Nk <= 32768)
+        per[name] = _oracle_rate(w2, q2, k2, v2, 3.0, threads, rng, full=whole)
+    return {"value": head["tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{head['rows']} {head['mode']} of {w.name} (all their visible keys), {head['seconds']} s, "
+                       f"FP64 C reference on {threads} threads"),
+            "single_thread_value": one["tflops"], "single_thread_sample": f"{one['rows']} rows, {one['seconds']} s",
+            "extrapolated_full_workload_s": head["full_workload_s"] if not full else None,
+            "full_workload_s": head["full_workload_s"] if full else None,
+            "per_config": per, "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "threads": threads}
 
 
 def _cpu_model() -> str:
@@ -120,6 +144,27 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def profile_figures(kernel_prof: str, mfma_prof: str, flops: float) -> dict:
+    """The same kernel's figures from the committed rocprofv3 summaries: the kernel-trace average over
+    the timed dispatches (and the fraction of the peak it gives) and the matrix-core counters
+    (MfmaUtil, clock); each marked with whether the kernel source is still the one measured."""
+    from exact_long_context_cqsa_amd import profiling
+    out = {}
+    sha = profiling.kernel_source_sha256()
+    kt = profiling.read_profile(kernel_prof)
+    if kt.get("avg_ns"):
+        ns = float(kt["avg_ns"])
+        out.update({"trace_source": os.path.relpath(kernel_prof, ROOT), "trace_avg_ms": round(ns / 1e6, 4),
+                    "trace_frac": round(flops / (ns * 1e-9) / 1e12 / PEAK_F16_TFLOPS, 4),
+                    "trace_same_kernel_source": kt.get("kernel_source_sha256") == sha})
+    mf = profiling.read_profile(mfma_prof)
+    if mf.get("mfma_util_pct"):
+        out.update({"mfma_source": os.path.relpath(mfma_prof, ROOT), "mfma_util_pct": float(mf["mfma_util_pct"]),
+                    "clock_ghz": float(mf["clock_ghz"]),
+                    "mfma_same_kernel_source": mf.get("kernel_source_sha256") == sha})
+    return out
+
+
 def measured_traffic(path: str):
     """HBM bytes per launch from a committed rocprofv3 summary, if it measured the current kernel source."""
     from exact_long_context_cqsa_amd import profiling
@@ -129,10 +174,87 @@ def measured_traffic(path: str):
     return int(float(prof["traffic_bytes_per_launch"])), os.path.relpath(path, ROOT)
 
 
-def run_streamed(cqsa, torch, synth, cqs=None, cqs_itr=1) -> dict:
+def run_configs(cqsa, torch, synth, steps: int) -> tuple[dict, dict]:
+    """The other measured configurations, each with its inputs in HBM: the 1,024-token parity case (4 KV
+    chunks of 256 merged by log-sum-exp; a time, no roofline claim), the 2,048-query GQA prompt at 8K,
+    32K and 131K keys, and the full-size softmax-stress case (16 KV chunks of 16,384, 15 merges).  Each
+    call is timed with HIP events on the current stream; TFLOP/s and the fraction of the 2.5 PFLOP/s
+    dense peak use the algorithmic count.  Sampled rows are checked against the FP64 reference (every
+    row for the 1,024-token case).  Returns (figures, inputs kept for the CPU baseline)."""
+    import numpy as np
+    import oracle
+    dev = "cuda:0"
+    res, keep = {}, {}
+    st = torch.cuda.current_stream()
+    cases = [(0, None), (2, 8192), (2, 32768), (2, 131072), (4, None)]
+    for idx, nk in cases:
+        w = synth.workload(idx, nk=nk)
+        t0 = time.perf_counter()
+        q, k, v, _ = synth.make_inputs(w)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        kw = {"kv_chunk": w.kv_chunk} if w.kv_chunk else {}
+        odt = torch.float32 if idx == 0 else w.dtype
+        out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=odt, device=dev)
+        reps = 3 if idx == 4 else max(5, steps)
+        cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, **kw)
+        info = cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, return_info=True, **kw)[1]
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a_, b_ in ev:
+            a_.record(st)
+            cqsa.attention(qd, kd, vd, is_causal=w.causal, out=out, **kw)
+            b_.record(st)
+        torch.cuda.synchronize()
+        ms = sorted(a_.elapsed_time(b_) for a_, b_ in ev)
+        med = ms[len(ms) // 2]
+        # parity: every row of the 1,024-token case, else seeded rows in several heads
+        o32, lse = cqsa.attention(qd, kd, vd, is_causal=w.causal, out_dtype=torch.float32, return_lse=True, **kw)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(77 + idx)
+        if idx == 0:
+            rows = None
+        else:
+            n_r = 16 if idx == 4 else 48
+            rows = np.stack([rng.integers(0, w.B, n_r), rng.integers(0, w.Hq, n_r), rng.integers(0, w.Nq, n_r)],
+                            1).astype(np.int64)
+        ref = oracle.attention_rows(q, k, v, causal=w.causal, scale=w.scale, rows=rows)
+        if rows is None:
+            got = o32.cpu().reshape(-1, w.D).double().numpy()
+            gl = lse.cpu().reshape(-1).double().numpy()
+        else:
+            b_, h_, i_ = (torch.from_numpy(rows[:, c]) for c in range(3))
+            got = o32.cpu()[b_, h_, i_].double().numpy()
+            gl = lse.cpu()[b_, h_, i_].double().numpy()
+        max_abs = float(np.abs(got - ref["o"]).max())
+        lse_rel = float((np.abs(gl - ref["lse"]) / np.maximum(1.0, np.abs(ref["lse"]))).max())
+        tol = 4e-3 if w.dtype == torch.float16 else 2e-2
+        entry = {"ms": round(med, 4), "ms_min": round(ms[0], 4), "calls_timed": reps,
+                 "algorithmic_flop": w.flops(), "kernel": cqsa.fwd_kernel_name(w.D),
+                 "plan": {x: info[x] for x in ("kv_splits", "n_kv_chunks", "chunk_pairs", "merges", "kernel_launches")},
+                 "parity_rows": "all" if rows is None else int(len(rows)), "max_abs_vs_fp64": max_abs,
+                 "lse_rel_vs_fp64": lse_rel, "tolerance": tol, "parity_ok": max_abs <= tol and lse_rel <= 1e-4}
+        if idx == 0:
+            entry["note"] = "launch-bound parity case: a time, no roofline claim"
+        else:
+            tf = w.flops() / (med / 1e3) / 1e12
+            entry.update({"tflops": round(tf, 2), "frac": round(tf / PEAK_F16_TFLOPS, 4),
+                          "tokens_per_s": round(w.B * w.Nq / (med / 1e3), 1)})
+        res[w.name] = entry
+        print(f"[bench] {w.name}: {med:.3f} ms" + (f" ({entry['tflops']} TFLOP/s)" if idx else "")
+              + f", max_abs {max_abs:.2e}, lse_rel {lse_rel:.1e} ({time.perf_counter() - t0:.1f} s)",
+              file=sys.stderr, flush=True)
+        keep[w.name] = (w, q, k, v)
+        del qd, kd, vd, out, o32, lse
+        torch.cuda.empty_cache()
+    return res, keep
+
+
+def run_streamed(cqsa, torch, synth, cqs=None, cqs_itr=1, keep=None) -> dict:
     w = synth.workload(3)
     t0 = time.perf_counter()
     q, k, v, _ = synth.make_inputs(w, pin=True)
+    if keep is not None:
+        keep[w.name] = (w, q, k, v)
     out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=torch.float16, pin_memory=True)
     gen_s = time.perf_counter() - t0
     print(f"[bench] streamed inputs ready ({gen_s:.1f} s)", file=sys.stderr, flush=True)
@@ -312,6 +434,8 @@ def main():
     import synth
     import exact_long_context_cqsa_amd as cqsa
 
+    if args.fwd_variant:
+        cqsa.set_test_controls(args.fwd_variant, -1)
     w = synth.workload(args.workload, nk=args.nk)
     if w.host_resident:
         raise SystemExit("use --streamed for the host-resident case")
@@ -446,6 +570,8 @@ def main():
     kernel = cqsa.fwd_kernel_name(w.D)
     prof_path = args.profile or os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_{w.name}.md")
     traffic, traffic_src = measured_traffic(prof_path)
+    prof = profile_figures(prof_path, os.path.join(ROOT, "profiles", f"{kernel.split()[0]}_mfma_counters_{w.name}.md"),
+                           flops)
     line = {
         "metric": "causal attention fwd TFLOP/s & % MFMA peak (1 GPU); tokens/s at 4M ctx",
         "value": round(value, 2),
@@ -472,6 +598,8 @@ def main():
                      "kernel_ms": round(ms_kernel, 4),
                      "launches_per_step": info["kernel_launches"]},
     }
+    if prof:
+        line["roofline"]["profile"] = prof
     if measured:
         line["roofline"]["measured_on_this_device"] = measured
     if cqs_resident:
@@ -480,14 +608,18 @@ def main():
         line["split_p"] = split_p
     if backward:
         line["backward"] = backward
+    kept = {}
+    if args.configs and args.workload == 1 and not args.kv_chunk:
+        line["configs"], kept = run_configs(cqsa, torch, synth, args.steps)
     if args.streamed:
-        line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None, cqs_itr=args.cqs_itr)
+        line["streamed_4m"] = run_streamed(cqsa, torch, synth, cqs=args.cqs or None, cqs_itr=args.cqs_itr,
+                                           keep=kept if args.configs else None)
     if args.merge:
         line["merge"] = run_merge(cqsa, torch, args.steps)
     if args.streamed_backward:
         line["streamed_backward_4m"] = run_streamed_backward(cqsa, torch, synth)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, kept, full=args.cpu_full)
     print(json.dumps(line), flush=True)
 
 

@@ -1763,8 +1763,8 @@ int32_t cqsa_version(void) { return CQSA_ABI_VERSION; }
 
 cqsa_status cqsa_set_test_controls(int32_t fwd_variant, int64_t fail_after_launches) {
     g_err.clear();
-    if (fwd_variant < 0 || fwd_variant > 4)
-        return fail(CQSA_ERR_INVALID, "fwd_variant %d is not in 0..4", fwd_variant);
+    if (fwd_variant < 0 || fwd_variant >= fwd_variant_count())
+        return fail(CQSA_ERR_INVALID, "fwd_variant %d is not in 0..%d", fwd_variant, fwd_variant_count() - 1);
     if (fail_after_launches < -1)
         return fail(CQSA_ERR_INVALID, "fail_after_launches %lld is below -1", (long long)fail_after_launches);
     set_fwd_variant(fwd_variant);

@@ -160,6 +160,7 @@ hipError_t launch_cast(const float* src, int64_t B, int64_t H, int64_t n, int64_
 
 // Which forward kernel shape the launches take (0 = the default); set by cqsa_set_test_controls.
 void set_fwd_variant(int v);
+int fwd_variant_count();
 
 // Bytes of the fixed device array behind cqsa_attention_noalloc (CQSA_NOALLOC_SCRATCH_BYTES).
 constexpr uint64_t kNoAllocScratchBytes = 128ull << 20;
