@@ -1779,31 +1779,56 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         dvacc[db] = f32x16{};
     }
 
-    // tile T: head hkv * group + T / nqt, query rows from i_start + (T % nqt) QT; its rows' stats
-#define CQSA_BWD_KV_TILE(T)                                                                                 \
-    do {                                                                                                  \
-        const int h_ = hkv * a.group + (T) / nqt;                                                         \
-        const int64_t q0_ = i_start + (int64_t)((T) % nqt) * QT;                                          \
-        const int64_t nv_ = min(a.Nq - q0_, (int64_t)QT);                                                 \
-        uint16_t* st_ = lds + ((T) & 1) * STAGE;                                                           \
-        dma_rows<NW, BPW, D>(st_, a.q + (int64_t)b * a.q_sb + (int64_t)h_ * a.q_sh, a.q_sn, q0_, nv_, qoff, wave); \
-        dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_,   \
-                             nv_, doff, wave);                                                            \
-        if (wave == NW - 1)   /* the rows' (lse2, Delta) by DMA too; rows past Nq read as zero */          \
-            dma_words<2 * QT * 4>(stl[(T) & 1], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.stats_rows + q0_), (int)(nv_ * 8), lane); \
-    } while (0)
+    // Tile (th, tq): query head hkv * group + th, query rows from i_start + tq QT, with its rows' stats.
+    // Tiles run head-major; the running pair replaces a division by nqt per tile.
+    auto issue_tile = [&](int th, int tq, int stage) {
+        const int h_ = hkv * a.group + th;
+        const int64_t q0_ = i_start + (int64_t)tq * QT;
+        const int64_t nv_ = min(a.Nq - q0_, (int64_t)QT);
+        uint16_t* st_ = lds + stage * STAGE;
+        dma_rows<NW, BPW, D>(st_, a.q + (int64_t)b * a.q_sb + (int64_t)h_ * a.q_sh, a.q_sn, q0_, nv_, qoff, wave);
+        dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_, nv_, doff,
+                             wave);
+        if (wave == NW - 1)   // the rows' (lse2, Delta) by DMA too; rows past Nq read as zero
+            dma_words<2 * QT * 4>(stl[stage], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.stats_rows + q0_),
+                                  (int)(nv_ * 8), lane);
+    };
+    // per-wave bounds on the query tile index, wave-uniform and taken to scalar registers once:
+    //   the wave works on tile tq when some row of it sees some valid key of the wave (tq >= tq_first),
+    //   and masks when the tile reaches the causal diagonal (tq < tq_diag), the end of the rows (the
+    //   last tile of a ragged row range) or the wave's keys reach the end of the key range
+    const int64_t jw = jw0;
+    int64_t first = 0, diag = 0;
+    if (a.causal) {
+        const int64_t x = jw - delta_c - QT + 1 - i_start;      // tile tq active iff tq QT >= x
+        first = x <= 0 ? 0 : (x + QT - 1) / QT;
+        const int64_t y = jw + 31 - delta_c - i_start;          // tile tq masks iff tq QT < y
+        diag = y <= 0 ? 0 : (y + QT - 1) / QT;
+    }
+    const int tq_first = __builtin_amdgcn_readfirstlane((int)min(first, (int64_t)nqt));
+    const int tq_diag = __builtin_amdgcn_readfirstlane((int)min(diag, (int64_t)nqt));
+    const int wave_live = __builtin_amdgcn_readfirstlane(jw < a.Nk ? 1 : 0);
+    const int key_ragged = __builtin_amdgcn_readfirstlane(jw + 32 > a.Nk ? 1 : 0);
+    const int row_ragged = (a.Nq - i_start) % QT != 0 ? 1 : 0;
 
-    if (total > 0) CQSA_BWD_KV_TILE(0);
+    int tq = 0;                             // query tile of tile it
+    int nh = 0, nq = nqt > 1 ? 1 : 0;       // head and query tile of tile it + 1
+    if (nqt == 1) nh = 1;
+    if (total > 0) issue_tile(0, 0, 0);
     for (int it = 0; it < total; ++it) {
         __syncthreads();
-        if (it + 1 < total) CQSA_BWD_KV_TILE(it + 1);
-        const int64_t q0 = i_start + (int64_t)(it % nqt) * QT;
-        // the wave works on the tile when some row of it sees some valid key of the wave
-        const bool active = jw0 < a.Nk && (!a.causal || q0 + QT - 1 + delta_c >= jw0);
-        if (!active) continue;
+        if (it + 1 < total) issue_tile(nh, nq, (it + 1) & 1);
+        const int cur_q = tq;
+        tq = nq;
+        if (++nq == nqt) {
+            nq = 0;
+            ++nh;
+        }
+        if (!wave_live || cur_q < tq_first) continue;
+        const int64_t q0 = i_start + (int64_t)cur_q * QT;
         const uint16_t* st = lds + (it & 1) * STAGE;
         const float* sl = stl[it & 1];
-        const bool need_mask = (q0 + QT > a.Nq) || (jw0 + 32 > a.Nk) || (a.causal && q0 + delta_c < jw0 + 31);
+        const bool need_mask = key_ragged || (a.causal && cur_q < tq_diag) || (row_ragged && cur_q == nqt - 1);
 
         u32x4 pp[NPQ], ps[NPQ];
 #pragma unroll
