@@ -315,6 +315,23 @@ __device__ __forceinline__ void dma_rows(uint16_t* st, const uint16_t* base, int
 #endif
 }
 
+// The same DMA in the form the lean forward loop uses: rows [0, nvalid) of the view starting at row0
+// (row stride sn_bytes), with the wave index a scalar, so that the LDS destinations, the row count and
+// the resource are all formed on the scalar unit.  Device pass only, like dma_rows.
+template <int NW, int BPW, int D>
+__device__ __forceinline__ void dma_rows_s(uint16_t* st, const uint16_t* row0, int sn_bytes, int nvalid,
+                                           const int (&off)[BPW], int wave_s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int bytes = nvalid > 0 ? (nvalid - 1) * sn_bytes + D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row0), (short)0, bytes, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < BPW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(st + (wave_s + i * NW) * 512), 16, off[i], 0, 0, 0);
+#endif
+}
+
 // One wave's DMA of NB bytes (a multiple of 256) of fp32 data from base into LDS at st, 4 bytes per
 // lane and instruction; bytes at or past nbytes read as zero.  Device pass only, like dma_rows.
 template <int NB>
@@ -973,13 +990,19 @@ fwd_dma_kernel(const FwdArgs a) {
         }
         const int wtiles = __builtin_amdgcn_readfirstlane(wt);
         const int mask_from = __builtin_amdgcn_readfirstlane(mf);
+        const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+        const int nkeys = (int)(khi - klo);                             // keys of the range (< 2^31)
+        const uint16_t* k0 = kp + klo * k_sn;
+        const uint16_t* v0 = vp + klo * v_sn;
+        const int ksb = (int)(k_sn * 2), vsb = (int)(v_sn * 2);
         auto tile = [&](int it, int S) {
             __syncthreads();   // tile it is in LDS; every wave is done with tile it - 1
             if (it + 1 < ntiles) {
-                const int64_t j0n = klo + (int64_t)(it + 1) * KT;
-                const int64_t nvn = min(khi - j0n, (int64_t)KT);
-                dma_rows<NW, BPW, D>(lds + (1 - S) * STAGE, kp, k_sn, j0n, nvn, koff, wave);
-                dma_rows<NW, BPW, D>(lds + (1 - S) * STAGE + TILE, vp, v_sn, j0n, nvn, voff, wave);
+                const int rem = nkeys - (it + 1) * KT;
+                const int nvn = rem < KT ? rem : KT;
+                const int64_t jn = (int64_t)(it + 1) * KT;
+                dma_rows_s<NW, BPW, D>(lds + (1 - S) * STAGE, k0 + jn * k_sn, ksb, nvn, koff, wave_s);
+                dma_rows_s<NW, BPW, D>(lds + (1 - S) * STAGE + TILE, v0 + jn * v_sn, vsb, nvn, voff, wave_s);
             }
             if (it >= wtiles) return;
             const int64_t j0 = klo + (int64_t)it * KT;
@@ -2189,8 +2212,8 @@ hipError_t launch_bwd_d(const BwdArgs& a, int pass, hipStream_t st) {
     if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (blocks > 0) {
         if constexpr (D == 64) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
-                               st, a, (int)n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks),
+                               dim3(KV_NW * 64), 0, st, a, (int)n_kt);
         } else {
             hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
                                st, a, (int)n_kt);
