@@ -1071,185 +1071,6 @@ fwd_dma_kernel(const FwdArgs a) {
     fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
-// The software-pipelined forward kernel.  A wave walks its keys in 32-key blocks; in step g it issues
-// the score products of block g + 1 and the PV products of block g - 1 on the matrix cores, and the
-// online softmax of block g (whose scores the previous step produced) on the VALU.  The three have no
-// dependency on one another inside a step, so the matrix cores and the VALU of one wave work side by
-// side instead of taking turns (scores, then softmax, then PV).  The PV products of block g - 1 come
-// before the softmax of block g in program order: when that softmax moves the running shift, the
-// rescale of O must include block g - 1.  K and V go to LDS by buffer-load DMA in two-stage rings of
-// 64-key tiles, K one tile ahead of V (a step reads the K tile of block g + 1 and the V tile of block
-// g - 1); one barrier per tile, at every odd step, releases the stages that both rings reuse.
-template <int D, int DT, int NW, int WPE>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
-fwd_sp_kernel(const FwdArgs a) {
-    constexpr int KT = 64;                                 // keys per LDS tile: two 32-key blocks
-    constexpr int BM = NW * 32;
-    constexpr int TILE = KT * D;
-    constexpr int GPR = D / 8;
-    constexpr int RPI = 64 / GPR;
-    constexpr int NBLK = KT / RPI;
-    constexpr int BPW = (NBLK + NW - 1) / NW;
-    constexpr int NDB = D / 32;
-    constexpr int NDK = D / 16;
-    static_assert(NBLK % NW == 0, "tile split");
-
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * TILE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TILE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
-
-    int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int qt_idx = w % a.n_qt;
-    w /= a.n_qt;
-    const int gi = w % a.group;
-    w /= a.group;
-    const int split = w % a.n_splits;
-    w /= a.n_splits;
-    const int hkv = w % a.Hkv;
-    const int b = w / a.Hkv;
-    const int hq = hkv * a.group + gi;
-    const int qt = a.n_qt - 1 - qt_idx;
-
-    const int64_t i0 = a.r0 + (int64_t)qt * BM;
-    const int64_t i_end = min(i0 + (int64_t)BM, a.r1);
-    const int64_t iw0 = i0 + (int64_t)wave * 32;
-    const int64_t iw_end = min(iw0 + 32, i_end);
-
-    const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
-    int64_t khi = min(a.k_hi, klo + a.split_len);
-    if (a.causal) khi = min(khi, i_end + a.causal_delta);
-    const int nblk = khi > klo ? (int)((khi - klo + 31) / 32) : 0;    // blocks of the workgroup
-    const int ntiles = (nblk + 1) / 2;
-    int64_t wend = khi;                                               // keys of this wave's rows
-    if (a.causal) wend = min(wend, iw_end + a.causal_delta);
-    const int wblk = (iw0 < i_end && wend > klo) ? (int)((wend - klo + 31) / 32) : 0;
-
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
-    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
-    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
-    const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
-
-    u32x4 qf[NDK];
-    {
-        const int64_t row = iw0 + l32;
-        const bool ok = row < i_end;
-        const uint16_t* p = qp + (ok ? row : 0) * a.q_sn + 8 * hi;
-#pragma unroll
-        for (int t = 0; t < NDK; ++t) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * t);
-            qf[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-
-    int koff[BPW], voff[BPW];
-#pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-        const int n = wave + i * NW;
-        const int r = n * RPI + lane / GPR;
-        const int pg = lane % GPR;
-        koff[i] = (int)((r * k_sn + ((pg ^ kswz<D>(r)) * 8)) * 2);
-        voff[i] = (int)((r * v_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
-    }
-    auto issue_k = [&](int t) {
-        const int64_t j0 = klo + (int64_t)t * KT;
-        dma_rows<NW, BPW, D>(lds_k + (t & 1) * TILE, kp, k_sn, j0, min(khi - j0, (int64_t)KT), koff, wave);
-    };
-    auto issue_v = [&](int t) {
-        const int64_t j0 = klo + (int64_t)t * KT;
-        dma_rows<NW, BPW, D>(lds_v + (t & 1) * TILE, vp, v_sn, j0, min(khi - j0, (int64_t)KT), voff, wave);
-    };
-
-    int kread[NDK];
-#pragma unroll
-    for (int t = 0; t < NDK; ++t) kread[t] = l32 * D + (((2 * t + hi) ^ kswz<D>(l32)) * 8);
-    int vread[NDB];
-    {
-        const int src = lane & 15;
-        const int row = 4 * hi + src / 4;
-        const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vread[db] = row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
-    }
-
-    f32x16 o[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float mrun = -INFINITY, lrun = 0.f;
-
-    // S^T of block bk (K rows from the K stage of its tile)
-    auto score_block = [&](int bk, f32x16& s) {
-        const uint16_t* st = lds_k + ((bk >> 1) & 1) * TILE + (bk & 1) * 32 * D;
-        s = f32x16{};
-#pragma unroll
-        for (int t = 0; t < NDK; ++t) s = mfma32<DT>(*reinterpret_cast<const u32x4*>(st + kread[t]), qf[t], s);
-    };
-    // O^T += V^T P^T for block bk: the two 16-key groups of the block within its V tile
-    auto pv_block = [&](int bk, const u32x4 (&p)[2]) {
-        const uint16_t* st = lds_v + ((bk >> 1) & 1) * TILE;
-        pv_group<D, NDB, DT, false>(st, vread, 2 * (bk & 1), p[0], p[0], o, o);
-        pv_group<D, NDB, DT, false>(st, vread, 2 * (bk & 1) + 1, p[1], p[1], o, o);
-    };
-    // the causal diagonal and the end of the key range, on the blocks that reach them
-    auto mask_block = [&](int bk, f32x16& s) {
-        const int64_t j0 = klo + (int64_t)bk * 32;
-        if ((j0 + 32 > khi) || (a.causal && j0 + 31 > iw0 + a.causal_delta)) {
-            int lim = (int)min(khi - j0, (int64_t)32);
-            if (a.causal) {
-                const int64_t c = iw0 + l32 + a.causal_delta - j0 + 1;
-                lim = min(lim, (int)max(min(c, (int64_t)32), (int64_t)0));
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = (r & 3) + 4 * hi + 8 * (r >> 2);
-                if (t >= lim) s[r] = -INFINITY;
-            }
-        }
-    };
-    // step g: scores of g + 1 into s_nxt, PV of g - 1 from p_prev, softmax of g from s_cur into p_new
-    auto step = [&](int g, f32x16& s_cur, f32x16& s_nxt, const u32x4 (&p_prev)[2], u32x4 (&p_new)[2]) {
-        const bool do_s = g + 1 < wblk, do_sm = g < wblk, do_pv = g >= 1 && g - 1 < wblk;
-        if (do_sm) mask_block(g, s_cur);
-        if (do_s && do_pv) {
-            score_block(g + 1, s_nxt);
-            pv_block(g - 1, p_prev);
-            softmax_tile<1, NDB, DT>(reinterpret_cast<const f32x16(&)[1]>(s_cur), p_new, mrun, lrun, o, a.scale_log2);
-        } else {
-            if (do_s) score_block(g + 1, s_nxt);
-            if (do_pv) pv_block(g - 1, p_prev);
-            if (do_sm)
-                softmax_tile<1, NDB, DT>(reinterpret_cast<const f32x16(&)[1]>(s_cur), p_new, mrun, lrun, o,
-                                         a.scale_log2);
-        }
-    };
-
-    if (ntiles > 0) issue_k(0);
-    if (ntiles > 1) issue_k(1);
-    if (ntiles > 0) issue_v(0);
-    __syncthreads();
-    f32x16 sa, sb;
-    u32x4 pa[2], pb[2];
-    if (wblk > 0) score_block(0, sa);
-    // two steps per trip, so that the score and probability registers swap roles without copies; the
-    // barrier of an odd step: every wave is done with the previous step (the K stage of block g - 1 and
-    // the V stage of block g - 2 are free) and this wave's DMA of the tiles read from step g on landed
-    for (int g = 0; g <= nblk; g += 2) {
-        step(g, sa, sb, pb, pa);
-        if (g + 1 <= nblk) {
-            __syncthreads();
-            const int t = (g + 1) >> 1;                 // step 2t + 1: K of tile t + 2, V of tile t + 1
-            if (t + 2 < ntiles) issue_k(t + 2);
-            if (t + 1 < ntiles) issue_v(t + 1);
-            step(g + 1, sb, sa, pa, pb);
-        }
-    }
-
-    const int64_t row = iw0 + l32;
-    fwd_epilogue<NDB>(a, o, mrun, lrun, b, hq, split, row, row < i_end, hi);
-}
-
 // The wave engine's kernel: the DMA kernel's tile loop walked over a list of key parts (segments).
 // A workgroup takes BM rows of one query part of the table and one (b, query head); its key loop
 // runs over the key parts in the part's mask in ascending order, each cut at the causal limit of the
@@ -1970,15 +1791,6 @@ hipError_t launch_dma_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int DT, int NW, int WPE>
-hipError_t launch_sp_t(const FwdArgs& a, hipStream_t stream) {
-    const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_sp_kernel<D, DT, NW, WPE>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
-    return hipGetLastError();
-}
-
 template <int D, int DT, int KT>
 hipError_t launch_pp_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
@@ -1999,20 +1811,19 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 // Kernel choice per head dim: kind 2 the DMA kernel (nw waves, kt keys per tile, wpe waves per SIMD
 // asked of the register allocator, pipe: softmax and PV products interleaved per 32-key block), kind 1
-// the register-staged kernel, kind 0 the ping-pong kernel, kind 3 the software-pipelined kernel (scores
-// of the next block and PV of the previous block beside the softmax of the current one).
+// the register-staged kernel, kind 0 the ping-pong kernel.
 // Entry 0 is the default (pipelined and lean at D=64, where each measured faster; neither at D=128,
-// where they did not); entry 4 is the default shape with the other pipelining choice, entry 7 the
+// where they did not); entry 4 is the default shape with the other pipelining choice, entry 5 the
 // default shape with the other lean choice.  cqsa_set_test_controls selects another entry for the
 // whole process, for measurement and for the tests that cover every kernel.
 struct Shape {
     int kind, nw, kt, wpe, pipe, lean;
 };
 constexpr Shape kShapes64[] = {{2, 4, 64, 4, 1, 1}, {2, 8, 128, 2, 0, 0}, {1, 8, 128, 2, 0, 0}, {0, 8, 128, 2, 0, 0},
-                               {2, 4, 64, 3, 0, 0}, {3, 4, 64, 3, 0, 0}, {3, 8, 64, 2, 0, 0}, {2, 4, 64, 3, 1, 0}};
+                               {2, 4, 64, 3, 0, 0}, {2, 4, 64, 3, 1, 0}};
 constexpr Shape kShapes128[] = {{2, 8, 64, 2, 0, 0}, {2, 8, 32, 2, 0, 0}, {1, 8, 64, 2, 0, 0}, {0, 8, 64, 2, 0, 0},
-                                {2, 8, 64, 2, 1, 0}, {3, 4, 64, 2, 0, 0}, {3, 8, 64, 2, 0, 0}, {2, 8, 64, 2, 0, 1}};
-constexpr int kNumShapes = 8;
+                                {2, 8, 64, 2, 1, 0}, {2, 8, 64, 2, 0, 1}};
+constexpr int kNumShapes = 6;
 
 std::atomic<int> g_variant{0};
 
@@ -2037,13 +1848,6 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
             return launch_dma_t<D, DT, kSplit128.kt, kSplit128.nw, kSplit128.wpe, true, (kSplit128.pipe != 0)>(a, st);
     }
     const Shape sh = (D == 64 ? kShapes64 : kShapes128)[variant()];
-    if (sh.kind == 3) {
-        if constexpr (D == 64)
-            if (sh.nw == 4 && sh.wpe == 3) return launch_sp_t<D, DT, 4, 3>(a, st);
-        if (sh.nw == 4 && sh.wpe == 2) return launch_sp_t<D, DT, 4, 2>(a, st);
-        if (sh.nw == 8 && sh.wpe == 2) return launch_sp_t<D, DT, 8, 2>(a, st);
-        return hipErrorInvalidValue;
-    }
     if (sh.kind == 2) {
 #define CQSA_DMA_CASE(NW_, KT_, WPE_, PIPE_, LEAN_)                                                        \
     if (sh.nw == NW_ && sh.kt == KT_ && sh.wpe == WPE_ && sh.pipe == PIPE_ && sh.lean == LEAN_)          \
@@ -2117,11 +1921,10 @@ const char* fwd_kernel_name(int D, int p_split) {
     if (D != 64 && D != 128) return "";
     const int v = p_split ? kNumShapes : variant();
     const Shape sh = shape_of(D, p_split);
-    static const char* const kind[4] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel", "fwd_sp_kernel"};
+    static const char* const kind[3] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel"};
     char* out = names[D == 64 ? 0 : 1][v];
-    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s%s%s%s", kind[sh.kind], sh.nw,
-             sh.kt, sh.pipe ? " pipelined" : "", sh.kind == 3 ? (sh.wpe == 3 ? " wpe3" : " wpe2") : "",
-             sh.lean ? " lean" : "", p_split ? " split_p" : "");
+    snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s%s%s", kind[sh.kind], sh.nw,
+             sh.kt, sh.pipe ? " pipelined" : "", sh.lean ? " lean" : "", p_split ? " split_p" : "");
     return out;
 }
 
@@ -2137,7 +1940,7 @@ namespace {
 
 // The wave kernel runs the DMA kernel's pipelined D=64 shape and default D=128 shape (the split-P
 // shape with p_split); its loop has its own bookkeeping, so the lean flag does not apply.
-constexpr Shape kWave64 = kShapes64[7];
+constexpr Shape kWave64 = kShapes64[5];
 constexpr Shape kWave128 = kShapes128[0];
 static_assert(kWave64.kind == 2 && kWave128.kind == 2, "the wave kernel is the DMA kernel's loop");
 static_assert(sizeof(FwdArgs) + sizeof(WaveTable) <= 4096, "the wave kernel's arguments fit the 4 KiB kernel-argument segment");

@@ -42,14 +42,12 @@ def test_forward_kernel_name(test_controls):
     assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ")
     assert m.fwd_kernel_name(96) == ""
     # the default shape is pipelined and lean at D=64 and neither at D=128; variant 4 is the other
-    # pipelining choice, variant 7 the other lean choice
+    # pipelining choice, variant 5 the other lean choice
     assert "pipelined" in m.fwd_kernel_name(64) and "pipelined" not in m.fwd_kernel_name(128)
     assert "lean" in m.fwd_kernel_name(64) and "lean" not in m.fwd_kernel_name(128)
-    test_controls(7, -1)
+    test_controls(5, -1)
     assert "pipelined" in m.fwd_kernel_name(64) and "lean" not in m.fwd_kernel_name(64)
     assert "lean" in m.fwd_kernel_name(128)
-    test_controls(5, -1)
-    assert m.fwd_kernel_name(64).startswith("fwd_sp_kernel ")
     test_controls(2, -1)
     assert m.fwd_kernel_name(64).startswith("fwd_kernel ")
     test_controls(4, -1)
