@@ -1470,22 +1470,38 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-#define CQSA_BWD_DQ_TILE(j)                                                                                 \
-    do {                                                                                                  \
-        const int64_t j0_ = (int64_t)(j) * KT;                                                            \
-        const int64_t nv_ = min(khi - j0_, (int64_t)KT);                                                  \
-        uint16_t* st_ = lds + ((j) & 1) * STAGE;                                                           \
-        dma_rows<NW, BPW, D>(st_, kp, a.k_sn, j0_, nv_, koff, wave);                                       \
-        dma_rows<NW, BPW, D>(st_ + TILE, vp, a.v_sn, j0_, nv_, voff, wave);                                \
-    } while (0)
+    // per-wave bounds, wave-uniform and taken to scalar registers once: the tiles this wave computes
+    // (its last row sees keys <= iw_end - 1 + delta) and the first tile it masks (the causal diagonal,
+    // or a ragged last tile); the DMA of a tile is formed on the scalar unit too
+    int wt = iw0 < i_end ? ntiles : 0;
+    if (a.causal) {
+        const int64_t span = iw_end - 1 + delta_c;
+        wt = span < 0 ? 0 : min(wt, (int)(span / KT) + 1);
+    }
+    int mf = khi % KT != 0 ? ntiles - 1 : ntiles;
+    if (a.causal) {
+        const int64_t x = iw0 + delta_c - KT + 1;                      // tile it masks iff it KT > x
+        mf = (int)min((int64_t)mf, x < 0 ? (int64_t)0 : x / KT + 1);
+    }
+    const int wtiles = __builtin_amdgcn_readfirstlane(wt);
+    const int mask_from = __builtin_amdgcn_readfirstlane(mf);
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int nkeys = (int)khi;
+    const int ksb = (int)(a.k_sn * 2), vsb = (int)(a.v_sn * 2);
+    auto issue = [&](int j) {
+        const int rem = nkeys - j * KT;
+        const int nv = rem < KT ? rem : KT;
+        uint16_t* st_ = lds + (j & 1) * STAGE;
+        dma_rows_s<NW, BPW, D>(st_, kp + (int64_t)j * KT * a.k_sn, ksb, nv, koff, wave_s);
+        dma_rows_s<NW, BPW, D>(st_ + TILE, vp + (int64_t)j * KT * a.v_sn, vsb, nv, voff, wave_s);
+    };
 
-    if (ntiles > 0) CQSA_BWD_DQ_TILE(0);
+    if (ntiles > 0) issue(0);
     for (int it = 0; it < ntiles; ++it) {
         __syncthreads();
-        if (it + 1 < ntiles) CQSA_BWD_DQ_TILE(it + 1);
+        if (it + 1 < ntiles) issue(it + 1);
         const int64_t j0 = (int64_t)it * KT;
-        const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + delta_c);
-        if (!active) continue;
+        if (it >= wtiles) continue;
         const uint16_t* st = lds + (it & 1) * STAGE;
 
         f32x16 sacc[NKB], dpacc[NKB];
@@ -1503,8 +1519,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
                 sacc[kb] = mfma32<DT>(kf, qf[t], sacc[kb]);
                 dpacc[kb] = mfma32<DT>(vf, dof[t], dpacc[kb]);
             }
-        const bool need_mask = (j0 + KT > khi) || (a.causal && (j0 + KT - 1 > iw0 + delta_c));
-        if (need_mask) {
+        if (it >= mask_from) {
             int lim = (int)min(khi - j0, (int64_t)KT);
             if (a.causal) {
                 const int64_t cl = row + delta_c - j0 + 1;
@@ -1536,7 +1551,6 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
             for (int db = 0; db < NDB; ++db)
                 dqacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), pf[t], dqacc[db]);
     }
-#undef CQSA_BWD_DQ_TILE
 
     if (!row_ok) return;
     const int64_t ob = (int64_t)b * a.dq_sb + (int64_t)hq * a.dq_sh + row * a.dq_sn;
@@ -1625,17 +1639,23 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 
     // Tile (th, tq): query head hkv * group + th, query rows from i_start + tq QT, with its rows' stats.
     // Tiles run head-major; the running pair replaces a division by nqt per tile.
+    // (the pointers of head 0 of the group at row i_start, stepped per head and per tile; row counts in
+    // 32 bits and the wave index a scalar, so the DMA issue stays on the scalar unit)
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const uint16_t* q_g = a.q + (int64_t)b * a.q_sb + (int64_t)hkv * a.group * a.q_sh + i_start * a.q_sn;
+    const uint16_t* do_g = a.dout + (int64_t)b * a.do_sb + (int64_t)hkv * a.group * a.do_sh + i_start * a.do_sn;
+    const float* st_g = a.stats + 2 * (((int64_t)b * a.Hq + (int64_t)hkv * a.group) * a.stats_rows + i_start);
+    const int rows_left = (int)(a.Nq - i_start);
+    const int qsb = (int)(a.q_sn * 2), dsb = (int)(a.do_sn * 2);
     auto issue_tile = [&](int th, int tq, int stage) {
-        const int h_ = hkv * a.group + th;
-        const int64_t q0_ = i_start + (int64_t)tq * QT;
-        const int64_t nv_ = min(a.Nq - q0_, (int64_t)QT);
+        const int rem = rows_left - tq * QT;
+        const int nv_ = rem < QT ? rem : QT;
         uint16_t* st_ = lds + stage * STAGE;
-        dma_rows<NW, BPW, D>(st_, a.q + (int64_t)b * a.q_sb + (int64_t)h_ * a.q_sh, a.q_sn, q0_, nv_, qoff, wave);
-        dma_rows<NW, BPW, D>(st_ + TILE, a.dout + (int64_t)b * a.do_sb + (int64_t)h_ * a.do_sh, a.do_sn, q0_, nv_, doff,
-                             wave);
-        if (wave == NW - 1)   // the rows' (lse2, Delta) by DMA too; rows past Nq read as zero
-            dma_words<2 * QT * 4>(stl[stage], a.stats + 2 * (((int64_t)b * a.Hq + h_) * a.stats_rows + q0_),
-                                  (int)(nv_ * 8), lane);
+        dma_rows_s<NW, BPW, D>(st_, q_g + th * a.q_sh + (int64_t)tq * QT * a.q_sn, qsb, nv_, qoff, wave_s);
+        dma_rows_s<NW, BPW, D>(st_ + TILE, do_g + th * a.do_sh + (int64_t)tq * QT * a.do_sn, dsb, nv_, doff, wave_s);
+        if (wave_s == NW - 1)   // the rows' (lse2, Delta) by DMA too; rows past Nq read as zero
+            dma_words<2 * QT * 4>(stl[stage], st_g + 2 * ((int64_t)th * a.stats_rows + (int64_t)tq * QT), nv_ * 8,
+                                  lane);
     };
     // per-wave bounds on the query tile index, wave-uniform and taken to scalar registers once:
     //   the wave works on tile tq when some row of it sees some valid key of the wave (tq >= tq_first),
