@@ -85,9 +85,10 @@ def counter_per_dispatch(path: str, counter: str, kernel: str, grid: int | None 
 
 def summarise(args) -> str:
     grid, select = getattr(args, "grid", None), getattr(args, "select", None)
+    csel = getattr(args, "counter_select", None) or select
     ts = trace_stats(args.trace, args.kernel, grid, select)
-    fk, fc = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel, grid, select)
-    wk, wc = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel, grid, select)
+    fk, fc = counter_per_dispatch(args.fetch, "FETCH_SIZE", args.kernel, grid, csel)
+    wk, wc = counter_per_dispatch(args.write, "WRITE_SIZE", args.kernel, grid, csel)
     f_scale = COPY_BYTES / (fc * 1024.0)     # the copy reads 1 GiB
     w_scale = COPY_BYTES / (wc * 1024.0)     # and writes 1 GiB
     fetch_b = fk * 1024.0 * f_scale
@@ -96,7 +97,9 @@ def summarise(args) -> str:
     if grid or select:
         sel.append(f"dispatches: grid size {grid}" if grid else "dispatches: every grid size")
         if select:
-            sel.append(f"selected: [{select}] of the matching dispatches, in dispatch order")
+            sel.append(f"selected: [{select}] of the matching dispatches, in dispatch order (kernel trace)")
+        if csel != select:
+            sel.append(f"selected: [{csel}] of the matching dispatches of the counter runs")
     lines = [
         f"# {args.name}",
         "",
@@ -256,6 +259,8 @@ def main():
     ap.add_argument("--link-gbs", type=float, default=0.0)
     ap.add_argument("--grid", type=int, default=None, help="only dispatches of this grid size (threads)")
     ap.add_argument("--select", default=None, help="python slice a:b of the matching dispatches")
+    ap.add_argument("--counter-select", default=None,
+                    help="the slice for the FETCH_SIZE / WRITE_SIZE runs when their command differs (default --select)")
     ap.add_argument("--command", required=True)
     ap.add_argument("--note", default="")
     ap.add_argument("--out", default=None)
