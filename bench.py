@@ -72,7 +72,10 @@ def parse():
                          "prompt at 8K/32K/131K keys, the full-size softmax-stress case)")
     ap.add_argument("--cpu-full", action="store_true",
                     help="time the FP64 reference in full on the 1,024-token case, the bench workload and the "
-                         "prompt at 8K and 32K keys (several minutes) instead of on bounded samples")
+                         "prompt at 8K and 32K keys whatever their predicted time (by default each runs in full "
+                         "only when a short sample predicts it within --cpu-full-limit seconds)")
+    ap.add_argument("--cpu-full-limit", type=float, default=45.0,
+                    help="longest predicted whole-workload oracle time that the default run still takes in full")
     ap.add_argument("--fwd-variant", type=int, default=0,
                     help="forward kernel shape (0 = the default; see cqsa_set_test_controls), for A/B runs")
     ap.add_argument("--profile", default=None, help="profile summary holding the measured traffic "
@@ -109,28 +112,32 @@ def _oracle_rate(w, q, k, v, seconds: float, threads: int, rng, full: bool = Fal
             "full_workload_s_is": "measured" if full else "extrapolated from the sampled rate"}
 
 
-def cpu_baseline(w, q, k, v, seconds: float, others: dict, full: bool = False) -> dict:
+def cpu_baseline(w, q, k, v, seconds: float, others: dict, full: bool = False, limit: float = 45.0) -> dict:
     """The FP64 reference on this host's cores, reported beside the GPU figures (never a target).  The
-    headline is the bench workload, sampled for `seconds` (or in full with --cpu-full); `others` maps the
-    names of the other configurations to (workload, q, k, v), each timed for a few seconds, or in full
-    where the plan times it in full (the 1,024-token case always; the prompt at 8K and 32K with
-    --cpu-full).  A one-thread figure of the headline workload is given too."""
+    headline is the bench workload, timed in full when a 2 s sample predicts at most `limit` seconds for
+    it (always with full=True), else sampled for `seconds`.  `others` maps the names of the other
+    configurations to (workload, q, k, v): the 1,024-token case always runs in full, the prompt at 8K
+    and 32K keys in full under the same rule, the rest on a 3 s sample.  A one-thread figure of the
+    headline workload is given too."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
     rng = np.random.default_rng(12345)
-    head = _oracle_rate(w, q, k, v, seconds, threads, rng, full=full)
+    first = _oracle_rate(w, q, k, v, 2.0, threads, rng)
+    head = _oracle_rate(w, q, k, v, seconds, threads, rng, full=full or first["full_workload_s"] <= limit)
     one = _oracle_rate(w, q, k, v, min(2.0, seconds / 4), 1, rng)
     per = {w.name: head}
     for name, (w2, q2, k2, v2) in others.items():
-        whole = w2.index == 0 or (full and w2.index == 2 and w2.Nk <= 32768)
+        whole = w2.index == 0
+        if w2.index == 2 and w2.Nk <= 32768:
+            whole = full or _oracle_rate(w2, q2, k2, v2, 1.0, threads, rng)["full_workload_s"] <= limit
         per[name] = _oracle_rate(w2, q2, k2, v2, 3.0, threads, rng, full=whole)
     return {"value": head["tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": (f"{head['rows']} {head['mode']} of {w.name} (all their visible keys), {head['seconds']} s, "
                        f"FP64 C reference on {threads} threads"),
             "single_thread_value": one["tflops"], "single_thread_sample": f"{one['rows']} rows, {one['seconds']} s",
-            "extrapolated_full_workload_s": head["full_workload_s"] if not full else None,
-            "full_workload_s": head["full_workload_s"] if full else None,
+            "extrapolated_full_workload_s": head["full_workload_s"] if head["mode"] != "every row" else None,
+            "full_workload_s": head["full_workload_s"] if head["mode"] == "every row" else None,
             "per_config": per, "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "threads": threads}
 
 
@@ -619,7 +626,7 @@ def main():
     if args.streamed_backward:
         line["streamed_backward_4m"] = run_streamed_backward(cqsa, torch, synth)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, kept, full=args.cpu_full)
+        line["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds, kept, full=args.cpu_full, limit=args.cpu_full_limit)
     print(json.dumps(line), flush=True)
 
 
