@@ -125,6 +125,26 @@ constexpr float kLazyBound = 256.f;
 // unit (no VALU lane-count work).
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// max(x[lane], x[lane ^ 32]) in every lane: v_permlane32_swap leaves the pair {x[lane], x[lane ^ 32]}
+// in its two results (one VALU instruction, no LDS round trip).
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Key masking of one tile's transposed scores: register r of block kb holds key offset
+// kb * 32 + (r & 3) + 4 * hi + 8 * (r >> 2); offsets at or past lim become -inf.  The lane's part
+// 4 * hi is taken out of lim once, so every compare is against a constant.
+template <int NKB>
+__device__ __forceinline__ void mask_keys(f32x16 (&s)[NKB], int lim, int hi) {
+    const int lh = lim - 4 * hi;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (kb * 32 + (r & 3) + 8 * (r >> 2) >= lh) s[kb][r] = -INFINITY;
+}
+
 // fp16/bf16 operand -> the eight fp32 values it holds (exact).
 template <int DT>
 __device__ __forceinline__ f32x8 unpack8(u32x4 u);
@@ -182,8 +202,7 @@ template <int NKB, int NDB, int DT, bool SPLIT, bool LEAN = false>
 __device__ __forceinline__ void softmax_exact(const f32x16 (&s)[NKB], u32x4 (&pf)[2 * NKB], u32x4 (&plo)[2 * NKB],
                                               float& m, float& l, f32x16 (&o)[NDB], f32x16 (&olo)[NDB], float c,
                                               float& rs) {
-    float mx = lane_max<NKB>(s);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = max_halves(lane_max<NKB>(s));
     const float mnew = fmaxf(m, mx * c);
     const float muse = mnew == -INFINITY ? 0.f : mnew;
     const float alpha = __builtin_amdgcn_exp2f(m - muse);   // m = -inf gives 0
@@ -1071,6 +1090,296 @@ fwd_dma_kernel(const FwdArgs a) {
     fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
 }
 
+// Barrier that waits only for this wave's LDS operations, not for its buffer loads, so LDS-DMA
+// issued in the phase before may still be in flight (the caller proves that no wave reads the
+// buffers those loads write until a later barrier that waits for them).  The memory clobber keeps
+// the compiler from moving loads or stores across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Ping-pong DMA forward kernel: 8 waves of 32 query rows in two groups, A = waves 0-3 and B = waves
+// 4-7, so that wave w of A and wave w of B share a SIMD.  Each group alternates a matrix phase (the
+// PV products of the previous tile, then the scores of the current tile) and a vector phase (the
+// online softmax of the current tile); B runs one phase behind A.  Every phase ends with a barrier, so
+// in each phase one wave of every SIMD keeps the matrix core busy while the other uses the VALU,
+// instead of both taking turns.
+// K and V tiles reach LDS by buffer-load DMA into the two stages of the DMA kernel's layout.  Only
+// group A issues it, at the end of its matrix phase 2i (after its operand reads): K(i+1) and V(i).
+// The barrier ending phase 2i + 1 waits for them (vmcnt(0)); the one ending phase 2i waits for LDS
+// operations only.  K(i) is read in phases 2i (A) and 2i+1 (B), V(i) in phases 2i+2 (A) and 2i+3
+// (B), so each DMA writes a buffer whose last reader finished before the phase it is issued in, and
+// is read only after the barrier that waited for it.
+// Instruction order for NM matrix products that each take RPM LDS operand reads, issued by one wave:
+// the reads of the first PD products, then one product and the reads PD products ahead, so that PD
+// products' worth of reads are always in flight behind the matrix core.
+template <int NM, int RPM, int PD>
+__device__ __forceinline__ void mfma_read_pipeline() {
+    __builtin_amdgcn_sched_group_barrier(0x100, PD * RPM, 0);
+#pragma unroll
+    for (int i = 0; i < NM - PD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
+}
+
+template <int D, int DT, int KT, int WPE>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE)))
+fwd_pp_dma_kernel(const FwdArgs a) {
+    // matrix-phase order: the scores first at D=128, the PV products first at D=64 (each measured
+    // about 1% faster than the other order at its head dim); three products' reads in flight
+    constexpr bool SFIRST = D == 128;
+    constexpr int PD = 3;
+    // the softmax block by block at D=64, where the whole-tile form spills at four waves per SIMD;
+    // over the whole tile at D=128
+    constexpr bool PERBLOCK = D == 64;
+    constexpr int NW = 8;
+    constexpr int BM = NW * 32;
+    constexpr int TILE = KT * D;
+    constexpr int STAGE = 2 * TILE;
+    constexpr int GPR = D / 8;
+    constexpr int RPI = 64 / GPR;
+    constexpr int NBLK = KT / RPI;                         // DMA instructions per tensor and tile
+    constexpr int NA = 4;                                  // the waves of group A issue them
+    constexpr int BPW = NBLK / NA;
+    constexpr int NKB = KT / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NDK = D / 16;
+    static_assert(NBLK % NA == 0, "tile split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int qt_idx = w % a.n_qt;
+    w /= a.n_qt;
+    const int gi = w % a.group;
+    w /= a.group;
+    const int split = w % a.n_splits;
+    w /= a.n_splits;
+    const int hkv = w % a.Hkv;
+    const int b = w / a.Hkv;
+    const int hq = hkv * a.group + gi;
+    const int qt = a.n_qt - 1 - qt_idx;
+
+    const int64_t i0 = a.r0 + (int64_t)qt * BM;
+    const int64_t i_end = min(i0 + (int64_t)BM, a.r1);
+    const int64_t iw0 = i0 + (int64_t)wave * 32;
+    const int64_t iw_end = min(iw0 + 32, i_end);
+
+    const int64_t klo = a.k_lo + (int64_t)split * a.split_len;
+    int64_t khi = min(a.k_hi, klo + a.split_len);
+    if (a.causal) khi = min(khi, i_end + a.causal_delta);
+    const int ntiles = khi > klo ? (int)((khi - klo + KT - 1) / KT) : 0;
+
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)hq * a.q_sh;
+    const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
+    const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
+    const int64_t k_sn = a.k_sn, v_sn = a.v_sn;
+
+    u32x4 qf[NDK];
+    {
+        const int64_t row = iw0 + l32;
+        const bool ok = row < i_end;
+        const uint16_t* p = qp + (ok ? row : 0) * a.q_sn + 8 * hi;
+#pragma unroll
+        for (int t = 0; t < NDK; ++t) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(p + 16 * t);
+            qf[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // DMA lane offsets for the waves of group A (the same for every tile)
+    int koff[BPW], voff[BPW];
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+        const int n = (wave & 3) + i * NA;
+        const int r = n * RPI + lane / GPR;
+        const int pg = lane % GPR;
+        koff[i] = (int)((r * k_sn + ((pg ^ kswz<D>(r)) * 8)) * 2);
+        voff[i] = (int)((r * v_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+    }
+    int kread[NDK];
+#pragma unroll
+    for (int t = 0; t < NDK; ++t) kread[t] = l32 * D + (((2 * t + hi) ^ kswz<D>(l32)) * 8);
+    int vread[NDB];
+    {
+        const int src = lane & 15;
+        const int row = 4 * hi + src / 4;
+        const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vread[db] = TILE + row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
+    }
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float mrun = -INFINITY, lrun = 0.f;
+
+    // per-wave bounds, wave-uniform scalars: tiles this wave computes and the first one it masks
+    const int64_t span = iw_end - 1 + a.causal_delta - klo;
+    int wt = iw0 < i_end ? ntiles : 0;
+    if (a.causal) wt = span < 0 ? 0 : min(wt, (int)(span / KT) + 1);
+    int mf = (khi - klo) % KT != 0 ? ntiles - 1 : ntiles;
+    if (a.causal) {
+        const int64_t x = iw0 + a.causal_delta - klo - KT + 1;
+        const int64_t first = x < 0 ? 0 : x / KT + 1;
+        mf = (int)min((int64_t)mf, first);
+    }
+    const int wtiles = __builtin_amdgcn_readfirstlane(wt);
+    const int mask_from = __builtin_amdgcn_readfirstlane(mf);
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+    const int wave_a = __builtin_amdgcn_readfirstlane(wave & 3);
+    const int nkeys = (int)(khi - klo);
+    const uint16_t* k0 = kp + klo * k_sn;
+    const uint16_t* v0 = vp + klo * v_sn;
+    const int ksb = (int)(k_sn * 2), vsb = (int)(v_sn * 2);
+
+    if (grp == 0 && ntiles > 0) dma_rows_s<NA, BPW, D>(lds, k0, ksb, min(nkeys, KT), koff, wave_a);
+    __syncthreads();
+
+    f32x16 sacc[NKB];
+    u32x4 pf[2 * NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < 2 * NKB; ++t) pf[t] = u32x4{0u, 0u, 0u, 0u};
+
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    // matrix phase of tile i: the PV products of tile i - 1 (P is zero where this wave had no keys),
+    // then the scores of tile i; with DMA (group A), the K(i + 1) and V(i) copies after the reads
+    auto mphase = [&](int i, int S, bool dma) __attribute__((always_inline)) {   // S = i & 1, a constant at every call
+        auto pv = [&]() __attribute__((always_inline)) {
+            if (i >= 1) {
+                const uint16_t* sv = lds + (S ^ 1) * STAGE;
+                s16x4 vt[2 * NKB][NDB][2];
+#pragma unroll
+                for (int t = 0; t < 2 * NKB; ++t)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            vt[t][db][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) s16x4*)(sv + vread[db] + (16 * t + 8 * r) * D));
+#pragma unroll
+                for (int t = 0; t < 2 * NKB; ++t)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        u32x4 vf;
+                        vf[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[t][db][0], vt[t][db][0], 0, 1));
+                        vf[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[t][db][0], vt[t][db][0], 2, 3));
+                        vf[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[t][db][1], vt[t][db][1], 0, 1));
+                        vf[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(vt[t][db][1], vt[t][db][1], 2, 3));
+                        oacc[db] = mfma32<DT>(vf, pf[t], oacc[db]);
+                    }
+                mfma_read_pipeline<2 * NKB * NDB, 2, PD>();
+            }
+        };
+        auto sc = [&]() __attribute__((always_inline)) {
+            if (i < ntiles) {
+                scores<D, NKB, NDK, DT>(lds + S * STAGE, kread, qf, sacc);
+                mfma_read_pipeline<NDK * NKB, 1, PD>();
+            }
+        };
+        if constexpr (SFIRST) {
+            sc();
+            pv();
+        } else {
+            pv();
+            sc();
+        }
+        if (dma) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 1 < ntiles) {
+                const int rem = nkeys - (i + 1) * KT;
+                dma_rows_s<NA, BPW, D>(lds + (S ^ 1) * STAGE, k0 + (int64_t)(i + 1) * KT * k_sn, ksb,
+                                       rem < KT ? rem : KT, koff, wave_a);
+            }
+            if (i < ntiles) {
+                const int rem = nkeys - i * KT;
+                dma_rows_s<NA, BPW, D>(lds + S * STAGE + TILE, v0 + (int64_t)i * KT * v_sn, vsb,
+                                       rem < KT ? rem : KT, voff, wave_a);
+            }
+        }
+    };
+    // vector phase of tile i: masks, online softmax, P into pf for the next matrix phase (zero for a
+    // tile past this wave's last key)
+    auto vphase = [&](int i) __attribute__((always_inline)) {
+        if (i >= wtiles) {
+#pragma unroll
+            for (int t = 0; t < 2 * NKB; ++t) pf[t] = u32x4{0u, 0u, 0u, 0u};
+            return;
+        }
+        if (i >= mask_from) {
+            const int64_t j0 = klo + (int64_t)i * KT;
+            int lim = (int)min(khi - j0, (int64_t)KT);
+            if (a.causal) {
+                const int64_t c = iw0 + l32 + a.causal_delta - j0 + 1;
+                lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
+            }
+            mask_keys<NKB>(sacc, lim, hi);
+        }
+        if constexpr (PERBLOCK) {
+            // block by block (fewer registers live); every block's P waits for the next matrix phase,
+            // so when a later block moves the shift, the earlier blocks' P are formed again at the
+            // final shift (l and O were rescaled by the exact path; only P is stale)
+            float m_first = mrun;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                softmax_tile<1, NDB, DT, false, true>(reinterpret_cast<const f32x16(&)[1]>(sacc[kb]),
+                                                      reinterpret_cast<u32x4(&)[2]>(pf[2 * kb]),
+                                                      reinterpret_cast<u32x4(&)[2]>(pf[2 * kb]), mrun, lrun, oacc,
+                                                      oacc, a.scale_log2);
+                if (kb == 0) m_first = mrun;
+            }
+            if (wave_any(mrun != m_first)) {
+                const float muse = mrun == -INFINITY ? 0.f : mrun;
+#pragma unroll
+                for (int kb = 0; kb + 1 < NKB; ++kb)
+                    (void)softmax_fast<1, DT, false>(reinterpret_cast<const f32x16(&)[1]>(sacc[kb]),
+                                                     reinterpret_cast<u32x4(&)[2]>(pf[2 * kb]),
+                                                     reinterpret_cast<u32x4(&)[2]>(pf[2 * kb]), muse, a.scale_log2);
+            }
+        } else {
+            // one shift for the whole tile
+            softmax_tile<NKB, NDB, DT, false, true>(sacc, pf, pf, mrun, lrun, oacc, oacc, a.scale_log2);
+        }
+    };
+    // phase 2i: A in the matrix phase of tile i, B in the vector phase of tile i - 1;
+    // phase 2i + 1: A in the vector phase of tile i, B in the matrix phase of tile i.
+    // One loop per group, so each keeps its accumulators in place; both pass the same barriers.  Each
+    // trip covers two tiles, so the LDS stage of every operand read is a constant.
+    if (grp == 0) {
+        auto step = [&](int i, int S) __attribute__((always_inline)) {
+            mphase(i, S, true);
+            barrier_lds();
+            if (i < ntiles) vphase(i);
+            __syncthreads();   // the DMA issued in phase 2i is in LDS
+        };
+        for (int i = 0; i <= ntiles; i += 2) {
+            step(i, 0);
+            if (i + 1 <= ntiles) step(i + 1, 1);
+        }
+    } else {
+        auto step = [&](int i, int S) __attribute__((always_inline)) {
+            if (i >= 1) vphase(i - 1);
+            barrier_lds();
+            mphase(i, S, false);
+            __syncthreads();
+        };
+        for (int i = 0; i <= ntiles; i += 2) {
+            step(i, 0);
+            if (i + 1 <= ntiles) step(i + 1, 1);
+        }
+    }
+
+    const int64_t row = iw0 + l32;
+    fwd_epilogue<NDB>(a, oacc, mrun, lrun, b, hq, split, row, row < i_end, hi);
+}
+
 // The wave engine's kernel: the DMA kernel's tile loop walked over a list of key parts (segments).
 // A workgroup takes BM rows of one query part of the table and one (b, query head); its key loop
 // runs over the key parts in the part's mask in ascending order, each cut at the causal limit of the
@@ -1820,6 +2129,15 @@ hipError_t launch_pp_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int DT, int KT, int WPE>
+hipError_t launch_ppdma_t(const FwdArgs& a, hipStream_t stream) {
+    const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_dma_kernel<D, DT, KT, WPE>), dim3((unsigned)blocks), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D, int DT, int QB, int NW, int KT>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     const int64_t blocks = (int64_t)a.n_splits * a.B * a.Hq * a.n_qt;
@@ -1829,21 +2147,23 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Kernel choice per head dim: kind 2 the DMA kernel (nw waves, kt keys per tile, wpe waves per SIMD
-// asked of the register allocator, pipe: softmax and PV products interleaved per 32-key block), kind 1
-// the register-staged kernel, kind 0 the ping-pong kernel.
-// Entry 0 is the default (pipelined and lean at D=64, where each measured faster; neither at D=128,
-// where they did not); entry 4 is the default shape with the other pipelining choice, entry 5 the
-// default shape with the other lean choice.  cqsa_set_test_controls selects another entry for the
-// whole process, for measurement and for the tests that cover every kernel.
+// Kernel choice per head dim: kind 3 the ping-pong DMA kernel (8 waves in two groups, wpe waves per
+// SIMD asked of the register allocator), kind 2 the DMA kernel (nw waves, kt keys per tile, pipe:
+// softmax and PV products interleaved per 32-key block, lean: scalar tile bounds), kind 1 the
+// register-staged kernel, kind 0 the register-staged ping-pong kernel.
+// Entry 0 is the default: the ping-pong DMA kernel, which measured faster than every DMA-kernel shape
+// at both head dims.  Entry 6 is the DMA kernel's best shape (pipelined and lean at D=64, plain at
+// D=128), entries 4 and 5 its other pipelining and lean choices, entry 7 the ping-pong DMA kernel in
+// its other shape.  cqsa_set_test_controls selects another entry for the whole process, for
+// measurement and for the tests that cover every kernel.
 struct Shape {
     int kind, nw, kt, wpe, pipe, lean;
 };
-constexpr Shape kShapes64[] = {{2, 4, 64, 4, 1, 1}, {2, 8, 128, 2, 0, 0}, {1, 8, 128, 2, 0, 0}, {0, 8, 128, 2, 0, 0},
-                               {2, 4, 64, 3, 0, 0}, {2, 4, 64, 3, 1, 0}};
-constexpr Shape kShapes128[] = {{2, 8, 64, 2, 0, 0}, {2, 8, 32, 2, 0, 0}, {1, 8, 64, 2, 0, 0}, {0, 8, 64, 2, 0, 0},
-                                {2, 8, 64, 2, 1, 0}, {2, 8, 64, 2, 0, 1}};
-constexpr int kNumShapes = 6;
+constexpr Shape kShapes64[] = {{3, 8, 64, 4, 0, 0}, {2, 8, 128, 2, 0, 0}, {1, 8, 128, 2, 0, 0}, {0, 8, 128, 2, 0, 0},
+                               {2, 4, 64, 3, 0, 0}, {2, 4, 64, 3, 1, 0}, {2, 4, 64, 4, 1, 1}, {3, 8, 64, 2, 0, 0}};
+constexpr Shape kShapes128[] = {{3, 8, 64, 2, 0, 0}, {2, 8, 32, 2, 0, 0}, {1, 8, 64, 2, 0, 0}, {0, 8, 64, 2, 0, 0},
+                                {2, 8, 64, 2, 1, 0}, {2, 8, 64, 2, 0, 1}, {2, 8, 64, 2, 0, 0}, {3, 8, 32, 2, 0, 0}};
+constexpr int kNumShapes = 8;
 
 std::atomic<int> g_variant{0};
 
@@ -1884,6 +2204,16 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
             CQSA_DMA_CASE(8, 64, 2, 0, 1)
         }
 #undef CQSA_DMA_CASE
+        return hipErrorInvalidValue;
+    }
+    if (sh.kind == 3) {
+        if constexpr (D == 64) {
+            if (sh.kt == 64 && sh.wpe == 4) return launch_ppdma_t<D, DT, 64, 4>(a, st);
+            if (sh.kt == 64 && sh.wpe == 2) return launch_ppdma_t<D, DT, 64, 2>(a, st);
+        } else {
+            if (sh.kt == 64) return launch_ppdma_t<D, DT, 64, 2>(a, st);
+            if (sh.kt == 32) return launch_ppdma_t<D, DT, 32, 2>(a, st);
+        }
         return hipErrorInvalidValue;
     }
     if (sh.kind == 0) {
@@ -1941,7 +2271,7 @@ const char* fwd_kernel_name(int D, int p_split) {
     if (D != 64 && D != 128) return "";
     const int v = p_split ? kNumShapes : variant();
     const Shape sh = shape_of(D, p_split);
-    static const char* const kind[3] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel"};
+    static const char* const kind[4] = {"fwd_pp_kernel", "fwd_kernel", "fwd_dma_kernel", "fwd_pp_dma_kernel"};
     char* out = names[D == 64 ? 0 : 1][v];
     snprintf(out, sizeof names[0][0], "%s waves=%d keys_per_tile=%d rows_per_wave=32%s%s%s", kind[sh.kind], sh.nw,
              sh.kt, sh.pipe ? " pipelined" : "", sh.lean ? " lean" : "", p_split ? " split_p" : "");
@@ -1958,10 +2288,10 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, hipStream_t stream) {
 
 namespace {
 
-// The wave kernel runs the DMA kernel's pipelined D=64 shape and default D=128 shape (the split-P
+// The wave kernel runs the DMA kernel's pipelined D=64 shape and plain D=128 shape (the split-P
 // shape with p_split); its loop has its own bookkeeping, so the lean flag does not apply.
 constexpr Shape kWave64 = kShapes64[5];
-constexpr Shape kWave128 = kShapes128[0];
+constexpr Shape kWave128 = kShapes128[6];
 static_assert(kWave64.kind == 2 && kWave128.kind == 2, "the wave kernel is the DMA kernel's loop");
 static_assert(sizeof(FwdArgs) + sizeof(WaveTable) <= 4096, "the wave kernel's arguments fit the 4 KiB kernel-argument segment");
 

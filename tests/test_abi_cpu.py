@@ -38,13 +38,15 @@ def test_library_exports_every_declared_function():
 def test_forward_kernel_name(test_controls):
     import exact_long_context_cqsa_amd as m
     test_controls(0, -1)
-    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
-    assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ")
+    # the default at both head dims is the ping-pong DMA kernel; variant 6 is the DMA kernel's best
+    # shape (pipelined and lean at D=64, plain at D=128), variants 4 and 5 its other choices
+    assert m.fwd_kernel_name(64).startswith("fwd_pp_dma_kernel waves=8 ")
+    assert m.fwd_kernel_name(128).startswith("fwd_pp_dma_kernel waves=8 ")
     assert m.fwd_kernel_name(96) == ""
-    # the default shape is pipelined and lean at D=64 and neither at D=128; variant 4 is the other
-    # pipelining choice, variant 5 the other lean choice
-    assert "pipelined" in m.fwd_kernel_name(64) and "pipelined" not in m.fwd_kernel_name(128)
-    assert "lean" in m.fwd_kernel_name(64) and "lean" not in m.fwd_kernel_name(128)
+    test_controls(6, -1)
+    assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ")
+    assert "pipelined" in m.fwd_kernel_name(64) and "lean" in m.fwd_kernel_name(64)
+    assert "pipelined" not in m.fwd_kernel_name(128) and "lean" not in m.fwd_kernel_name(128)
     test_controls(5, -1)
     assert "pipelined" in m.fwd_kernel_name(64) and "lean" not in m.fwd_kernel_name(64)
     assert "lean" in m.fwd_kernel_name(128)
@@ -53,16 +55,19 @@ def test_forward_kernel_name(test_controls):
     test_controls(4, -1)
     assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ") and "pipelined" not in m.fwd_kernel_name(64)
     assert m.fwd_kernel_name(128).startswith("fwd_dma_kernel ") and "pipelined" in m.fwd_kernel_name(128)
-    for bad in ((99, -1), (-1, -1), (0, -2)):   # out of range: rejected, nothing changes
+    test_controls(7, -1)
+    assert m.fwd_kernel_name(64).startswith("fwd_pp_dma_kernel ")
+    assert "keys_per_tile=32" in m.fwd_kernel_name(128)
+    for bad in ((99, -1), (-1, -1), (0, -2), (8, -1)):   # out of range: rejected, nothing changes
         with pytest.raises(m.CqsaError, match="INVALID"):
             test_controls(*bad)
-        assert m.fwd_kernel_name(64).startswith("fwd_dma_kernel ") and "pipelined" not in m.fwd_kernel_name(64)
+        assert m.fwd_kernel_name(64).startswith("fwd_pp_dma_kernel ")
     # split-P runs the DMA kernel in its own shape whatever the variant
     test_controls(2, -1)
     assert m.fwd_kernel_name(64, 1).startswith("fwd_dma_kernel ") and m.fwd_kernel_name(64, 1).endswith("split_p")
     assert m.fwd_kernel_name(128, 1).endswith("split_p")
     test_controls(0, -1)
-    assert "pipelined" in m.fwd_kernel_name(64)
+    assert m.fwd_kernel_name(64).startswith("fwd_pp_dma_kernel ")
 
 
 def test_struct_layout_and_version():

@@ -70,7 +70,7 @@ def test_small_full_parity(case):
 VARIANT_CASES = [SMALL[1], SMALL[2], SMALL[3], SMALL[4], SMALL[7]]
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("variant", [1, 2, 3, 4, 5, 6, 7])
 def test_every_forward_kernel_variant(variant, test_controls):
     """The non-default forward kernels (selected by cqsa_set_test_controls) on ragged, GQA,
     non-causal and long-key cases, monolithic and with a forced KV split."""
@@ -382,7 +382,7 @@ SHIFT_CASES = [
 ]
 
 
-@pytest.mark.parametrize("variant", [0, 4, 5])
+@pytest.mark.parametrize("variant", [0, 4, 5, 6, 7])
 @pytest.mark.parametrize("case", SHIFT_CASES, ids=lambda c: f"d{c[0]}{'f16' if c[1] == torch.float16 else 'bf16'}"
                          f"{'c' if c[2] else 'n'}")
 def test_shift_moves_inside_a_tile(case, variant, test_controls):
@@ -390,8 +390,10 @@ def test_shift_moves_inside_a_tile(case, variant, test_controls):
     the start of other tiles), by growing amounts, so the exact path of the online softmax runs in the
     middle of a tile, after the first block's probabilities were formed (and, in the pipelined kernel,
     after its PV products were issued).  Every query gets q[..., 0] = 3; the chosen keys get
-    k[..., 0] raised so that their logit rises by 8 + 1.5 t (natural log) in tile t.  Both choices of
-    the pipelined order (the default and kernel variant 4) are compared with the FP64 reference."""
+    k[..., 0] raised so that their logit rises by 8 + 1.5 t (natural log) in tile t.  The kernels whose
+    softmax runs per 32-key block (the ping-pong DMA kernel in both shapes, variants 0 and 7, and the
+    DMA kernel's pipelined shapes) and the DMA kernel's plain order are compared with the FP64
+    reference."""
     D, dtype, causal = case
     test_controls(variant, -1)
     B, H, N = 1, 2, 1100
