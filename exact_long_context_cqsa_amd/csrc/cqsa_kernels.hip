@@ -1096,18 +1096,6 @@ fwd_dma_kernel(const FwdArgs a) {
 // the compiler from moving loads or stores across it.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Ping-pong DMA forward kernel: 8 waves of 32 query rows in two groups, A = waves 0-3 and B = waves
-// 4-7, so that wave w of A and wave w of B share a SIMD.  Each group alternates a matrix phase (the
-// PV products of the previous tile, then the scores of the current tile) and a vector phase (the
-// online softmax of the current tile); B runs one phase behind A.  Every phase ends with a barrier, so
-// in each phase one wave of every SIMD keeps the matrix core busy while the other uses the VALU,
-// instead of both taking turns.
-// K and V tiles reach LDS by buffer-load DMA into the two stages of the DMA kernel's layout.  Only
-// group A issues it, at the end of its matrix phase 2i (after its operand reads): K(i+1) and V(i).
-// The barrier ending phase 2i + 1 waits for them (vmcnt(0)); the one ending phase 2i waits for LDS
-// operations only.  K(i) is read in phases 2i (A) and 2i+1 (B), V(i) in phases 2i+2 (A) and 2i+3
-// (B), so each DMA writes a buffer whose last reader finished before the phase it is issued in, and
-// is read only after the barrier that waited for it.
 // Instruction order for NM matrix products that each take RPM LDS operand reads, issued by one wave:
 // the reads of the first PD products, then one product and the reads PD products ahead, so that PD
 // products' worth of reads are always in flight behind the matrix core.
@@ -1122,6 +1110,18 @@ __device__ __forceinline__ void mfma_read_pipeline() {
     __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
 }
 
+// Ping-pong DMA forward kernel: 8 waves of 32 query rows in two groups, A = waves 0-3 and B = waves
+// 4-7, so that wave w of A and wave w of B share a SIMD.  Each group alternates a matrix phase (the
+// PV products of the previous tile, then the scores of the current tile) and a vector phase (the
+// online softmax of the current tile); B runs one phase behind A.  Every phase ends with a barrier, so
+// in each phase one wave of every SIMD keeps the matrix core busy while the other uses the VALU,
+// instead of both taking turns.
+// K and V tiles reach LDS by buffer-load DMA into the two stages of the DMA kernel's layout.  Only
+// group A issues it, at the end of its matrix phase 2i (after its operand reads): K(i+1) and V(i).
+// The barrier ending phase 2i + 1 waits for them (vmcnt(0)); the one ending phase 2i waits for LDS
+// operations only.  K(i) is read in phases 2i (A) and 2i+1 (B), V(i) in phases 2i+2 (A) and 2i+3
+// (B), so each DMA writes a buffer whose last reader finished before the phase it is issued in, and
+// is read only after the barrier that waited for it.
 template <int D, int DT, int KT, int WPE>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(WPE)))
 fwd_pp_dma_kernel(const FwdArgs a) {

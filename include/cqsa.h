@@ -410,8 +410,9 @@ const char* cqsa_fwd_kernel_name(int64_t head_dim, int32_t precision);
 /*
  * Test and measurement controls, process-wide (not part of the attention contract; every call
  * runs with the defaults, 0 and -1, unless a test or a measurement sets them):
- *   fwd_variant          0 = the default forward kernel of each head dim; 1..5 = the alternative
- *                        kernel shapes, so that tests can run every kernel and measurements can
+ *   fwd_variant          0 = the default forward kernel of each head dim (the ping-pong DMA
+ *                        kernel); 1..7 = the alternative kernels and shapes (6 = the DMA kernel's
+ *                        best shape), so that tests can run every kernel and measurements can
  *                        compare them (cqsa_fwd_kernel_name names the choice).
  *   fail_after_launches  -1 = off; n >= 0 makes every forward launch of a call after its first n
  *                        fail from the host, as a failed launch would (CQSA_ERR_HIP), so that tests
