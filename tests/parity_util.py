@@ -16,15 +16,20 @@ LSE_RTOL = 1e-4
 
 
 def sample_rows(B: int, H: int, N: int, *, seed: int = 0, n_random: int = 512, edge: int = 64,
-                boundaries=(), cap: int = 256, heads=None) -> np.ndarray:
-    """Rows checked at scale, in every (b, h): the first and last `edge` rows, rows +-1 around
-    each boundary (chunk and tile edges; at most `cap` of them), and `n_random` seeded rows."""
+                boundaries=(), tiles=(), cap: int = 256, heads=None) -> np.ndarray:
+    """Rows checked at scale, in every (b, h): the first and last `edge` rows, rows +-1 around each
+    chunk boundary and around evenly spread tile boundaries (at most `cap` boundary rows, chunk
+    boundaries first), and `n_random` seeded rows."""
     rng = np.random.default_rng(seed)
     idx = set(range(min(edge, N))) | set(range(max(0, N - edge), N))
     bl = sorted({int(x) for x in boundaries if 0 < x < N})
     if len(bl) > cap // 2:
         bl = list(np.array(bl)[np.linspace(0, len(bl) - 1, cap // 2).astype(int)])
-    for x in bl:
+    tl = sorted({int(x) for x in tiles if 0 < x < N} - set(bl))
+    room = cap // 2 - len(bl)
+    if len(tl) > room:
+        tl = list(np.array(tl)[np.linspace(0, len(tl) - 1, room).astype(int)]) if room > 0 else []
+    for x in bl + tl:
         idx |= {x - 1, x}
     idx |= set(rng.integers(0, N, size=min(n_random, N)).tolist())
     idx = np.array(sorted(i for i in idx if 0 <= i < N), dtype=np.int64)
