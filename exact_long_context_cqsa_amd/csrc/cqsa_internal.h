@@ -109,7 +109,7 @@ struct MergeArgs {
 
 // Backward: gradients of out = softmax(scale q k^T [+ causal]) v for an upstream gradient dout, over
 // Nq query rows and Nk keys (the whole problem, or one query chunk against one key chunk).  stats is
-// an fp32 array of (lse * log2 e, Delta = rowsum(dout * out)) pairs: row i of head (b, h) at
+// an fp32 array of (lse * log2 e, -Delta) pairs, Delta = rowsum(dout * out): row i of head (b, h) at
 // 2 ((b Hq + h) stats_rows + i), written by the first pass and read by the two gradient kernels.  The
 // causal rule is key j visible to row i iff j <= i + causal_delta (Nk - Nq for a whole, bottom-right
 // aligned problem).  dq is [B, Hq, Nq, D]; dk, dv are [B, Hkv, Nk, D] and sum over the query heads of

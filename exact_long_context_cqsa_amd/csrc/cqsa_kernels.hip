@@ -351,18 +351,20 @@ __device__ __forceinline__ void dma_rows_s(uint16_t* st, const uint16_t* row0, i
 #endif
 }
 
-// One wave's DMA of NB bytes (a multiple of 256) of fp32 data from base into LDS at st, 4 bytes per
-// lane and instruction; bytes at or past nbytes read as zero.  Device pass only, like dma_rows.
-template <int NB>
-__device__ __forceinline__ void dma_words(float* st, const float* base, int nbytes, int lane) {
-    static_assert(NB % 256 == 0, "whole instructions");
+// The row statistics of a query tile into LDS by buffer-load DMA, rearranged on the way: HBM holds
+// (lse2, -Delta) pairs per row, LDS receives the tile's lse2 values and then its -Delta values, so that
+// the 4 rows of a score register group load as one f32x4 of each.  Lane l of instruction i writes LDS
+// word 64 i + l from the byte offset off[i] (pair word 2 j for lse2 word j, 2 j + 1 for -Delta word j);
+// rows at or past nrows read as zero.  Device pass only, like dma_rows.
+template <int NSI>
+__device__ __forceinline__ void dma_stats(float* st, const float* base, int nrows, const int (&off)[NSI]) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nbytes > 0 ? nbytes : 0, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, nrows > 0 ? nrows * 8 : 0, kRsrcWord3);
 #pragma unroll
-    for (int i = 0; i < NB / 256; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(st + 64 * i), 4,
-                                                 lane * 4 + 256 * i, 0, 0, 0);
+    for (int i = 0; i < NSI; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(st + 64 * i), 4, off[i],
+                                                 0, 0, 0);
 #endif
 }
 
@@ -1602,35 +1604,56 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
 }
 
 // =============================================================================================
-// Backward.  Three launches: bwd_stats_kernel (Delta_i = dO_i . O_i and the base-2 lse per row),
+// Backward.  Three launches: bwd_stats_kernel (-Delta_i = -dO_i . O_i and the base-2 lse per row),
 // bwd_dq_kernel (per query tile, over key tiles: dQ^T += K^T dS^T) and bwd_dkdv_kernel (per key
 // tile, over the group's query heads and query tiles: dV^T += dO^T P, dK^T += Q^T dS).  Each
 // gradient element is accumulated by one wave in a fixed order: no atomics, deterministic.  The
 // derivative itself: P = exp(s - lse), dP = dO V^T, dS = P (dP - Delta), dQ = scale dS K,
-// dK = scale dS^T Q, dV = P^T dO.  All tiles in LDS use the V swizzle (vswz), which serves both the
-// row reads (A operand = rows of the tile) and the transpose reads (A operand = the tile transposed,
-// in the key-slot order of the packed B operand).
+// dK = scale dS^T Q, dV = P^T dO.  Every staged tile is read both ways: row reads (ds_read_b128, A
+// operand = rows of the tile) and transposed reads (ds_read_b64_tr_b16, A operand = the tile
+// transposed, in the key-slot order of the packed B operand).  The tiles therefore use their own
+// swizzle, bswz: granule g of row r sits at g ^ bswz(r).  LDS has 64 banks of 4 bytes; a row read is
+// served 16 lanes (16 rows) at a time and bswz gives those 16 rows 16 distinct 16-byte bank groups; a
+// transposed read is served 32 lanes (4 rows, 64 bytes each) at a time and bswz puts those 4 row
+// pieces on disjoint banks.  (The forward's kswz suits only the first pattern and vswz only the
+// second: with vswz a row read takes 4 times its conflict-free cycles.)
+
+template <int D>
+__device__ __forceinline__ int bswz(int r) {
+    return D == 64 ? ((4 * ((r >> 1) & 1)) | ((r >> 2) & 3)) : ((4 * (r & 3)) | ((r >> 2) & 3));
+}
 
 template <int D>
 __device__ __forceinline__ int rows_read(int l32, int t, int hi) {
-    return l32 * D + (((2 * t + hi) ^ vswz<D>(l32)) * 8);
+    return l32 * D + (((2 * t + hi) ^ bswz<D>(l32)) * 8);
 }
 
+// Element offset of this lane's transposed read of dim block db, rows 8 sec .. 8 sec + 7 of a 16-row
+// group (the group's offset, 16 t D, is added by the caller: bswz ignores row bits 4 and up).
 template <int D>
-__device__ __forceinline__ int tr_read(int lane, int db) {
+__device__ __forceinline__ int tr_read(int lane, int db, int sec) {
     const int hi = lane >> 5;
     const int src = lane & 15;
-    const int row = 4 * hi + src / 4;
+    const int row = 8 * sec + 4 * hi + src / 4;
     const int sub = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    return row * D + (((db * 4 + sub) ^ vswz<D>(row)) * 8) + 4 * (lane & 1);
+    return row * D + (((db * 4 + sub) ^ bswz<D>(row)) * 8) + 4 * (lane & 1);
 }
 
-// The transposed operand of one 16-slot group: p = tile + tr_read + 16 t D.
+// Offset from the first to the second read of tr_operand.  Rows r and r + 8 (r < 8) differ in bswz
+// by 2, so the granule moves by +-2 according to bit 1 of (sub ^ bswz(r)) = bit 1 of sub: the offset
+// depends on the lane but not on db.
 template <int D>
-__device__ __forceinline__ u32x4 tr_operand(const uint16_t* p) {
+__device__ __forceinline__ int tr_second(int lane) {
+    return 8 * D + (((lane >> 4) & 1) ? -16 : 16);
+}
+
+// The transposed operand of one 16-slot group: p = tile + tr_read(lane, db, 0) + 16 t D, p2 its
+// tr_second offset.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* p, int p2) {
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8 * D));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + p2));
     u32x4 x;
     x[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 0, 1));
     x[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(v0, v0, 2, 3));
@@ -1650,7 +1673,7 @@ __device__ __forceinline__ f32x8 load8(const void* base, int64_t off, int dt) {
     return dt == ET_F16 ? unpack8<ET_F16>(u) : unpack8<ET_BF16>(u);
 }
 
-// stats[row] = (lse * log2 e, sum_d dO O); D / 8 threads per row, 8 dims each.
+
 // A gradient store: four values at element off of base, in dtype dt; with accumulate (fp32 only)
 // added to what the four elements hold.
 __device__ __forceinline__ void store_grad(void* base, int64_t off, int dt, int accumulate, f32x4 v) {
@@ -1676,6 +1699,7 @@ __global__ void __launch_bounds__(256) cast_kernel(const float* src, int64_t B, 
     store4(dst, b * sb + h * sh + i * sn + d0, dtype, v);
 }
 
+// stats[row] = (lse * log2 e, -sum_d dO O) = (lse2, -Delta); D / 8 threads per row, 8 dims each.
 template <int D, int DT>
 __global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
     constexpr int TPR = D / 8;
@@ -1700,7 +1724,7 @@ __global__ void __launch_bounds__(256) bwd_stats_kernel(const BwdArgs a) {
         const float l = a.lse[b * a.l_sb + h * a.l_sh + i];
         const int64_t sr = (b * a.Hq + h) * a.stats_rows + i;
         a.stats[2 * sr] = l == -INFINITY ? INFINITY : l * kLog2e;   // no visible key: P = 0
-        a.stats[2 * sr + 1] = acc;
+        a.stats[2 * sr + 1] = -acc;
     }
 }
 
@@ -1739,7 +1763,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const uint16_t* kp = a.k + (int64_t)b * a.k_sb + (int64_t)hkv * a.k_sh;
     const uint16_t* vp = a.v + (int64_t)b * a.v_sb + (int64_t)hkv * a.v_sh;
 
-    // B operands: this lane's query row of q and of dO; its (lse2, Delta)
+    // B operands: this lane's query row of q and of dO; its (lse2, -Delta)
     const int64_t row = iw0 + l32;
     const bool row_ok = row < i_end;
     u32x4 qf[NDK], dof[NDK];
@@ -1754,26 +1778,30 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
             dof[t] = row_ok ? y : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    float lse2 = INFINITY, dlt = 0.f;
+    float lse2 = INFINITY, ndlt = 0.f;
     if (row_ok) {
         const float* sp = a.stats + 2 * (((int64_t)b * a.Hq + hq) * a.stats_rows + row);
         lse2 = sp[0];
-        dlt = sp[1];
+        ndlt = sp[1];
     }
+    f32x16 dpinit;   // the dP^T accumulators start from the row's -Delta, so dS = P dP
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpinit[r] = ndlt;
 
     int koff[BPW], voff[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
         const int r = (wave + i * NW) * RPI + lane / GPR;
         const int pg = lane % GPR;
-        koff[i] = (int)((r * a.k_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
-        voff[i] = (int)((r * a.v_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+        koff[i] = (int)((r * a.k_sn + ((pg ^ bswz<D>(r)) * 8)) * 2);
+        voff[i] = (int)((r * a.v_sn + ((pg ^ bswz<D>(r)) * 8)) * 2);
     }
     int rread[NDK], tread[NDB];
 #pragma unroll
     for (int t = 0; t < NDK; ++t) rread[t] = rows_read<D>(l32, t, hi);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db);
+    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db, 0);
+    const int tsec = tr_second<D>(lane);
 
     f32x16 dqacc[NDB];
 #pragma unroll
@@ -1817,7 +1845,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             sacc[kb] = f32x16{};
-            dpacc[kb] = f32x16{};
+            dpacc[kb] = dpinit;
         }
 #pragma unroll
         for (int t = 0; t < NDK; ++t)
@@ -1850,7 +1878,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * u + e], a.scale_log2, -lse2));
-                x[e] = p * (dpacc[kb][8 * u + e] - dlt);
+                x[e] = p * dpacc[kb][8 * u + e];
             }
             pf[t] = pack8<DT>(x);
         }
@@ -1858,7 +1886,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         for (int t = 0; t < NPK; ++t)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
-                dqacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), pf[t], dqacc[db]);
+                dqacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D, tsec), pf[t], dqacc[db]);
     }
 
     if (!row_ok) return;
@@ -1878,6 +1906,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 // at D = 128 the two accumulators and both operand sets of PART 0 need more than the 256 VGPRs of
 // two waves per SIMD, so dV and dK run as two launches that each recompute S (10 D FLOP per visible
 // pair instead of 8) at twice the occupancy.
+// Per tile: the dP accumulator starts from the rows' -Delta (so dS = P dP needs no subtraction); the
+// operand reads of the S and dP products run three products ahead of the matrix core; a tile that
+// reaches the causal diagonal or a ragged end masks by one compare pair per score against the lane's
+// visible row range; the next tile's DMA addresses are running scalar pointers.
 template <int D, int DT, int QT, int NW, int WPE, int PART>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) bwd_dkdv_kernel(const BwdArgs a, int n_kt) {
     constexpr int BN = NW * 32;
@@ -1885,11 +1917,12 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     constexpr int STAGE = 2 * TILE;                    // Q tile, then dO tile
     constexpr int GPR = D / 8, RPI = 64 / GPR, NBLK = QT / RPI, BPW = NBLK / NW;
     constexpr int NQB = QT / 32, NPQ = QT / 16, NDB = D / 32, NDK = D / 16;
+    constexpr int NSI = 2 * QT / 64;                   // stats DMA instructions per tile
     static_assert(NBLK % NW == 0, "tile split");
+    static_assert(2 * QT % 64 == 0, "the row statistics of a tile are whole 64-lane DMA instructions");
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) float stl[2][2 * QT];  // [stage][row][lse2, Delta]
-    static_assert(2 * QT * 4 % 256 == 0, "the row statistics of a tile are whole 256-byte DMA instructions");
+    __shared__ __attribute__((aligned(16))) float stl[2][2 * QT];  // [stage][lse2 of the rows, then -Delta]
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -1925,19 +1958,25 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int nqt = i_start < a.Nq ? (int)((a.Nq - i_start + QT - 1) / QT) : 0;
     const int total = nqt * a.group;
 
-    int qoff[BPW], doff[BPW];
+    int qoff[BPW], doff[BPW], soff[NSI];
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
         const int r = (wave + i * NW) * RPI + lane / GPR;
         const int pg = lane % GPR;
-        qoff[i] = (int)((r * a.q_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
-        doff[i] = (int)((r * a.do_sn + ((pg ^ vswz<D>(r)) * 8)) * 2);
+        qoff[i] = (int)((r * a.q_sn + ((pg ^ bswz<D>(r)) * 8)) * 2);
+        doff[i] = (int)((r * a.do_sn + ((pg ^ bswz<D>(r)) * 8)) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < NSI; ++i) {
+        const int j = 64 * i + lane;
+        soff[i] = 4 * (j < QT ? 2 * j : 2 * (j - QT) + 1);
     }
     int rread[NDK], tread[NDB];
 #pragma unroll
     for (int t = 0; t < NDK; ++t) rread[t] = rows_read<D>(l32, t, hi);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db);
+    for (int db = 0; db < NDB; ++db) tread[db] = tr_read<D>(lane, db, 0);
+    const int tsec = tr_second<D>(lane);
 
     f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -1946,25 +1985,26 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
         dvacc[db] = f32x16{};
     }
 
-    // Tile (th, tq): query head hkv * group + th, query rows from i_start + tq QT, with its rows' stats.
-    // Tiles run head-major; the running pair replaces a division by nqt per tile.
-    // (the pointers of head 0 of the group at row i_start, stepped per head and per tile; row counts in
-    // 32 bits and the wave index a scalar, so the DMA issue stays on the scalar unit)
+    // Tiles run head-major over (query head th of the group, query tile tq from row i_start).  The next
+    // tile's Q, dO and statistics are addressed by running scalar pointers (stepped by a tile, or reset
+    // to the next head's row i_start), its row count by a running remainder; the wave index is a scalar
+    // too, so the whole DMA issue stays on the scalar unit.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const uint16_t* q_g = a.q + (int64_t)b * a.q_sb + (int64_t)hkv * a.group * a.q_sh + i_start * a.q_sn;
-    const uint16_t* do_g = a.dout + (int64_t)b * a.do_sb + (int64_t)hkv * a.group * a.do_sh + i_start * a.do_sn;
-    const float* st_g = a.stats + 2 * (((int64_t)b * a.Hq + (int64_t)hkv * a.group) * a.stats_rows + i_start);
+    const uint16_t* qh = a.q + (int64_t)b * a.q_sb + (int64_t)hkv * a.group * a.q_sh + i_start * a.q_sn;
+    const uint16_t* dh = a.dout + (int64_t)b * a.do_sb + (int64_t)hkv * a.group * a.do_sh + i_start * a.do_sn;
+    const float* sh = a.stats + 2 * (((int64_t)b * a.Hq + (int64_t)hkv * a.group) * a.stats_rows + i_start);
     const int rows_left = (int)(a.Nq - i_start);
     const int qsb = (int)(a.q_sn * 2), dsb = (int)(a.do_sn * 2);
-    auto issue_tile = [&](int th, int tq, int stage) {
-        const int rem = rows_left - tq * QT;
+    const uint16_t* qn = qh;
+    const uint16_t* dn = dh;
+    const float* sn = sh;
+    int rem = rows_left;
+    auto issue_next = [&](int stage) __attribute__((always_inline)) {
         const int nv_ = rem < QT ? rem : QT;
         uint16_t* st_ = lds + stage * STAGE;
-        dma_rows_s<NW, BPW, D>(st_, q_g + th * a.q_sh + (int64_t)tq * QT * a.q_sn, qsb, nv_, qoff, wave_s);
-        dma_rows_s<NW, BPW, D>(st_ + TILE, do_g + th * a.do_sh + (int64_t)tq * QT * a.do_sn, dsb, nv_, doff, wave_s);
-        if (wave_s == NW - 1)   // the rows' (lse2, Delta) by DMA too; rows past Nq read as zero
-            dma_words<2 * QT * 4>(stl[stage], st_g + 2 * ((int64_t)th * a.stats_rows + (int64_t)tq * QT), nv_ * 8,
-                                  lane);
+        dma_rows_s<NW, BPW, D>(st_, qn, qsb, nv_, qoff, wave_s);
+        dma_rows_s<NW, BPW, D>(st_ + TILE, dn, dsb, nv_, doff, wave_s);
+        if (wave_s == NW - 1) dma_stats<NSI>(stl[stage], sn, nv_, soff);
     };
     // per-wave bounds on the query tile index, wave-uniform and taken to scalar registers once:
     //   the wave works on tile tq when some row of it sees some valid key of the wave (tq >= tq_first),
@@ -1983,30 +2023,66 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int wave_live = __builtin_amdgcn_readfirstlane(jw < a.Nk ? 1 : 0);
     const int key_ragged = __builtin_amdgcn_readfirstlane(jw + 32 > a.Nk ? 1 : 0);
     const int row_ragged = (a.Nq - i_start) % QT != 0 ? 1 : 0;
+    // the lane's key sees tile rows t >= key - delta - (i_start + tq QT) (causal), all rows when not
+    // causal, none when the key does not exist; kept relative to row i_start and clamped
+    const int64_t vis0 = !key_ok ? (int64_t)a.Nq : (a.causal ? max(key - delta_c - i_start, (int64_t)0) : (int64_t)0);
+    const int vis_row = (int)min(vis0, (int64_t)rows_left + QT);
 
     int tq = 0;                             // query tile of tile it
-    int nh = 0, nq = nqt > 1 ? 1 : 0;       // head and query tile of tile it + 1
-    if (nqt == 1) nh = 1;
-    if (total > 0) issue_tile(0, 0, 0);
-    for (int it = 0; it < total; ++it) {
-        __syncthreads();
-        if (it + 1 < total) issue_tile(nh, nq, (it + 1) & 1);
-        const int cur_q = tq;
-        tq = nq;
+    int nq = 0;                             // query tile of the next tile to issue
+    auto advance = [&]() __attribute__((always_inline)) {
         if (++nq == nqt) {
             nq = 0;
-            ++nh;
+            qh += a.q_sh;
+            dh += a.do_sh;
+            sh += 2 * a.stats_rows;
+            qn = qh;
+            dn = dh;
+            sn = sh;
+            rem = rows_left;
+        } else {
+            qn += (int64_t)QT * a.q_sn;
+            dn += (int64_t)QT * a.do_sn;
+            sn += 2 * QT;
+            rem -= QT;
+        }
+    };
+    if (total > 0) {
+        issue_next(0);
+        advance();
+    }
+    for (int it = 0; it < total; ++it) {
+        __syncthreads();
+        const int cur_q = tq;
+        tq = nq;
+        if (it + 1 < total) {
+            issue_next((it + 1) & 1);
+            advance();
         }
         if (!wave_live || cur_q < tq_first) continue;
-        const int64_t q0 = i_start + (int64_t)cur_q * QT;
         const uint16_t* st = lds + (it & 1) * STAGE;
         const float* sl = stl[it & 1];
         const bool need_mask = key_ragged || (a.causal && cur_q < tq_diag) || (row_ragged && cur_q == nqt - 1);
+        // visible rows [mlo, mhi) of this tile for the lane's key, less the lane's row offset 4 hi
+        const int mlo = vis_row - cur_q * QT - 4 * hi;
+        const int mhi = rows_left - cur_q * QT - 4 * hi;
 
         u32x4 pp[NPQ], ps[NPQ];
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
+            // register r of the lane holds query row qb 32 + 8 (r / 4) + 4 hi + r % 4 of the tile
+            f32x4 l4[4];
             f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                l4[g] = *reinterpret_cast<const f32x4*>(sl + qb * 32 + 8 * g + 4 * hi);
+                if constexpr (WANT_DK) {
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + QT + qb * 32 + 8 * g + 4 * hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dpacc[4 * g + e] = d4[e];
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int t = 0; t < NDK; ++t) {
                 const u32x4 qa = *reinterpret_cast<const u32x4*>(st + rread[t] + qb * 32 * D);
@@ -2016,30 +2092,23 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
                     dpacc = mfma32<DT>(da, vf[t], dpacc);
                 }
             }
-            // register r of the lane holds query row qb 32 + 8 (r / 4) + 4 hi + r % 4 of the tile
+            mfma_read_pipeline<(WANT_DK ? 2 : 1) * NDK, 1, 3>();
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c = qb * 32 + 8 * (r >> 2) + (r & 3);
+                    if (c < mlo || c >= mhi) sacc[r] = -INFINITY;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 f32x8 xp, xs;
 #pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int rr = qb * 32 + 8 * (2 * u + g) + 4 * hi;    // rows rr .. rr + 3
-                    const f32x4 s01 = *reinterpret_cast<const f32x4*>(sl + 2 * rr);
-                    const f32x4 s23 = *reinterpret_cast<const f32x4*>(sl + 2 * rr + 4);
-                    const f32x4 l4 = {s01[0], s01[2], s23[0], s23[2]};
-                    const f32x4 d4 = {s01[1], s01[3], s23[1], s23[3]};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 8 * u + 4 * g + e;
-                        float s = sacc[r];
-                        if (need_mask) {
-                            const int64_t qi = q0 + rr + e;
-                            const bool vis = key_ok && qi < a.Nq && (!a.causal || key <= qi + delta_c);
-                            if (!vis) s = -INFINITY;
-                        }
-                        const float p = __builtin_amdgcn_exp2f(fmaf(s, a.scale_log2, -l4[e]));
-                        xp[4 * g + e] = p;
-                        if constexpr (WANT_DK) xs[4 * g + e] = p * (dpacc[r] - d4[e]);
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * u + e;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], a.scale_log2, -l4[r >> 2][r & 3]));
+                    xp[e] = p;
+                    if constexpr (WANT_DK) xs[e] = p * dpacc[r];
                 }
                 if constexpr (WANT_DV) pp[2 * qb + u] = pack8<DT>(xp);
                 if constexpr (WANT_DK) ps[2 * qb + u] = pack8<DT>(xs);
@@ -2050,12 +2119,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 if constexpr (WANT_DV)
-                    dvacc[db] = mfma32<DT>(tr_operand<D>(st + TILE + tread[db] + 16 * t * D), pp[t], dvacc[db]);
+                    dvacc[db] = mfma32<DT>(tr_operand<D>(st + TILE + tread[db] + 16 * t * D, tsec), pp[t], dvacc[db]);
                 if constexpr (WANT_DK)
-                    dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D), ps[t], dkacc[db]);
+                    dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D, tsec), ps[t], dkacc[db]);
             }
     }
-#undef CQSA_BWD_KV_TILE
 
     if (!key_ok) return;
     const int64_t kbase = (int64_t)b * a.dk_sb + (int64_t)hkv * a.dk_sh + key * a.dk_sn;
