@@ -1236,6 +1236,8 @@ fwd_pp_dma_kernel(const FwdArgs a) {
     const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
     const int wave_a = __builtin_amdgcn_readfirstlane(wave & 3);
     const int nkeys = (int)(khi - klo);
+    // causal: this lane's row sees the keys klo + j for j < vis_end (32 bits, clamped to the range)
+    const int vis_end = (int)max(min(iw0 + l32 + a.causal_delta - klo + 1, (int64_t)nkeys + KT), (int64_t)-KT);
     const uint16_t* k0 = kp + klo * k_sn;
     const uint16_t* v0 = vp + klo * v_sn;
     const int ksb = (int)(k_sn * 2), vsb = (int)(v_sn * 2);
@@ -1316,12 +1318,9 @@ fwd_pp_dma_kernel(const FwdArgs a) {
             return;
         }
         if (i >= mask_from) {
-            const int64_t j0 = klo + (int64_t)i * KT;
-            int lim = (int)min(khi - j0, (int64_t)KT);
-            if (a.causal) {
-                const int64_t c = iw0 + l32 + a.causal_delta - j0 + 1;
-                lim = min(lim, (int)max(min(c, (int64_t)KT), (int64_t)0));
-            }
+            const int rem = nkeys - i * KT;
+            int lim = rem < KT ? rem : KT;
+            if (a.causal) lim = min(lim, max(min(vis_end - i * KT, KT), 0));
             mask_keys<NKB>(sacc, lim, hi);
         }
         if constexpr (PERBLOCK) {
@@ -1618,6 +1617,16 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
 // pieces on disjoint banks.  (The forward's kswz suits only the first pattern and vswz only the
 // second: with vswz a row read takes 4 times its conflict-free cycles.)
 
+// Workgroup barrier for the backward tile loops: each wave first waits for all of its buffer loads,
+// LDS DMA included, and its LDS operations, then meets the others.  A tile's DMA is split over the
+// waves, so only a wait before the barrier makes every wave's rows visible to all.  (The compiler's own
+// waits cannot be relied on here: the stages are separate LDS arrays, and it sees that the DMA in
+// flight writes the stage not being read.)
+__device__ __forceinline__ void barrier_dma() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0), a wait the compiler accounts for
+    __syncthreads();
+}
+
 template <int D>
 __device__ __forceinline__ int bswz(int r) {
     return D == 64 ? ((4 * ((r >> 1) & 1)) | ((r >> 2) & 3)) : ((4 * (r & 3)) | ((r >> 2) & 3));
@@ -1738,7 +1747,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     constexpr int NKB = KT / 32, NPK = KT / 16, NDB = D / 32, NDK = D / 16;
     static_assert(NBLK % NW == 0, "tile split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    // two stages, each its own LDS array, named at compile time by every read and DMA (so the next
+    // tile's DMA costs no wait inside the current tile)
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[STAGE];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -1825,21 +1837,19 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int nkeys = (int)khi;
     const int ksb = (int)(a.k_sn * 2), vsb = (int)(a.v_sn * 2);
-    auto issue = [&](int j) {
+    auto issue = [&](int j, uint16_t* st_) __attribute__((always_inline)) {
         const int rem = nkeys - j * KT;
         const int nv = rem < KT ? rem : KT;
-        uint16_t* st_ = lds + (j & 1) * STAGE;
         dma_rows_s<NW, BPW, D>(st_, kp + (int64_t)j * KT * a.k_sn, ksb, nv, koff, wave_s);
         dma_rows_s<NW, BPW, D>(st_ + TILE, vp + (int64_t)j * KT * a.v_sn, vsb, nv, voff, wave_s);
     };
 
-    if (ntiles > 0) issue(0);
-    for (int it = 0; it < ntiles; ++it) {
-        __syncthreads();
-        if (it + 1 < ntiles) issue(it + 1);
+    // tile it: reads stage st, issues tile it + 1 into stage nst
+    auto tile = [&](int it, const uint16_t* st, uint16_t* nst) __attribute__((always_inline)) {
+        barrier_dma();
+        if (it + 1 < ntiles) issue(it + 1, nst);
         const int64_t j0 = (int64_t)it * KT;
-        if (it >= wtiles) continue;
-        const uint16_t* st = lds + (it & 1) * STAGE;
+        if (it >= wtiles) return;
 
         f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
@@ -1887,6 +1897,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
                 dqacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D, tsec), pf[t], dqacc[db]);
+    };
+    if (ntiles > 0) issue(0, lds0);
+    for (int it = 0; it < ntiles; it += 2) {
+        tile(it, lds0, lds1);
+        if (it + 1 < ntiles) tile(it + 1, lds1, lds0);
     }
 
     if (!row_ok) return;
@@ -1921,8 +1936,13 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     static_assert(NBLK % NW == 0, "tile split");
     static_assert(2 * QT % 64 == 0, "the row statistics of a tile are whole 64-lane DMA instructions");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-    __shared__ __attribute__((aligned(16))) float stl[2][2 * QT];  // [stage][lse2 of the rows, then -Delta]
+    // two stages, each its own LDS array (tiles, then the rows' lse2 and -Delta): every read and every
+    // DMA below names its array at compile time, so the compiler can tell that the next tile's DMA does
+    // not write what the current tile reads and inserts no wait for it inside the tile
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[STAGE];
+    __shared__ __attribute__((aligned(16))) float stl0[2 * QT];
+    __shared__ __attribute__((aligned(16))) float stl1[2 * QT];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
@@ -1999,12 +2019,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
     const uint16_t* dn = dh;
     const float* sn = sh;
     int rem = rows_left;
-    auto issue_next = [&](int stage) __attribute__((always_inline)) {
+    auto issue_next = [&](uint16_t* st_, float* sl_) __attribute__((always_inline)) {
         const int nv_ = rem < QT ? rem : QT;
-        uint16_t* st_ = lds + stage * STAGE;
         dma_rows_s<NW, BPW, D>(st_, qn, qsb, nv_, qoff, wave_s);
         dma_rows_s<NW, BPW, D>(st_ + TILE, dn, dsb, nv_, doff, wave_s);
-        if (wave_s == NW - 1) dma_stats<NSI>(stl[stage], sn, nv_, soff);
+        if (wave_s == NW - 1) dma_stats<NSI>(sl_, sn, nv_, soff);
     };
     // per-wave bounds on the query tile index, wave-uniform and taken to scalar registers once:
     //   the wave works on tile tq when some row of it sees some valid key of the wave (tq >= tq_first),
@@ -2047,21 +2066,17 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
             rem -= QT;
         }
     };
-    if (total > 0) {
-        issue_next(0);
-        advance();
-    }
-    for (int it = 0; it < total; ++it) {
-        __syncthreads();
+    // tile it: reads stage st / sl, issues tile it + 1 into stage nst / nsl
+    auto tile = [&](int it, const uint16_t* st, const float* sl, uint16_t* nst, float* nsl)
+                    __attribute__((always_inline)) {
+        barrier_dma();
         const int cur_q = tq;
         tq = nq;
         if (it + 1 < total) {
-            issue_next((it + 1) & 1);
+            issue_next(nst, nsl);
             advance();
         }
-        if (!wave_live || cur_q < tq_first) continue;
-        const uint16_t* st = lds + (it & 1) * STAGE;
-        const float* sl = stl[it & 1];
+        if (!wave_live || cur_q < tq_first) return;
         const bool need_mask = key_ragged || (a.causal && cur_q < tq_diag) || (row_ragged && cur_q == nqt - 1);
         // visible rows [mlo, mhi) of this tile for the lane's key, less the lane's row offset 4 hi
         const int mlo = vis_row - cur_q * QT - 4 * hi;
@@ -2071,12 +2086,10 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             // register r of the lane holds query row qb 32 + 8 (r / 4) + 4 hi + r % 4 of the tile
-            f32x4 l4[4];
             f32x16 sacc = f32x16{}, dpacc = f32x16{};
+            if constexpr (WANT_DK) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                l4[g] = *reinterpret_cast<const f32x4*>(sl + qb * 32 + 8 * g + 4 * hi);
-                if constexpr (WANT_DK) {
+                for (int g = 0; g < 4; ++g) {
                     const f32x4 d4 = *reinterpret_cast<const f32x4*>(sl + QT + qb * 32 + 8 * g + 4 * hi);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) dpacc[4 * g + e] = d4[e];
@@ -2093,6 +2106,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
                 }
             }
             mfma_read_pipeline<(WANT_DK ? 2 : 1) * NDK, 1, 3>();
+            f32x4 l4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(sl + qb * 32 + 8 * g + 4 * hi);
             if (need_mask) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -2123,6 +2139,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WP
                 if constexpr (WANT_DK)
                     dkacc[db] = mfma32<DT>(tr_operand<D>(st + tread[db] + 16 * t * D, tsec), ps[t], dkacc[db]);
             }
+    };
+    if (total > 0) {
+        issue_next(lds0, stl0);
+        advance();
+    }
+    for (int it = 0; it < total; it += 2) {
+        tile(it, lds0, stl0, lds1, stl1);
+        if (it + 1 < total) tile(it + 1, lds1, stl1, lds0, stl0);
     }
 
     if (!key_ok) return;
@@ -2416,8 +2440,9 @@ hipError_t launch_bwd_d(const BwdArgs& a, int pass, hipStream_t st) {
         return hipGetLastError();
     }
     constexpr int DQ_NW = D == 64 ? 8 : 4, DQ_KT = D == 64 ? 64 : 32, DQ_WPE = 2;
-    // D=64: dK and dV in one pass; D=128: a dV pass, then a dK pass, each at two waves per SIMD
-    constexpr int KV_NW = 4, KV_QT = 32, KV_WPE = 2;
+    // D=64: dK and dV in one pass at three waves per SIMD; D=128: a dV pass at three waves, then a dK
+    // pass at two (its 224 registers)
+    constexpr int KV_NW = 4, KV_QT = 32;
     if (pass == BWD_DQ) {
         const int64_t n_qt = (a.Nq + DQ_NW * 32 - 1) / (DQ_NW * 32);
         const int64_t blocks = (int64_t)a.B * a.Hq * n_qt;
@@ -2433,14 +2458,14 @@ hipError_t launch_bwd_d(const BwdArgs& a, int pass, hipStream_t st) {
     if (blocks > 0x7FFFFFFF || n_kt > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (blocks > 0) {
         if constexpr (D == 64) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 0>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, 3, 0>), dim3((unsigned)blocks),
                                dim3(KV_NW * 64), 0, st, a, (int)n_kt);
         } else {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, 3, 1>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
                                st, a, (int)n_kt);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, KV_WPE, 2>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, KV_QT, KV_NW, 2, 2>), dim3((unsigned)blocks), dim3(KV_NW * 64), 0,
                                st, a, (int)n_kt);
         }
     }
