@@ -1098,6 +1098,16 @@ fwd_dma_kernel(const FwdArgs a) {
 // the compiler from moving loads or stores across it.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Workgroup barrier for tile loops with two LDS stages: each wave first waits for all of its buffer loads,
+// LDS DMA included, and its LDS operations, then meets the others.  A tile's DMA is split over the
+// waves, so only a wait before the barrier makes every wave's rows visible to all.  (The compiler's own
+// waits cannot be relied on here: the stages are separate LDS arrays, and it sees that the DMA in
+// flight writes the stage not being read.)
+__device__ __forceinline__ void barrier_dma() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0), a wait the compiler accounts for
+    __syncthreads();
+}
+
 // Instruction order for NM matrix products that each take RPM LDS operand reads, issued by one wave:
 // the reads of the first PD products, then one product and the reads PD products ahead, so that PD
 // products' worth of reads are always in flight behind the matrix core.
@@ -1419,7 +1429,10 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
     constexpr int NDK = D / 16;
     static_assert(NBLK % NW == 0, "tile split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    // two stages, each its own LDS array named at compile time by every read and DMA, so the next
+    // tile's DMA costs no wait inside the current tile
+    __shared__ __attribute__((aligned(16))) uint16_t lds0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds1[STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -1537,10 +1550,12 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
     int cj0 = 0, clen = flen;
     int64_t cdelta = pos0 - t.ki[fs].lo;
     int cs = fs;
-    dma_rows<NW, BPW, D>(lds, fk, ksn, 0, min(flen, KT), koff, wave);
-    dma_rows<NW, BPW, D>(lds + TILE, fv, vsn, 0, min(flen, KT), voff, wave);
-    for (int it = 0;; ++it) {
-        __syncthreads();   // tile it is in LDS; every wave is done with tile it - 1
+    dma_rows<NW, BPW, D>(lds0, fk, ksn, 0, min(flen, KT), koff, wave);
+    dma_rows<NW, BPW, D>(lds0 + TILE, fv, vsn, 0, min(flen, KT), voff, wave);
+    // one tile: computes from stage st, prefetches the next tile into stage nst; false once the
+    // compute cursor has passed the last segment
+    auto tile = [&](const uint16_t* st, uint16_t* nst) __attribute__((always_inline)) -> bool {
+        barrier_dma();   // this tile is in LDS; every wave is done with the previous one
         if (fs >= 0) {
             fj0 += KT;
             if (fj0 >= flen) {
@@ -1553,17 +1568,15 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
                 }
             }
             if (fs >= 0) {
-                uint16_t* st = lds + ((it + 1) & 1) * STAGE;
                 const int nv = min(flen - fj0, KT);
-                dma_rows<NW, BPW, D>(st, fk, ksn, fj0, nv, koff, wave);
-                dma_rows<NW, BPW, D>(st + TILE, fv, vsn, fj0, nv, voff, wave);
+                dma_rows<NW, BPW, D>(nst, fk, ksn, fj0, nv, koff, wave);
+                dma_rows<NW, BPW, D>(nst + TILE, fv, vsn, fj0, nv, voff, wave);
             }
         }
 
         const int j0 = cj0;   // first key of the tile, local to the segment
         const bool active = iw0 < i_end && (!a.causal || j0 <= iw_end - 1 + cdelta);
         if (active) {
-            const uint16_t* st = lds + (it & 1) * STAGE;
             f32x16 sacc[NKB];
             scores<D, NKB, NDK, DT>(st, kread, qf, sacc);
             const bool need_mask = (j0 + KT > clen) || (a.causal && (j0 + KT - 1 > iw0 + cdelta));
@@ -1587,11 +1600,14 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
         cj0 += KT;
         if (cj0 >= clen) {
             cs = next_seg(cs);
-            if (cs < 0) break;
+            if (cs < 0) return false;
             cj0 = 0;
             clen = seg_len(cs);
             cdelta = pos0 - t.ki[cs].lo;
         }
+        return true;
+    };
+    while (tile(lds0, lds1) && tile(lds1, lds0)) {
     }
 
     if constexpr (SPLIT) {
@@ -1616,16 +1632,6 @@ fwd_wave_kernel(const FwdArgs a, const WaveTable t) {
 // transposed read is served 32 lanes (4 rows, 64 bytes each) at a time and bswz puts those 4 row
 // pieces on disjoint banks.  (The forward's kswz suits only the first pattern and vswz only the
 // second: with vswz a row read takes 4 times its conflict-free cycles.)
-
-// Workgroup barrier for the backward tile loops: each wave first waits for all of its buffer loads,
-// LDS DMA included, and its LDS operations, then meets the others.  A tile's DMA is split over the
-// waves, so only a wait before the barrier makes every wave's rows visible to all.  (The compiler's own
-// waits cannot be relied on here: the stages are separate LDS arrays, and it sees that the DMA in
-// flight writes the stage not being read.)
-__device__ __forceinline__ void barrier_dma() {
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0), a wait the compiler accounts for
-    __syncthreads();
-}
 
 template <int D>
 __device__ __forceinline__ int bswz(int r) {
