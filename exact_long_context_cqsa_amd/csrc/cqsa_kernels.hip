@@ -1368,7 +1368,7 @@ fwd_pp_dma_kernel(const FwdArgs a) {
             mphase(i, S, true);
             barrier_lds();
             if (i < ntiles) vphase(i);
-            __syncthreads();   // the DMA issued in phase 2i is in LDS
+            barrier_dma();   // the DMA issued in phase 2i is in LDS
         };
         for (int i = 0; i <= ntiles; i += 2) {
             step(i, 0);
@@ -1379,7 +1379,7 @@ fwd_pp_dma_kernel(const FwdArgs a) {
             if (i >= 1) vphase(i - 1);
             barrier_lds();
             mphase(i, S, false);
-            __syncthreads();
+            __syncthreads();   // group B issues no DMA: a plain barrier
         };
         for (int i = 0; i <= ntiles; i += 2) {
             step(i, 0);
