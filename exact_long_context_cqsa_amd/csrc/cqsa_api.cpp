@@ -62,6 +62,12 @@ constexpr double kSafety = 0.85;           // fraction of the budget the planner
 constexpr int64_t kRowGrain = 256;         // chunk sizes are multiples of this (then clipped)
 constexpr int64_t kKvCap = 262144;         // largest automatic KV chunk (keys)
 constexpr int64_t kKvMinStream = 4096;     // smallest automatic KV chunk worth streaming
+// Device-resident inputs whose key range exceeds kLongKeys run one launch per KV chunk of kKvResident
+// keys (folded by the kernel epilogue), not one pass: a workgroup sweeping millions of keys loses the
+// cache reuse that every workgroup sweeping the same 128K-key chunk keeps (4M causal keys, H=8, D=64:
+// 20.4 s one pass, 17.6 s in 128K chunks)
+constexpr int64_t kLongKeys = 524288;
+constexpr int64_t kKvResident = 131072;
 
 int esize_of(int dt) { return dt == CQSA_F32 ? 4 : 2; }
 
@@ -653,8 +659,12 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
     if (opt.q_chunk < 0 || opt.kv_chunk < 0 || opt.kv_splits < 0)
         return fail(CQSA_ERR_INVALID, "negative chunk option");
     const bool forced = opt.q_chunk > 0 || opt.kv_chunk > 0;
+    // long key ranges on the device: KV chunks of kKvResident keys when their accumulator fits
+    bool long_keys = false;
+    if (!P.streamed && !forced && opt.kv_splits == 0 && P.Nk > kLongKeys)
+        long_keys = chunk_bytes(P, P.Nq, kKvResident, req_merge == 0 ? CQSA_MERGE_FUSED : req_merge, false, pl) <= budget;
 
-    if (!P.streamed && !forced) {
+    if (!P.streamed && !forced && !long_keys) {
         // one pass over all keys; optional side-by-side KV splits to fill the GPU
         const int64_t n_qt = ceil_div(P.Nq, pl->bm);
         const int64_t wgs = P.B * P.Hq * n_qt;
@@ -702,10 +712,13 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
     // chunked plan
     pl->chunked = true;
     pl->kv_splits = 1;
-    pl->merge = req_merge == 0 ? (P.streamed ? CQSA_MERGE_FUSED : CQSA_MERGE_KERNEL) : req_merge;
+    pl->merge = req_merge == 0 ? ((P.streamed || long_keys) ? CQSA_MERGE_FUSED : CQSA_MERGE_KERNEL) : req_merge;
     int64_t qc = opt.q_chunk > 0 ? std::min(opt.q_chunk, P.Nq) : 0;
     int64_t kc = opt.kv_chunk > 0 ? std::min(opt.kv_chunk, P.Nk) : 0;
-    if (qc > 0 && kc > 0) {
+    if (long_keys) {
+        qc = P.Nq;
+        kc = kKvResident;
+    } else if (qc > 0 && kc > 0) {
         // both forced
     } else if (!P.streamed) {
         if (qc == 0) qc = P.Nq;

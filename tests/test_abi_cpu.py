@@ -155,6 +155,22 @@ def test_plan_split_kv_when_few_query_tiles():
     assert p1["kv_splits"] == 1 and p1["workspace_bytes"] == 0
 
 
+def test_plan_resident_long_key_range():
+    """Device-resident inputs over more than 512K keys run one launch per 128K-key chunk, folded by the
+    kernel epilogue into one fp32 accumulator, when that accumulator fits the budget; otherwise, with
+    forced kv_splits, or at 512K keys and below, one pass with no workspace."""
+    s = shp(1, 8, 4194304, 64)
+    p = plan(s, s, s, True, 16 * GB)
+    assert (p["q_chunk"], p["kv_chunk"], p["n_kv_chunks"], p["merge_mode"]) == (4194304, 131072, 32, 2)
+    assert (p["chunk_pairs"], p["merges"], p["kernel_launches"]) == (32, 31, 33)
+    assert p["workspace_bytes"] == 8 * 4194304 * (64 + 2) * 4 and p["h2d_bytes"] == 0
+    for kw, budget in (({}, 8 * GB), ({"kv_splits": 1}, 16 * GB)):
+        p1 = plan(s, s, s, True, budget, **kw)
+        assert (p1["n_kv_chunks"], p1["workspace_bytes"], p1["kernel_launches"]) == (1, 0, 1)
+    s2 = shp(1, 8, 524288, 64)
+    assert plan(s2, s2, s2, True, 16 * GB)["n_kv_chunks"] == 1
+
+
 def test_plan_errors():
     import exact_long_context_cqsa_amd as m
     s = shp(1, 8, 4194304, 64)
