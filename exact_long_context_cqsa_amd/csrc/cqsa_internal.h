@@ -171,6 +171,8 @@ hipError_t noalloc_scratch(void** ptr);
 
 // Query rows per workgroup of the forward kernel for a head dim (and the split-P mode).
 int fwd_block_m(int D, int p_split);
+// Workgroups of the forward kernel (the default or the split-P shape) that one CU holds at once.
+int fwd_wgs_per_cu(int D, int p_split);
 
 // Name and shape of the forward kernel launched for a head dim ("" if none).
 const char* fwd_kernel_name(int D, int p_split);

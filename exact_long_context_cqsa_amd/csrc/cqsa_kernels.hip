@@ -23,6 +23,7 @@
 // LDS that way, fwd_dma_kernel assembles it from row-major tiles with transpose loads.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <math.h>
 #include <mutex>
@@ -2363,6 +2364,11 @@ hipError_t noalloc_scratch(void** ptr) {
 }
 
 int fwd_block_m(int D, int p_split) { return shape_of(D, p_split).nw * 32; }
+
+int fwd_wgs_per_cu(int D, int p_split) {
+    const Shape sh = shape_of(D, p_split);
+    return std::max(1, 4 * sh.wpe / sh.nw);   // 4 SIMDs, wpe waves each, nw waves per workgroup
+}
 
 const char* fwd_kernel_name(int D, int p_split) {
     static char names[2][kNumShapes + 1][112];
