@@ -184,7 +184,7 @@ def measured_traffic(path: str):
 def run_configs(cqsa, torch, synth, steps: int) -> tuple[dict, dict]:
     """The other measured configurations, each with its inputs in HBM: the 1,024-token parity case (4 KV
     chunks of 256 merged by log-sum-exp; a time, no roofline claim), the 2,048-query GQA prompt at 8K,
-    32K and 131K keys, and the full-size softmax-stress case (16 KV chunks of 16,384, 15 merges).  Each
+    32K and 131K keys, and the full-size softmax-stress case (16 KV chunks of 16,384, 15 folds).  Each
     call is timed with HIP events on the current stream; TFLOP/s and the fraction of the 2.5 PFLOP/s
     dense peak use the algorithmic count.  Sampled rows are checked against the FP64 reference (every
     row for the 1,024-token case).  Returns (figures, inputs kept for the CPU baseline)."""

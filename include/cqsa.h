@@ -78,7 +78,8 @@ typedef struct {
 
 /* Merge strategies for multi-chunk plans. */
 typedef enum {
-    CQSA_MERGE_AUTO = 0,   /* the planner's choice */
+    CQSA_MERGE_AUTO = 0,   /* the planner's choice: CQSA_MERGE_FUSED for chunked plans, the merge kernel
+                              for side-by-side KV splits */
     CQSA_MERGE_KERNEL = 1, /* each KV chunk writes a partial; a separate LSE-merge kernel folds it in */
     CQSA_MERGE_FUSED = 2   /* the forward kernel folds its partial into the running triple in its epilogue */
 } cqsa_merge_mode;

@@ -133,7 +133,8 @@ def test_plan_streamed_4m_context():
 def test_plan_forced_splits():
     s = shp(1, 1, 1024, 64)
     p = plan(s, s, s, True, 16 * GB, kv_chunk=256)
-    assert (p["n_kv_chunks"], p["chunk_pairs"], p["merges"], p["merge_mode"]) == (4, 4, 3, 1)
+    assert (p["n_kv_chunks"], p["chunk_pairs"], p["merges"], p["merge_mode"]) == (4, 4, 3, 2)
+    assert plan(s, s, s, True, 16 * GB, kv_chunk=256, merge=1)["merge_mode"] == 1
     s2 = shp(1, 8, 32768, 64)
     p2 = plan(s2, s2, s2, True, 16 * GB, kv_chunk=4096)
     assert (p2["n_kv_chunks"], p2["chunk_pairs"], p2["merges"]) == (8, 8, 7)

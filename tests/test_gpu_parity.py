@@ -310,7 +310,7 @@ def test_config2_monolithic_and_8way_split_agree():
     q, k, v, _ = synth.make_inputs(w)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     mono, lse_m = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True)
-    split, lse_s, info = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, out_dtype=torch.float32,
+    split, lse_s, info = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, merge=1, out_dtype=torch.float32,
                                           return_lse=True, return_info=True)
     fused, lse_f = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=4096, merge=2, out_dtype=torch.float32,
                                     return_lse=True)

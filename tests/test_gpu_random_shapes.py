@@ -45,6 +45,8 @@ def draw_cases(n: int, seed: int = 0xC05A0123) -> list:
             opt["q_chunk"] = int(rng.integers(max(1, Nq // 6), Nq + 1))
         if mode == "fused":
             opt["merge"] = 2
+        if mode == "kv_chunk":
+            opt["merge"] = 1   # the merge kernel (the planner's choice for chunks is the fused fold)
         if mode == "kv_splits":
             opt["kv_splits"] = int(rng.integers(2, 5))
         if mode == "cqs":
