@@ -157,6 +157,7 @@ struct Problem {
     bool empty = false;
     bool streamed = false;
     int p_split = 0;   // precision 1: split-P PV product
+    bool one_pass = false;   // the caller runs single-pass plans only (the no-allocation entry point)
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -661,7 +662,7 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
     const bool forced = opt.q_chunk > 0 || opt.kv_chunk > 0;
     // long key ranges on the device: KV chunks of kKvResident keys when their accumulator fits
     bool long_keys = false;
-    if (!P.streamed && !forced && opt.kv_splits == 0 && P.Nk > kLongKeys)
+    if (!P.streamed && !P.one_pass && !forced && opt.kv_splits == 0 && P.Nk > kLongKeys)
         long_keys = chunk_bytes(P, P.Nq, kKvResident, req_merge == 0 ? CQSA_MERGE_FUSED : req_merge, false, pl) <= budget;
 
     if (!P.streamed && !forced && !long_keys) {
@@ -2013,6 +2014,7 @@ cqsa_status cqsa_attention_noalloc(const cqsa_tensor* q, const cqsa_tensor* k, c
         if (info) std::memset(info, 0, sizeof *info);
         return CQSA_OK;
     }
+    P.one_pass = true;
     // a forced split: its partial triples must fit the fixed array as asked, not halved to fit
     const uint64_t rows = (uint64_t)P.B * P.Hq * P.Nq;
     if (kv_splits > 1) {

@@ -71,6 +71,23 @@ def test_noalloc_planner_split_and_single_pass():
     compare(out, None, ref, torch.bfloat16, label="noalloc planner split, bf16 out")
 
 
+def test_noalloc_long_key_range_stays_single_pass():
+    """Past 512K keys the planner cuts a resident key range into chunks with an accumulator; the
+    no-allocation entry point keeps its single-pass plan (here the planner's side-by-side split) and
+    matches cqsa_attention_ex with that split exactly and the oracle within tolerance."""
+    B, Hq, Hkv, Nq, Nk, D = 1, 2, 1, 256, 600000, 64
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, torch.float16, seed=92)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out = torch.empty((B, Hq, Nq, D), dtype=torch.float16, device=DEV)
+    info = m.attention_noalloc(qd, kd, vd, out, None, is_causal=True)
+    assert info["n_kv_chunks"] == 1 and info["kv_splits"] > 1
+    ref_out = m.attention(qd, kd, vd, is_causal=True, kv_splits=info["kv_splits"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
+    ref = reference(q, k, v, causal=True, scale=1.0 / math.sqrt(D))
+    say("noalloc long keys", info["kv_splits"], compare(out, None, ref, torch.float16, label="noalloc long keys"))
+
+
 def test_noalloc_refuses_what_it_cannot_hold():
     B, Hq, Hkv, Nq, Nk, D = 1, 32, 8, 2048, 65536, 128
     q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, torch.bfloat16, seed=91)
