@@ -119,7 +119,7 @@ def test_cqs_schedule_parity(case):
     compare(out_h, lse_h, ref, dtype, label=f"cqs host {case}")
 
 
-def test_cqs_config2_shape_matches_grid_and_oracle():
+def test_cqs_causal_n32768_matches_grid_and_oracle():
     """The 32K causal bench shape under the quorum-set schedule (c = 7 and c = 31): sampled rows
     against the oracle, and the whole output against the monolithic pass."""
     w = synth.workload(1)
@@ -202,7 +202,7 @@ def test_split_p_bench_shape_sampled():
     assert float(np.abs(got - ref["o"]).max()) <= SPLIT_TOL[torch.float16]
 
 
-def test_config1_four_kv_chunks_merged():
+def test_causal_n1024_four_kv_chunks_merged():
     """1024 causal rows, D=64, fp16, KV chunk 256: each Q block folds its visible chunks by LSE."""
     w = synth.workload(0)
     say("workload", w.name)
@@ -214,11 +214,11 @@ def test_config1_four_kv_chunks_merged():
                                           out_dtype=torch.float32, return_lse=True, return_info=True)
         torch.cuda.synchronize()
         assert info["n_kv_chunks"] == 4 and info["chunk_pairs"] == 4 and info["merges"] == 3
-        compare(out, lse, ref, torch.float16, label=f"config1 merge={merge}")
+        compare(out, lse, ref, torch.float16, label=f"causal 1024 merge={merge}")
     # the default output dtype is the input's
     out16 = cqsa().attention(qd, kd, vd, is_causal=True, kv_chunk=256)
     assert out16.dtype == torch.float16
-    compare(out16, None, ref, torch.float16, label="config1 fp16 out")
+    compare(out16, None, ref, torch.float16, label="causal 1024 fp16 out")
 
 
 def test_fwd_partial_matches_oracle_partial():
@@ -302,7 +302,7 @@ def test_finalize():
     assert np.all(got_o[~ok] == 0) and np.all(np.isneginf(got_lse[~ok]))
 
 
-def test_config2_monolithic_and_8way_split_agree():
+def test_causal_n32768_monolithic_and_8way_split_agree():
     """B=1, H=8, N=32768, D=64 causal fp16: one pass, and a forced split into 8 KV chunks (merge kernel
     and fused merges), each checked in full (all 262,144 rows) against the FP64 reference."""
     w = synth.workload(1)
@@ -317,11 +317,11 @@ def test_config2_monolithic_and_8way_split_agree():
     torch.cuda.synchronize()
     assert info["n_kv_chunks"] == 8 and info["chunk_pairs"] == 8
     ref = reference(q, k, v, causal=True, scale=w.scale)
-    r1 = compare(mono, lse_m, ref, torch.float16, label="config2 mono")
-    r2 = compare(split, lse_s, ref, torch.float16, label="config2 split")
-    r3 = compare(fused, lse_f, ref, torch.float16, label="config2 fused")
+    r1 = compare(mono, lse_m, ref, torch.float16, label="causal 32K mono")
+    r2 = compare(split, lse_s, ref, torch.float16, label="causal 32K split")
+    r3 = compare(fused, lse_f, ref, torch.float16, label="causal 32K fused")
     agree = (mono - split).abs().max().item()
-    say("config2", r1, r2, r3, "max|mono-split|", agree)
+    say("causal 32K", r1, r2, r3, "max|mono-split|", agree)
     assert agree <= 1e-3
     assert (fused - split).abs().max().item() <= 1e-3
 
@@ -329,13 +329,13 @@ def test_config2_monolithic_and_8way_split_agree():
 # Rows checked at the sizes the reference cannot finish in full within the test's time: every (b, h),
 # with the first and last EDGE rows, rows +-1 around Q-chunk, KV-chunk and 128-row tile edges (at most
 # CAP rows of them), and RANDOM seeded rows.  (edge, random, cap) per workload; the row count per
-# (b, h) is logged.  The edge and random counts are the survey's; the boundary rows are capped where
+# (b, h) is logged.  64 edge rows and 512 random rows in every (b, h); the boundary rows are capped where
 # the oracle's cost per row is largest (up to 4M visible keys a row).
-C14_SAMPLED = {"prompt_131072": (64, 512, 256), "streamed_4m": (64, 512, 64), "stress_full": (64, 512, 64)}
+LARGE_SAMPLED = {"prompt_131072": (64, 512, 256), "streamed_4m": (64, 512, 64), "stress_full": (64, 512, 64)}
 
 
 @pytest.mark.parametrize("nk", [8192, 32768, 131072])
-def test_config3_prompt_gqa(nk):
+def test_prompt_q2048_gqa(nk):
     """2048 queries at the end of the context, 32 query heads over 8 KV heads, D=128, bf16: every row
     at 8K and 32K keys; at 131K, sampled rows in every head."""
     w = synth.workload(2, nk=nk)
@@ -344,9 +344,9 @@ def test_config3_prompt_gqa(nk):
     if nk <= 32768:
         rows = None
     else:
-        edge, n_random, cap = C14_SAMPLED["prompt_131072"]
+        edge, n_random, cap = LARGE_SAMPLED["prompt_131072"]
         rows = sample_rows(1, 32, 2048, seed=3, n_random=n_random, edge=edge, boundaries=range(0, 2048, 128), cap=cap)
-        say("config3", nk, "rows per head", len(rows) // 32)
+        say("prompt", nk, "rows per head", len(rows) // 32)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True,
                                       return_info=True)
@@ -355,8 +355,8 @@ def test_config3_prompt_gqa(nk):
                                   return_lse=True)
     torch.cuda.synchronize()
     ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
-    say("config3", nk, info["kv_splits"], compare(out, lse, ref, torch.bfloat16, rows=rows, label=f"config3 {nk}"))
-    compare(out2, lse2, ref, torch.bfloat16, rows=rows, label=f"config3 {nk} splits=4")
+    say("prompt", nk, info["kv_splits"], compare(out, lse, ref, torch.bfloat16, rows=rows, label=f"prompt {nk}"))
+    compare(out2, lse2, ref, torch.bfloat16, rows=rows, label=f"prompt {nk} splits=4")
 
 
 def test_resident_long_key_range_runs_in_key_chunks():
@@ -384,7 +384,7 @@ def test_resident_long_key_range_runs_in_key_chunks():
     assert (lse - lse1).abs().max().item() <= 1e-4
 
 
-def test_config5_softmax_stress_reduced():
+def test_softmax_stress_reduced():
     """Large logits (N(0, 9^2)) with +20 spikes on 5% of keys, uniform v, non-causal, bf16, KV chunk
     16384; the batch, heads and length are cut so the reference runs in seconds."""
     w = synth.workload(4)
@@ -397,7 +397,7 @@ def test_config5_softmax_stress_reduced():
                                       return_lse=True, return_info=True)
     torch.cuda.synchronize()
     assert info["n_kv_chunks"] == 4
-    say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 reduced"))
+    say("stress", compare(out, lse, ref, torch.bfloat16, rows=rows, label="stress reduced"))
 
 
 SHIFT_CASES = [
@@ -537,7 +537,7 @@ def test_errors():
     assert e.shape == (1, 2, 0, 64)
 
 
-def test_config4_streamed_4m_full_size():
+def test_streamed_causal_n4194304_full_size():
     """4,194,304-token causal attention, H=8, D=64, fp16, q/k/v and out in pinned host memory, device budget
     16e9 bytes: the planner must cut Q in two and stream KV; sampled rows in every head against the FP64
     reference."""
@@ -547,20 +547,20 @@ def test_config4_streamed_4m_full_size():
     out = torch.empty((w.B, w.Hq, w.Nq, w.D), dtype=torch.float16, pin_memory=True)
     o, lse, info = cqsa().attention(q, k, v, is_causal=True, mem_budget=w.mem_budget, out=out, return_lse=True,
                                     return_info=True)
-    say("config4", {x: info[x] for x in ("q_chunk", "kv_chunk", "chunk_pairs", "workspace_bytes", "h2d_bytes",
+    say("streamed 4M", {x: info[x] for x in ("q_chunk", "kv_chunk", "chunk_pairs", "workspace_bytes", "h2d_bytes",
                                          "h2d_ms")})
     assert info["streamed"] == 1 and info["n_q_chunks"] == 2
     assert info["workspace_bytes"] <= 16e9 * 0.85
     assert info["h2d_bytes"] == 16 * 2**30
-    edge, n_random, cap = C14_SAMPLED["streamed_4m"]
+    edge, n_random, cap = LARGE_SAMPLED["streamed_4m"]
     rows = sample_rows(1, 8, w.Nq, seed=6, n_random=n_random, edge=edge, boundaries=[info["q_chunk"]] +
                        list(range(0, w.Nq, info["kv_chunk"])), tiles=range(0, w.Nq, 128), cap=cap)
-    say("config4", "rows per head", len(rows) // 8)
+    say("streamed 4M", "rows per head", len(rows) // 8)
     ref = reference(q, k, v, causal=True, scale=w.scale, rows=rows)
-    say("config4", compare(o, lse, ref, torch.float16, rows=rows, label="config4 streamed"))
+    say("streamed 4M", compare(o, lse, ref, torch.float16, rows=rows, label="streamed 4M"))
 
 
-def test_config5_softmax_stress_full_size():
+def test_softmax_stress_full_size():
     """B=2, H=16, N=262,144, D=128, bf16, non-causal, logits N(0, 9^2) with +20 spikes on 5% of keys,
     KV chunk 16,384 (16 LSE merges); sampled rows in every (b, h) against the FP64 reference."""
     w = synth.workload(4)
@@ -572,12 +572,12 @@ def test_config5_softmax_stress_full_size():
                                       return_lse=True, return_info=True)
     torch.cuda.synchronize()
     assert info["n_kv_chunks"] == 16 and info["merges"] == 15
-    edge, n_random, cap = C14_SAMPLED["stress_full"]
+    edge, n_random, cap = LARGE_SAMPLED["stress_full"]
     rows = sample_rows(2, 16, w.Nq, seed=7, n_random=n_random, edge=edge,
                        boundaries=range(0, w.Nq, 16384), tiles=range(0, w.Nq, 128), cap=cap)
-    say("config5", "rows per (b, h)", len(rows) // 32)
+    say("stress full", "rows per (b, h)", len(rows) // 32)
     ref = reference(q, k, v, causal=False, scale=w.scale, rows=rows)
-    say("config5", compare(out, lse, ref, torch.bfloat16, rows=rows, label="config5 full"))
+    say("stress full", compare(out, lse, ref, torch.bfloat16, rows=rows, label="stress full"))
 
 
 def test_launch_failure_mid_stream_is_reported_and_the_next_call_is_exact(test_controls):
