@@ -62,10 +62,11 @@ constexpr double kSafety = 0.85;           // fraction of the budget the planner
 constexpr int64_t kRowGrain = 256;         // chunk sizes are multiples of this (then clipped)
 constexpr int64_t kKvCap = 262144;         // largest automatic KV chunk (keys)
 constexpr int64_t kKvMinStream = 4096;     // smallest automatic KV chunk worth streaming
-// Device-resident inputs whose key range exceeds kLongKeys run one launch per KV chunk of kKvResident
-// keys (folded by the kernel epilogue), not one pass: a workgroup sweeping millions of keys loses the
-// cache reuse that every workgroup sweeping the same 128K-key chunk keeps (4M causal keys, H=8, D=64:
-// 20.4 s one pass, 17.6 s in 128K chunks)
+// Device-resident inputs whose key range exceeds kLongKeys, with query tiles for several rounds of
+// workgroups, run one launch per KV chunk of kKvResident keys (folded by the kernel epilogue), not one
+// pass: workgroups that start their sweeps of millions of keys at different times lose the cache reuse
+// that every workgroup sweeping the same 128K-key chunk keeps (4M causal keys, H=8, D=64: 20.4 s one
+// pass, 17.3 s in 128K chunks)
 constexpr int64_t kLongKeys = 524288;
 constexpr int64_t kKvResident = 131072;
 
@@ -660,21 +661,26 @@ cqsa_status make_plan(const Problem& P, uint64_t budget, const cqsa_options& opt
     if (opt.q_chunk < 0 || opt.kv_chunk < 0 || opt.kv_splits < 0)
         return fail(CQSA_ERR_INVALID, "negative chunk option");
     const bool forced = opt.q_chunk > 0 || opt.kv_chunk > 0;
-    // long key ranges on the device: KV chunks of kKvResident keys when their accumulator fits
+    // workgroups of one pass, and how many the CUs hold at once
+    const int64_t wgs_one_pass = P.B * P.Hq * ceil_div(P.Nq, pl->bm);
+    const int64_t wgs_target = (int64_t)fwd_wgs_per_cu((int)P.D, P.p_split) * std::max(num_cus, 1);
+    // long key ranges on the device: KV chunks of kKvResident keys when their accumulator fits and the
+    // query tiles make several rounds of workgroups, whose sweeps drift apart (a 2,048-query prompt over
+    // 1M keys, one round, measured 1% faster in one pass; with few tiles side-by-side splits fill the CUs)
     bool long_keys = false;
-    if (!P.streamed && !P.one_pass && !forced && opt.kv_splits == 0 && P.Nk > kLongKeys)
+    if (!P.streamed && !P.one_pass && !forced && opt.kv_splits == 0 && P.Nk > kLongKeys &&
+        wgs_one_pass >= 4 * wgs_target)
         long_keys = chunk_bytes(P, P.Nq, kKvResident, req_merge == 0 ? CQSA_MERGE_FUSED : req_merge, false, pl) <= budget;
 
     if (!P.streamed && !forced && !long_keys) {
         // one pass over all keys; optional side-by-side KV splits to fill the GPU: up to as many
         // workgroups as the CUs hold at once (more only add merges: the 2,048-query prompt at 32K keys
         // and D=128, 256 workgroups of one per CU, measured 2.5% slower in two splits)
-        const int64_t n_qt = ceil_div(P.Nq, pl->bm);
-        const int64_t wgs = P.B * P.Hq * n_qt;
+        const int64_t wgs = wgs_one_pass;
         int splits = opt.kv_splits;
         if (splits == 0) {
             splits = 1;
-            const int64_t target = (int64_t)fwd_wgs_per_cu((int)P.D, P.p_split) * std::max(num_cus, 1);
+            const int64_t target = wgs_target;
             const int64_t min_keys = P.causal ? (P.Nk - P.Nq + 1) : P.Nk;  // fewest keys a row sees
             if (wgs < target && min_keys >= 16384) {
                 splits = (int)std::min<int64_t>({ceil_div(target, wgs), min_keys / 8192, 16});

@@ -158,8 +158,9 @@ def test_plan_split_kv_when_few_query_tiles():
 
 def test_plan_resident_long_key_range():
     """Device-resident inputs over more than 512K keys run one launch per 128K-key chunk, folded by the
-    kernel epilogue into one fp32 accumulator, when that accumulator fits the budget; otherwise, with
-    forced kv_splits, or at 512K keys and below, one pass with no workspace."""
+    kernel epilogue into one fp32 accumulator, when that accumulator fits the budget and the query tiles
+    make several rounds of workgroups; otherwise, with forced kv_splits, or at 512K keys and below, one
+    pass."""
     s = shp(1, 8, 4194304, 64)
     p = plan(s, s, s, True, 16 * GB)
     assert (p["q_chunk"], p["kv_chunk"], p["n_kv_chunks"], p["merge_mode"]) == (4194304, 131072, 32, 2)
@@ -170,6 +171,12 @@ def test_plan_resident_long_key_range():
         assert (p1["n_kv_chunks"], p1["workspace_bytes"], p1["kernel_launches"]) == (1, 0, 1)
     s2 = shp(1, 8, 524288, 64)
     assert plan(s2, s2, s2, True, 16 * GB)["n_kv_chunks"] == 1
+    # few query tiles (8 heads, one query): side-by-side splits fill the GPU instead
+    p3 = plan(shp(1, 8, 1, 64), shp(1, 8, 1 << 20, 64), shp(1, 8, 1 << 20, 64), False, 16 * GB)
+    assert p3["n_kv_chunks"] == 1 and p3["kv_splits"] > 1
+    # one round of workgroups (a 2,048-query prompt over 1M keys at D=128): one pass
+    p4 = plan(shp(1, 32, 2048, 128), shp(1, 8, 1 << 20, 128), shp(1, 8, 1 << 20, 128), True, 16 * GB)
+    assert p4["n_kv_chunks"] == 1 and p4["kv_splits"] == 1
 
 
 def test_plan_errors():
