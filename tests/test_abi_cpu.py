@@ -179,6 +179,20 @@ def test_plan_resident_long_key_range():
     assert p4["n_kv_chunks"] == 1 and p4["kv_splits"] == 1
 
 
+def test_plan_split_target_is_the_workgroups_the_cus_hold():
+    """Side-by-side KV splits fill the CUs with as many workgroups as they hold at once: one 8-wave
+    workgroup per CU at D=128, two at D=64 (256 CUs here)."""
+    bf, f16 = torch.bfloat16, torch.float16
+    prompt = lambda nk, D, dt: (shp(1, 32, 2048, D, dt), shp(1, 8, nk, D, dt))
+    for nk in (32768, 131072):        # 256 workgroups at D=128 already fill the CUs
+        q, kv = prompt(nk, 128, bf)
+        assert plan(q, kv, kv, True, 16 * GB)["kv_splits"] == 1
+    q, kv = prompt(131072, 64, f16)   # 256 workgroups at D=64: two per CU wanted
+    assert plan(q, kv, kv, True, 16 * GB)["kv_splits"] == 2
+    q, kv = shp(1, 8, 2048, 128, bf), shp(1, 8, 65536, 128, bf)   # 64 workgroups at D=128
+    assert plan(q, kv, kv, True, 16 * GB)["kv_splits"] == 4
+
+
 def test_plan_errors():
     import exact_long_context_cqsa_amd as m
     s = shp(1, 8, 4194304, 64)

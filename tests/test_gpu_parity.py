@@ -359,27 +359,35 @@ def test_prompt_q2048_gqa(nk):
     compare(out2, lse2, ref, torch.bfloat16, rows=rows, label=f"prompt {nk} splits=4")
 
 
-def test_resident_long_key_range_runs_in_key_chunks():
-    """Device-resident causal attention over more than 512K keys: by default the plan runs one launch
-    per 128K-key chunk, folded into one fp32 accumulator by the kernel epilogue.  Sampled rows in every
+# (Hq, Hkv, N, D, dtype, causal, key chunks): past 512K keys, with several rounds of workgroups
+LONG_KEY_CASES = [
+    (2, 1, 532000, 64, torch.float16, True, 5),      # GQA 2/1, a ragged last chunk
+    (4, 2, 540000, 128, torch.bfloat16, False, 5),   # D=128 bf16, non-causal
+]
+
+
+@pytest.mark.parametrize("case", LONG_KEY_CASES, ids=lambda c: f"n{c[2]}d{c[3]}{'c' if c[5] else 'n'}")
+def test_resident_long_key_range_runs_in_key_chunks(case):
+    """Device-resident attention over more than 512K keys: by default the plan runs one launch per
+    128K-key chunk, folded into one fp32 accumulator by the kernel epilogue.  Sampled rows in every
     head (chunk edges included) match the oracle, and the forced single pass (kv_splits=1) agrees up to
-    the fp32 summation order.  GQA 2/1, 532,000 tokens (a ragged last chunk), D=64, fp16."""
-    N, D = 532000, 64
-    say("resident long keys", N)
-    q, k, v = gen(1, 2, 1, N, N, D, torch.float16, seed=41)
+    the fp32 summation order."""
+    Hq, Hkv, N, D, dtype, causal, nchunks = case
+    say("resident long keys", case)
+    q, k, v = gen(1, Hq, Hkv, N, N, D, dtype, seed=41 + D)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=True, out_dtype=torch.float32, return_lse=True,
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
                                       return_info=True)
-    one, lse1, info1 = cqsa().attention(qd, kd, vd, is_causal=True, kv_splits=1, out_dtype=torch.float32,
+    one, lse1, info1 = cqsa().attention(qd, kd, vd, is_causal=causal, kv_splits=1, out_dtype=torch.float32,
                                         return_lse=True, return_info=True)
     torch.cuda.synchronize()
-    assert (info["kv_chunk"], info["n_kv_chunks"], info["n_q_chunks"], info["merge_mode"]) == (131072, 5, 1, 2)
+    assert (info["kv_chunk"], info["n_kv_chunks"], info["n_q_chunks"], info["merge_mode"]) == (131072, nchunks, 1, 2)
     assert info1["n_kv_chunks"] == 1 and info1["workspace_bytes"] == 0
-    rows = sample_rows(1, 2, N, seed=5, n_random=256, edge=64, boundaries=range(131072, N, 131072), cap=64)
-    ref = reference(q, k, v, causal=True, scale=1.0 / math.sqrt(D), rows=rows)
-    say("resident long keys", len(rows) // 2, "rows per head",
-        compare(out, lse, ref, torch.float16, rows=rows, label="key chunks"))
-    compare(one, lse1, ref, torch.float16, rows=rows, label="one pass")
+    rows = sample_rows(1, Hq, N, seed=5, n_random=256, edge=64, boundaries=range(131072, N, 131072), cap=64)
+    ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D), rows=rows)
+    say("resident long keys", len(rows) // Hq, "rows per head",
+        compare(out, lse, ref, dtype, rows=rows, label="key chunks"))
+    compare(one, lse1, ref, dtype, rows=rows, label="one pass")
     assert (out - one).abs().max().item() <= 1e-4
     assert (lse - lse1).abs().max().item() <= 1e-4
 
