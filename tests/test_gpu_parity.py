@@ -176,7 +176,7 @@ def test_split_p_precision(case):
     base = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32)
     torch.cuda.synchronize()
     e_base = err(base)
-    for kw in ({}, {"kv_chunk": 200}):
+    for kw in ({}, {"kv_chunk": 200}, {"kv_chunk": 200, "merge": 1}):   # the fused fold, then the merge kernel
         out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
                                     precision=1, **kw)
         torch.cuda.synchronize()
