@@ -15,6 +15,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import glob
 import hashlib
 import os
 import re
@@ -186,6 +187,93 @@ def summarise_mfma(args) -> str:
     return "\n".join(lines) + "\n"
 
 
+WAVE_STATE_PASS1 = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                    "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+WAVE_STATE_PASS2 = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+                    "SQ_INSTS_VALU_TRANS_F32", "SQ_ACTIVE_INST_SCA", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
+
+
+def _pass_means(directory: str, kernel: str, grid, select) -> tuple[dict, list]:
+    """Per-dispatch means of every counter of one rocprofv3 --kernel-trace --pmc run (its directory holds
+    the run's kernel_trace.csv and counter_collection.csv), over the selected dispatches of the kernel;
+    and those dispatches' durations."""
+    trace = sorted(glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True))
+    ctr = sorted(glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True))
+    if not trace or not ctr:
+        raise SystemExit(f"{directory}: kernel_trace.csv or counter_collection.csv missing")
+    durs = {int(r["Dispatch_Id"]): int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            for r in _pick(_rows(trace[0]), kernel, grid, select)}
+    per = {}
+    for r in _pick(_rows(ctr[0]), kernel, grid, None):
+        d = int(r["Dispatch_Id"])
+        if d in durs:
+            c = per.setdefault(d, {})
+            c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{directory}: no counter rows for the selected dispatches of {kernel!r}")
+    names = set().union(*per.values())
+    return {n: statistics.mean(v.get(n, 0.0) for v in per.values()) for n in names}, [durs[d] for d in per]
+
+
+def summarise_wave_state(args) -> str:
+    """Where a kernel's waves spend their time, from two rocprofv3 --kernel-trace --pmc runs of the same
+    command (WAVE_STATE_PASS1, then WAVE_STATE_PASS2; each counter summed over the chip, per dispatch):
+    the shares of the waves' resident cycles spent issuing an instruction (SQ_ACTIVE_INST_ANY), ready but
+    waiting for an issue slot (SQ_WAIT_INST_ANY) and waiting on a dependency or barrier (SQ_WAIT_ANY);
+    VALUBusy as rocprofv3 defines it for gfx950 (SQ_ACTIVE_INST_VALU per CU over GRBM_GUI_ACTIVE per XCD);
+    the matrix cores' busy share of SIMD cycles; and the instructions each wave issued."""
+    grid, select = getattr(args, "grid", None), getattr(args, "select", None)
+    dirs = [d for d in args.wave_state.split(",") if d]
+    if len(dirs) != 2:
+        raise SystemExit("--wave-state takes the two run directories, comma-separated")
+    a, durs = _pass_means(dirs[0], args.kernel, grid, select)
+    b, _ = _pass_means(dirs[1], args.kernel, grid, select)
+    cus = args.cus
+    cyc = a["GRBM_GUI_ACTIVE"] / args.xcds
+    wave = a["SQ_WAVE_CYCLES"]
+    waves = b["SQ_WAVES"]
+    mfma = b["SQ_INSTS_MFMA"]
+    trace = sorted(glob.glob(os.path.join(dirs[0], "**", "*kernel_trace.csv"), recursive=True))[0]
+    name = next(r["Kernel_Name"] for r in _pick(_rows(trace), args.kernel, grid, select))
+    avg_ns = statistics.mean(durs)
+    lines = [
+        f"# {args.name}",
+        "",
+        f"kernel: `{name}`",
+        f"kernel_source_sha256: {kernel_source_sha256()}",
+        "",
+        "## Commands",
+        "",
+        "```",
+        args.command.strip(),
+        "```",
+        "",
+        "## Wave states (rocprofv3 --kernel-trace --pmc, two passes)",
+        "",
+        f"calls: {len(durs)}",
+        f"avg_ns: {avg_ns:.0f}",
+        f"gui_active_cycles_per_xcd: {cyc:.0f}",
+        f"clock_ghz: {cyc / avg_ns:.3f}",
+        f"wave_share_issuing: {a['SQ_ACTIVE_INST_ANY'] / wave:.3f}",
+        f"wave_share_waiting_for_issue: {a['SQ_WAIT_INST_ANY'] / wave:.3f}",
+        f"wave_share_waiting_on_dependency: {a['SQ_WAIT_ANY'] / wave:.3f}",
+        f"wave_share_lds_active: {a['SQ_ACTIVE_INST_LDS'] / wave:.3f}",
+        f"valu_busy_pct: {100.0 * a['SQ_ACTIVE_INST_VALU'] / cus / cyc:.1f}",
+        f"mfma_busy_pct: {100.0 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cus) / cyc:.1f}",
+        f"waves_per_launch: {waves:.0f}",
+        f"valu_insts_per_wave: {b['SQ_INSTS_VALU'] / waves:.1f}  (the MFMA instructions included)",
+        f"mfma_insts_per_wave: {mfma / waves:.1f}",
+        f"trans_f32_insts_per_wave: {b['SQ_INSTS_VALU_TRANS_F32'] / waves:.1f}",
+        f"salu_insts_per_wave: {b['SQ_INSTS_SALU'] / waves:.1f}",
+        f"lds_insts_per_wave: {b['SQ_INSTS_LDS'] / waves:.1f}",
+        f"per_mfma: valu_other {(b['SQ_INSTS_VALU'] - mfma) / mfma:.2f}, trans {b['SQ_INSTS_VALU_TRANS_F32'] / mfma:.2f}, "
+        f"salu {b['SQ_INSTS_SALU'] / mfma:.2f}, lds {b['SQ_INSTS_LDS'] / mfma:.2f}",
+    ]
+    if args.note:
+        lines += ["", "## Notes", "", args.note.strip()]
+    return "\n".join(lines) + "\n"
+
+
 def summarise_copies(args) -> str:
     """Host-to-device streaming from a rocprofv3 --memory-copy-trace run.  The trace gives each copy's
     stream and duration but not its size, so the bytes are the plan's (cqsa_plan_info.h2d_bytes, as the
@@ -253,6 +341,9 @@ def main():
     ap.add_argument("--counters", help="counter_collection.csv with the matrix-core counters: summarise those")
     ap.add_argument("--algorithmic-flop", type=float, default=0.0, help="algorithmic FLOP per launch (--counters)")
     ap.add_argument("--xcds", type=int, default=8, help="XCDs GRBM_GUI_ACTIVE is summed over (--counters)")
+    ap.add_argument("--wave-state", default=None,
+                    help="the two run directories of the wave-state counter passes, comma-separated: summarise those")
+    ap.add_argument("--cus", type=int, default=256, help="compute units of the device (--wave-state)")
     ap.add_argument("--copy-trace", help="memory_copy_trace.csv: summarise the H2D streaming instead")
     ap.add_argument("--h2d-stream", type=int, default=1)
     ap.add_argument("--h2d-bytes", type=int, default=0)
@@ -265,7 +356,11 @@ def main():
     ap.add_argument("--note", default="")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
-    if args.counters:
+    if args.wave_state:
+        if not args.kernel:
+            ap.error("--wave-state needs --kernel")
+        text = summarise_wave_state(args)
+    elif args.counters:
         if not (args.kernel and args.trace and args.algorithmic_flop > 0):
             ap.error("--counters needs --kernel, --trace and --algorithmic-flop")
         text = summarise_mfma(args)

@@ -105,3 +105,39 @@ def test_copy_summary(tmp_path):
     args.h2d_stream = 3
     with pytest.raises(SystemExit):
         profiling.summarise_copies(args)
+
+
+def test_wave_state_summary(tmp_path):
+    """Wave-state shares, VALUBusy and the matrix-core busy share from two counter passes, each read
+    from its run directory (kernel trace + counter collection), over the selected dispatches only."""
+    hdr_t = ["Dispatch_Id", "Kernel_Name", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z", "Start_Timestamp",
+             "End_Timestamp"]
+    hdr_c = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    k = "void fwd_k<64>()"
+    dirs = []
+    for i, (counters, scale) in enumerate(((profiling.WAVE_STATE_PASS1, 1.0), (profiling.WAVE_STATE_PASS2, 1.0))):
+        d = tmp_path / f"p{i}"
+        (d / "host").mkdir(parents=True)
+        _csv(d / "host" / "run_kernel_trace.csv", hdr_t, [[1, k, 256, 1, 1, 0, 1000], [2, k, 256, 1, 1, 5000, 6000],
+                                                           [3, k, 256, 1, 1, 7000, 8000]])
+        vals = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 360.0, "SQ_WAIT_INST_ANY": 350.0,
+                "SQ_ACTIVE_INST_ANY": 290.0, "SQ_ACTIVE_INST_LDS": 50.0, "SQ_BUSY_CYCLES": 10.0,
+                "SQ_ACTIVE_INST_VALU": 2 * 256 * 0.5 * 1000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 4 * 2 * 256 * 0.25 * 1000.0,
+                "GRBM_GUI_ACTIVE": 8 * 2000.0, "SQ_WAVES": 100.0, "SQ_INSTS_VALU": 1360.0, "SQ_INSTS_MFMA": 160.0,
+                "SQ_INSTS_SALU": 300.0, "SQ_INSTS_LDS": 240.0, "SQ_INSTS_VALU_TRANS_F32": 320.0,
+                "SQ_ACTIVE_INST_SCA": 5.0, "SQ_WAIT_INST_LDS": 6.0}
+        rows = []
+        for disp in (1, 2, 3):
+            f = 1e6 if disp == 1 else 1.0     # the first (warm-up) dispatch is left out by the slice
+            rows += [[disp, k, 256, c, vals[c] * f] for c in counters]
+        _csv(d / "host" / "run_counter_collection.csv", hdr_c, rows)
+        dirs.append(str(d))
+    args = argparse.Namespace(name="fwd_k_waves", kernel="fwd_k<", wave_state=",".join(dirs), cus=256, xcds=8,
+                              grid=None, select="1:", command="rocprofv3 ...", note="")
+    out = tmp_path / "w.md"
+    out.write_text(profiling.summarise_wave_state(args))
+    p = profiling.read_profile(str(out))
+    assert p["calls"] == "2" and float(p["avg_ns"]) == 1000.0 and float(p["clock_ghz"]) == 2.0
+    assert float(p["wave_share_issuing"]) == 0.29 and float(p["wave_share_waiting_on_dependency"]) == 0.36
+    assert float(p["valu_busy_pct"]) == 50.0 and float(p["mfma_busy_pct"]) == 25.0
+    assert p["valu_insts_per_wave"].startswith("13.6") and float(p["mfma_insts_per_wave"]) == 1.6
