@@ -76,7 +76,9 @@ typedef struct {
     int64_t stride[4];  /* element strides; stride[3] == 1 */
 } cqsa_tensor;
 
-/* Merge strategies for multi-chunk plans. */
+/* Merge strategies for multi-chunk plans.  The request applies to chunked plans (KV chunks run one
+ * after another); side-by-side KV splits (kv_splits > 1) run at the same time, so their partials always
+ * go through the merge kernel, whatever is requested. */
 typedef enum {
     CQSA_MERGE_AUTO = 0,   /* the planner's choice: CQSA_MERGE_FUSED for chunked plans, the merge kernel
                               for side-by-side KV splits */

@@ -152,6 +152,8 @@ def test_plan_split_kv_when_few_query_tiles():
     kv = shp(1, 1, 131072, 128, torch.bfloat16)
     p = plan(q, kv, kv, True, 16 * GB)
     assert p["kv_splits"] > 1 and p["merge_mode"] == 1
+    # side-by-side splits run at the same time: the merge kernel folds them whatever is requested
+    assert plan(q, kv, kv, True, 16 * GB, kv_splits=4, merge=2)["merge_mode"] == 1
     p1 = plan(q, kv, kv, True, 16 * GB, kv_splits=1)
     assert p1["kv_splits"] == 1 and p1["workspace_bytes"] == 0
 
