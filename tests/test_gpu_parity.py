@@ -392,6 +392,38 @@ def test_resident_long_key_range_runs_in_key_chunks(case):
     assert (lse - lse1).abs().max().item() <= 1e-4
 
 
+DECODE_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, options, side-by-side KV splits (0: the planner's, more than one)
+    (1, 32, 8, 1, 131075, 128, torch.bfloat16, True, {}, 0),     # one query per head at the end of 131K keys
+    (1, 8, 1, 16, 150001, 64, torch.float16, True, {}, 0),       # 16 queries, one KV head
+    (1, 4, 4, 7, 65537, 64, torch.bfloat16, False, {"kv_splits": 16}, 16),
+    (1, 8, 2, 3, 100000, 128, torch.float16, True, {"kv_chunk": 30000, "merge": 2}, 1),   # the fused fold
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}"
+                         f"{'-' + '-'.join(c[8]) if c[8] else ''}")
+def test_decode_shapes_over_long_keys(case):
+    """A few queries against a long key range: the planner runs side-by-side KV splits (one pass per
+    split, folded by the merge kernel) so that the CUs are filled; with a forced KV chunk, the chunks
+    are folded in the kernel epilogue.  Every row against the FP64 oracle."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, opt, splits = case
+    say("decode", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=4400 + Nq + D)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, info = cqsa().attention(qd, kd, vd, is_causal=causal, out_dtype=torch.float32, return_lse=True,
+                                      return_info=True, **opt)
+    torch.cuda.synchronize()
+    if splits == 0:
+        assert info["kv_splits"] > 1
+    else:
+        assert info["kv_splits"] == splits
+    if info["kv_splits"] > 1:
+        assert info["merge_mode"] == 1 and info["n_kv_chunks"] == 1
+    ref = reference(q, k, v, causal=causal, scale=1.0 / math.sqrt(D))
+    say("decode", compare(out, lse, ref, dtype, label=f"decode {case[:8]}"))
+
+
 def test_softmax_stress_reduced():
     """Large logits (N(0, 9^2)) with +20 spikes on 5% of keys, uniform v, non-causal, bf16, KV chunk
     16384; the batch, heads and length are cut so the reference runs in seconds."""
