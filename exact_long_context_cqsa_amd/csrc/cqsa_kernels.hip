@@ -1145,6 +1145,10 @@ fwd_pp_dma_kernel(const FwdArgs a) {
     // the softmax block by block at D=64, where the whole-tile form spills at four waves per SIMD;
     // over the whole tile at D=128
     constexpr bool PERBLOCK = D == 64;
+    // D=64 holds one DMA offset per tensor and one K and one V^T read address, and forms the others
+    // from them each tile (an add or an XOR): the shape runs at four waves per SIMD, where every VGPR
+    // freed is one the register allocator need not spill
+    constexpr bool DERIVE = D == 64;
     constexpr int NW = 8;
     constexpr int BM = NW * 32;
     constexpr int TILE = KT * D;
@@ -1270,6 +1274,16 @@ fwd_pp_dma_kernel(const FwdArgs a) {
         auto pv = [&]() __attribute__((always_inline)) {
             if (i >= 1) {
                 const uint16_t* sv = lds + (S ^ 1) * STAGE;
+                int vr[NDB];
+                if constexpr (DERIVE) {
+                    int v0r = vread[0];
+                    asm volatile("" : "+v"(v0r));   // formed here each tile, not kept in registers
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) vr[db] = v0r ^ (32 * db);
+                } else {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) vr[db] = vread[db];
+                }
                 s16x4 vt[2 * NKB][NDB][2];
 #pragma unroll
                 for (int t = 0; t < 2 * NKB; ++t)
@@ -1278,7 +1292,7 @@ fwd_pp_dma_kernel(const FwdArgs a) {
 #pragma unroll
                         for (int r = 0; r < 2; ++r)
                             vt[t][db][r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) s16x4*)(sv + vread[db] + (16 * t + 8 * r) * D));
+                                (__attribute__((address_space(3))) s16x4*)(sv + vr[db] + (16 * t + 8 * r) * D));
 #pragma unroll
                 for (int t = 0; t < 2 * NKB; ++t)
 #pragma unroll
@@ -1295,7 +1309,17 @@ fwd_pp_dma_kernel(const FwdArgs a) {
         };
         auto sc = [&]() __attribute__((always_inline)) {
             if (i < ntiles) {
-                scores<D, NKB, NDK, DT>(lds + S * STAGE, kread, qf, sacc);
+                int kr[NDK];
+                if constexpr (DERIVE) {
+                    int k0r = kread[0];
+                    asm volatile("" : "+v"(k0r));
+#pragma unroll
+                    for (int t = 0; t < NDK; ++t) kr[t] = k0r ^ (16 * t);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NDK; ++t) kr[t] = kread[t];
+                }
+                scores<D, NKB, NDK, DT>(lds + S * STAGE, kr, qf, sacc);
                 mfma_read_pipeline<NDK * NKB, 1, PD>();
             }
         };
@@ -1308,15 +1332,31 @@ fwd_pp_dma_kernel(const FwdArgs a) {
         }
         if (dma) {
             __builtin_amdgcn_sched_barrier(0);
+            int ko[BPW], vo[BPW];
+            if constexpr (DERIVE) {
+                int k0o = koff[0], v0o = voff[0];
+                asm volatile("" : "+v"(k0o), "+v"(v0o));
+#pragma unroll
+                for (int j = 0; j < BPW; ++j) {
+                    ko[j] = k0o + j * (NA * RPI) * ksb;   // the swizzles repeat every NA * RPI rows
+                    vo[j] = v0o + j * (NA * RPI) * vsb;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < BPW; ++j) {
+                    ko[j] = koff[j];
+                    vo[j] = voff[j];
+                }
+            }
             if (i + 1 < ntiles) {
                 const int rem = nkeys - (i + 1) * KT;
                 dma_rows_s<NA, BPW, D>(lds + (S ^ 1) * STAGE, k0 + (int64_t)(i + 1) * KT * k_sn, ksb,
-                                       rem < KT ? rem : KT, koff, wave_a);
+                                       rem < KT ? rem : KT, ko, wave_a);
             }
             if (i < ntiles) {
                 const int rem = nkeys - i * KT;
                 dma_rows_s<NA, BPW, D>(lds + S * STAGE + TILE, v0 + (int64_t)i * KT * v_sn, vsb,
-                                       rem < KT ? rem : KT, voff, wave_a);
+                                       rem < KT ? rem : KT, vo, wave_a);
             }
         }
     };
