@@ -424,6 +424,33 @@ def test_decode_shapes_over_long_keys(case):
     say("decode", compare(out, lse, ref, dtype, label=f"decode {case[:8]}"))
 
 
+SCALE_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, scale
+    (1, 2, 2, 1000, 1000, 64, torch.float16, True, 8.0),      # logits with sd 64: one key per row dominates
+    (1, 4, 2, 700, 1300, 128, torch.bfloat16, True, 4.0),     # sd 45, bottom-right causal, GQA
+    (1, 2, 2, 900, 900, 64, torch.bfloat16, False, 1e-4),     # nearly uniform weights
+    (2, 2, 1, 333, 2048, 128, torch.float16, False, 1e-3),
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}-s{c[8]:g}")
+def test_extreme_softmax_scales(case):
+    """Softmax scales far outside the default: at 4 and 8 the scaled logits have standard deviations of
+    45-64, so the running shift moves by large steps and all but a few keys underflow; at 1e-3 and
+    1e-4 the weights are almost uniform and the output is close to the mean of the visible values.
+    Single pass and forced KV chunks (both merges), every row against the FP64 oracle."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, scale = case
+    say("scale", case)
+    q, k, v = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=4500 + D + Nq)
+    ref = reference(q, k, v, causal=causal, scale=scale)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    for kw in ({}, {"kv_chunk": 300, "merge": 1}, {"kv_chunk": 300, "merge": 2}):
+        out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, scale=scale, out_dtype=torch.float32,
+                                    return_lse=True, **kw)
+        torch.cuda.synchronize()
+        say("scale", compare(out, lse, ref, dtype, label=f"scale {case} {kw}"))
+
+
 def test_softmax_stress_reduced():
     """Large logits (N(0, 9^2)) with +20 spikes on 5% of keys, uniform v, non-causal, bf16, KV chunk
     16384; the batch, heads and length are cut so the reference runs in seconds."""
