@@ -75,6 +75,34 @@ def test_backward_parity(case):
     assert all(torch.isfinite(g).all() for g in (dq, dk, dv))
 
 
+SCALE_CASES = [
+    # B, Hq, Hkv, Nq, Nk, D, dtype, causal, scale
+    (1, 2, 2, 600, 600, 64, torch.float16, True, 4.0),       # logits with sd 32: near one-key rows
+    (1, 4, 2, 300, 900, 128, torch.bfloat16, True, 2.0),     # GQA, bottom-right causal
+    (1, 2, 2, 500, 700, 64, torch.bfloat16, False, 1e-3),    # nearly uniform weights
+]
+
+
+@pytest.mark.parametrize("case", SCALE_CASES, ids=lambda c: f"q{c[3]}k{c[4]}d{c[5]}{'c' if c[7] else 'n'}-s{c[8]:g}")
+def test_backward_extreme_scales(case):
+    """The backward at softmax scales far from 1/sqrt(D): sharp rows (dS concentrated on a few keys per
+    row) and nearly uniform ones, against the FP64 oracle at the same bound."""
+    B, Hq, Hkv, Nq, Nk, D, dtype, causal, scale = case
+    say("backward scale", case)
+    q, k, v, do = gen(B, Hq, Hkv, Nq, Nk, D, dtype, seed=5300 + Nq + D)
+    rq, rk, rv = oracle.backward(q, k, v, do, causal=causal, scale=scale)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    out, lse = cqsa().attention(qd, kd, vd, is_causal=causal, scale=scale, return_lse=True)
+    dq, dk, dv = cqsa().attention_backward(qd, kd, vd, out, dod, lse, is_causal=causal, scale=scale,
+                                           grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    errs = {n: rel_err(g, r) for n, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv))}
+    say("errors", errs)
+    for n, e in errs.items():
+        assert e <= 8 * U[dtype], (n, e)
+    assert all(torch.isfinite(g).all() for g in (dq, dk, dv))
+
+
 def test_backward_deterministic_and_grad_dtypes():
     B, Hq, Hkv, N, D = 1, 4, 2, 777, 64
     q, k, v, do = gen(B, Hq, Hkv, N, N, D, torch.float16, seed=77)
